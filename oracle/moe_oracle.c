@@ -1,0 +1,438 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle for one MoE layer's expert computation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or load
+ * this file: only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark use it.  It shares no source with the HIP library.
+ *
+ * Every floating-point step runs in IEEE double (the pages fix no precision);
+ * inputs given in fp32 or bf16 are upcast exactly by the caller.  Loops are the
+ * plain definitions: a per-token loop over the token's selected experts, with no
+ * blocking, fusion or reordering.  OpenMP only splits independent tokens (or,
+ * for dW, independent experts); each output is produced by exactly one thread in
+ * a fixed order, so results do not depend on the thread count.
+ *
+ * What is computed, and where the pages describe it:
+ *  - routing of each token to k of E experts, and token dispatch into per-expert
+ *    groups of rows: npu-train issue #14 "[MoE] Hot experts on RNGD during
+ *    training (host dispatch, device expert graphs)", sections Evidence (k = 1..8
+ *    experts per token) and Proposal (routing and dispatch, rows grouped per
+ *    expert, results scattered back);
+ *  - expert forward, backward dx (LoRA, experts frozen) and dW (full
+ *    fine-tuning): issue #14, sections Proposal and Scope;
+ *  - saved forward activations reused by backward: npu-train pull request #44,
+ *    section Changes (HostMLP keep_graph);
+ *  - retention quotas, per-pair selection within quotas, physical compaction and
+ *    a backward restricted to the retained token-expert pairs: LRMoE
+ *    (arXiv:2610.37720), abstract.
+ * The pages print no formula.  The readings taken here (softmax over the k
+ * selected logits, SwiGLU experts without biases, ties to the lower index,
+ * retained pairs summed without rescaling) are listed with the design notes.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* ------------------------------------------------------------------------- */
+/* Router logits  l[t,e] = sum_h x[t,h] * Wr[h,e]  (used to build the inputs of
+ * the routing step for the tiny fp32 layer; the router itself lies before the
+ * expert path).                                                              */
+void oracle_router_logits(int T, int H, int E, const double* x, const double* Wr, double* logits) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int h = 0; h < H; ++h) s += x[(size_t)t * H + h] * Wr[(size_t)h * E + e];
+      logits[(size_t)t * E + e] = s;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Top-k routing (issue #14, Evidence/Proposal).  For each token the experts are
+ * ordered by (logit descending, expert index ascending) -- a full stable sort,
+ * written as an insertion sort -- and the first k are kept.  Weights are the
+ * softmax over the k selected logits:
+ *     w[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ * which equals a softmax over all E renormalised to the selected k.           */
+void oracle_route_topk(int T, int E, int k, const double* logits, int32_t* idx, double* w) {
+#pragma omp parallel
+  {
+    int* order = (int*)malloc(sizeof(int) * (size_t)E);
+#pragma omp for schedule(static)
+    for (int t = 0; t < T; ++t) {
+      const double* l = logits + (size_t)t * E;
+      for (int e = 0; e < E; ++e) {
+        /* insert e after every earlier expert whose logit is >= l[e] */
+        int pos = e;
+        while (pos > 0 && l[order[pos - 1]] < l[e]) {
+          order[pos] = order[pos - 1];
+          --pos;
+        }
+        order[pos] = e;
+      }
+      double denom = 0.0;
+      for (int j = 0; j < k; ++j) denom += exp(l[order[j]] - l[order[0]]);
+      for (int j = 0; j < k; ++j) {
+        idx[(size_t)t * k + j] = order[j];
+        w[(size_t)t * k + j] = exp(l[order[j]] - l[order[0]]) / denom;
+      }
+    }
+    free(order);
+  }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Dispatch (issue #14, Proposal: rows grouped per expert).  Pair id p = t*k+j.
+ * For each expert in ascending order, append every pair routed to it in
+ * ascending p.  perm[s] is the pair at sorted position s; inv_perm inverts it.
+ * Returns 0, or -1 if an index is out of range.                              */
+int oracle_dispatch(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                    int32_t* perm, int32_t* inv_perm) {
+  const int64_t N = (int64_t)T * k;
+  for (int64_t p = 0; p < N; ++p)
+    if (idx[p] < 0 || idx[p] >= E) return -1;
+  int64_t s = 0;
+  for (int e = 0; e < E; ++e) {
+    offsets[e] = (int32_t)s;
+    for (int64_t p = 0; p < N; ++p)
+      if (idx[p] == e) perm[s++] = (int32_t)p;
+    counts[e] = (int32_t)(s - offsets[e]);
+  }
+  offsets[E] = (int32_t)s;
+  for (int64_t q = 0; q < N; ++q) inv_perm[perm[q]] = (int32_t)q;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Retention quota (LRMoE abstract: quotas planned during forward).  The
+ * per-expert quota is q_e = min(count_e, cap) with cap = ceil(rho * T * k / E);
+ * rho = 1 is evaluated in integers.                                          */
+int64_t oracle_quota_cap(int T, int E, int k, double rho) {
+  if (rho == 1.0) return ((int64_t)T * k + E - 1) / E;
+  return (int64_t)ceil(rho * (double)T * (double)k / (double)E);
+}
+
+typedef struct {
+  double score;
+  int32_t p;
+} scored_pair;
+
+static int by_score_desc_p_asc(const void* a, const void* b) {
+  const scored_pair* x = (const scored_pair*)a;
+  const scored_pair* y = (const scored_pair*)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->p < y->p) ? -1 : (x->p > y->p);
+}
+
+/* Selection within quotas and physical compaction (LRMoE abstract).  The score
+ * of pair p is score[p] (pair-indexed).  Each expert keeps its q_e pairs with
+ * the largest (score, then lower p); kept pairs stay in ascending p within the
+ * expert.  Outputs: kept_counts[E], kept_offsets[E+1], kept_perm[R] (pair id),
+ * kept_src[R] (position in the uncompacted sorted order), kept_inv[N]
+ * (compacted position, or -1 when dropped), retained[N] (0/1).  Returns R.   */
+int64_t oracle_compact(int T, int E, int k, const int32_t* counts, const int32_t* offsets,
+                       const int32_t* perm, const double* score, double rho, int32_t* kept_counts,
+                       int32_t* kept_offsets, int32_t* kept_perm, int32_t* kept_src, int32_t* kept_inv,
+                       uint8_t* retained) {
+  const int64_t N = (int64_t)T * k;
+  const int64_t cap = oracle_quota_cap(T, E, k, rho);
+  for (int64_t p = 0; p < N; ++p) {
+    retained[p] = 0;
+    kept_inv[p] = -1;
+  }
+  int64_t r = 0;
+  for (int e = 0; e < E; ++e) {
+    const int n = counts[e];
+    const int64_t q = n < cap ? n : cap;
+    scored_pair* list = (scored_pair*)malloc(sizeof(scored_pair) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < n; ++i) {
+      list[i].p = perm[offsets[e] + i];
+      list[i].score = score[list[i].p];
+    }
+    qsort(list, (size_t)n, sizeof(scored_pair), by_score_desc_p_asc);
+    for (int64_t i = 0; i < q; ++i) retained[list[i].p] = 1;
+    free(list);
+    kept_offsets[e] = (int32_t)r;
+    for (int i = 0; i < n; ++i) {
+      const int32_t p = perm[offsets[e] + i];
+      if (retained[p]) {
+        kept_perm[r] = p;
+        kept_src[r] = offsets[e] + i;
+        kept_inv[p] = (int32_t)r;
+        ++r;
+      }
+    }
+    kept_counts[e] = (int32_t)(r - kept_offsets[e]);
+  }
+  kept_offsets[E] = (int32_t)r;
+  return r;
+}
+
+/* ------------------------------------------------------------------------- */
+/* One SwiGLU expert on one token row (issue #14, Proposal: expert forward):
+ *   hg[f] = sum_h x[h] Wg[e,h,f],  hu[f] = sum_h x[h] Wu[e,h,f]
+ *   a[f]  = silu(hg[f]) * hu[f],   silu(z) = z * sigmoid(z)
+ *   o[h]  = sum_f a[f] Wd[e,f,h]
+ * Weights are row-major Wg, Wu [E,H,F] and Wd [E,F,H].                       */
+static void expert_forward(int H, int F, const double* xt, const double* Wg, const double* Wu,
+                           const double* Wd, double* hg, double* hu, double* a, double* o) {
+  for (int f = 0; f < F; ++f) {
+    double sg = 0.0, su = 0.0;
+    for (int h = 0; h < H; ++h) {
+      sg += xt[h] * Wg[(size_t)h * F + f];
+      su += xt[h] * Wu[(size_t)h * F + f];
+    }
+    hg[f] = sg;
+    hu[f] = su;
+    a[f] = sg * sigmoid(sg) * su;
+  }
+  for (int h = 0; h < H; ++h) {
+    double s = 0.0;
+    for (int f = 0; f < F; ++f) s += a[f] * Wd[(size_t)f * H + h];
+    o[h] = s;
+  }
+}
+
+/* Forward of the layer for a list of tokens (all tokens when toks == NULL):
+ *   y[t,:] = sum_{j ascending} w[t,j] * Expert_{idx[t,j]}(x[t,:])
+ * Optional pair-indexed intermediates: hg, hu, a [N,F] and o [N,H].          */
+void oracle_forward(int T, int H, int F, int E, int k, const double* x, const int32_t* idx,
+                    const double* w, const double* Wg, const double* Wu, const double* Wd, int n_tok,
+                    const int32_t* toks, double* y, double* hg_out, double* hu_out, double* a_out,
+                    double* o_out) {
+  (void)E;
+  const int count = toks ? n_tok : T;
+#pragma omp parallel
+  {
+    double* hg = (double*)malloc(sizeof(double) * (size_t)F);
+    double* hu = (double*)malloc(sizeof(double) * (size_t)F);
+    double* a = (double*)malloc(sizeof(double) * (size_t)F);
+    double* o = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < count; ++i) {
+      const int t = toks ? toks[i] : i;
+      const double* xt = x + (size_t)t * H;
+      double* yt = y + (size_t)t * H;
+      for (int h = 0; h < H; ++h) yt[h] = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const int64_t p = (int64_t)t * k + j;
+        const int e = idx[p];
+        expert_forward(H, F, xt, Wg + (size_t)e * H * F, Wu + (size_t)e * H * F,
+                       Wd + (size_t)e * F * H, hg, hu, a, o);
+        for (int h = 0; h < H; ++h) yt[h] += w[p] * o[h];
+        if (hg_out) memcpy(hg_out + (size_t)p * F, hg, sizeof(double) * (size_t)F);
+        if (hu_out) memcpy(hu_out + (size_t)p * F, hu, sizeof(double) * (size_t)F);
+        if (a_out) memcpy(a_out + (size_t)p * F, a, sizeof(double) * (size_t)F);
+        if (o_out) memcpy(o_out + (size_t)p * H, o, sizeof(double) * (size_t)H);
+      }
+    }
+    free(hg);
+    free(hu);
+    free(a);
+    free(o);
+  }
+}
+
+/* Backward of one pair with routing held fixed (issue #14, Proposal/Scope:
+ * backward dx, and dW for full fine-tuning).  With dO = w * dy[t]:
+ *   dA[f]  = sum_h dO[h] Wd[e,f,h]
+ *   dHg[f] = dA[f] * hu[f] * s * (1 + hg[f] * (1 - s)),  s = sigmoid(hg[f])
+ *   dHu[f] = dA[f] * hg[f] * s
+ *   dX[h]  = sum_f dHg[f] Wg[e,h,f] + dHu[f] Wu[e,h,f]
+ * (d/dz silu(z) = s * (1 + z * (1 - s)).)                                     */
+static void expert_backward(int H, int F, double wp, const double* dyt, const double* Wg,
+                            const double* Wu, const double* Wd, const double* hg, const double* hu,
+                            double* dO, double* dHg, double* dHu, double* dX) {
+  for (int h = 0; h < H; ++h) dO[h] = wp * dyt[h];
+  for (int f = 0; f < F; ++f) {
+    double dA = 0.0;
+    for (int h = 0; h < H; ++h) dA += dO[h] * Wd[(size_t)f * H + h];
+    const double s = sigmoid(hg[f]);
+    dHg[f] = dA * hu[f] * s * (1.0 + hg[f] * (1.0 - s));
+    dHu[f] = dA * hg[f] * s;
+  }
+  for (int h = 0; h < H; ++h) {
+    double sx = 0.0;
+    for (int f = 0; f < F; ++f) sx += dHg[f] * Wg[(size_t)h * F + f] + dHu[f] * Wu[(size_t)h * F + f];
+    dX[h] = sx;
+  }
+}
+
+/* Input gradient and router-weight gradient for a list of tokens (all when
+ * toks == NULL).  dg[t,j] = <dy[t], o_p> for every pair; dx[t] sums dX over the
+ * token's retained pairs only (retained == NULL keeps every pair), in
+ * ascending j.  Optional pair-indexed intermediates: dO [N,H], dh [N,2F] laid
+ * out as [dHg | dHu], dX [N,H]; rows of dropped pairs are left untouched.      */
+void oracle_backward(int T, int H, int F, int E, int k, const double* x, const int32_t* idx,
+                     const double* w, const double* Wg, const double* Wu, const double* Wd,
+                     const double* dy, const uint8_t* retained, int n_tok, const int32_t* toks,
+                     double* dx, double* dg, double* dO_out, double* dh_out, double* dX_out) {
+  (void)E;
+  const int count = toks ? n_tok : T;
+#pragma omp parallel
+  {
+    double* hg = (double*)malloc(sizeof(double) * (size_t)F);
+    double* hu = (double*)malloc(sizeof(double) * (size_t)F);
+    double* a = (double*)malloc(sizeof(double) * (size_t)F);
+    double* o = (double*)malloc(sizeof(double) * (size_t)H);
+    double* dO = (double*)malloc(sizeof(double) * (size_t)H);
+    double* dHg = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dHu = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dX = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < count; ++i) {
+      const int t = toks ? toks[i] : i;
+      const double* xt = x + (size_t)t * H;
+      const double* dyt = dy + (size_t)t * H;
+      double* dxt = dx + (size_t)t * H;
+      for (int h = 0; h < H; ++h) dxt[h] = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const int64_t p = (int64_t)t * k + j;
+        const int e = idx[p];
+        const double* wg = Wg + (size_t)e * H * F;
+        const double* wu = Wu + (size_t)e * H * F;
+        const double* wd = Wd + (size_t)e * F * H;
+        expert_forward(H, F, xt, wg, wu, wd, hg, hu, a, o);
+        double g = 0.0;
+        for (int h = 0; h < H; ++h) g += dyt[h] * o[h];
+        dg[p] = g;
+        if (retained && !retained[p]) continue;
+        expert_backward(H, F, w[p], dyt, wg, wu, wd, hg, hu, dO, dHg, dHu, dX);
+        for (int h = 0; h < H; ++h) dxt[h] += dX[h];
+        if (dO_out) memcpy(dO_out + (size_t)p * H, dO, sizeof(double) * (size_t)H);
+        if (dh_out) {
+          memcpy(dh_out + (size_t)p * 2 * F, dHg, sizeof(double) * (size_t)F);
+          memcpy(dh_out + (size_t)p * 2 * F + F, dHu, sizeof(double) * (size_t)F);
+        }
+        if (dX_out) memcpy(dX_out + (size_t)p * H, dX, sizeof(double) * (size_t)H);
+      }
+    }
+    free(hg);
+    free(hu);
+    free(a);
+    free(o);
+    free(dO);
+    free(dHg);
+    free(dHu);
+    free(dX);
+  }
+}
+
+/* Full weight gradients of every expert (issue #14, Scope: dW for full FT),
+ * summed over the retained pairs routed to it, in ascending p:
+ *   dWd[e,f,h] = sum_p a_p[f] dO_p[h]
+ *   dWg[e,h,f] = sum_p x_t[h] dHg_p[f],  dWu[e,h,f] = sum_p x_t[h] dHu_p[f]
+ * An expert with no retained pair gets exact zeros.  Parallel over experts.  */
+void oracle_backward_dw(int T, int H, int F, int E, int k, const double* x, const int32_t* idx,
+                        const double* w, const double* Wg, const double* Wu, const double* Wd,
+                        const double* dy, const uint8_t* retained, double* dWg, double* dWu,
+                        double* dWd) {
+  const int64_t N = (int64_t)T * k;
+#pragma omp parallel
+  {
+    double* hg = (double*)malloc(sizeof(double) * (size_t)F);
+    double* hu = (double*)malloc(sizeof(double) * (size_t)F);
+    double* a = (double*)malloc(sizeof(double) * (size_t)F);
+    double* o = (double*)malloc(sizeof(double) * (size_t)H);
+    double* dO = (double*)malloc(sizeof(double) * (size_t)H);
+    double* dHg = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dHu = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dX = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int e = 0; e < E; ++e) {
+      double* gWg = dWg + (size_t)e * H * F;
+      double* gWu = dWu + (size_t)e * H * F;
+      double* gWd = dWd + (size_t)e * F * H;
+      memset(gWg, 0, sizeof(double) * (size_t)H * F);
+      memset(gWu, 0, sizeof(double) * (size_t)H * F);
+      memset(gWd, 0, sizeof(double) * (size_t)F * H);
+      const double* wg = Wg + (size_t)e * H * F;
+      const double* wu = Wu + (size_t)e * H * F;
+      const double* wd = Wd + (size_t)e * F * H;
+      for (int64_t p = 0; p < N; ++p) {
+        if (idx[p] != e) continue;
+        if (retained && !retained[p]) continue;
+        const double* xt = x + (size_t)(p / k) * H;
+        const double* dyt = dy + (size_t)(p / k) * H;
+        expert_forward(H, F, xt, wg, wu, wd, hg, hu, a, o);
+        expert_backward(H, F, w[p], dyt, wg, wu, wd, hg, hu, dO, dHg, dHu, dX);
+        for (int f = 0; f < F; ++f)
+          for (int h = 0; h < H; ++h) gWd[(size_t)f * H + h] += a[f] * dO[h];
+        for (int h = 0; h < H; ++h)
+          for (int f = 0; f < F; ++f) {
+            gWg[(size_t)h * F + f] += xt[h] * dHg[f];
+            gWu[(size_t)h * F + f] += xt[h] * dHu[f];
+          }
+      }
+    }
+    free(hg);
+    free(hu);
+    free(a);
+    free(o);
+    free(dO);
+    free(dHg);
+    free(dHu);
+    free(dX);
+  }
+}
+
+/* Single entries of the weight gradients, one by one, for layers too large to
+ * differentiate whole.  Query i asks for matrix mat[i] (0 = dW_gate[e,r,c],
+ * 1 = dW_up[e,r,c], 2 = dW_down[e,r,c]) of expert e[i]; the sum runs over the
+ * expert's retained pairs in ascending p with the same per-pair terms as
+ * oracle_backward_dw, evaluating only the feature that the entry needs.       */
+void oracle_dw_entries(int T, int H, int F, int E, int k, const double* x, const int32_t* idx,
+                       const double* w, const double* Wg, const double* Wu, const double* Wd,
+                       const double* dy, const uint8_t* retained, int n_q, const int32_t* q_e,
+                       const int32_t* q_mat, const int32_t* q_r, const int32_t* q_c, double* out) {
+  (void)E;
+  const int64_t N = (int64_t)T * k;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = 0; i < n_q; ++i) {
+    const int e = q_e[i], mat = q_mat[i], r = q_r[i], c = q_c[i];
+    const double* wg = Wg + (size_t)e * H * F;
+    const double* wu = Wu + (size_t)e * H * F;
+    const double* wd = Wd + (size_t)e * F * H;
+    /* feature index f of the entry: dW_down[f,h] -> f = r; dW_gate/up[h,f] -> f = c */
+    const int f = (mat == 2) ? r : c;
+    double acc = 0.0;
+    for (int64_t p = 0; p < N; ++p) {
+      if (idx[p] != e) continue;
+      if (retained && !retained[p]) continue;
+      const double* xt = x + (size_t)(p / k) * H;
+      const double* dyt = dy + (size_t)(p / k) * H;
+      double hg = 0.0, hu = 0.0;
+      for (int h = 0; h < H; ++h) {
+        hg += xt[h] * wg[(size_t)h * F + f];
+        hu += xt[h] * wu[(size_t)h * F + f];
+      }
+      const double s = sigmoid(hg);
+      if (mat == 2) {
+        const double a = hg * s * hu;
+        acc += a * (w[p] * dyt[c]);
+      } else {
+        double dA = 0.0;
+        for (int h = 0; h < H; ++h) dA += (w[p] * dyt[h]) * wd[(size_t)f * H + h];
+        const double d = (mat == 0) ? dA * hu * s * (1.0 + hg * (1.0 - s)) : dA * hg * s;
+        acc += xt[r] * d;
+      }
+    }
+    out[i] = acc;
+  }
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

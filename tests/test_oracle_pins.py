@@ -1,0 +1,405 @@
+"""Pins of the CPU oracle against facts other than itself.
+
+Each test pins one step of the oracle to something it does not share code with:
+hand-worked fixtures (tests/golden), brute force over all subsets, a library
+sort, torch's float64 autograd on a dense all-experts formulation, central
+finite differences, closed forms and exact invariants.  These run on the CPU.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_grouped_gemm_top_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TINY = W.WORKLOADS["tiny_fp32"]
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    d = W.generate(TINY, seed=0)
+    d = {k: v.astype(np.float64) for k, v in d.items()}
+    d["logits"] = oracle.router_logits(d["x"], d["W_r"]).astype(np.float32).astype(np.float64)
+    d["idx"], d["w"] = oracle.route_topk(d["logits"], TINY.k)
+    return d
+
+
+# ----------------------------------------------------------------------------- golden
+def test_golden_route_dispatch():
+    g = json.load(open(os.path.join(GOLDEN, "route_dispatch_tiny.json")))
+    idx, w = oracle.route_topk(np.array(g["logits"]), g["k"])
+    assert idx.tolist() == g["idx"]
+    np.testing.assert_allclose(w, np.array(g["w"]), rtol=0, atol=1e-15)
+    counts, offsets, perm, inv = oracle.dispatch(idx, g["E"])
+    assert counts.tolist() == g["counts"]
+    assert offsets.tolist() == g["offsets"]
+    assert perm.tolist() == g["perm"]
+    assert inv.tolist() == g["inv_perm"]
+
+
+def test_golden_swiglu_expert():
+    g = json.load(open(os.path.join(GOLDEN, "swiglu_expert_tiny.json")))
+    x, Wg, Wu, Wd, dy = (np.array(g[n]) for n in ("x", "W_gate", "W_up", "W_down", "dy"))
+    idx = np.zeros((1, 1), np.int32)
+    w = np.ones((1, 1))
+    y = oracle.forward(x, idx, w, Wg, Wu, Wd)
+    np.testing.assert_allclose(y, np.array(g["y"]), rtol=1e-15, atol=0)
+    dx, dg = oracle.backward(x, idx, w, Wg, Wu, Wd, dy)
+    np.testing.assert_allclose(dx, np.array(g["dx"]), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(dg, y[:, :1], rtol=1e-15)  # <dy, o> with dy = (1, 0)
+    dWg, dWu, dWd = oracle.backward_dw(x, idx, w, Wg, Wu, Wd, dy)
+    np.testing.assert_allclose(dWg, np.array(g["dW_gate"]), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(dWu, np.array(g["dW_up"]), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(dWd, np.array(g["dW_down"]), rtol=1e-15, atol=0)
+
+
+# ----------------------------------------------------------------------------- routing
+def _tie_rich_logits(rng, T, E):
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 0.25, 1.0, 2.0], np.float64)
+    return rng.choice(vals, size=(T, E))
+
+
+@pytest.mark.parametrize("kind", ["random", "ties"])
+def test_route_bruteforce_all_subsets(tiny, kind):
+    """The selected set is the unique k-subset that dominates every other expert
+    (larger logit, or equal logit and lower index); it is also the max-sum
+    subset (exact rational sums) with the lexicographically smallest index list."""
+    rng = np.random.default_rng(11)
+    E, k = TINY.E, TINY.k
+    logits = tiny["logits"] if kind == "random" else _tie_rich_logits(rng, 64, E)
+    for kk in (1, 2, 3):
+        idx, _ = oracle.route_topk(logits, kk)
+        for t in range(logits.shape[0]):
+            l = logits[t]
+            dominating = []
+            best_key = None
+            for S in itertools.combinations(range(E), kk):
+                rest = [e for e in range(E) if e not in S]
+                if all(l[i] > l[j] or (l[i] == l[j] and i < j) for i in S for j in rest):
+                    dominating.append(S)
+                key = (sum(Fraction(float(l[i])) for i in S), tuple(-i for i in S))
+                if best_key is None or key > best_key:
+                    best_key, best = key, S
+            assert len(dominating) == 1
+            assert tuple(sorted(idx[t])) == dominating[0] == best
+            # order inside the selection: logit descending, equal logits by index
+            sel = list(idx[t])
+            for a, b in zip(sel, sel[1:]):
+                assert l[a] > l[b] or (l[a] == l[b] and a < b)
+
+
+def test_route_closed_forms():
+    E = 8
+    eq = np.full((5, E), 0.7)
+    for k in (1, 2, 3, 8):
+        idx, w = oracle.route_topk(eq, k)
+        assert (idx == np.arange(k)[None, :]).all()
+        assert (w == 1.0 / k).all()
+    rng = np.random.default_rng(3)
+    l = rng.standard_normal((16, E))
+    idx, w = oracle.route_topk(l, 1)
+    assert (w == 1.0).all()
+    assert (idx[:, 0] == np.argmax(l, axis=1)).all()
+    # k = E: the textbook softmax over all experts, listed in selection order
+    idx, w = oracle.route_topk(l, E)
+    sm = torch.softmax(torch.tensor(l, dtype=torch.float64), dim=1).numpy()
+    np.testing.assert_allclose(w, np.take_along_axis(sm, idx.astype(np.int64), 1), rtol=1e-14)
+
+
+def test_route_weights_sum_to_one(tiny):
+    rng = np.random.default_rng(5)
+    for k in (1, 2, 4, 8):
+        l = rng.standard_normal((200, 32)) * 3
+        _, w = oracle.route_topk(l, k)
+        assert np.abs(w.sum(1) - 1).max() <= 4e-16 * k
+        assert (w > 0).all() and (np.diff(w, axis=1) <= 0).all()
+    assert np.abs(tiny["w"].sum(1) - 1).max() <= 1e-15
+
+
+# ----------------------------------------------------------------------------- dispatch
+@pytest.mark.parametrize("E,T,k", [(8, 64, 2), (128, 300, 8), (5, 7, 5)])
+def test_dispatch_against_library_stable_sort(E, T, k):
+    rng = np.random.default_rng(E + T)
+    idx, _ = oracle.route_topk(rng.standard_normal((T, E)) + np.linspace(0, -3, E), k)
+    counts, offsets, perm, inv = oracle.dispatch(idx, E)
+    flat = idx.reshape(-1)
+    assert (perm == np.argsort(flat, kind="stable")).all()
+    assert (counts == np.bincount(flat, minlength=E)).all()
+    assert offsets[0] == 0 and (offsets[1:] == np.cumsum(counts)).all() and offsets[E] == T * k
+    assert (np.sort(perm) == np.arange(T * k)).all()       # bijection
+    assert (inv[perm] == np.arange(T * k)).all()            # inv o perm = id
+    keys = flat[perm]
+    assert (np.diff(keys) >= 0).all()
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert (np.diff(seg) > 0).all() and (flat[seg] == e).all()
+    x = rng.standard_normal((T, 6))
+    xs = x[perm // k]
+    assert np.array_equal(xs[inv], np.repeat(x, k, axis=0))  # row round trip
+
+
+def test_dispatch_closed_form_equal_logits():
+    T, E, k = 10, 6, 3
+    idx, _ = oracle.route_topk(np.zeros((T, E)), k)
+    counts, offsets, perm, inv = oracle.dispatch(idx, E)
+    assert counts.tolist() == [T] * k + [0] * (E - k)
+    for e in range(k):
+        for t in range(T):
+            assert perm[e * T + t] == t * k + e
+
+
+def test_dispatch_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.array([[0, 9]], np.int32), 4)
+
+
+# ----------------------------------------------------------------------------- forward / backward
+def _dense_torch(x, idx, w, Wg, Wu, Wd, retained=None):
+    """Every expert on every token, gated by G (zero off the selection); a
+    dropped pair's expert output is detached, so it adds to y but not to dx/dW."""
+    f64 = torch.float64
+    T, H = x.shape
+    E = Wg.shape[0]
+    X = torch.tensor(x, dtype=f64, requires_grad=True)
+    Wt = [torch.tensor(a, dtype=f64, requires_grad=True) for a in (Wg, Wu, Wd)]
+    wt = torch.tensor(w, dtype=f64, requires_grad=True)
+    it = torch.tensor(idx, dtype=torch.int64)
+    G = torch.zeros(T, E, dtype=f64).scatter(1, it, wt)
+    keep = torch.ones(T, E, dtype=f64)
+    if retained is not None:
+        keep = torch.ones(T, E, dtype=f64).scatter(1, it, torch.tensor(retained.reshape(idx.shape), dtype=f64))
+    y = torch.zeros(T, H, dtype=f64)
+    for e in range(E):
+        Hg = X @ Wt[0][e]
+        Hu = X @ Wt[1][e]
+        O = (torch.nn.functional.silu(Hg) * Hu) @ Wt[2][e]
+        m = keep[:, e:e + 1]
+        y = y + G[:, e:e + 1] * (m * O + (1 - m) * O.detach())
+    return y, X, Wt, wt
+
+
+def test_forward_dense_bruteforce(tiny):
+    d = tiny
+    y = oracle.forward(d["x"], d["idx"], d["w"], d["W_gate"], d["W_up"], d["W_down"])
+    yt, *_ = _dense_torch(d["x"], d["idx"], d["w"], d["W_gate"], d["W_up"], d["W_down"])
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_forward_intermediates_consistent(tiny):
+    d = tiny
+    y, it = oracle.forward(d["x"], d["idx"], d["w"], d["W_gate"], d["W_up"], d["W_down"], intermediates=True)
+    k = TINY.k
+    p = 37
+    t, e = p // k, d["idx"].reshape(-1)[p]
+    hg = d["x"][t] @ d["W_gate"][e]
+    np.testing.assert_allclose(it["hg"][p], hg, rtol=1e-12)
+    np.testing.assert_allclose(it["o"][p], it["a"][p] @ d["W_down"][e], rtol=1e-12)
+    # y is the weighted sum of the token's pair outputs
+    np.testing.assert_allclose(y[t], sum(d["w"][t, j] * it["o"][t * k + j] for j in range(k)), rtol=1e-13)
+
+
+def test_forward_single_expert_is_plain_swiglu_mlp():
+    rng = np.random.default_rng(7)
+    T, H, F = 9, 24, 16
+    x = rng.standard_normal((T, H))
+    Wg, Wu, Wd = (0.3 * rng.standard_normal(s) for s in ((1, H, F), (1, H, F), (1, F, H)))
+    idx = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1))
+    y = oracle.forward(x, idx, w, Wg, Wu, Wd)
+    X = torch.tensor(x)
+    ref = (torch.nn.functional.silu(X @ torch.tensor(Wg[0])) * (X @ torch.tensor(Wu[0]))) @ torch.tensor(Wd[0])
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_forward_zero_input_and_linearity(tiny):
+    d = tiny
+    args = (d["idx"], d["w"], d["W_gate"], d["W_up"])
+    assert (oracle.forward(np.zeros_like(d["x"]), *args, d["W_down"]) == 0).all()
+    y1 = oracle.forward(d["x"], *args, d["W_down"])
+    y2 = oracle.forward(d["x"], *args, 2.0 * d["W_down"])
+    assert np.array_equal(y2, 2.0 * y1)
+
+
+def test_backward_against_autograd(tiny):
+    d = tiny
+    a = (d["x"], d["idx"], d["w"], d["W_gate"], d["W_up"], d["W_down"])
+    dx, dg = oracle.backward(*a, d["dy"])
+    dWg, dWu, dWd = oracle.backward_dw(*a, d["dy"])
+    y, X, Wt, wt = _dense_torch(*a)
+    (y * torch.tensor(d["dy"])).sum().backward()
+    for got, ref in ((dx, X.grad), (dg, wt.grad), (dWg, Wt[0].grad), (dWu, Wt[1].grad), (dWd, Wt[2].grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def _loss(d, tokens=None, **over):
+    p = {n: over.get(n, d[n]) for n in ("x", "w", "W_gate", "W_up", "W_down")}
+    y = oracle.forward(p["x"], d["idx"], p["w"], p["W_gate"], p["W_up"], p["W_down"], tokens=tokens)
+    return float((y * d["dy"]).sum())
+
+
+def test_backward_finite_differences(tiny):
+    """Central differences (h = 1e-6, float64) of L = sum(y * dy)."""
+    d = tiny
+    h = 1e-6
+    a = (d["x"], d["idx"], d["w"], d["W_gate"], d["W_up"], d["W_down"])
+    dx, dg = oracle.backward(*a, d["dy"])
+    dWg, dWu, dWd = oracle.backward_dw(*a, d["dy"])
+    rng = np.random.default_rng(9)
+    # every coordinate of x for 8 tokens (only y[t] depends on x[t])
+    for t in rng.choice(TINY.T, 8, replace=False):
+        for hh in range(TINY.H):
+            xp, xm = d["x"].copy(), d["x"].copy()
+            xp[t, hh] += h
+            xm[t, hh] -= h
+            fd = (_loss(d, [t], x=xp) - _loss(d, [t], x=xm)) / (2 * h)
+            assert abs(fd - dx[t, hh]) <= 1e-7 * max(1.0, abs(dx[t, hh]))
+    # every routing weight
+    for t in range(TINY.T):
+        for j in range(TINY.k):
+            wp, wm = d["w"].copy(), d["w"].copy()
+            wp[t, j] += h
+            wm[t, j] -= h
+            fd = (_loss(d, [t], w=wp) - _loss(d, [t], w=wm)) / (2 * h)
+            assert abs(fd - dg[t, j]) <= 1e-7 * max(1.0, abs(dg[t, j]))
+    # 600 random weight coordinates (only tokens routed to the expert matter)
+    flat = d["idx"].reshape(-1)
+    for name, grad in (("W_gate", dWg), ("W_up", dWu), ("W_down", dWd)):
+        for _ in range(200):
+            e = int(rng.integers(TINY.E))
+            r, c = (int(rng.integers(s)) for s in grad.shape[1:])
+            toks = np.unique(np.nonzero(flat == e)[0] // TINY.k)
+            Wp, Wm = d[name].copy(), d[name].copy()
+            Wp[e, r, c] += h
+            Wm[e, r, c] -= h
+            fd = (_loss(d, toks, **{name: Wp}) - _loss(d, toks, **{name: Wm})) / (2 * h)
+            assert abs(fd - grad[e, r, c]) <= 1e-7 * max(1.0, abs(grad[e, r, c]))
+
+
+def test_backward_zero_and_linear_in_dy(tiny):
+    d = tiny
+    a = (d["x"], d["idx"], d["w"], d["W_gate"], d["W_up"], d["W_down"])
+    z = np.zeros_like(d["dy"])
+    dx, dg = oracle.backward(*a, z)
+    assert (dx == 0).all() and (dg == 0).all()
+    assert all((g == 0).all() for g in oracle.backward_dw(*a, z))
+    dx1, dg1 = oracle.backward(*a, d["dy"])
+    dx2, dg2 = oracle.backward(*a, 2.0 * d["dy"])
+    assert np.array_equal(dx2, 2.0 * dx1) and np.array_equal(dg2, 2.0 * dg1)
+
+
+def test_empty_expert_has_zero_weight_gradient(tiny):
+    d = tiny
+    logits = d["logits"].copy()
+    logits[:, 5] -= 100.0
+    idx, w = oracle.route_topk(logits, TINY.k)
+    assert not (idx == 5).any()
+    dWg, dWu, dWd = oracle.backward_dw(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"], d["dy"])
+    assert (dWg[5] == 0).all() and (dWu[5] == 0).all() and (dWd[5] == 0).all()
+    assert np.abs(dWd[0]).max() > 0
+
+
+def test_dw_entries_match_full_dw(tiny):
+    d = tiny
+    a = (d["x"], d["idx"], d["w"], d["W_gate"], d["W_up"], d["W_down"], d["dy"])
+    full = oracle.backward_dw(*a)
+    rng = np.random.default_rng(4)
+    q = [(int(rng.integers(TINY.E)), m, int(rng.integers(full[m].shape[1])), int(rng.integers(full[m].shape[2])))
+         for m in (0, 1, 2) for _ in range(40)]
+    qe, qm, qr, qc = (np.array(v) for v in zip(*q))
+    got = oracle.dw_entries(*a, qe, qm, qr, qc)
+    ref = np.array([full[m][e, r, c] for e, m, r, c in q])
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-16)
+
+
+def test_sampled_tokens_match_full(tiny):
+    d = tiny
+    a = (d["x"], d["idx"], d["w"], d["W_gate"], d["W_up"], d["W_down"])
+    y = oracle.forward(*a)
+    dx, dg = oracle.backward(*a, d["dy"])
+    toks = [3, 17, 63]
+    ys = oracle.forward(*a, tokens=toks)
+    dxs, dgs = oracle.backward(*a, d["dy"], tokens=toks)
+    assert np.array_equal(ys[toks], y[toks]) and np.array_equal(dxs[toks], dx[toks])
+    assert np.array_equal(dgs[toks], dg[toks])
+
+
+# ----------------------------------------------------------------------------- compaction
+def _compact_bruteforce(idx, score, E, cap):
+    flat = idx.reshape(-1)
+    kept = []
+    for e in range(E):
+        pairs = [p for p in range(len(flat)) if flat[p] == e]
+        best = sorted(pairs, key=lambda p: (-score[p], p))[:min(len(pairs), cap)]
+        kept.append(sorted(best))
+    return kept
+
+
+@pytest.mark.parametrize("rho", [1.0, 0.5, 0.26, 3.0])
+def test_compaction_bruteforce(rho):
+    rng = np.random.default_rng(21)
+    T, E, k = 96, 8, 2
+    logits = rng.standard_normal((T, E)) + W.skew_bias(E).astype(np.float64)
+    idx, w = oracle.route_topk(logits, k)
+    score = np.round(w.reshape(-1) * 8) / 8  # coarse scores: many ties
+    counts, offsets, perm, inv = oracle.dispatch(idx, E)
+    cap = oracle.quota_cap(T, E, k, rho)
+    assert cap == math.ceil(rho * T * k / E)
+    c = oracle.compact(T, E, k, counts, offsets, perm, score, rho)
+    ref = _compact_bruteforce(idx, score, E, cap)
+    assert c["counts"].tolist() == [len(r) for r in ref]
+    assert c["R"] == sum(min(int(n), cap) for n in counts)
+    assert c["perm"].tolist() == [p for r in ref for p in r]
+    assert (c["offsets"][1:] == np.cumsum(c["counts"])).all()
+    for r, p in enumerate(c["perm"]):
+        assert c["inv"][p] == r and perm[c["src"][r]] == p
+    dropped = np.setdiff1d(np.arange(T * k), c["perm"])
+    assert (c["inv"][dropped] == -1).all() and (c["retained"][dropped] == 0).all()
+
+
+def test_compaction_keeps_everything_when_quota_is_large():
+    rng = np.random.default_rng(2)
+    T, E, k = 40, 8, 2
+    idx, w = oracle.route_topk(rng.standard_normal((T, E)), k)
+    counts, offsets, perm, inv = oracle.dispatch(idx, E)
+    c = oracle.compact(T, E, k, counts, offsets, perm, w.reshape(-1), 100.0)
+    assert c["R"] == T * k
+    assert np.array_equal(c["perm"], perm) and np.array_equal(c["inv"], inv)
+    assert np.array_equal(c["src"], np.arange(T * k)) and np.array_equal(c["counts"], counts)
+
+
+def test_compaction_cap_one_keeps_best_pair():
+    rng = np.random.default_rng(8)
+    T, E, k = 50, 8, 2
+    idx, w = oracle.route_topk(rng.standard_normal((T, E)), k)
+    counts, offsets, perm, inv = oracle.dispatch(idx, E)
+    score = w.reshape(-1)
+    c = oracle.compact(T, E, k, counts, offsets, perm, score, 1e-9)
+    flat = idx.reshape(-1)
+    for e in range(E):
+        pairs = np.nonzero(flat == e)[0]
+        if len(pairs):
+            best = pairs[np.argmax(score[pairs])]  # argmax takes the first (lowest p) of ties
+            assert c["perm"][c["offsets"][e]:c["offsets"][e + 1]].tolist() == [best]
+
+
+def test_masked_backward_against_autograd(tiny):
+    """Dropped pairs add to y (and to dg) but not to dx or dW."""
+    d = tiny
+    counts, offsets, perm, inv = oracle.dispatch(d["idx"], TINY.E)
+    c = oracle.compact(TINY.T, TINY.E, TINY.k, counts, offsets, perm, d["w"].reshape(-1), 0.6)
+    ret = c["retained"]
+    assert 0 < ret.sum() < TINY.N
+    a = (d["x"], d["idx"], d["w"], d["W_gate"], d["W_up"], d["W_down"])
+    dx, dg = oracle.backward(*a, d["dy"], retained=ret)
+    dW = oracle.backward_dw(*a, d["dy"], retained=ret)
+    y, X, Wt, wt = _dense_torch(*a, retained=ret)
+    (y * torch.tensor(d["dy"])).sum().backward()
+    for got, ref in ((dx, X.grad), (dg, wt.grad), (dW[0], Wt[0].grad), (dW[1], Wt[1].grad), (dW[2], Wt[2].grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-13)
