@@ -1,0 +1,185 @@
+"""Benchmark of one MoE layer's expert computation in training on one MI355X.
+
+One step = the whole path on one batch: route -> dispatch -> grouped SwiGLU
+forward -> combine -> backward dx (+ dg), plus compaction and dW for the
+workloads that train experts.  Inputs are seeded synthetic tensors already
+resident in HBM when timing starts.  Default workload: the Qwen3-30B-A3B
+expert shape in a LoRA step (T=128 tokens, H=2048, F=768, E=128, top-8, bf16,
+experts frozen: forward + dx).
+
+Prints ONE JSON line: tokens/s over K timed steps, the roofline of the
+dominant kernel (its duration from HIP events on its own stream, inside the
+timed steps), and the CPU oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd+bwd tokens/sec and TFLOPS (% bf16 MFMA peak), Qwen3-30B-A3B shape"
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3
+
+# kernel ids of include/moe.h (moe_kernel)
+K_GATEUP, K_DOWN, K_COMBINE, K_GRAD_ROWS, K_DA, K_DX, K_DW, K_DISPATCH_ROWS = 2, 3, 4, 5, 6, 7, 8, 1
+KERNEL_NAMES = {K_GATEUP: "row_gemm_bf16_kernel<GATEUP>", K_DOWN: "row_gemm_bf16_kernel<DOWN>",
+                K_DA: "row_gemm_bf16_kernel<DA>", K_DX: "row_gemm_bf16_kernel<DX>", K_DW: "dw_bf16_kernel",
+                K_DISPATCH_ROWS: "dispatch_rows_kernel", K_GRAD_ROWS: "grad_rows_kernel",
+                K_COMBINE: "combine_kernel"}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="qwen3_lora_t128")
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    p.add_argument("--cpu-tokens", type=int, default=0, help="tokens of the CPU-oracle sample (0: auto)")
+    return p.parse_args()
+
+
+def algorithmic(wl, counts, kept_counts=None):
+    """Per-kernel algorithmic bytes and flops (real rows only, no padding)."""
+    b = 2 if wl.dtype == "bf16" else 4
+    H, F, T, k = wl.H, wl.F, wl.T, wl.k
+    N = wl.N
+    Ea = int((counts > 0).sum())
+    R = int(kept_counts.sum()) if kept_counts is not None else N
+    Ea_b = int((kept_counts > 0).sum()) if kept_counts is not None else Ea
+    return {
+        K_DISPATCH_ROWS: (T * H * b + N * H * b + 4 * N, 0.0),
+        K_GATEUP: (2 * H * F * b * Ea + N * H * b + N * 2 * F * b + N * F * b, 4.0 * H * F * N),
+        K_DOWN: (H * F * b * Ea + N * F * b + N * H * b, 2.0 * H * F * N),
+        K_COMBINE: (N * H * b + 8 * N + T * H * b, 0.0),
+        K_GRAD_ROWS: (T * H * b + R * H * b + 8 * N + N * H * b, 0.0),
+        K_DA: (H * F * b * Ea_b + R * H * b + 2 * R * 2 * F * b, 2.0 * H * F * R),
+        K_DX: (2 * H * F * b * Ea_b + R * 2 * F * b + R * H * b, 4.0 * H * F * R),
+        K_DW: (R * (2 * H + 3 * F) * b + 3 * H * F * wl.E * b, 6.0 * H * F * R),
+    }
+
+
+def cpu_baseline(wl, d, logits, sample_tokens):
+    """The oracle (as it stands) on a token prefix of the same workload:
+    route -> dispatch -> forward/combine -> backward dx, dg (-> dW)."""
+    import numpy as np
+
+    import oracle
+    T = sample_tokens
+    # inputs upcast to float64 once, outside the timed region (input marshalling)
+    sub = {n: np.ascontiguousarray(d[n][:T], dtype=np.float64) for n in ("x", "dy")}
+    W64 = {n: np.ascontiguousarray(d[n], dtype=np.float64) for n in ("W_gate", "W_up", "W_down")}
+    lg = np.ascontiguousarray(logits[:T], dtype=np.float64)
+    t0 = time.perf_counter()
+    idx, w = oracle.route_topk(lg, wl.k)
+    oracle.dispatch(idx, wl.E)
+    oracle.forward(sub["x"], idx, w, W64["W_gate"], W64["W_up"], W64["W_down"])
+    oracle.backward(sub["x"], idx, w, W64["W_gate"], W64["W_up"], W64["W_down"], sub["dy"])
+    if wl.dw:
+        oracle.backward_dw(sub["x"], idx, w, W64["W_gate"], W64["W_up"], W64["W_down"], sub["dy"])
+    dt = time.perf_counter() - t0
+    return {"value": T / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{T} of {wl.T} tokens of {wl.name} (fp64 oracle, route+dispatch+forward+combine+dx+dg"
+                      f"{'+dW' if wl.dw else ''}), {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from expert_grouped_gemm_top_amd import moe
+    from expert_grouped_gemm_top_amd import workloads as W
+    from expert_grouped_gemm_top_amd.layer import MoeLayerBuffers
+
+    wl = W.WORKLOADS[args.workload]
+    assert wl.dtype == "bf16", "the benchmark runs the bf16 workloads"
+    d = W.generate(wl, seed=0)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in ("x", "W_gate", "W_up", "W_down", "dy")}
+    logits = torch.from_numpy(d["logits"]).to(dev)
+    L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho, dw=wl.dw, dg=True)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], stream)
+        L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    timed_kernels = [K_GATEUP, K_DOWN, K_DA, K_DX] + ([K_DW] if wl.dw else [])
+    events = {kk: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)] for kk in timed_kernels}
+    for pairs in events.values():  # torch creates the underlying hipEvent at the first record
+        for a, b in pairs:
+            a.record(stream)
+            b.record(stream)
+    lib = moe.lib()
+    lib.moe_profile_kernel.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for kk in timed_kernels:
+            a, b = events[kk][s]
+            lib.moe_profile_kernel(kk, ctypes.c_void_p(a.cuda_event), ctypes.c_void_p(b.cuda_event))
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = wl.T * args.steps / elapsed
+
+    counts = L.counts.cpu().numpy()
+    kept = L.kept_counts.cpu().numpy() if wl.rho is not None else None
+    alg = algorithmic(wl, counts, kept)
+    kernel_ms = {kk: float(np.mean([a.elapsed_time(b) for a, b in events[kk]])) for kk in timed_kernels}
+    step_flops = sum(alg[kk][1] for kk in timed_kernels)
+    dom = max(timed_kernels, key=lambda kk: kernel_ms[kk])
+    byts, flops = alg[dom]
+    ai = flops / byts
+    mfma_bound = ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    sec = kernel_ms[dom] * 1e-3
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": byts / sec / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["kernel_us"] = kernel_ms[dom] * 1e3
+    roof["algorithmic_bytes"] = byts
+    roof["algorithmic_flops"] = flops
+
+    out = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "F": wl.F, "E": wl.E, "k": wl.k,
+                   "pass": "fwd+dx+dg" + ("+dW" if wl.dw else "") + (f"+compact(rho={wl.rho})" if wl.rho else ""),
+                   "experts_with_rows": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max())},
+        "tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
+        "mfma_frac_of_step": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "kernel_us": {KERNEL_NAMES[kk]: kernel_ms[kk] * 1e3 for kk in timed_kernels},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens or min(wl.T, 128)
+        out["cpu_baseline"] = cpu_baseline(wl, d, d["logits"], n)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

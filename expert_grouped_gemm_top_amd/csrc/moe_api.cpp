@@ -1,0 +1,384 @@
+// moe_api.cpp -- the C ABI of libmoe (declared in include/moe.h): argument
+// validation, then the kernel launches on the caller's stream.  Validation runs
+// before anything is enqueued, so a rejected call leaves the stream untouched.
+// No C++ exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// one-shot event pairs armed by moe_profile_kernel, per kernel kind
+struct Armed {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local Armed g_armed[MOE_K_COUNT];
+
+// Runs one kernel launch `f` (returning hipError_t) between the armed events of `kind`.
+template <typename Fn>
+hipError_t timed(int kind, hipStream_t s, Fn&& f) {
+  Armed& a = g_armed[kind];
+  if (a.start == nullptr) return f();
+  hipError_t err = hipEventRecord(a.start, s);
+  if (err == hipSuccess) err = f();
+  if (err == hipSuccess) err = hipEventRecord(a.stop, s);
+  a = Armed{};
+  return err;
+}
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_status(hipError_t err, const char* where) {
+  if (err == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(err), (int)err);
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int esize_of(int dtype) { return dtype == MOE_F32 ? 4 : (dtype == MOE_BF16 ? 2 : 0); }
+
+#define REQUIRE(cond, status, ...)        \
+  do {                                    \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+#define NONNULL(p) REQUIRE((p) != nullptr, MOE_ERR_INVALID_ARGUMENT, "%s: %s must not be NULL", fn, #p)
+
+int check_routing_dims(const char* fn, int T, int E, int k) {
+  REQUIRE(T >= 1 && E >= 1 && k >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: T=%d, E=%d, k=%d must be >= 1", fn, T, E, k);
+  REQUIRE(k <= E, MOE_ERR_INVALID_ARGUMENT, "%s: k=%d exceeds E=%d", fn, k, E);
+  REQUIRE(E <= moe::kMaxExpertsHost, MOE_ERR_UNSUPPORTED, "%s: E=%d exceeds 256", fn, E);
+  REQUIRE(k <= 16, MOE_ERR_UNSUPPORTED, "%s: k=%d exceeds 16", fn, k);
+  REQUIRE((int64_t)T * k < (int64_t)1 << 31, MOE_ERR_UNSUPPORTED, "%s: T*k=%lld reaches 2^31", fn,
+          (long long)T * k);
+  return MOE_OK;
+}
+
+int check_dtype(const char* fn, int dtype) {
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, MOE_ERR_INVALID_ARGUMENT, "%s: dtype %d is neither MOE_F32 nor MOE_BF16",
+          fn, dtype);
+  return MOE_OK;
+}
+
+int check_row_width(const char* fn, const char* name, int v) {
+  REQUIRE(v >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: %s=%d must be >= 1", fn, name, v);
+  REQUIRE(v % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: %s=%d is not a multiple of 8", fn, name, v);
+  return MOE_OK;
+}
+
+int check_expert_dims(const char* fn, int H, int F, int E, int dtype) {
+  int rc = check_dtype(fn, dtype);
+  if (rc) return rc;
+  if ((rc = check_row_width(fn, "H", H)) || (rc = check_row_width(fn, "F", F))) return rc;
+  REQUIRE(E >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: E=%d must be >= 1", fn, E);
+  REQUIRE(E <= moe::kMaxExpertsHost, MOE_ERR_UNSUPPORTED, "%s: E=%d exceeds 256", fn, E);
+  if (dtype == MOE_BF16)
+    REQUIRE(H % 128 == 0 && F % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: bf16 needs H=%d and F=%d to be multiples of 128", fn,
+            H, F);
+  REQUIRE((int64_t)E * H * F < ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "%s: weights too large", fn);
+  return MOE_OK;
+}
+
+const int kGemmKind[4] = {MOE_K_GEMM_GATEUP, MOE_K_GEMM_DOWN, MOE_K_GEMM_DA, MOE_K_GEMM_DX};
+
+int check_rows(const char* fn, int max_rows) {
+  REQUIRE(max_rows >= 0, MOE_ERR_INVALID_ARGUMENT, "%s: max_rows=%d is negative", fn, max_rows);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "unknown moe_status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_abi_version(void) { return 1; }
+
+int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
+  const char* fn = "moe_profile_kernel";
+  REQUIRE(kernel >= 0 && kernel < MOE_K_COUNT, MOE_ERR_INVALID_ARGUMENT, "%s: unknown kernel %d", fn, kernel);
+  REQUIRE((start_event == nullptr) == (stop_event == nullptr), MOE_ERR_INVALID_ARGUMENT,
+          "%s: give both events or neither", fn);
+  g_armed[kernel].start = reinterpret_cast<hipEvent_t>(start_event);
+  g_armed[kernel].stop = reinterpret_cast<hipEvent_t>(stop_event);
+  return MOE_OK;
+}
+
+int moe_route_topk(int T, int E, int k, const float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  const char* fn = "moe_route_topk";
+  int rc = check_routing_dims(fn, T, E, k);
+  if (rc) return rc;
+  NONNULL(logits);
+  NONNULL(topk_idx);
+  NONNULL(topk_w);
+  hipStream_t s = as_stream(stream);
+  return hip_status(timed(MOE_K_ROUTE, s, [&] { return moe::launch_route_topk(T, E, k, logits, topk_idx, topk_w, s); }), fn);
+}
+
+size_t moe_dispatch_workspace_bytes(int T, int E, int k) {
+  if (T < 1 || E < 1 || k < 1) return 0;
+  return moe::dispatch_workspace_bytes((int64_t)T * k, E);
+}
+
+int moe_dispatch(int T, int H, int E, int k, int dtype, const int32_t* topk_idx, const void* x, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_sorted, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_dispatch";
+  int rc = check_routing_dims(fn, T, E, k);
+  if (rc) return rc;
+  if ((rc = check_dtype(fn, dtype)) || (rc = check_row_width(fn, "H", H))) return rc;
+  NONNULL(topk_idx);
+  NONNULL(counts);
+  NONNULL(offsets);
+  NONNULL(perm);
+  NONNULL(inv_perm);
+  REQUIRE((x == nullptr) == (x_sorted == nullptr), MOE_ERR_INVALID_ARGUMENT,
+          "%s: x and x_sorted must both be given or both be NULL", fn);
+  const size_t need = moe::dispatch_workspace_bytes((int64_t)T * k, E);
+  REQUIRE(workspace_bytes >= need, MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn,
+          workspace_bytes, need);
+  REQUIRE(need == 0 || workspace != nullptr, MOE_ERR_INVALID_ARGUMENT, "%s: workspace must not be NULL", fn);
+  hipStream_t s = as_stream(stream);
+  if ((rc = hip_status(
+           moe::launch_dispatch_index(T, E, k, topk_idx, counts, offsets, perm, inv_perm, workspace, s), fn)))
+    return rc;
+  if (x_sorted == nullptr) return MOE_OK;
+  return hip_status(timed(MOE_K_DISPATCH_ROWS, s,
+                          [&] { return moe::launch_dispatch_rows(T, H, k, esize_of(dtype), x, inv_perm, x_sorted, s); }),
+                    fn);
+}
+
+int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int dtype, const int32_t* offsets, const void* x_sorted,
+                           const void* w_gate, const void* w_up, const void* w_down, void* h_save, void* a_save,
+                           void* o_sorted, void* stream) {
+  const char* fn = "moe_grouped_swiglu_fwd";
+  int rc = check_expert_dims(fn, H, F, E, dtype);
+  if (rc || (rc = check_rows(fn, max_rows))) return rc;
+  NONNULL(offsets);
+  NONNULL(x_sorted);
+  NONNULL(w_gate);
+  NONNULL(w_up);
+  NONNULL(w_down);
+  NONNULL(h_save);
+  NONNULL(a_save);
+  NONNULL(o_sorted);
+  if (max_rows == 0) return MOE_OK;
+  moe::RowGemmArgs g{};
+  g.offsets = offsets;
+  g.E = E;
+  g.H = H;
+  g.F = F;
+  hipStream_t s = as_stream(stream);
+  auto run = [&](int mode) {
+    return timed(kGemmKind[mode], s, [&] {
+      return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, s)
+                               : moe::launch_row_gemm_f32(mode, g, max_rows, s);
+    });
+  };
+  g.a = (const uint16_t*)x_sorted;
+  g.w0 = (const uint16_t*)w_gate;
+  g.w1 = (const uint16_t*)w_up;
+  g.out0 = (uint16_t*)h_save;
+  g.out1 = (uint16_t*)a_save;
+  if ((rc = hip_status(run(moe::kGemmGateUp), fn))) return rc;
+  g.a = (const uint16_t*)a_save;
+  g.w0 = (const uint16_t*)w_down;
+  g.w1 = nullptr;
+  g.out0 = (uint16_t*)o_sorted;
+  g.out1 = nullptr;
+  return hip_status(run(moe::kGemmDown), fn);
+}
+
+int moe_combine(int T, int H, int k, int dtype, const void* rows, const int32_t* inv, const float* topk_w, void* out,
+                void* stream) {
+  const char* fn = "moe_combine";
+  REQUIRE(T >= 1 && k >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: T=%d, k=%d must be >= 1", fn, T, k);
+  REQUIRE(k <= 16, MOE_ERR_UNSUPPORTED, "%s: k=%d exceeds 16", fn, k);
+  REQUIRE((int64_t)T * k < (int64_t)1 << 31, MOE_ERR_UNSUPPORTED, "%s: T*k reaches 2^31", fn);
+  int rc;
+  if ((rc = check_dtype(fn, dtype)) || (rc = check_row_width(fn, "H", H))) return rc;
+  NONNULL(rows);
+  NONNULL(inv);
+  NONNULL(out);
+  hipStream_t s = as_stream(stream);
+  return hip_status(
+      timed(MOE_K_COMBINE, s, [&] { return moe::launch_combine(T, H, k, esize_of(dtype), rows, inv, topk_w, out, s); }),
+      fn);
+}
+
+int moe_grouped_bwd_dx(int T, int H, int F, int E, int k, int max_rows, int dtype, const int32_t* offsets,
+                       const int32_t* inv, const void* dy, const float* topk_w, const void* h_rows,
+                       const void* w_gate, const void* w_up, const void* w_down, const int32_t* inv_all,
+                       const void* o_sorted, float* dg, void* dO_rows, void* dh_rows, void* dX_rows, void* dx,
+                       void* stream) {
+  const char* fn = "moe_grouped_bwd_dx";
+  int rc = check_routing_dims(fn, T, E, k);
+  if (rc || (rc = check_expert_dims(fn, H, F, E, dtype)) || (rc = check_rows(fn, max_rows))) return rc;
+  REQUIRE(max_rows <= T * k, MOE_ERR_INVALID_ARGUMENT, "%s: max_rows=%d exceeds T*k=%d", fn, max_rows, T * k);
+  NONNULL(offsets);
+  NONNULL(inv);
+  NONNULL(dy);
+  NONNULL(topk_w);
+  NONNULL(h_rows);
+  NONNULL(w_gate);
+  NONNULL(w_up);
+  NONNULL(w_down);
+  NONNULL(dO_rows);
+  NONNULL(dh_rows);
+  NONNULL(dX_rows);
+  NONNULL(dx);
+  if (dg != nullptr) {
+    NONNULL(inv_all);
+    NONNULL(o_sorted);
+  }
+  hipStream_t s = as_stream(stream);
+  const int es = esize_of(dtype);
+  if ((rc = hip_status(timed(MOE_K_GRAD_ROWS, s,
+                             [&] {
+                               return moe::launch_grad_rows(T, H, k, es, dy, topk_w, inv, dO_rows, inv_all, o_sorted,
+                                                            dg, s);
+                             }),
+                       fn)))
+    return rc;
+  if (max_rows > 0) {
+    moe::RowGemmArgs g{};
+    g.offsets = offsets;
+    g.E = E;
+    g.H = H;
+    g.F = F;
+    auto run = [&](int mode) {
+      return timed(kGemmKind[mode], s, [&] {
+        return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, s)
+                                 : moe::launch_row_gemm_f32(mode, g, max_rows, s);
+      });
+    };
+    g.a = (const uint16_t*)dO_rows;
+    g.w0 = (const uint16_t*)w_down;
+    g.h = (const uint16_t*)h_rows;
+    g.out0 = (uint16_t*)dh_rows;
+    if ((rc = hip_status(run(moe::kGemmDA), fn))) return rc;
+    g.a = (const uint16_t*)dh_rows;
+    g.w0 = (const uint16_t*)w_gate;
+    g.w1 = (const uint16_t*)w_up;
+    g.h = nullptr;
+    g.out0 = (uint16_t*)dX_rows;
+    if ((rc = hip_status(run(moe::kGemmDX), fn))) return rc;
+  }
+  return hip_status(timed(MOE_K_COMBINE, s, [&] { return moe::launch_combine(T, H, k, es, dX_rows, inv, nullptr, dx, s); }),
+                    fn);
+}
+
+int moe_grouped_bwd_dw(int H, int F, int E, int max_rows, int dtype, const int32_t* offsets, const void* x_rows,
+                       const void* a_rows, const void* dO_rows, const void* dh_rows, void* dw_gate, void* dw_up,
+                       void* dw_down, void* stream) {
+  const char* fn = "moe_grouped_bwd_dw";
+  int rc = check_expert_dims(fn, H, F, E, dtype);
+  if (rc || (rc = check_rows(fn, max_rows))) return rc;
+  NONNULL(offsets);
+  NONNULL(dw_gate);
+  NONNULL(dw_up);
+  NONNULL(dw_down);
+  if (max_rows > 0) {
+    NONNULL(x_rows);
+    NONNULL(a_rows);
+    NONNULL(dO_rows);
+    NONNULL(dh_rows);
+  }
+  moe::DwArgs g{};
+  g.offsets = offsets;
+  g.E = E;
+  g.H = H;
+  g.F = F;
+  g.x = (const uint16_t*)x_rows;
+  g.a = (const uint16_t*)a_rows;
+  g.dO = (const uint16_t*)dO_rows;
+  g.dh = (const uint16_t*)dh_rows;
+  g.dwg = (uint16_t*)dw_gate;
+  g.dwu = (uint16_t*)dw_up;
+  g.dwd = (uint16_t*)dw_down;
+  hipStream_t s = as_stream(stream);
+  return hip_status(
+      timed(MOE_K_GEMM_DW, s, [&] { return dtype == MOE_BF16 ? moe::launch_dw_bf16(g, s) : moe::launch_dw_f32(g, s); }),
+      fn);
+}
+
+int64_t moe_quota_cap(int T, int E, int k, double rho) {
+  if (T < 1 || E < 1 || k < 1 || !(rho > 0.0) || !std::isfinite(rho)) return -1;
+  if (rho == 1.0) return ((int64_t)T * k + E - 1) / E;
+  const double c = std::ceil(rho * (double)T * (double)k / (double)E);
+  const double n = (double)T * k;
+  return (int64_t)(c < n ? c : n);
+}
+
+int moe_compact_pairs(int T, int H, int F, int E, int k, int dtype, double rho, const int32_t* counts,
+                      const int32_t* offsets, const int32_t* perm, const float* score, int32_t* kept_counts,
+                      int32_t* kept_offsets, int32_t* kept_perm, int32_t* kept_src, int32_t* kept_inv,
+                      const void* x_sorted, const void* a_save, const void* h_save, void* x_kept, void* a_kept,
+                      void* h_kept, void* stream) {
+  const char* fn = "moe_compact_pairs";
+  int rc = check_routing_dims(fn, T, E, k);
+  if (rc || (rc = check_dtype(fn, dtype))) return rc;
+  REQUIRE(rho > 0.0 && std::isfinite(rho), MOE_ERR_INVALID_ARGUMENT, "%s: rho=%g must be positive and finite", fn,
+          rho);
+  NONNULL(counts);
+  NONNULL(offsets);
+  NONNULL(perm);
+  NONNULL(score);
+  NONNULL(kept_counts);
+  NONNULL(kept_offsets);
+  NONNULL(kept_perm);
+  NONNULL(kept_src);
+  NONNULL(kept_inv);
+  REQUIRE(x_sorted == nullptr || x_kept != nullptr, MOE_ERR_INVALID_ARGUMENT, "%s: x_kept must not be NULL", fn);
+  REQUIRE(a_save == nullptr || a_kept != nullptr, MOE_ERR_INVALID_ARGUMENT, "%s: a_kept must not be NULL", fn);
+  REQUIRE(h_save == nullptr || h_kept != nullptr, MOE_ERR_INVALID_ARGUMENT, "%s: h_kept must not be NULL", fn);
+  if (x_sorted && (rc = check_row_width(fn, "H", H))) return rc;
+  if ((a_save || h_save) && (rc = check_row_width(fn, "F", F))) return rc;
+  const int64_t N = (int64_t)T * k;
+  const int64_t cap64 = moe_quota_cap(T, E, k, rho);
+  const int cap = (int)(cap64 < N ? cap64 : N);
+  hipStream_t s = as_stream(stream);
+  if ((rc = hip_status(moe::launch_fill_i32(kept_inv, N, -1, s), fn))) return rc;
+  if ((rc = hip_status(timed(MOE_K_COMPACT, s,
+                             [&] {
+                               return moe::launch_compact(N, E, cap, counts, offsets, perm, score, kept_counts,
+                                                          kept_offsets, kept_perm, kept_src, kept_inv, s);
+                             }),
+                       fn)))
+    return rc;
+  if (!x_sorted && !a_save && !h_save) return MOE_OK;
+  const int64_t bound64 = (int64_t)E * cap < N ? (int64_t)E * cap : N;
+  const int es = esize_of(dtype);
+  return hip_status(moe::launch_gather_rows(kept_offsets + E, kept_src, (int)bound64, x_sorted, x_kept, H * es, a_save,
+                                            a_kept, F * es, h_save, h_kept, 2 * F * es, s),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,201 @@
+// moe_dispatch.hip -- stable counting sort of token-expert pairs by expert,
+// and the copy of token rows into rows contiguous per expert.
+//
+// Dispatch of tokens into per-expert groups of rows (npu-train issue #14,
+// section Proposal), done on the GPU instead of the host.  Pair p = t*k + j
+// goes to expert idx[p]; within an expert pairs keep ascending p, so the
+// permutation is unique and bit-reproducible.
+//
+// Kernels (all on the caller's stream):
+//   hist  per block of 1024 pairs: expert histogram in LDS     (order-free LDS atomics)
+//   scan  one block: offsets = exclusive scan of counts, and every block's base
+//   rank  per block: stable rank of each pair among equal experts, from
+//         ballots on the bits of the expert id and popcounts below the lane,
+//         plus per-wave running bases in LDS; writes perm and inv_perm
+//   rows  per token: read x[t] once, write its k copies to x_sorted
+// With a single block of pairs (N <= 1024) hist, scan and rank run fused in one
+// workgroup.
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPairsPerWave = 256;
+constexpr int kPairsPerBlock = 4 * kPairsPerWave;
+
+__device__ __forceinline__ int expert_bits(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(int64_t N, int E, const int32_t* __restrict__ idx,
+                                                            int32_t* __restrict__ ws_hist) {
+  __shared__ int s_cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < E) s_cnt[tid] = 0;
+  __syncthreads();
+  const int64_t p0 = (int64_t)blockIdx.x * kPairsPerBlock;
+  for (int i = tid; i < kPairsPerBlock; i += 256) {
+    const int64_t p = p0 + i;
+    if (p < N) {
+      const int e = idx[p];
+      if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  if (tid < E) ws_hist[(size_t)blockIdx.x * E + tid] = s_cnt[tid];
+}
+
+// One block; thread e walks the blocks in order.  ws_base[b][e] = offsets[e] +
+// pairs of expert e in blocks before b.
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int nblocks, int E, const int32_t* __restrict__ ws_hist,
+                                                            int32_t* __restrict__ ws_base, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int s_tmp[4];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E)
+    for (int b = 0; b < nblocks; ++b) {
+      ws_base[(size_t)b * E + e] = run;
+      run += ws_hist[(size_t)b * E + e];
+    }
+  int total;
+  const int off = block256_exclusive_scan(e < E ? run : 0, s_tmp, total);
+  if (e < E) {
+    counts[e] = run;
+    offsets[e] = off;
+    for (int b = 0; b < nblocks; ++b) ws_base[(size_t)b * E + e] += off;
+  }
+  if (e == 0) offsets[E] = total;
+}
+
+// FUSED: this is the only block; counts/offsets are produced here.
+template <bool FUSED>
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(int64_t N, int E, const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ ws_base,
+                                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  __shared__ int s_cnt[4][kMaxExperts];   // per-wave histograms, then per-wave running bases
+  __shared__ int s_tmp[4];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int64_t pw = (int64_t)blockIdx.x * kPairsPerBlock + (int64_t)w * kPairsPerWave;
+  for (int i = tid; i < 4 * kMaxExperts; i += 256) (&s_cnt[0][0])[i] = 0;
+  __syncthreads();
+  for (int c = 0; c < kPairsPerWave; c += kWave) {
+    const int64_t p = pw + c + lane;
+    if (p < N) {
+      const int e = idx[p];
+      if (e >= 0 && e < E) atomicAdd(&s_cnt[w][e], 1);
+    }
+  }
+  __syncthreads();
+  // thread e turns the four wave histograms into running bases
+  int base = 0;
+  if (FUSED) {
+    int tot = 0;
+    if (tid < E) tot = s_cnt[0][tid] + s_cnt[1][tid] + s_cnt[2][tid] + s_cnt[3][tid];
+    int total;
+    base = block256_exclusive_scan(tot, s_tmp, total);
+    if (tid < E) {
+      counts[tid] = tot;
+      offsets[tid] = base;
+    }
+    if (tid == 0) offsets[E] = total;
+  } else if (tid < E) {
+    base = ws_base[(size_t)blockIdx.x * E + tid];
+  }
+  if (tid < E) {
+    const int c0 = s_cnt[0][tid], c1 = s_cnt[1][tid], c2 = s_cnt[2][tid];
+    s_cnt[0][tid] = base;
+    s_cnt[1][tid] = base + c0;
+    s_cnt[2][tid] = base + c0 + c1;
+    s_cnt[3][tid] = base + c0 + c1 + c2;
+  }
+  __syncthreads();
+  const int nbits = expert_bits(E);
+  const uint64_t lt = lanemask_lt();
+  for (int c = 0; c < kPairsPerWave; c += kWave) {
+    const int64_t p = pw + c + lane;
+    int e = (p < N) ? idx[p] : -1;
+    const bool ok = e >= 0 && e < E;
+    if (!ok) e = 0;
+    uint64_t peers = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt);
+    if (ok) {
+      const int s = s_cnt[w][e] + rank;
+      perm[s] = (int32_t)p;
+      inv_perm[p] = s;
+    } else if (p < N) {
+      inv_perm[p] = -1;  // out-of-range expert id: the pair is dropped
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (ok && (peers & lt) == 0) s_cnt[w][e] += __popcll(peers);  // lowest lane of each group
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+}
+
+// One block per token (grid-stride): 16-byte chunks of the row; every chunk of
+// x[t] is read once and written to the k sorted positions of the token's pairs.
+__global__ __launch_bounds__(256) void dispatch_rows_kernel(int T, int k, int row_chunks, const u32x4* __restrict__ x,
+                                                            const int32_t* __restrict__ inv_perm,
+                                                            u32x4* __restrict__ x_sorted) {
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    int dst[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) dst[j] = (j < k) ? inv_perm[(size_t)t * k + j] : -1;
+    for (int c = threadIdx.x; c < row_chunks; c += 256) {
+      const u32x4 v = x[(size_t)t * row_chunks + c];
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k && dst[j] >= 0) x_sorted[(size_t)dst[j] * row_chunks + c] = v;
+    }
+  }
+}
+
+}  // namespace
+
+size_t dispatch_workspace_bytes(int64_t N, int E) {
+  const int64_t nblocks = (N + kPairsPerBlock - 1) / kPairsPerBlock;
+  if (nblocks <= 1) return 0;
+  return (size_t)(2 * nblocks * E) * sizeof(int32_t);
+}
+
+hipError_t launch_dispatch_index(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                                 int32_t* perm, int32_t* inv_perm, void* ws, hipStream_t stream) {
+  const int64_t N = (int64_t)T * k;
+  const int64_t nblocks = (N + kPairsPerBlock - 1) / kPairsPerBlock;
+  if (nblocks <= 1) {
+    hipLaunchKernelGGL(dispatch_rank_kernel<true>, dim3(1), dim3(256), 0, stream, N, E, idx, nullptr, counts, offsets,
+                       perm, inv_perm);
+  } else {
+    int32_t* hist = (int32_t*)ws;
+    int32_t* base = hist + nblocks * E;
+    hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, N, E, idx, hist);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, stream, (int)nblocks, E, hist, base, counts,
+                       offsets);
+    hipLaunchKernelGGL(dispatch_rank_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream, N, E, idx, base,
+                       counts, offsets, perm, inv_perm);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_rows(int T, int H, int k, int esize, const void* x, const int32_t* inv_perm, void* x_sorted,
+                                hipStream_t stream) {
+  const int row_chunks = (int)((int64_t)H * esize / 16);
+  const int grid = T < 16384 ? T : 16384;
+  hipLaunchKernelGGL(dispatch_rows_kernel, dim3(grid), dim3(256), 0, stream, T, k, row_chunks, (const u32x4*)x,
+                     inv_perm, (u32x4*)x_sorted);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,73 @@
+// moe_launch.h -- internal launchers behind the C ABI (include/moe.h).  Each
+// returns the HIP status of its launches; the ABI layer validates arguments
+// before any of them is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExpertsHost = 256;  // expert ids fit in 8 bits
+
+enum RowGemmMode { kGemmGateUp = 0, kGemmDown = 1, kGemmDA = 2, kGemmDX = 3 };
+
+// Pointers of one row-ragged grouped GEMM.  Element type is bf16 (uint16_t
+// bits) or fp32 depending on the launcher; all buffers are device memory.
+//   GATEUP: a = x rows [R,H], w0 = W_gate, w1 = W_up, out0 = h [R,2F], out1 = a [R,F]
+//   DOWN:   a = a rows [R,F], w0 = W_down, out0 = o [R,H]
+//   DA:     a = dO rows [R,H], w0 = W_down, h = h rows [R,2F], out0 = dh [R,2F]
+//   DX:     a = dh rows [R,2F], w0 = W_gate, w1 = W_up, out0 = dX [R,H]
+struct RowGemmArgs {
+  const int32_t* offsets;
+  int E, H, F;
+  const uint16_t* a;
+  const uint16_t* w0;
+  const uint16_t* w1;
+  const uint16_t* h;
+  uint16_t* out0;
+  uint16_t* out1;
+};
+
+struct DwArgs {
+  const int32_t* offsets;
+  int E, H, F;
+  const uint16_t* x;   // [R,H]
+  const uint16_t* a;   // [R,F]
+  const uint16_t* dO;  // [R,H]
+  const uint16_t* dh;  // [R,2F]
+  uint16_t* dwg;       // [E,H,F]
+  uint16_t* dwu;       // [E,H,F]
+  uint16_t* dwd;       // [E,F,H]
+  int tiles_job1;      // filled by the launcher
+  int tiles_per_expert;
+};
+
+hipError_t launch_route_topk(int T, int E, int k, const float* logits, int32_t* idx, float* w, hipStream_t stream);
+
+size_t dispatch_workspace_bytes(int64_t N, int E);
+hipError_t launch_dispatch_index(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                                 int32_t* perm, int32_t* inv_perm, void* ws, hipStream_t stream);
+hipError_t launch_dispatch_rows(int T, int H, int k, int esize, const void* x, const int32_t* inv_perm, void* x_sorted,
+                                hipStream_t stream);
+
+hipError_t launch_combine(int T, int H, int k, int esize, const void* rows, const int32_t* inv, const float* w,
+                          void* out, hipStream_t stream);
+hipError_t launch_grad_rows(int T, int H, int k, int esize, const void* dy, const float* w, const int32_t* inv,
+                            void* dO_rows, const int32_t* inv_all, const void* o_sorted, float* dg,
+                            hipStream_t stream);
+hipError_t launch_gather_rows(const int32_t* R_ptr, const int32_t* src, int max_rows, const void* a_src, void* a_dst,
+                              int a_bytes, const void* b_src, void* b_dst, int b_bytes, const void* c_src,
+                              void* c_dst, int c_bytes, hipStream_t stream);
+
+hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
+hipError_t launch_dw_bf16(DwArgs g, hipStream_t stream);
+hipError_t launch_row_gemm_f32(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
+hipError_t launch_dw_f32(DwArgs g, hipStream_t stream);
+
+hipError_t launch_fill_i32(int32_t* a, int64_t n, int32_t v, hipStream_t stream);
+hipError_t launch_compact(int64_t N, int E, int cap, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                          const float* score, int32_t* kept_counts, int32_t* kept_offsets, int32_t* kept_perm,
+                          int32_t* kept_src, int32_t* kept_inv, hipStream_t stream);
+
+}  // namespace moe

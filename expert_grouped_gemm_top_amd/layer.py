@@ -1,0 +1,94 @@
+"""One MoE layer's expert computation in training, driven through the C ABI.
+
+``MoeLayerBuffers`` owns every device buffer of the path (torch allocations,
+sized once from the host capacities) and ``forward`` / ``backward`` enqueue the
+library calls in order on one stream -- route, dispatch, grouped SwiGLU
+forward, combine; then optionally compaction, backward dx (+ dg) and dW.  No
+step here computes anything itself: every value comes from libmoe's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import moe
+
+
+class MoeLayerBuffers:
+    def __init__(self, T, H, F, E, k, dtype=torch.bfloat16, device="cuda", rho=None, dw=True, dg=True):
+        self.T, self.H, self.F, self.E, self.k = T, H, F, E, k
+        self.N = N = T * k
+        self.dtype, self.rho, self.dw, self.want_dg = dtype, rho, dw, dg
+        dev = torch.device(device)
+        i32, f32 = torch.int32, torch.float32
+        em = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+        self.topk_idx = em(T, k, dt=i32)
+        self.topk_w = em(T, k, dt=f32)
+        self.counts = em(E, dt=i32)
+        self.offsets = em(E + 1, dt=i32)
+        self.perm = em(N, dt=i32)
+        self.inv_perm = em(N, dt=i32)
+        ws = moe.moe_dispatch_workspace_bytes(T, E, k)
+        self.ws = em(max(ws, 16), dt=torch.uint8)
+        self.x_sorted = em(N, H)
+        self.h_save = em(N, 2 * F)
+        self.a_save = em(N, F)
+        self.o_sorted = em(N, H)
+        self.y = em(T, H)
+        if rho is not None:
+            cap = moe.moe_quota_cap(T, E, k, rho)
+            self.R = min(N, E * cap)
+            self.kept_counts = em(E, dt=i32)
+            self.kept_offsets = em(E + 1, dt=i32)
+            self.kept_perm = em(self.R, dt=i32)
+            self.kept_src = em(self.R, dt=i32)
+            self.kept_inv = em(N, dt=i32)
+            self.x_kept = em(self.R, H)
+            self.a_kept = em(self.R, F)
+            self.h_kept = em(self.R, 2 * F)
+        else:
+            self.R = N
+        R = self.R
+        self.dO = em(R, H)
+        self.dh = em(R, 2 * F)
+        self.dX = em(R, H)
+        self.dx = em(T, H)
+        self.dg = em(T, k, dt=f32) if dg else None
+        if dw:
+            self.dw_gate = em(E, H, F)
+            self.dw_up = em(E, H, F)
+            self.dw_down = em(E, F, H)
+
+    # ------------------------------------------------------------------ forward
+    def forward(self, logits, x, w_gate, w_up, w_down, stream=None):
+        moe.moe_route_topk(logits, self.topk_idx, self.topk_w, self.k, stream)
+        moe.moe_dispatch(self.topk_idx, x, self.counts, self.offsets, self.perm, self.inv_perm, self.x_sorted,
+                         self.ws, self.E, stream)
+        moe.moe_grouped_swiglu_fwd(self.offsets, self.x_sorted, w_gate, w_up, w_down, self.h_save, self.a_save,
+                                   self.o_sorted, self.N, stream)
+        moe.moe_combine(self.o_sorted, self.inv_perm, self.topk_w, self.y, self.k, stream)
+        return self.y
+
+    # ----------------------------------------------------------------- backward
+    def compact(self, score, stream=None):
+        moe.moe_compact_pairs(self.counts, self.offsets, self.perm, score, self.rho, self.kept_counts,
+                              self.kept_offsets, self.kept_perm, self.kept_src, self.kept_inv, self.T, self.k,
+                              self.x_sorted, self.a_save if self.dw else None, self.h_save, self.x_kept,
+                              self.a_kept if self.dw else None, self.h_kept, stream)
+
+    def backward(self, dy, w_gate, w_up, w_down, score=None, stream=None):
+        """dx (+ dg) and, for full fine-tuning, dW.  With a quota ratio the
+        backward runs on the compacted retained pairs (score defaults to the
+        routing weights)."""
+        if self.rho is not None:
+            self.compact(self.topk_w.view(-1) if score is None else score, stream)
+            offsets, inv, x_rows, a_rows, h_rows = (self.kept_offsets, self.kept_inv, self.x_kept, self.a_kept,
+                                                    self.h_kept)
+        else:
+            offsets, inv, x_rows, a_rows, h_rows = self.offsets, self.inv_perm, self.x_sorted, self.a_save, self.h_save
+        moe.moe_grouped_bwd_dx(offsets, inv, dy, self.topk_w, h_rows, w_gate, w_up, w_down, self.dO, self.dh,
+                               self.dX, self.dx, self.R, inv_all=self.inv_perm if self.want_dg else None,
+                               o_sorted=self.o_sorted if self.want_dg else None, dg=self.dg, stream=stream)
+        if self.dw:
+            moe.moe_grouped_bwd_dw(offsets, x_rows, a_rows, self.dO, self.dh, self.dw_gate, self.dw_up,
+                                   self.dw_down, self.R, stream)
+        return self.dx

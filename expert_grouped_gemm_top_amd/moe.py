@@ -1,0 +1,206 @@
+"""Thin ctypes binding of libmoe (C ABI in include/moe.h), one function per
+entry point with the same name.
+
+Arguments are torch tensors on the GPU (device memory only -- torch is used for
+allocation and streams, never for the computation).  Each wrapper checks device,
+dtype, contiguity and sizes before handing raw pointers to the library, so a
+wrong tensor raises here instead of reaching a kernel.  Every call enqueues on
+``stream`` (default: torch's current stream) and returns without synchronising.
+The library is loaded on first use; if it has not been built the call fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+_STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
+           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
+
+_lib = None
+_vp, _i, _sz, _d, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double, ctypes.c_int64
+
+_SIGS = {
+    "moe_status_string": ([_i], ctypes.c_char_p),
+    "moe_last_error": ([], ctypes.c_char_p),
+    "moe_abi_version": ([], _i),
+    "moe_route_topk": ([_i, _i, _i, _vp, _vp, _vp, _vp], _i),
+    "moe_dispatch_workspace_bytes": ([_i, _i, _i], _sz),
+    "moe_dispatch": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
+    "moe_grouped_swiglu_fwd": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i),
+    "moe_combine": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
+    "moe_grouped_bwd_dx": ([_i, _i, _i, _i, _i, _i, _i] + [_vp] * 16, _i),
+    "moe_grouped_bwd_dw": ([_i, _i, _i, _i, _i] + [_vp] * 9, _i),
+    "moe_quota_cap": ([_i, _i, _i, _d], _i64),
+    "moe_compact_pairs": ([_i, _i, _i, _i, _i, _i, _d] + [_vp] * 16, _i),
+}
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libmoe.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        L = lib()
+        raise MoeError(f"{L.moe_status_string(rc).decode()}: {L.moe_last_error().decode()}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return MOE_F32
+    if x.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise MoeError(f"unsupported dtype {x.dtype}")
+
+
+def _ptr(t, name, dtype=None, numel=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise MoeError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise MoeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise MoeError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+I32, F32 = torch.int32, torch.float32
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
+    return int(lib().moe_dispatch_workspace_bytes(T, E, k))
+
+
+def moe_quota_cap(T: int, E: int, k: int, rho: float) -> int:
+    return int(lib().moe_quota_cap(T, E, k, float(rho)))
+
+
+def moe_route_topk(logits, topk_idx, topk_w, k: int, stream=None):
+    T, E = logits.shape
+    _check(lib().moe_route_topk(T, E, k, _ptr(logits, "logits", F32, T * E),
+                                _ptr(topk_idx, "topk_idx", I32, T * k), _ptr(topk_w, "topk_w", F32, T * k),
+                                _stream(stream)))
+
+
+def moe_dispatch(topk_idx, x, counts, offsets, perm, inv_perm, x_sorted, workspace, E: int, stream=None):
+    T, k = topk_idx.shape
+    H = x.shape[1] if x is not None else 8
+    dt = _dt(x) if x is not None else MOE_BF16
+    N = T * k
+    ws_need = moe_dispatch_workspace_bytes(T, E, k)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().moe_dispatch(T, H, E, k, dt, _ptr(topk_idx, "topk_idx", I32, N),
+                              _ptr(x, "x", None, T * H, allow_none=True), _ptr(counts, "counts", I32, E),
+                              _ptr(offsets, "offsets", I32, E + 1), _ptr(perm, "perm", I32, N),
+                              _ptr(inv_perm, "inv_perm", I32, N),
+                              _ptr(x_sorted, "x_sorted", x.dtype if x is not None else None, N * H, allow_none=True),
+                              _ptr(workspace, "workspace", None, None, allow_none=ws_need == 0), ws_bytes,
+                              _stream(stream)))
+
+
+def moe_grouped_swiglu_fwd(offsets, x_sorted, w_gate, w_up, w_down, h_save, a_save, o_sorted, max_rows: int,
+                           stream=None):
+    E, H, F = w_gate.shape
+    dt, d = _dt(w_gate), w_gate.dtype
+    R = max_rows
+    _check(lib().moe_grouped_swiglu_fwd(
+        H, F, E, R, dt, _ptr(offsets, "offsets", I32, E + 1), _ptr(x_sorted, "x_sorted", d, R * H),
+        _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F), _ptr(w_down, "w_down", d, E * F * H),
+        _ptr(h_save, "h_save", d, R * 2 * F), _ptr(a_save, "a_save", d, R * F), _ptr(o_sorted, "o_sorted", d, R * H),
+        _stream(stream)))
+
+
+def moe_combine(rows, inv, topk_w, out, k: int, stream=None):
+    T, H = out.shape
+    d = out.dtype
+    rows_needed = int(rows.shape[0])
+    _check(lib().moe_combine(T, H, k, _dt(out), _ptr(rows, "rows", d, rows_needed * H), _ptr(inv, "inv", I32, T * k),
+                             _ptr(topk_w, "topk_w", F32, T * k, allow_none=True), _ptr(out, "out", d, T * H),
+                             _stream(stream)))
+
+
+def moe_grouped_bwd_dx(offsets, inv, dy, topk_w, h_rows, w_gate, w_up, w_down, dO_rows, dh_rows, dX_rows, dx,
+                       max_rows: int, inv_all=None, o_sorted=None, dg=None, stream=None):
+    T, H = dy.shape
+    E, _, F = w_gate.shape
+    k = topk_w.shape[1]
+    d = dy.dtype
+    R = max_rows
+    N = T * k
+    _check(lib().moe_grouped_bwd_dx(
+        T, H, F, E, k, R, _dt(dy), _ptr(offsets, "offsets", I32, E + 1), _ptr(inv, "inv", I32, N), _ptr(dy, "dy", d, T * H), _ptr(topk_w, "topk_w", F32, N),
+        _ptr(h_rows, "h_rows", d, R * 2 * F), _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F),
+        _ptr(w_down, "w_down", d, E * F * H), _ptr(inv_all, "inv_all", I32, N, allow_none=dg is None),
+        _ptr(o_sorted, "o_sorted", d, N * H, allow_none=dg is None), _ptr(dg, "dg", F32, N, allow_none=True),
+        _ptr(dO_rows, "dO_rows", d, R * H), _ptr(dh_rows, "dh_rows", d, R * 2 * F), _ptr(dX_rows, "dX_rows", d, R * H),
+        _ptr(dx, "dx", d, T * H), _stream(stream)))
+
+
+def moe_grouped_bwd_dw(offsets, x_rows, a_rows, dO_rows, dh_rows, dw_gate, dw_up, dw_down, max_rows: int, stream=None):
+    E, H, F = dw_gate.shape
+    d = dw_gate.dtype
+    R = max_rows
+    _check(lib().moe_grouped_bwd_dw(
+        H, F, E, R, _dt(dw_gate), _ptr(offsets, "offsets", I32, E + 1), _ptr(x_rows, "x_rows", d, R * H),
+        _ptr(a_rows, "a_rows", d, R * F), _ptr(dO_rows, "dO_rows", d, R * H), _ptr(dh_rows, "dh_rows", d, R * 2 * F),
+        _ptr(dw_gate, "dw_gate", d, E * H * F), _ptr(dw_up, "dw_up", d, E * H * F),
+        _ptr(dw_down, "dw_down", d, E * F * H), _stream(stream)))
+
+
+def moe_compact_pairs(counts, offsets, perm, score, rho: float, kept_counts, kept_offsets, kept_perm, kept_src,
+                      kept_inv, T: int, k: int, x_sorted=None, a_save=None, h_save=None, x_kept=None, a_kept=None,
+                      h_kept=None, stream=None):
+    E = counts.shape[0]
+    N = T * k
+    ref = next((t for t in (x_sorted, a_save, h_save) if t is not None), None)
+    d = ref.dtype if ref is not None else torch.bfloat16
+    H = x_sorted.shape[1] if x_sorted is not None else 8
+    F = a_save.shape[1] if a_save is not None else (h_save.shape[1] // 2 if h_save is not None else 8)
+    cap = moe_quota_cap(T, E, k, rho)
+    R = min(N, E * cap) if cap > 0 else 0
+    _check(lib().moe_compact_pairs(
+        T, H, F, E, k, MOE_F32 if d == torch.float32 else MOE_BF16, float(rho), _ptr(counts, "counts", I32, E),
+        _ptr(offsets, "offsets", I32, E + 1), _ptr(perm, "perm", I32, N), _ptr(score, "score", F32, N),
+        _ptr(kept_counts, "kept_counts", I32, E), _ptr(kept_offsets, "kept_offsets", I32, E + 1),
+        _ptr(kept_perm, "kept_perm", I32, R), _ptr(kept_src, "kept_src", I32, R), _ptr(kept_inv, "kept_inv", I32, N),
+        _ptr(x_sorted, "x_sorted", d, N * H, allow_none=True), _ptr(a_save, "a_save", d, N * F, allow_none=True),
+        _ptr(h_save, "h_save", d, N * 2 * F, allow_none=True),
+        _ptr(x_kept, "x_kept", d, R * H, allow_none=x_sorted is None),
+        _ptr(a_kept, "a_kept", d, R * F, allow_none=a_save is None),
+        _ptr(h_kept, "h_kept", d, R * 2 * F, allow_none=h_save is None), _stream(stream)))

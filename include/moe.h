@@ -1,0 +1,211 @@
+/*
+ * moe.h -- C ABI of libmoe: one MoE layer's expert computation in training on
+ * one AMD Instinct MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * The path (pages: npu-train issue #14 "[MoE] Hot experts on RNGD during
+ * training (host dispatch, device expert graphs)", sections Evidence, Proposal
+ * and Scope; npu-train pull request #44, section Changes; LRMoE,
+ * arXiv:2610.37720, abstract):
+ *
+ *   moe_route_topk          router logits -> top-k experts and weights per token
+ *   moe_dispatch            token-expert pairs -> rows contiguous per expert
+ *   moe_grouped_swiglu_fwd  SwiGLU expert MLP over every expert's rows (ragged
+ *                           grouped GEMM); keeps the activations backward needs
+ *   moe_combine             router-weighted sum of each token's expert rows
+ *   moe_compact_pairs       keep at most a quota of pairs per expert and gather
+ *                           their rows into smaller contiguous buffers
+ *   moe_grouped_bwd_dx      input gradient (experts frozen) + routing-weight
+ *                           gradient, over all or only the retained pairs
+ *   moe_grouped_bwd_dw      expert weight gradients (full fine-tuning)
+ *
+ * Conventions for every call:
+ *  - Pointers marked (device) are device pointers owned by the caller; the
+ *    library allocates no memory and keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  A call only
+ *    enqueues work on it: no device synchronisation, no device-to-host copy.
+ *    Data-dependent sizes (row counts, offsets, the retained total) stay on the
+ *    device; the host passes capacities only.
+ *  - Arguments are validated before anything is enqueued; on any error nothing
+ *    is enqueued and the status says why (moe_last_error() has the detail).
+ *  - dtype: MOE_F32 or MOE_BF16 for activations and weights (all of one call
+ *    are of that dtype); logits, routing weights, scores and dg are always
+ *    fp32; indices int32.  Accumulation is fp32; bf16 results are rounded to
+ *    nearest even once, at the store.
+ *  - Layouts are row-major.  Pair id p = t*k + j (token t, slot j of its top-k).
+ *    Expert weights: W_gate and W_up [E, H, F], W_down [E, F, H].
+ *  - Limits: 1 <= k <= E <= 256, k <= 16, T*k < 2^31.  bf16: H and F multiples
+ *    of 128.  fp32: H and F multiples of 8.
+ *  - Results are deterministic: the same inputs on the same GPU give bitwise
+ *    identical outputs (no order-dependent atomics).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, k > E, ... */
+  MOE_ERR_UNSUPPORTED = 2,        /* outside the limits above */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a HIP launch failed; see moe_last_error() */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+/* ABI version, currently 1. */
+int moe_abi_version(void);
+
+/* Kernels that moe_profile_kernel can bracket with events. */
+typedef enum moe_kernel {
+  MOE_K_ROUTE = 0,         /* moe_route_topk */
+  MOE_K_DISPATCH_ROWS = 1, /* the row copy of moe_dispatch */
+  MOE_K_GEMM_GATEUP = 2,   /* gate/up GEMM + SwiGLU of moe_grouped_swiglu_fwd */
+  MOE_K_GEMM_DOWN = 3,     /* down GEMM of moe_grouped_swiglu_fwd */
+  MOE_K_COMBINE = 4,       /* moe_combine, and the dx sum of moe_grouped_bwd_dx */
+  MOE_K_GRAD_ROWS = 5,     /* dO rows and dg of moe_grouped_bwd_dx */
+  MOE_K_GEMM_DA = 6,       /* dA GEMM + SwiGLU backward of moe_grouped_bwd_dx */
+  MOE_K_GEMM_DX = 7,       /* dX GEMM of moe_grouped_bwd_dx */
+  MOE_K_GEMM_DW = 8,       /* moe_grouped_bwd_dw */
+  MOE_K_COMPACT = 9,       /* the selection kernel of moe_compact_pairs */
+  MOE_K_COUNT = 10
+} moe_kernel;
+
+/* Profiling hook.  Arms a one-shot request on the calling thread: the next
+ * launch of `kernel` made from this thread records `start_event` on its stream
+ * immediately before the launch and `stop_event` immediately after, so
+ * hipEventElapsedTime(start, stop) is that kernel's duration.  Both events are
+ * hipEvent_t created by the caller; NULL events disarm.  Several kernels may be
+ * armed at once.  Results of the calls are unaffected. */
+int moe_profile_kernel(int kernel, void* start_event, void* stop_event);
+
+/* Top-k routing (issue #14, Evidence and Proposal: each token is routed to k
+ * of E experts).  For token t the experts are ranked by logit descending, equal
+ * logits by lower expert index; topk_idx[t, 0..k) lists the first k in that
+ * order.  The weights are the softmax over the k selected logits,
+ *   topk_w[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+ * logits [T, E] fp32 (device, finite); topk_idx [T, k] int32 (device, out);
+ * topk_w [T, k] fp32 (device, out). */
+int moe_route_topk(int T, int E, int k, const float* logits, int32_t* topk_idx, float* topk_w,
+                   void* stream);
+
+/* Workspace bytes moe_dispatch needs for T tokens, E experts, top-k. */
+size_t moe_dispatch_workspace_bytes(int T, int E, int k);
+
+/* Dispatch (issue #14, Proposal: rows gathered per expert; here on the GPU).
+ * A stable counting sort of the N = T*k pairs by expert:
+ *   counts[e]   pairs routed to expert e;  offsets = exclusive scan, offsets[E] = N
+ *   perm[s]     pair id at sorted position s, ascending p within each expert
+ *   inv_perm[p] sorted position of pair p
+ *   x_sorted[s] = x[perm[s] / k]  (exact copy; skipped when x_sorted is NULL)
+ * topk_idx [T, k] int32 (device, values in [0, E)); x [T, H] (device);
+ * counts [E], offsets [E+1], perm [N], inv_perm [N] int32 (device, out);
+ * x_sorted [N, H] (device, out, may be NULL together with x);
+ * workspace (device) of at least moe_dispatch_workspace_bytes(T, E, k). */
+int moe_dispatch(int T, int H, int E, int k, int dtype, const int32_t* topk_idx, const void* x,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_sorted,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* SwiGLU expert forward as a ragged grouped GEMM (issue #14, Proposal: expert
+ * forward graphs; pull request #44, Changes: forward keeps the activations that
+ * backward reuses).  For each expert e, over its rows s in
+ * [offsets[e], offsets[e+1]):
+ *   hg = x_sorted[s] W_gate[e],  hu = x_sorted[s] W_up[e]        (length F)
+ *   a  = silu(hg) * hu,  silu(z) = z / (1 + exp(-z))
+ *   o_sorted[s] = a W_down[e]                                      (length H)
+ * h_save[s] = [hg | hu] ([rows, 2F]) and a_save[s] = a ([rows, F]) are kept for
+ * backward.  offsets [E+1] int32 (device); max_rows >= offsets[E] is a host
+ * capacity (T*k) used only to size the launch; x_sorted [rows, H],
+ * w_gate/w_up [E, H, F], w_down [E, F, H] (device); h_save, a_save, o_sorted
+ * (device, out).  Rows of empty experts: nothing. */
+int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int dtype, const int32_t* offsets,
+                           const void* x_sorted, const void* w_gate, const void* w_up,
+                           const void* w_down, void* h_save, void* a_save, void* o_sorted,
+                           void* stream);
+
+/* Router-weighted combine (issue #14, Proposal: results scattered back):
+ *   out[t] = sum_{j = 0..k-1, inv[t*k+j] >= 0} w[t,j] * rows[inv[t*k+j]]
+ * accumulated in fp32 in ascending j and rounded once.  With topk_w == NULL the
+ * weight is 1 (this sums expert input-gradients into dx).  rows [*, H]
+ * (device); inv [T*k] int32 (device; -1 skips the pair); topk_w [T, k] fp32
+ * (device) or NULL; out [T, H] (device, out). */
+int moe_combine(int T, int H, int k, int dtype, const void* rows, const int32_t* inv,
+                const float* topk_w, void* out, void* stream);
+
+/* Backward dx with routing held fixed (issue #14, Proposal and Scope: expert
+ * backward dx, LoRA with frozen experts; LRMoE abstract: backward over the
+ * retained, compacted pairs only).  Rows are either all pairs (offsets, inv
+ * from moe_dispatch; h_rows = h_save) or the retained ones (kept_offsets,
+ * kept_inv from moe_compact_pairs; h_rows = h_kept).  For each pair p with
+ * r = inv[p] >= 0 (t = p / k):
+ *   dO_rows[r]  = w[p] * dy[t]                                      [R, H]
+ *   dA          = dO_rows[r] W_down[e]^T                             (length F)
+ *   dh_rows[r]  = [dHg | dHu],  s = sigmoid(hg):                     [R, 2F]
+ *                 dHg = dA * hu * s * (1 + hg * (1 - s)),  dHu = dA * hg * s
+ *   dX_rows[r]  = dHg W_gate[e]^T + dHu W_up[e]^T                    [R, H]
+ *   dx[t]       = sum_{j ascending, inv[t*k+j] >= 0} dX_rows[inv[t*k+j]]
+ * and, when dg != NULL, for every pair (retained or not)
+ *   dg[p] = <dy[p / k], o_sorted[inv_all[p]]>  (fp32).
+ * offsets [E+1], inv [T*k] int32 (device; every row r < offsets[E] is the
+ * image of exactly one pair); dy [T, H];
+ * topk_w [T, k] fp32; h_rows [max_rows, 2F]; weights as in the forward;
+ * inv_all [T*k] and o_sorted [T*k, H] (device, only read when dg != NULL);
+ * dO_rows, dh_rows, dX_rows [max_rows, *], dx [T, H] (device, out). */
+int moe_grouped_bwd_dx(int T, int H, int F, int E, int k, int max_rows, int dtype,
+                       const int32_t* offsets, const int32_t* inv,
+                       const void* dy, const float* topk_w, const void* h_rows, const void* w_gate,
+                       const void* w_up, const void* w_down, const int32_t* inv_all,
+                       const void* o_sorted, float* dg, void* dO_rows, void* dh_rows,
+                       void* dX_rows, void* dx, void* stream);
+
+/* Expert weight gradients (issue #14, Scope: dW for full fine-tuning), over the
+ * rows r of each expert e (all pairs or the retained ones):
+ *   dW_gate[e] = sum_r x_rows[r]^T dHg[r],  dW_up[e] = sum_r x_rows[r]^T dHu[r]
+ *   dW_down[e] = sum_r a_rows[r]^T dO_rows[r]
+ * in fp32, rounded once to the weight dtype; overwritten, not accumulated; an
+ * expert without rows gets exact zeros.  offsets [E+1] int32 (device);
+ * x_rows [*, H], a_rows [*, F], dO_rows [*, H], dh_rows [*, 2F] (device);
+ * dw_gate, dw_up [E, H, F], dw_down [E, F, H] (device, out). */
+int moe_grouped_bwd_dw(int H, int F, int E, int max_rows, int dtype, const int32_t* offsets,
+                       const void* x_rows, const void* a_rows, const void* dO_rows,
+                       const void* dh_rows, void* dw_gate, void* dw_up, void* dw_down,
+                       void* stream);
+
+/* Quota cap used by moe_compact_pairs: ceil(rho * T * k / E) (integer
+ * arithmetic when rho == 1, else evaluated in double).  Host-only. */
+int64_t moe_quota_cap(int T, int E, int k, double rho);
+
+/* Selection within retention quotas and physical compaction (LRMoE abstract:
+ * quotas, a per-pair score, selection within quotas, compaction into smaller
+ * buffers for variable-size grouped GEMMs).  Expert e keeps its
+ * q_e = min(counts[e], moe_quota_cap(T, E, k, rho)) pairs of largest score,
+ * equal scores to the lower pair id; kept pairs stay in ascending pair id.
+ *   kept_counts[e] = q_e, kept_offsets = exclusive scan (kept_offsets[E] = R)
+ *   kept_perm[r] pair id, kept_src[r] its position in the uncompacted order,
+ *   kept_inv[p] compacted position or -1 when dropped
+ *   x_kept[r] = x_sorted[kept_src[r]], a_kept[r] = a_save[..], h_kept[r] = h_save[..]
+ * The row gathers are skipped for NULL sources.  counts [E], offsets [E+1],
+ * perm [T*k] int32 and score [T*k] fp32 (device, pair-indexed, finite);
+ * kept_* int32 (device, out; kept_perm and kept_src hold T*k entries of which
+ * the first R are written). */
+int moe_compact_pairs(int T, int H, int F, int E, int k, int dtype, double rho,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                      const float* score, int32_t* kept_counts, int32_t* kept_offsets,
+                      int32_t* kept_perm, int32_t* kept_src, int32_t* kept_inv,
+                      const void* x_sorted, const void* a_save, const void* h_save, void* x_kept,
+                      void* a_kept, void* h_kept, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,135 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and the CPU oracle on the same seeded inputs, and compare.
+
+The oracle computes in double from the same fp32 / bf16-exact inputs; the GPU
+path is compared element by element with max|gpu - ref| / max|ref| per tensor
+(bit-exact for every index output).  For the full-size layers the oracle runs
+on sampled tokens (all experts those tokens use) and on sampled weight-gradient
+entries, restricted to the experts involved so its inputs stay small.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from expert_grouped_gemm_top_amd import workloads as W
+from expert_grouped_gemm_top_amd.layer import MoeLayerBuffers
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def note(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), "non-finite values"
+    den = np.abs(ref).max()
+    num = np.abs(got - ref).max()
+    return num / den if den > 0 else num
+
+
+def assert_close(name, got, ref, tol):
+    e = rel_err(got, ref)
+    assert e <= tol, f"{name}: max|err|/max|ref| = {e:.3e} > {tol:.0e}"
+    return e
+
+
+def np32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def logits_of(wl, d):
+    """Router logits as fp32: drawn (most layers) or x @ W_r (tiny fp32 layer,
+    evaluated by the oracle in double and rounded once)."""
+    if wl.router == "wr":
+        return oracle.router_logits(d["x"], d["W_r"]).astype(np.float32)
+    return d["logits"]
+
+
+def to_dev(wl, d, dev="cuda"):
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    return {n: torch.from_numpy(np.ascontiguousarray(d[n])).to(dev).to(dt) for n in ("x", "W_gate", "W_up", "W_down", "dy")}
+
+
+def run_gpu(wl, d, logits, rho=None, score=None, dw=None, dg=True):
+    note(f"gpu run {wl.name} T={wl.T} H={wl.H} F={wl.F} E={wl.E} k={wl.k} {wl.dtype} rho={rho}")
+    t = to_dev(wl, d)
+    dt = t["x"].dtype
+    L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, dt, "cuda", rho=rho, dw=wl.dw if dw is None else dw, dg=dg)
+    L.forward(torch.from_numpy(np.ascontiguousarray(logits)).cuda(), t["x"], t["W_gate"], t["W_up"], t["W_down"])
+    sc = None if score is None else torch.from_numpy(np.ascontiguousarray(score, dtype=np.float32)).cuda()
+    L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], score=sc)
+    torch.cuda.synchronize()
+    note("gpu run done")
+    return L
+
+
+def subset(idx, tokens):
+    """Experts used by `tokens`, and idx with those experts renumbered 0..n-1
+    (other experts -> n, a placeholder the oracle never evaluates)."""
+    ex = np.unique(idx[tokens])
+    remap = np.full(idx.max() + 2, len(ex), np.int32)
+    remap[ex] = np.arange(len(ex), dtype=np.int32)
+    return ex, remap[idx]
+
+
+def oracle_tokens(wl, d, idx, w, tokens, retained=None):
+    """y, dx, dg and pair intermediates for the sampled tokens, with only the
+    experts they use."""
+    ex, idx_s = subset(idx, tokens)
+    Wg, Wu, Wd = (d[n][ex] for n in ("W_gate", "W_up", "W_down"))
+    y, it = oracle.forward(d["x"], idx_s, w, Wg, Wu, Wd, tokens=tokens, intermediates=True)
+    dx, dg, bt = oracle.backward(d["x"], idx_s, w, Wg, Wu, Wd, d["dy"], retained=retained, tokens=tokens,
+                                 intermediates=True)
+    return y, dx, dg, it, bt
+
+
+def oracle_dw_sample(wl, d, idx, w, queries, retained=None):
+    """queries: list of (e, mat, r, c); returns the oracle's entries."""
+    es = sorted({q[0] for q in queries})
+    remap = np.full(wl.E + 1, len(es), np.int32)
+    remap[es] = np.arange(len(es), dtype=np.int32)
+    idx_s = remap[idx]
+    Wg, Wu, Wd = (d[n][es] for n in ("W_gate", "W_up", "W_down"))
+    qe, qm, qr, qc = (np.array(v) for v in zip(*queries))
+    return oracle.dw_entries(d["x"], idx_s, w, Wg, Wu, Wd, d["dy"], remap[qe], qm, qr, qc, retained=retained)
+
+
+def dw_queries(wl, counts, rng, n_per=16, experts=None):
+    """Sampled (e, mat, r, c): the hottest expert, a median one, an empty one
+    (if any) and random others."""
+    order = np.argsort(-counts, kind="stable")
+    picks = [int(order[0]), int(order[len(order) // 2])]
+    empty = np.nonzero(counts == 0)[0]
+    if len(empty):
+        picks.append(int(empty[0]))
+    if experts is not None:
+        picks = list(experts)
+    picks += [int(e) for e in rng.choice(wl.E, 2, replace=False)]
+    q = []
+    for e in dict.fromkeys(picks):
+        for m in (0, 1, 2):
+            rows, cols = (wl.H, wl.F) if m < 2 else (wl.F, wl.H)
+            for _ in range(n_per):
+                q.append((e, m, int(rng.integers(rows)), int(rng.integers(cols))))
+    return q
+
+
+def gpu_dw_entries(L, queries):
+    mats = (L.dw_gate, L.dw_up, L.dw_down)
+    out = []
+    for m in range(3):
+        sel = [(i, q) for i, q in enumerate(queries) if q[1] == m]
+        if not sel:
+            continue
+        e, r, c = (torch.tensor([q[j] for _, q in sel], device=mats[m].device) for j in (0, 2, 3))
+        vals = mats[m][e, r, c].float().cpu().numpy()
+        out += [(i, v) for (i, _), v in zip(sel, vals)]
+    return np.array([v for _, v in sorted(out)])
