@@ -77,8 +77,8 @@ __device__ __forceinline__ int block256_exclusive_scan(int v, int* s_tmp, int& t
 // ---- ragged per-expert tile schedule ---------------------------------------
 // Given device offsets[0..E] (rows of expert e are [offsets[e], offsets[e+1])),
 // every workgroup derives the prefix of per-expert tile counts ceil(n_e / rows)
-// itself and finds the (expert, tile) that its linear tile id falls on.  No
-// host synchronisation and no padding of experts to a fixed bucket.
+// itself and finds the (expert, tile) that a linear tile id falls on.  No host
+// synchronisation and no padding of experts to a fixed bucket.
 struct TileSlot {
   int expert;      // -1 when the id is past the last real tile
   int tile;        // tile index within the expert
@@ -87,10 +87,11 @@ struct TileSlot {
   int expert_rows; // n_e
 };
 
-// s_start: kMaxExperts + 1 ints, s_off: kMaxExperts + 1 ints, s_tmp: 4 ints.
+// Block-level part: s_start[e] = first tile id of expert e, s_start[E] = total;
+// s_off = offsets.  s_start and s_off need kMaxExperts + 1 ints, s_tmp 4 ints.
 // Must be called by all 256 threads of the block.
-__device__ __forceinline__ TileSlot find_row_tile(const int32_t* __restrict__ offsets, int E, int tile_rows,
-                                                  int tile_id, int* s_start, int* s_off, int* s_tmp) {
+__device__ __forceinline__ void build_tile_starts(const int32_t* __restrict__ offsets, int E, int tile_rows,
+                                                  int* s_start, int* s_off, int* s_tmp) {
   const int tid = threadIdx.x;
   if (tid <= E) s_off[tid] = offsets[tid];
   __syncthreads();
@@ -101,13 +102,17 @@ __device__ __forceinline__ TileSlot find_row_tile(const int32_t* __restrict__ of
   if (tid < E) s_start[tid] = start;
   if (tid == 0) s_start[E] = total;
   __syncthreads();
+}
+
+// Per-thread part: the slot of `tile_id` (binary search over s_start).
+__device__ __forceinline__ TileSlot lookup_tile(const int* s_start, const int* s_off, int E, int tile_rows,
+                                                int tile_id) {
   TileSlot s;
-  if (tile_id >= total) {
+  if (tile_id >= s_start[E]) {
     s.expert = -1;
     s.tile = s.row_begin = s.rows = s.expert_rows = 0;
     return s;
   }
-  // largest e with s_start[e] <= tile_id; that expert has at least one tile
   int lo = 0, hi = E;  // invariant: s_start[lo] <= tile_id < s_start[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;

@@ -40,8 +40,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kTileRows = 32;  // rows of one expert per workgroup tile
-constexpr int kRedPitch = 132; // fp32 pitch of the LDS reduction tile (128 + 4)
+constexpr int kTileRows = 16;  // rows of one expert per wave tile (one MFMA row block)
 
 // ---- register transposes of bf16 blocks -------------------------------------
 // rows[r] holds 8 bf16 (columns 0..7) of row r; returns the 8 k-values (rows
@@ -79,9 +78,13 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 first, u32x4 second, f32x4 acc)
 }
 
 // ---- row GEMMs --------------------------------------------------------------
+// N-contiguous weights (GATEUP, DOWN): a wave covers 128 output columns; per
+// K-step of 32 a lane loads 8 rows x 16 B, so one load instruction reads 4 rows
+// x 256 contiguous bytes.  K-contiguous weights (DA, DX): a wave covers 64
+// output columns; per K-stage of 128 a lane loads 4 consecutive 16 B chunks of
+// each of its 4 weight rows, so every row is read in 256-byte runs.
 template <int MODE>
 struct RowGemmShape;
-// K (reduced length), columns per block, whether the weights are N-contiguous
 template <>
 struct RowGemmShape<kGemmGateUp> { static constexpr bool kNN = true; };
 template <>
@@ -92,135 +95,183 @@ template <>
 struct RowGemmShape<kGemmDX> { static constexpr bool kNN = false; };
 
 template <int MODE>
-__device__ __forceinline__ int row_gemm_K(const RowGemmArgs& g) {
-  return (MODE == kGemmGateUp || MODE == kGemmDA) ? g.H : (MODE == kGemmDown ? g.F : 2 * g.F);
+__host__ __device__ constexpr int row_gemm_cols() { return RowGemmShape<MODE>::kNN ? 128 : 64; }
+
+// column blocks of one expert tile
+template <int MODE>
+__host__ __device__ inline int row_gemm_blocks(int H, int F) {
+  return MODE == kGemmGateUp ? (2 * F) / 128 : (MODE == kGemmDown ? H / 128 : (MODE == kGemmDA ? F / 64 : H / 64));
 }
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g) {
   constexpr bool NN = RowGemmShape<MODE>::kNN;
   __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
-  __shared__ float s_red[4][kTileRows][kRedPitch];
+  build_tile_starts(g.offsets, g.E, kTileRows, s_start, s_off, s_tmp);
 
-  const TileSlot ts = find_row_tile(g.offsets, g.E, kTileRows, blockIdx.x, s_start, s_off, s_tmp);
-  if (ts.expert < 0) return;  // uniform across the workgroup
-  const int e = ts.expert;
-  const int nb = blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
   const int H = g.H, F = g.F;
-  const int K = row_gemm_K<MODE>(g);
-  const int Kq = K / 4;
-  const int k_begin = w * Kq;
-  const int steps = Kq / 32;
-  const int ms = (ts.rows + 15) >> 4;  // 16-row sub-tiles with real rows: 1 or 2
+  const int nblk = row_gemm_blocks<MODE>(H, F);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
+  // work item of this wave: (tile, column block); the four waves of a workgroup
+  // take adjacent column blocks of the same tile
+  const int item = blockIdx.x * 4 + w;
+  const TileSlot ts = lookup_tile(s_start, s_off, g.E, kTileRows, item / nblk);
+  if (ts.expert < 0) return;  // uniform across the wave; no block barrier follows
+  const int nb = item % nblk;
+  const int e = ts.expert;
+  const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? H : (MODE == kGemmDown ? F : 2 * F);
 
+  const bool a_ok = c < ts.rows;
   const uint16_t* __restrict__ A = (const uint16_t*)g.a;
-  const uint16_t* a_ptr[2];
-  bool a_ok[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = 16 * i + c;
-    a_ok[i] = m < ts.rows;
-    a_ptr[i] = A + (size_t)(ts.row_begin + (a_ok[i] ? m : 0)) * K + k_begin + 8 * gq;
-  }
+  // rows past the tile read the tile's last row (always valid) and are zeroed at use
+  const uint16_t* a_row = A + (size_t)(ts.row_begin + (a_ok ? c : ts.rows - 1)) * K;
 
-  // B operand base pointer and strides
-  const uint16_t* b_ptr;
-  size_t b_step;  // elements per K-step of 32
-  size_t b_sub;   // NN: elements between the 8 rows a lane loads; NT: between the 8 columns
-  if (MODE == kGemmGateUp) {
-    const uint16_t* W = (c < 8) ? g.w0 : g.w1;
-    b_ptr = W + (size_t)e * H * F + (size_t)(k_begin + 8 * gq) * F + nb * 64 + 8 * (c & 7);
-    b_step = (size_t)32 * F;
-    b_sub = F;
-  } else if (MODE == kGemmDown) {
-    b_ptr = g.w0 + (size_t)e * F * H + (size_t)(k_begin + 8 * gq) * H + nb * 128 + 8 * c;
-    b_step = (size_t)32 * H;
-    b_sub = H;
-  } else if (MODE == kGemmDA) {
-    b_ptr = g.w0 + (size_t)e * F * H + (size_t)(nb * 128 + 8 * c) * H + k_begin + 8 * gq;
-    b_step = 32;
-    b_sub = H;
-  } else {  // DX: waves 0,1 reduce over dHg (W_gate), waves 2,3 over dHu (W_up)
-    const uint16_t* W = (w < 2) ? g.w0 : g.w1;
-    const int kloc = k_begin - ((w < 2) ? 0 : F);
-    b_ptr = W + (size_t)e * H * F + (size_t)(nb * 128 + 8 * c) * F + kloc + 8 * gq;
-    b_step = 32;
-    b_sub = F;
-  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  f32x4 acc[2][8];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto load = [&](int s, u32x4* bq, u32x4* aq) {
-    const uint16_t* bp = b_ptr + (size_t)s * b_step;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) bq[r] = *(const u32x4*)(bp + (size_t)r * b_sub);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) aq[i] = a_ok[i] ? *(const u32x4*)(a_ptr[i] + (size_t)s * 32) : u32x4{0u, 0u, 0u, 0u};
-  };
-  auto compute = [&](const u32x4* bq, const u32x4* aq) {
-    u32x4 bf[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) bf[jj] = NN ? column_of_8x8(bq, jj) : bq[jj];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc[0][jj] = mfma_bf16(bf[jj], aq[0], acc[0][jj]);
-    if (ms > 1) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) acc[1][jj] = mfma_bf16(bf[jj], aq[1], acc[1][jj]);
+  if constexpr (NN) {
+    // B operand: lane c reads columns [col, col+8) of rows k0 + 8gq + (0..7)
+    const uint16_t* b_ptr;
+    size_t ldb;
+    if (MODE == kGemmGateUp) {
+      // even lanes read W_gate, odd lanes W_up, at the same 8 features f
+      const uint16_t* W = (c & 1) ? g.w1 : g.w0;
+      b_ptr = W + (size_t)e * H * F + nb * 64 + 8 * (c >> 1);
+      ldb = F;
+    } else {
+      b_ptr = g.w0 + (size_t)e * F * H + nb * 128 + 8 * c;
+      ldb = H;
     }
-  };
-
-  u32x4 bA[8], aA[2], bB[8], aB[2];
-  load(0, bA, aA);
-  int s = 0;
-  for (; s + 2 <= steps; s += 2) {
-    load(s + 1, bB, aB);
-    compute(bA, aA);
-    if (s + 2 < steps) load(s + 2, bA, aA);
-    compute(bB, aB);
-  }
-  if (s < steps) compute(bA, aA);
-
-  // partial tiles -> LDS: lane (c, gq) holds row 16i + c, columns 32gq + 8r + jj
+    b_ptr += (size_t)(8 * gq) * ldb;
+    const uint16_t* a_ptr = a_row + 8 * gq;
+    const int steps = K / 32, last = steps - 1;
+    auto load = [&](int s, u32x4* bq, u32x4& aq) {
+      const uint16_t* bp = b_ptr + (size_t)s * 32 * ldb;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int r = 0; r < 8; ++r) bq[r] = *(const u32x4*)(bp + (size_t)r * ldb);
+      aq = *(const u32x4*)(a_ptr + (size_t)s * 32);
+    };
+    auto compute = [&](const u32x4* bq, const u32x4& aq) {
+      const u32x4 av = a_ok ? aq : zero4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float* dst = &s_red[w][16 * i + c][32 * gq + 8 * r];
-      *(f32x4*)dst = f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
-      *(f32x4*)(dst + 4) = f32x4{acc[i][4][r], acc[i][5][r], acc[i][6][r], acc[i][7][r]};
+      for (int jj = 0; jj < 8; ++jj) acc[jj] = mfma_bf16(column_of_8x8(bq, jj), av, acc[jj]);
+    };
+    u32x4 b0[8], b1[8], b2[8], a0, a1, a2;
+    load(0, b0, a0);
+    load(min(1, last), b1, a1);
+    for (int s = 0; s < steps; s += 3) {
+      load(min(s + 2, last), b2, a2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(s + 3, last), b0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < steps) compute(b1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(s + 4, last), b1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 2 < steps) compute(b2, a2);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  __syncthreads();
-
-  // epilogue: thread -> one row, 16 (or 8+8) columns of the block
-  const int row = tid >> 3, q = tid & 7;
-  if (row >= ts.rows) return;
-  const size_t grow = (size_t)ts.row_begin + row;
-  if (MODE == kGemmGateUp) {
-    float hg[8], hu[8], av[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      hg[i] = s_red[0][row][8 * q + i] + s_red[1][row][8 * q + i] + s_red[2][row][8 * q + i] + s_red[3][row][8 * q + i];
-      hu[i] = s_red[0][row][64 + 8 * q + i] + s_red[1][row][64 + 8 * q + i] + s_red[2][row][64 + 8 * q + i] +
-              s_red[3][row][64 + 8 * q + i];
-      av[i] = hg[i] * sigmoidf_fast(hg[i]) * hu[i];
-    }
-    const int f = nb * 64 + 8 * q;
-    uint16_t* hrow = g.out0 + grow * 2 * F;
-    *(u32x4*)(hrow + f) = u32x4{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3]), pack_bf2(hg[4], hg[5]), pack_bf2(hg[6], hg[7])};
-    *(u32x4*)(hrow + F + f) = u32x4{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3]), pack_bf2(hu[4], hu[5]), pack_bf2(hu[6], hu[7])};
-    *(u32x4*)(g.out1 + grow * F + f) =
-        u32x4{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3]), pack_bf2(av[4], av[5]), pack_bf2(av[6], av[7])};
   } else {
+    // B operand: weight rows n = col0 + 4c + jj (jj = 0..3), k chunks
+    // k0 + 32gq + 8q (q = 0..3) -- 64 contiguous bytes per lane and row
+    const uint16_t* w_lo;  // rows for k in [0, Kw)
+    const uint16_t* w_hi;  // DX only: rows for k in [F, 2F)
+    size_t ldw;
+    int Kw;
+    if (MODE == kGemmDA) {
+      w_lo = g.w0 + (size_t)e * F * H + (size_t)(nb * 64 + 4 * c) * H;
+      w_hi = w_lo;
+      ldw = H;
+      Kw = K;
+    } else {
+      w_lo = g.w0 + (size_t)e * H * F + (size_t)(nb * 64 + 4 * c) * F;
+      w_hi = g.w1 + (size_t)e * H * F + (size_t)(nb * 64 + 4 * c) * F;
+      ldw = F;
+      Kw = F;
+    }
+    const uint16_t* a_ptr = a_row + 32 * gq;
+    const int stages = K / 128, last = stages - 1;
+    auto load = [&](int s, u32x4* bq, u32x4* aq) {
+      const int k0 = s * 128;
+      const uint16_t* wp = (k0 < Kw) ? w_lo + k0 : w_hi + (k0 - Kw);
+      wp += 32 * gq;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bq[4 * jj + q] = *(const u32x4*)(wp + (size_t)jj * ldw + 8 * q);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) aq[q] = *(const u32x4*)(a_ptr + (size_t)k0 + 8 * q);
+    };
+    auto compute = [&](const u32x4* bq, const u32x4* aq) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 av = a_ok ? aq[q] : zero4;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[jj] = mfma_bf16(bq[4 * jj + q], av, acc[jj]);
+      }
+    };
+    u32x4 b0[16], b1[16], a0[4], a1[4];
+    load(0, b0, a0);
+    for (int s = 0; s < stages; s += 2) {
+      load(min(s + 1, last), b1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(s + 2, last), b0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < stages) compute(b1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // epilogue straight from registers: lane (c, gq) owns tile row c
+  if (!a_ok) return;
+  const size_t grow = (size_t)ts.row_begin + c;
+  if (MODE == kGemmGateUp) {
+    // MFMA jj, register r: gate (r even) / up (r odd) of feature
+    // f = 64 nb + 16 gq + 8 (r >> 1) + jj
+    float hg[16], hu[16], av[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        hg[8 * h + jj] = acc[jj][2 * h];
+        hu[8 * h + jj] = acc[jj][2 * h + 1];
+      }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) av[i] = hg[i] * sigmoidf_fast(hg[i]) * hu[i];
+    const int f = nb * 64 + 16 * gq;
+    uint16_t* hrow = g.out0 + grow * 2 * F;
+    uint16_t* arow = g.out1 + grow * F;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* G = hg + 8 * h;
+      const float* U = hu + 8 * h;
+      const float* V = av + 8 * h;
+      *(u32x4*)(hrow + f + 8 * h) = u32x4{pack_bf2(G[0], G[1]), pack_bf2(G[2], G[3]), pack_bf2(G[4], G[5]), pack_bf2(G[6], G[7])};
+      *(u32x4*)(hrow + F + f + 8 * h) =
+          u32x4{pack_bf2(U[0], U[1]), pack_bf2(U[2], U[3]), pack_bf2(U[4], U[5]), pack_bf2(U[6], U[7])};
+      *(u32x4*)(arow + f + 8 * h) = u32x4{pack_bf2(V[0], V[1]), pack_bf2(V[2], V[3]), pack_bf2(V[4], V[5]), pack_bf2(V[6], V[7])};
+    }
+  } else if (MODE == kGemmDown) {
+    // MFMA jj, register r: column 128 nb + 32 gq + 8 r + jj
+    uint16_t* orow = g.out0 + grow * H + nb * 128 + 32 * gq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *(u32x4*)(orow + 8 * r) = u32x4{pack_bf2(acc[0][r], acc[1][r]), pack_bf2(acc[2][r], acc[3][r]),
+                                      pack_bf2(acc[4][r], acc[5][r]), pack_bf2(acc[6][r], acc[7][r])};
+  } else {
+    // MFMA jj, register r: column 64 nb + 16 gq + 4 r + jj
     float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      v[i] = s_red[0][row][16 * q + i] + s_red[1][row][16 * q + i] + s_red[2][row][16 * q + i] + s_red[3][row][16 * q + i];
-    const int col = nb * 128 + 16 * q;
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) v[4 * r + jj] = acc[jj][r];
+    const int col = nb * 64 + 16 * gq;
     if (MODE == kGemmDA) {
       // SwiGLU backward with the saved pre-activations hg, hu
       const uint16_t* hrow = g.h + grow * 2 * F;
@@ -231,25 +282,30 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g) {
       for (int i = 0; i < 16; ++i) {
         const uint32_t gw = (i < 8) ? g0[(i & 7) >> 1] : g1[(i & 7) >> 1];
         const uint32_t uw = (i < 8) ? u0[(i & 7) >> 1] : u1[(i & 7) >> 1];
-        const float hg = (i & 1) ? bf_hi(gw) : bf_lo(gw);
-        const float hu = (i & 1) ? bf_hi(uw) : bf_lo(uw);
-        const float sg = sigmoidf_fast(hg);
-        dg[i] = v[i] * hu * sg * (1.0f + hg * (1.0f - sg));
-        du[i] = v[i] * hg * sg;
+        const float hgv = (i & 1) ? bf_hi(gw) : bf_lo(gw);
+        const float huv = (i & 1) ? bf_hi(uw) : bf_lo(uw);
+        const float sg = sigmoidf_fast(hgv);
+        dg[i] = v[i] * huv * sg * (1.0f + hgv * (1.0f - sg));
+        du[i] = v[i] * hgv * sg;
       }
       uint16_t* drow = g.out0 + grow * 2 * F;
-      *(u32x4*)(drow + col) = u32x4{pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]), pack_bf2(dg[4], dg[5]), pack_bf2(dg[6], dg[7])};
-      *(u32x4*)(drow + col + 8) =
-          u32x4{pack_bf2(dg[8], dg[9]), pack_bf2(dg[10], dg[11]), pack_bf2(dg[12], dg[13]), pack_bf2(dg[14], dg[15])};
-      *(u32x4*)(drow + F + col) =
-          u32x4{pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]), pack_bf2(du[4], du[5]), pack_bf2(du[6], du[7])};
-      *(u32x4*)(drow + F + col + 8) =
-          u32x4{pack_bf2(du[8], du[9]), pack_bf2(du[10], du[11]), pack_bf2(du[12], du[13]), pack_bf2(du[14], du[15])};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float* G = dg + 8 * h;
+        const float* U = du + 8 * h;
+        *(u32x4*)(drow + col + 8 * h) =
+            u32x4{pack_bf2(G[0], G[1]), pack_bf2(G[2], G[3]), pack_bf2(G[4], G[5]), pack_bf2(G[6], G[7])};
+        *(u32x4*)(drow + F + col + 8 * h) =
+            u32x4{pack_bf2(U[0], U[1]), pack_bf2(U[2], U[3]), pack_bf2(U[4], U[5]), pack_bf2(U[6], U[7])};
+      }
     } else {
-      uint16_t* orow = g.out0 + grow * H + col;  // DOWN: o rows, DX: dX rows (both [rows, H])
-      *(u32x4*)orow = u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
-      *(u32x4*)(orow + 8) =
-          u32x4{pack_bf2(v[8], v[9]), pack_bf2(v[10], v[11]), pack_bf2(v[12], v[13]), pack_bf2(v[14], v[15])};
+      uint16_t* orow = g.out0 + grow * H + col;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float* V = v + 8 * h;
+        *(u32x4*)(orow + 8 * h) =
+            u32x4{pack_bf2(V[0], V[1]), pack_bf2(V[2], V[3]), pack_bf2(V[4], V[5]), pack_bf2(V[6], V[7])};
+      }
     }
   }
 }
@@ -289,8 +345,8 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(DwArgs g) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
   const int mb = mt * 128 + (w & 1) * 64;
   const int nb = nt * 128 + (w >> 1) * 64;
-  const uint16_t* p_ptr = P + (size_t)(row0 + 8 * gq) * ldp + mb + 4 * c;
-  const uint16_t* q_ptr = Q + (size_t)(row0 + 8 * gq) * ldq + nb + 4 * c;
+  const uint16_t* p_base = P + (size_t)row0 * ldp + mb + 4 * c;
+  const uint16_t* q_base = Q + (size_t)row0 * ldq + nb + 4 * c;
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -299,16 +355,26 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(DwArgs g) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int steps = (n_e + 31) / 32;
+  // Unconditional loads (rows past n_e read the expert's last row and are
+  // zeroed by a select), so the load pipeline keeps a counted depth.
   auto load = [&](int s, u32x2* pq, u32x2* qq) {
-    const int rbase = 32 * s + 8 * gq;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const bool ok = rbase + r < n_e;
-      pq[r] = ok ? *(const u32x2*)(p_ptr + (size_t)(32 * s + r) * ldp) : u32x2{0u, 0u};
-      qq[r] = ok ? *(const u32x2*)(q_ptr + (size_t)(32 * s + r) * ldq) : u32x2{0u, 0u};
+      const int rr = 32 * s + 8 * gq + r;
+      const int rc = rr < n_e ? rr : n_e - 1;
+      pq[r] = *(const u32x2*)(p_base + (size_t)rc * ldp);
+      qq[r] = *(const u32x2*)(q_base + (size_t)rc * ldq);
     }
   };
-  auto compute = [&](const u32x2* pq, const u32x2* qq) {
+  auto compute = [&](int s, const u32x2* pq_in, const u32x2* qq_in) {
+    u32x2 pq[8], qq[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const bool ok = 32 * s + 8 * gq + r < n_e;
+      const u32x2 z = {0u, 0u};
+      pq[r] = ok ? pq_in[r] : z;
+      qq[r] = ok ? qq_in[r] : z;
+    }
     u32x4 pf[4], qf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -324,14 +390,12 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(DwArgs g) {
   if (steps > 0) {
     u32x2 pA[8], qA[8], pB[8], qB[8];
     load(0, pA, qA);
-    int s = 0;
-    for (; s + 2 <= steps; s += 2) {
-      load(s + 1, pB, qB);
-      compute(pA, qA);
-      if (s + 2 < steps) load(s + 2, pA, qA);
-      compute(pB, qB);
+    for (int s = 0; s < steps; s += 2) {
+      load(min(s + 1, steps - 1), pB, qB);
+      compute(s, pA, qA);
+      load(min(s + 2, steps - 1), pA, qA);
+      if (s + 1 < steps) compute(s + 1, pB, qB);
     }
-    if (s < steps) compute(pA, qA);
   }
 
   // lane (c, gq) holds rows mb + 4c + ja and columns nb + 16gq + 4r + jb
@@ -356,13 +420,15 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(DwArgs g) {
 hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream) {
   const int64_t tiles = ((int64_t)max_rows + (int64_t)g.E * (kTileRows - 1)) / kTileRows;
   if (tiles <= 0) return hipSuccess;
-  int nblocks;
+  int nblk;
   switch (mode) {
-    case kGemmGateUp: nblocks = g.F / 64; break;
-    case kGemmDA: nblocks = g.F / 128; break;
-    default: nblocks = g.H / 128; break;
+    case kGemmGateUp: nblk = row_gemm_blocks<kGemmGateUp>(g.H, g.F); break;
+    case kGemmDown: nblk = row_gemm_blocks<kGemmDown>(g.H, g.F); break;
+    case kGemmDA: nblk = row_gemm_blocks<kGemmDA>(g.H, g.F); break;
+    default: nblk = row_gemm_blocks<kGemmDX>(g.H, g.F); break;
   }
-  const dim3 grid((unsigned)tiles, (unsigned)nblocks);
+  const int64_t items = tiles * nblk;
+  const dim3 grid((unsigned)((items + 3) / 4));
   switch (mode) {
     case kGemmGateUp: hipLaunchKernelGGL(row_gemm_bf16_kernel<kGemmGateUp>, grid, dim3(256), 0, stream, g); break;
     case kGemmDown: hipLaunchKernelGGL(row_gemm_bf16_kernel<kGemmDown>, grid, dim3(256), 0, stream, g); break;
