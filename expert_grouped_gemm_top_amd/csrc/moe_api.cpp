@@ -10,7 +10,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_launch.h"
 
 namespace {

@@ -90,18 +90,36 @@ struct TileSlot {
 // Block-level part: s_start[e] = first tile id of expert e, s_start[E] = total;
 // s_off = offsets.  s_start and s_off need kMaxExperts + 1 ints, s_tmp 4 ints.
 // Must be called by all 256 threads of the block.
+// Only experts with min_rows <= n_e < max_rows get tiles (the others are served
+// by a kernel tuned for their row count).
 __device__ __forceinline__ void build_tile_starts(const int32_t* __restrict__ offsets, int E, int tile_rows,
-                                                  int* s_start, int* s_off, int* s_tmp) {
+                                                  int* s_start, int* s_off, int* s_tmp, int min_rows = 0,
+                                                  int max_rows = 0x7fffffff) {
   const int tid = threadIdx.x;
   if (tid <= E) s_off[tid] = offsets[tid];
   __syncthreads();
   int n_tiles = 0;
-  if (tid < E) n_tiles = (s_off[tid + 1] - s_off[tid] + tile_rows - 1) / tile_rows;
+  if (tid < E) {
+    const int n = s_off[tid + 1] - s_off[tid];
+    if (n >= min_rows && n < max_rows) n_tiles = (n + tile_rows - 1) / tile_rows;
+  }
   int total;
   const int start = block256_exclusive_scan(n_tiles, s_tmp, total);
   if (tid < E) s_start[tid] = start;
   if (tid == 0) s_start[E] = total;
   __syncthreads();
+}
+
+// XCD-aware order.  Workgroups are dealt round-robin to the 8 XCDs, each with
+// its own L2.  Map workgroup `wg` of a launch segment to a work item so that
+// every XCD walks a contiguous range of the `real` items (neighbouring items
+// share rows or weights and then meet in one L2), while the real items stay
+// spread evenly over the XCDs when the grid was sized for more items than
+// exist.  A bijection on [0, real & ~7); the identity elsewhere.
+__device__ __forceinline__ int xcd_item(int wg, int real) {
+  const int r8 = real & ~7;
+  if (wg >= r8) return wg;
+  return (wg & 7) * (r8 >> 3) + (wg >> 3);
 }
 
 // Per-thread part: the slot of `tile_id` (binary search over s_start).

@@ -33,6 +33,8 @@
 // transposes them in registers.  The reduction runs in a fixed order over all
 // of the expert's rows (deterministic, no atomics); an empty expert stores
 // exact zeros.
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -40,7 +42,12 @@ namespace moe {
 
 namespace {
 
-constexpr int kTileRows = 16;  // rows of one expert per wave tile (one MFMA row block)
+constexpr int kTileRows = 16;  // rows of one expert per wave tile of the streaming kernel (one MFMA row block)
+constexpr int kBigRows = kMidTileMinRows;  // experts with at least this many rows use an LDS-tiled kernel
+constexpr int kTBM = 128;      // LDS-tiled kernel: rows per workgroup tile
+constexpr int kTBN = 128;      //   output columns per workgroup tile
+constexpr int kTBK = 64;       //   reduction depth per stage
+constexpr int kTPitch = kTBK;  // LDS row pitch (elements); 16-byte chunks XOR-swizzled by row & 7
 
 // ---- register transposes of bf16 blocks -------------------------------------
 // rows[r] holds 8 bf16 (columns 0..7) of row r; returns the 8 k-values (rows
@@ -104,17 +111,16 @@ __host__ __device__ inline int row_gemm_blocks(int H, int F) {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g) {
+__device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s_start, int* s_off, int* s_tmp) {
   constexpr bool NN = RowGemmShape<MODE>::kNN;
-  __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
-  build_tile_starts(g.offsets, g.E, kTileRows, s_start, s_off, s_tmp);
+  build_tile_starts(g.offsets, g.E, kTileRows, s_start, s_off, s_tmp, 0, kBigRows);
 
   const int H = g.H, F = g.F;
   const int nblk = row_gemm_blocks<MODE>(H, F);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
   // work item of this wave: (tile, column block); the four waves of a workgroup
   // take adjacent column blocks of the same tile
-  const int item = blockIdx.x * 4 + w;
+  const int item = wg * 4 + w;
   const TileSlot ts = lookup_tile(s_start, s_off, g.E, kTileRows, item / nblk);
   if (ts.expert < 0) return;  // uniform across the wave; no block barrier follows
   const int nb = item % nblk;
@@ -310,6 +316,271 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g) {
   }
 }
 
+// ---- LDS-tiled row GEMM for experts with many rows ---------------------------
+// Workgroup tile: 128 rows of one expert x 128 output columns, four waves as
+// 2 x 2 of 64 x 64; the reduction advances 64 at a time through double-buffered
+// LDS tiles, so each weight tile read from memory serves 128 rows and each row
+// tile serves 128 columns.  Operand tiles are stored [row][k] (k contiguous):
+// activations are copied as they are, K-contiguous weights likewise, and
+// N-contiguous weights are transposed in registers (8 k x 4 columns per
+// thread) on the way in.  Column c of a wave's 64 is kept in LDS row
+// 16 (c % 4) + c / 4, so that after the MFMA (weights as the first operand) a
+// lane owns 16 consecutive output columns; for gate/up, LDS rows alternate
+// W_gate / W_up features so each lane owns hg and hu of the same 8 features.
+template <int MODE>
+__host__ __device__ inline int tile_gemm_blocks(int H, int F) {
+  return MODE == kGemmGateUp ? (2 * F) / kTBN : (MODE == kGemmDA ? F / kTBN : H / kTBN);
+}
+
+template <int MODE>
+__device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_start, int* s_off, int* s_tmp,
+                                          uint16_t* s_a, uint16_t* s_b) {
+  constexpr bool NN = RowGemmShape<MODE>::kNN;
+  build_tile_starts(g.offsets, g.E, kTBM, s_start, s_off, s_tmp, kBigRows, g.big_min_rows);
+  const int H = g.H, F = g.F;
+  const int nblk = tile_gemm_blocks<MODE>(H, F);
+  const int item = xcd_item(wg, s_start[g.E] * nblk);
+  // Items of one expert are walked in groups of up to 8 row tiles x all column
+  // blocks, column-major inside a group, so the workgroups resident together
+  // share both row tiles and weight tiles.
+  if (item >= s_start[g.E] * nblk) return;
+  int lo = 0, hi = g.E;  // expert: s_start[lo] * nblk <= item < s_start[hi] * nblk
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_start[mid] * nblk <= item) lo = mid; else hi = mid;
+  }
+  const int tiles_e = s_start[lo + 1] - s_start[lo];
+  const int li = item - s_start[lo] * nblk;
+  const int grp = li / (8 * nblk);
+  const int gm = min(8, tiles_e - 8 * grp);
+  const int within = li - grp * 8 * nblk;
+  const int mt = 8 * grp + within % gm;
+  const int nb = within / gm;
+  const TileSlot ts = lookup_tile(s_start, s_off, g.E, kTBM, s_start[lo] + mt);
+  const int e = ts.expert;
+  const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? H : (MODE == kGemmDown ? F : 2 * F);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lm = l & 15, gq = l >> 4;
+  const int wm = w & 1, wn = w >> 1;
+  const uint16_t* __restrict__ A = g.a;
+
+  // ---- loader assignments
+  // A: 128 rows x 8 chunks of 16 B; thread handles chunks tid + 256 i
+  const uint16_t* a_src[4];
+  bool a_ok[4];
+  int a_dst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ch = tid + 256 * i, row = ch >> 3, kc = ch & 7;
+    a_ok[i] = row < ts.rows;
+    a_src[i] = A + (size_t)(ts.row_begin + (a_ok[i] ? row : ts.rows - 1)) * K + 8 * kc;
+    a_dst[i] = row * kTPitch + 8 * (kc ^ (row & 7));
+  }
+  // B, N-contiguous: thread -> 8 k-rows (8 kb .. 8 kb + 7) x 4 columns of one matrix
+  // B, K-contiguous: thread -> 4 chunks (16 B) of weight rows
+  const uint16_t* b_src[4];
+  int b_dst[4];
+  size_t ldb = 0;
+  const uint16_t* b_hi = nullptr;  // DX: same rows in W_up for k >= F
+  if (NN) {
+    const int kb = tid >> 5, cb = tid & 31;
+    const int bw = cb >> 4, cq = cb & 15;  // wave column block, quad within it
+    const uint16_t* W;
+    int gcol;
+    if (MODE == kGemmGateUp) {
+      W = (cq & 1) ? g.w1 : g.w0;
+      gcol = nb * 64 + 32 * bw + 4 * (cq >> 1);
+      ldb = F;
+      W += (size_t)e * H * F;
+    } else {
+      W = g.w0 + (size_t)e * F * H;
+      gcol = nb * 128 + 64 * bw + 4 * cq;
+      ldb = H;
+    }
+    b_src[0] = W + (size_t)(8 * kb) * ldb + gcol;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 64 * bw + 16 * i + cq;
+      b_dst[i] = row * kTPitch + 8 * (kb ^ (row & 7));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = tid + 256 * i, nl = ch >> 3, kc = ch & 7;
+      const int n = nb * kTBN + nl;
+      const int bw = nl >> 6, nw = nl & 63;
+      const int brow = 64 * bw + 16 * (nw & 3) + (nw >> 2);
+      b_dst[i] = brow * kTPitch + 8 * (kc ^ (brow & 7));
+      if (MODE == kGemmDA) {
+        b_src[i] = g.w0 + (size_t)e * F * H + (size_t)n * H + 8 * kc;
+      } else {
+        b_src[i] = g.w0 + (size_t)e * H * F + (size_t)n * F + 8 * kc;
+      }
+    }
+    if (MODE == kGemmDX) b_hi = g.w1 + (size_t)e * H * F;
+  }
+
+  // global -> register staging of one K-step
+  struct Stage {
+    u32x4 a[4];
+    u32x2 bn[8];
+    u32x4 bt[4];
+  };
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  const int steps = K / kTBK;
+  auto gload = [&](int s, Stage& st) {
+    const int k0 = s * kTBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.a[i] = *(const u32x4*)(a_src[i] + k0);
+    if (NN) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) st.bn[r] = *(const u32x2*)(b_src[0] + (size_t)(k0 + r) * ldb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t* src = b_src[i] + k0;
+        if (MODE == kGemmDX && k0 >= F) src = b_src[i] - (g.w0 + (size_t)e * H * F) + b_hi + (k0 - F);
+        st.bt[i] = *(const u32x4*)src;
+      }
+    }
+  };
+  auto lstore = [&](int buf, const Stage& st) {
+    uint16_t* sa = s_a + buf * (kTBM * kTPitch);
+    uint16_t* sb = s_b + buf * (kTBN * kTPitch);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)(sa + a_dst[i]) = a_ok[i] ? st.a[i] : z4;
+    if (NN) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4*)(sb + b_dst[i]) = column_of_8x4(st.bn, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4*)(sb + b_dst[i]) = st.bt[i];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+    // rows 64 wm + 16 i + lm (A) / 64 wn + 16 j + lm (B): row & 7 == lm & 7
+    const uint16_t* sa = s_a + buf * (kTBM * kTPitch) + (64 * wm + lm) * kTPitch;
+    const uint16_t* sb = s_b + buf * (kTBN * kTPitch) + (64 * wn + lm) * kTPitch;
+#pragma unroll
+    for (int kh = 0; kh < kTBK / 32; ++kh) {
+      const int pos = 8 * ((4 * kh + gq) ^ (lm & 7));
+      u32x4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const u32x4*)(sa + 16 * i * kTPitch + pos);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = *(const u32x4*)(sb + 16 * j * kTPitch + pos);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
+    }
+  };
+
+  // one register stage: step s+1's loads are in flight while step s is
+  // multiplied out of LDS
+  Stage st;
+  gload(0, st);
+  lstore(0, st);
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    if (s + 1 < steps) gload(s + 1, st);
+    compute(s & 1);
+    if (s + 1 < steps) lstore((s + 1) & 1, st);
+    __syncthreads();
+  }
+
+  // epilogue: acc[ia][jb] register r -> row 64 wm + 16 ia + lm, virtual column
+  // (c' = 4 gq + r, jb)
+#pragma unroll
+  for (int ia = 0; ia < 4; ++ia) {
+    const int row = 64 * wm + 16 * ia + lm;
+    if (row >= ts.rows) continue;
+    const size_t grow = (size_t)ts.row_begin + row;
+    if (MODE == kGemmGateUp) {
+      // r even: gate, r odd: up, of feature 64 nb + 32 wn + 8 gq + 4 (r >> 1) + jb
+      float hg[8], hu[8], av[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          hg[4 * h + jb] = acc[ia][jb][2 * h];
+          hu[4 * h + jb] = acc[ia][jb][2 * h + 1];
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) av[i] = hg[i] * sigmoidf_fast(hg[i]) * hu[i];
+      const int f = nb * 64 + 32 * wn + 8 * gq;
+      uint16_t* hrow = g.out0 + grow * 2 * F;
+      *(u32x4*)(hrow + f) = u32x4{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3]), pack_bf2(hg[4], hg[5]), pack_bf2(hg[6], hg[7])};
+      *(u32x4*)(hrow + F + f) =
+          u32x4{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3]), pack_bf2(hu[4], hu[5]), pack_bf2(hu[6], hu[7])};
+      *(u32x4*)(g.out1 + grow * F + f) =
+          u32x4{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3]), pack_bf2(av[4], av[5]), pack_bf2(av[6], av[7])};
+    } else {
+      // column 128 nb + 64 wn + 16 gq + 4 r + jb
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) v[4 * r + jb] = acc[ia][jb][r];
+      const int col = nb * kTBN + 64 * wn + 16 * gq;
+      if (MODE == kGemmDA) {
+        const uint16_t* hrow = g.h + grow * 2 * F;
+        const u32x4 g0 = *(const u32x4*)(hrow + col), g1 = *(const u32x4*)(hrow + col + 8);
+        const u32x4 u0 = *(const u32x4*)(hrow + F + col), u1 = *(const u32x4*)(hrow + F + col + 8);
+        float dgv[16], duv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t gw = (i < 8) ? g0[(i & 7) >> 1] : g1[(i & 7) >> 1];
+          const uint32_t uw = (i < 8) ? u0[(i & 7) >> 1] : u1[(i & 7) >> 1];
+          const float hgv = (i & 1) ? bf_hi(gw) : bf_lo(gw);
+          const float huv = (i & 1) ? bf_hi(uw) : bf_lo(uw);
+          const float sg = sigmoidf_fast(hgv);
+          dgv[i] = v[i] * huv * sg * (1.0f + hgv * (1.0f - sg));
+          duv[i] = v[i] * hgv * sg;
+        }
+        uint16_t* drow = g.out0 + grow * 2 * F;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float* G = dgv + 8 * h;
+          const float* U = duv + 8 * h;
+          *(u32x4*)(drow + col + 8 * h) =
+              u32x4{pack_bf2(G[0], G[1]), pack_bf2(G[2], G[3]), pack_bf2(G[4], G[5]), pack_bf2(G[6], G[7])};
+          *(u32x4*)(drow + F + col + 8 * h) =
+              u32x4{pack_bf2(U[0], U[1]), pack_bf2(U[2], U[3]), pack_bf2(U[4], U[5]), pack_bf2(U[6], U[7])};
+        }
+      } else {
+        uint16_t* orow = g.out0 + grow * H + col;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float* V = v + 8 * h;
+          *(u32x4*)(orow + 8 * h) =
+              u32x4{pack_bf2(V[0], V[1]), pack_bf2(V[2], V[3]), pack_bf2(V[4], V[5]), pack_bf2(V[6], V[7])};
+        }
+      }
+    }
+  }
+}
+
+// One launch serves both regimes: workgroups [0, n_stream) run the streaming
+// kernel over experts with fewer than kBigRows rows, the rest run the LDS-tiled
+// kernel over the others.  Both schedules are derived on the device.
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, int n_stream, int n_tile) {
+  __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kTBM * kTPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[2 * kTBN * kTPitch];
+  if ((int)blockIdx.x < n_stream)
+    stream_gemm<MODE>(g, blockIdx.x, s_start, s_off, s_tmp);
+  else
+    tile_gemm<MODE>(g, blockIdx.x - n_stream, s_start, s_off, s_tmp, s_a, s_b);
+}
+
 // ---- dW GEMM ------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(DwArgs g) {
   const int e = blockIdx.x / g.tiles_per_expert;
@@ -417,25 +688,36 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(DwArgs g) {
 
 }  // namespace
 
+template <int MODE>
+hipError_t launch_row_gemm_mode(const RowGemmArgs& args, int max_rows, hipStream_t stream) {
+  RowGemmArgs g = args;
+  g.big_min_rows = big_gemm_min_rows(MODE, g.H, g.F);
+  const int64_t N = max_rows, E = g.E;
+  // streaming kernel: experts with n_e < kBigRows, ceil(n_e / 16) tiles each
+  const int64_t small_tiles = std::min<int64_t>((N + E * (kTileRows - 1)) / kTileRows,
+                                                 E * ((kBigRows - 1 + kTileRows - 1) / kTileRows));
+  const int64_t n_stream = (small_tiles * row_gemm_blocks<MODE>(g.H, g.F) + 3) / 4;
+  // tiled kernel: experts with kBigRows <= n_e < g.big_min_rows, ceil(n_e / 128) tiles each
+  const int64_t big_experts = std::min<int64_t>(E, N / kBigRows);
+  const int64_t big_tiles = std::min<int64_t>((N + big_experts * (kTBM - 1)) / kTBM,
+                                              big_experts * ((g.big_min_rows + kTBM - 2) / kTBM));
+  const int64_t n_tile = (big_experts == 0) ? 0 : ((big_tiles * tile_gemm_blocks<MODE>(g.H, g.F) + 7) / 8) * 8;
+  const int64_t grid = n_stream + n_tile;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_gemm_bf16_kernel<MODE>, dim3((unsigned)grid), dim3(256), 0, stream, g, (int)n_stream,
+                     (int)n_tile);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_big_gemm_bf16(MODE, g, max_rows, stream);
+}
+
 hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream) {
-  const int64_t tiles = ((int64_t)max_rows + (int64_t)g.E * (kTileRows - 1)) / kTileRows;
-  if (tiles <= 0) return hipSuccess;
-  int nblk;
   switch (mode) {
-    case kGemmGateUp: nblk = row_gemm_blocks<kGemmGateUp>(g.H, g.F); break;
-    case kGemmDown: nblk = row_gemm_blocks<kGemmDown>(g.H, g.F); break;
-    case kGemmDA: nblk = row_gemm_blocks<kGemmDA>(g.H, g.F); break;
-    default: nblk = row_gemm_blocks<kGemmDX>(g.H, g.F); break;
+    case kGemmGateUp: return launch_row_gemm_mode<kGemmGateUp>(g, max_rows, stream);
+    case kGemmDown: return launch_row_gemm_mode<kGemmDown>(g, max_rows, stream);
+    case kGemmDA: return launch_row_gemm_mode<kGemmDA>(g, max_rows, stream);
+    default: return launch_row_gemm_mode<kGemmDX>(g, max_rows, stream);
   }
-  const int64_t items = tiles * nblk;
-  const dim3 grid((unsigned)((items + 3) / 4));
-  switch (mode) {
-    case kGemmGateUp: hipLaunchKernelGGL(row_gemm_bf16_kernel<kGemmGateUp>, grid, dim3(256), 0, stream, g); break;
-    case kGemmDown: hipLaunchKernelGGL(row_gemm_bf16_kernel<kGemmDown>, grid, dim3(256), 0, stream, g); break;
-    case kGemmDA: hipLaunchKernelGGL(row_gemm_bf16_kernel<kGemmDA>, grid, dim3(256), 0, stream, g); break;
-    default: hipLaunchKernelGGL(row_gemm_bf16_kernel<kGemmDX>, grid, dim3(256), 0, stream, g); break;
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_dw_bf16(DwArgs g, hipStream_t stream) {

@@ -1,0 +1,430 @@
+// moe_gemm_big.hip -- row GEMMs of the SwiGLU experts for experts with many
+// rows (>= 256), where the grouped GEMM is bound by the matrix cores.
+//
+// Same four products as the other row GEMMs (expert forward and backward dx:
+// npu-train issue #14, sections Proposal and Scope; variable-size grouped GEMMs:
+// LRMoE abstract), tiled for gfx950:
+//   * workgroup tile BM rows x BN columns, waves laid out WM x (NW / WM), each
+//     wave a grid of 32 x 32 blocks on v_mfma_f32_32x32x16_bf16
+//     (on gfx950 it sustains ~2.4 PFLOP/s where the 16x16x32 form stops near
+//     1.4 PFLOP/s);
+//   * operands move global -> LDS with global_load_lds_dwordx4 (no register
+//     staging), several K-stages of BK in flight;
+//   * K-contiguous operands (activation rows, backward weights) land as
+//     [row][BK] rows with the 16-byte chunks XOR-swizzled per row, keys that
+//     measured conflict-free for 16-byte fragment reads of 16 consecutive rows;
+//   * N-contiguous weights (forward) land as [32 k][BN] and are read with the
+//     gfx950 transpose read ds_read_b64_tr_b16: lane r of a 16-lane group
+//     points at row r / 4, column quad r % 4, and receives 4 consecutive k of
+//     one column -- half of a 32x32x16 B fragment; 64-byte chunk groups are
+//     XOR-swizzled by 4 (k & 3) so the rows of one read fall in distinct banks;
+//   * rows past the tile's real rows re-read the tile's last row: they only
+//     produce output rows that are never stored.
+#include <algorithm>
+
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+namespace {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D = first x second + D on the 32x32x16 bf16 matrix core.  Lane l supplies
+// row (first) / column (second) l % 32 and k-group l / 32 (8 consecutive k);
+// register r of lane l is D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+__device__ __forceinline__ f32x16 mfma32(u32x4 first, u32x4 second, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, first), __builtin_bit_cast(bf16x8, second),
+                                                  acc, 0, 0, 0);
+}
+
+// 16 B from global straight into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void g2lds(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would make the compiler wait for every outstanding global load (including
+// the stages still meant to be in flight).  LDS data written by the direct
+// loads is made complete explicitly with wait_vmcnt before this barrier; the
+// asm clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt vmcnt(N); expcnt and lgkmcnt left unconstrained
+  static_assert(N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+template <int MODE>
+struct BigShape {
+  static constexpr bool kNN = (MODE == kGemmGateUp || MODE == kGemmDown);
+};
+
+template <int MODE>
+__host__ __device__ inline int big_out_cols(int H, int F) {
+  return MODE == kGemmGateUp ? 2 * F : (MODE == kGemmDA ? F : H);
+}
+
+// K-contiguous tile rows of BK elements (CPR 16-byte chunks): swizzled chunk
+// position; measured conflict-free for 16-byte fragment reads of 16
+// consecutive rows (64 B rows: key (row >> 1) & 3; 128 B rows: key row & 7).
+template <int CPR>
+__device__ __forceinline__ int kc_swz(int row, int chunk) {
+  return CPR == 4 ? (chunk ^ ((row >> 1) & 3)) : (chunk ^ (row & 7));
+}
+// k row of an N-contiguous tile -> XOR on the 16-byte chunk index (keeps the
+// 4-chunk groups one transpose read covers aligned)
+__device__ __forceinline__ int nn_swz(int k) { return 4 * (k & 3); }
+
+// Tile of BM rows x BN columns, reduction depth BK per stage, NW waves laid out
+// WM x (NW / WM); STAGES stages resident in LDS; WPC workgroups per CU.
+template <int MODE, int BM, int BN, int BK, int NW, int WM, int STAGES, int WPC>
+__global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs g) {
+  constexpr bool NN = BigShape<MODE>::kNN;
+  const int kMinRows = g.big_min_rows;  // experts with at least this many rows use this kernel
+  constexpr int WNW = NW / WM;          // waves along N
+  constexpr int TM = BM / WM;           // rows per wave
+  constexpr int TN = BN / WNW;          // columns per wave
+  constexpr int MI = TM / 32, NJ = TN / 32;
+  constexpr int CPR = BK / 8;           // 16-byte chunks per K-contiguous row
+  constexpr int A_BYTES = BM * BK * 2;
+  constexpr int B_BYTES = BN * BK * 2;
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  constexpr int A_INS = A_BYTES / 1024 / NW;  // direct loads per wave per stage
+  constexpr int B_INS = B_BYTES / 1024 / NW;
+  constexpr int INS = A_INS + B_INS;
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "tile / wave split");
+  static_assert(MI >= 1 && NJ >= 1, "wave tile");
+  __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+
+  // schedule (the builder needs 256 threads; larger workgroups run it on the first 256)
+  if (NW == 4) {
+    build_tile_starts(g.offsets, g.E, BM, s_start, s_off, s_tmp, kMinRows);
+  } else {
+    const bool first = threadIdx.x < 256;
+    if (first) {
+      if (threadIdx.x <= g.E) s_off[threadIdx.x] = g.offsets[threadIdx.x];
+    }
+    __syncthreads();
+    int n_tiles = 0;
+    if (first && threadIdx.x < g.E) {
+      const int n = s_off[threadIdx.x + 1] - s_off[threadIdx.x];
+      if (n >= kMinRows) n_tiles = (n + BM - 1) / BM;
+    }
+    // exclusive scan by the first four waves
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int inc = wave_inclusive_scan(n_tiles);
+    if (w < 4 && l == 63) s_tmp[w] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < 4; ++i) base += (i < w) ? s_tmp[i] : 0;
+    if (first && threadIdx.x < g.E) s_start[threadIdx.x] = base + inc - n_tiles;
+    if (threadIdx.x == 0) s_start[g.E] = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+    __syncthreads();
+  }
+  const int H = g.H, F = g.F;
+  const int nblk = big_out_cols<MODE>(H, F) / BN;
+  const int item = xcd_item(blockIdx.x, s_start[g.E] * nblk);
+  if (item >= s_start[g.E] * nblk) return;
+  int lo = 0, hi = g.E;  // expert of this item
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_start[mid] * nblk <= item) lo = mid; else hi = mid;
+  }
+  // groups of up to 4 row tiles x all column blocks, column-major within a group
+  const int tiles_e = s_start[lo + 1] - s_start[lo];
+  const int li = item - s_start[lo] * nblk;
+  const int grp = li / (4 * nblk);
+  const int gm = min(4, tiles_e - 4 * grp);
+  const int within = li - grp * 4 * nblk;
+  const int mt = 4 * grp + within % gm;
+  const int nb = within / gm;
+  const TileSlot ts = lookup_tile(s_start, s_off, g.E, BM, s_start[lo] + mt);
+  const int e = ts.expert;
+  const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? H : (MODE == kGemmDown ? F : 2 * F);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int wm = w % WM, wn = w / WM;
+  const int l32 = l & 31, hk = l >> 5;  // MFMA row/column and k-group of this lane
+
+  // ---- loader: 1 KiB per direct-load instruction
+  // A (K-contiguous rows of 2 BK bytes): instruction covers 64 / CPR rows
+  const uint16_t* a_src[A_INS];
+#pragma unroll
+  for (int i = 0; i < A_INS; ++i) {
+    const int row = (64 / CPR) * (A_INS * w + i) + l / CPR;
+    const int chunk = kc_swz<CPR>(row, l % CPR);  // LDS position l % CPR holds this chunk
+    const int r = row < ts.rows ? row : ts.rows - 1;
+    a_src[i] = g.a + (size_t)(ts.row_begin + r) * K + 8 * chunk;
+  }
+  const uint16_t* b_src[B_INS];
+  const uint16_t* b_hi[B_INS];  // DX: the same rows in W_up for k >= F
+  size_t b_kstride;             // elements per k for NN (row stride), 1 for NT
+  if (NN) {
+    // [BK k][BN]: a k row is BN/8 chunks; instruction covers 512 / BN k rows
+    constexpr int ROWS_PER_INS = 512 / BN;
+    b_kstride = (MODE == kGemmGateUp) ? F : H;
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+      const int k = ROWS_PER_INS * (B_INS * w + i) + l / (BN / 8);
+      const int pos = l % (BN / 8);
+      const int vchunk = pos ^ nn_swz(k);  // virtual 8-column chunk stored at pos
+      const uint16_t* W;
+      int col;
+      if (MODE == kGemmGateUp) {
+        // virtual chunks alternate W_gate / W_up over the same 8 features
+        W = ((vchunk & 1) ? g.w1 : g.w0) + (size_t)e * H * F;
+        col = nb * (BN / 2) + 8 * (vchunk >> 1);
+      } else {
+        W = g.w0 + (size_t)e * F * H;
+        col = nb * BN + 8 * vchunk;
+      }
+      b_src[i] = W + (size_t)k * b_kstride + col;
+      b_hi[i] = b_src[i];
+    }
+  } else {
+    b_kstride = 1;
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+      const int row = (64 / CPR) * (B_INS * w + i) + l / CPR;  // output column within the tile
+      const int chunk = kc_swz<CPR>(row, l % CPR);
+      const int n = nb * BN + row;
+      if (MODE == kGemmDA) {
+        b_src[i] = g.w0 + (size_t)e * F * H + (size_t)n * H + 8 * chunk;
+        b_hi[i] = b_src[i];
+      } else {  // DX: k < F from W_gate, k >= F from W_up
+        b_src[i] = g.w0 + (size_t)e * H * F + (size_t)n * F + 8 * chunk;
+        b_hi[i] = g.w1 + (size_t)e * H * F + (size_t)n * F + 8 * chunk;
+      }
+    }
+  }
+
+  auto issue = [&](int s) {
+    unsigned char* st = s_dyn + (s % STAGES) * STAGE_BYTES;
+    const int k0 = s * BK;
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) g2lds(a_src[i] + k0, st + 1024 * (A_INS * w + i));
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+      const uint16_t* src;
+      if (NN) src = b_src[i] + (size_t)k0 * b_kstride;
+      else src = (MODE == kGemmDX && k0 >= F) ? b_hi[i] + (k0 - F) : b_src[i] + k0;
+      g2lds(src, st + A_BYTES + 1024 * (B_INS * w + i));
+    }
+  };
+
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  struct Frags {
+    u32x4 a[MI];
+    u32x4 b[NJ];
+  };
+  // fragments of sub-step `sub` (16 k) of the stage in LDS buffer `st`
+  auto read_frags = [&](const unsigned char* st, int sub, Frags& fr) {
+    const unsigned char* sb = st + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int row = TM * wm + 32 * i + l32;
+      fr.a[i] = *(const u32x4*)(st + row * (2 * BK) + 16 * kc_swz<CPR>(row, 2 * sub + hk));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (NN) {
+        // 16-lane group G = l / 16 reads k rows 16 sub + 8 (G >> 1) + 4 h + (r >> 2)
+        // and columns TN wn + 32 j + 16 (G & 1) + 4 (r & 3) .. + 3, r = l % 16
+        const int G = l >> 4, r = l & 15;
+        const int col = TN * wn + 32 * j + 16 * (G & 1) + 4 * (r & 3);
+        v4i16 part[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = 16 * sub + 8 * (G >> 1) + 4 * h + (r >> 2);
+          const int chunk = (col >> 3) ^ nn_swz(k);
+          part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(sb + k * (BN * 2) + 16 * chunk + 2 * (col & 7)));
+        }
+        fr.b[j] = u32x4{(uint32_t)(uint16_t)part[0][0] | ((uint32_t)(uint16_t)part[0][1] << 16),
+                        (uint32_t)(uint16_t)part[0][2] | ((uint32_t)(uint16_t)part[0][3] << 16),
+                        (uint32_t)(uint16_t)part[1][0] | ((uint32_t)(uint16_t)part[1][1] << 16),
+                        (uint32_t)(uint16_t)part[1][2] | ((uint32_t)(uint16_t)part[1][3] << 16)};
+      } else {
+        const int row = TN * wn + 32 * j + l32;
+        fr.b[j] = *(const u32x4*)(sb + row * (2 * BK) + 16 * kc_swz<CPR>(row, 2 * sub + hk));
+      }
+    }
+  };
+  auto mfmas = [&](const Frags& fr) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < MI; ++i) acc[i][j] = mfma32(fr.b[j], fr.a[i], acc[i][j]);
+  };
+  // Sub-steps are software-pipelined: the fragments of sub-step t+1 are read
+  // from LDS while the MFMAs of sub-step t run.
+  auto compute = [&](int s) {
+    const unsigned char* st = s_dyn + (s % STAGES) * STAGE_BYTES;
+    constexpr int SUBS = BK / 16;
+    Frags f0, f1;
+    read_frags(st, 0, f0);
+#pragma unroll
+    for (int t = 0; t < SUBS; t += 2) {
+      if (t + 1 < SUBS) read_frags(st, t + 1, f1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < SUBS) {
+        if (t + 2 < SUBS) read_frags(st, t + 2, f0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(f1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  const int steps = K / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < steps) issue(s);
+  for (int s = 0; s < steps; ++s) {
+    // stage s is complete once at most (stages issued after it) x INS loads remain
+    const int ahead = min(STAGES - 2, steps - 1 - s);
+    if (ahead >= 3) wait_vmcnt<3 * INS>();
+    else if (ahead == 2) wait_vmcnt<2 * INS>();
+    else if (ahead == 1) wait_vmcnt<INS>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    if (s + STAGES - 1 < steps) issue(s + STAGES - 1);
+    compute(s);
+  }
+
+  // ---- epilogue.  acc[i][j] register r -> row TM wm + 32 i + l32, tile
+  // column TN wn + 32 j + 8 q + 4 hk + e with q = r / 4, e = r % 4.
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int row = TM * wm + 32 * i + l32;
+    if (row >= ts.rows) continue;
+    const size_t grow = (size_t)ts.row_begin + row;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (MODE == kGemmGateUp) {
+        // 8-column chunk (TN wn + 32 j) / 8 + q: even q -> W_gate, odd q -> W_up,
+        // feature (BN/2) nb + (TN wn + 32 j) / 2 + 8 (q >> 1) + 4 hk + e
+        const int f0 = (BN / 2) * nb + (TN * wn + 32 * j) / 2 + 4 * hk;
+        uint16_t* hrow = g.out0 + grow * 2 * F;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int f = f0 + 8 * p;
+          float hg[4], hu[4], av[4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            hg[e2] = acc[i][j][8 * p + e2];
+            hu[e2] = acc[i][j][8 * p + 4 + e2];
+            av[e2] = hg[e2] * sigmoidf_fast(hg[e2]) * hu[e2];
+          }
+          *(u32x2*)(hrow + f) = u32x2{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3])};
+          *(u32x2*)(hrow + F + f) = u32x2{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3])};
+          *(u32x2*)(g.out1 + grow * F + f) = u32x2{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3])};
+        }
+      } else {
+        const int width = (MODE == kGemmDA) ? 2 * F : H;
+        uint16_t* orow = g.out0 + grow * width;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nb * BN + TN * wn + 32 * j + 8 * q + 4 * hk;
+          if (MODE == kGemmDA) {
+            const uint16_t* hrow = g.h + grow * 2 * F;
+            const u32x2 gw = *(const u32x2*)(hrow + col), uw = *(const u32x2*)(hrow + F + col);
+            float dgv[4], duv[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const uint32_t gg = gw[e2 >> 1], uu = uw[e2 >> 1];
+              const float hgv = (e2 & 1) ? bf_hi(gg) : bf_lo(gg);
+              const float huv = (e2 & 1) ? bf_hi(uu) : bf_lo(uu);
+              const float sg = sigmoidf_fast(hgv);
+              const float dA = acc[i][j][4 * q + e2];
+              dgv[e2] = dA * huv * sg * (1.0f + hgv * (1.0f - sg));
+              duv[e2] = dA * hgv * sg;
+            }
+            *(u32x2*)(orow + col) = u32x2{pack_bf2(dgv[0], dgv[1]), pack_bf2(dgv[2], dgv[3])};
+            *(u32x2*)(orow + F + col) = u32x2{pack_bf2(duv[0], duv[1]), pack_bf2(duv[2], duv[3])};
+          } else {
+            *(u32x2*)(orow + col) = u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                          pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+          }
+        }
+      }
+    }
+  }
+}
+
+#ifndef MOE_BIG_CFG
+#define MOE_BIG_CFG 256, 256, 64, 8, 2, 2, 1   // BM, BN, BK, waves, waves along M, stages, workgroups per CU
+#endif
+
+template <int MODE, int BM, int BN, int BK, int NW, int WM, int STAGES, int WPC>
+struct BigCfg {
+  static int min_rows(int H, int F) {
+    // The product with the transposed down projection (DA) measured faster on
+    // 128-row tiles at every row count; the others need whole column blocks.
+    if (MODE == kGemmDA || big_out_cols<MODE>(H, F) % BN != 0) return kNoBigTiles;
+    return kBigTileMinRows;
+  }
+
+  static hipError_t launch(const RowGemmArgs& g, int max_rows, hipStream_t stream) {
+    const int64_t N = max_rows, E = g.E;
+    const int64_t big_experts = std::min<int64_t>(E, N / g.big_min_rows);
+    if (big_experts == 0) return hipSuccess;
+    const int64_t tiles = (N + big_experts * (BM - 1)) / BM;
+    const int64_t wgs = ((tiles * (big_out_cols<MODE>(g.H, g.F) / BN) + 7) / 8) * 8;
+    const size_t lds = (size_t)STAGES * (BM + BN) * BK * 2;
+    auto kern = big_gemm_bf16_kernel<MODE, BM, BN, BK, NW, WM, STAGES, WPC>;
+    // dynamic LDS above 64 KiB must be allowed explicitly, once per device
+    static bool attr_set[64] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+      err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (err != hipSuccess) return err;
+      if (dev >= 0 && dev < 64) attr_set[dev] = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(64 * NW), lds, stream, g);
+    return hipGetLastError();
+  }
+};
+
+template <int MODE>
+using Big = BigCfg<MODE, MOE_BIG_CFG>;
+
+}  // namespace
+
+int big_gemm_min_rows(int mode, int H, int F) {
+  switch (mode) {
+    case kGemmGateUp: return Big<kGemmGateUp>::min_rows(H, F);
+    case kGemmDown: return Big<kGemmDown>::min_rows(H, F);
+    case kGemmDX: return Big<kGemmDX>::min_rows(H, F);
+    default: return kNoBigTiles;
+  }
+}
+
+hipError_t launch_big_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream) {
+  switch (mode) {
+    case kGemmGateUp: return Big<kGemmGateUp>::launch(g, max_rows, stream);
+    case kGemmDown: return Big<kGemmDown>::launch(g, max_rows, stream);
+    case kGemmDX: return Big<kGemmDX>::launch(g, max_rows, stream);
+    default: return hipSuccess;  // DA always runs on 128-row tiles
+  }
+}
+
+}  // namespace moe

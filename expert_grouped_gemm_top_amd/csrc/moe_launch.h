@@ -9,8 +9,14 @@
 namespace moe {
 
 constexpr int kMaxExpertsHost = 256;  // expert ids fit in 8 bits
-
 enum RowGemmMode { kGemmGateUp = 0, kGemmDown = 1, kGemmDA = 2, kGemmDX = 3 };
+
+// Row GEMM regimes by an expert's row count n_e: n_e < kMidTileMinRows -> streaming
+// kernel (16-row wave tiles); up to big_gemm_min_rows(...) -> 128 x 128 LDS
+// tiles; above -> 256 x 256 LDS tiles fed by direct global->LDS loads.
+constexpr int kMidTileMinRows = 48;
+constexpr int kBigTileMinRows = 256;
+constexpr int kNoBigTiles = 0x40000000;  // above every row count
 
 // Pointers of one row-ragged grouped GEMM.  Element type is bf16 (uint16_t
 // bits) or fp32 depending on the launcher; all buffers are device memory.
@@ -27,6 +33,7 @@ struct RowGemmArgs {
   const uint16_t* h;
   uint16_t* out0;
   uint16_t* out1;
+  int big_min_rows;  // set by launch_row_gemm_bf16: experts from this row count take the 256-row kernel
 };
 
 struct DwArgs {
@@ -62,6 +69,10 @@ hipError_t launch_gather_rows(const int32_t* R_ptr, const int32_t* src, int max_
 
 hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
 hipError_t launch_dw_bf16(DwArgs g, hipStream_t stream);
+hipError_t launch_big_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
+// Row count from which an expert takes the 256-row kernel for this product and
+// shape; kNoBigTiles where that kernel does not apply.
+int big_gemm_min_rows(int mode, int H, int F);
 hipError_t launch_row_gemm_f32(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
 hipError_t launch_dw_f32(DwArgs g, hipStream_t stream);
 

@@ -85,6 +85,9 @@ SMALL_BF16 = [
     W.custom("bf16_single_token", T=1, H=128, F=128, E=4, k=4, dtype="bf16", skew=False, dw=True),
     W.custom("bf16_k1", T=77, H=128, F=256, E=5, k=1, dtype="bf16", skew=True, dw=True),
     W.custom("fp32_ragged", T=90, H=64, F=40, E=6, k=3, dtype="f32", skew=True, dw=True),
+    # experts past 256 rows (256-row tiles with ragged tails), 128-row tiles, and the streaming path together
+    W.custom("bf16_big_tiles", T=700, H=256, F=256, E=4, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_big_tiles_f384", T=600, H=384, F=384, E=6, k=1, dtype="bf16", skew=True, dw=True),
 ]
 
 
