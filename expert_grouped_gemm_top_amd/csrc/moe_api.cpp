@@ -4,6 +4,7 @@
 // No C++ exception crosses the ABI.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -175,12 +176,13 @@ int moe_dispatch(int T, int H, int E, int k, int dtype, const int32_t* topk_idx,
                     fn);
 }
 
-int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int dtype, const int32_t* offsets, const void* x_sorted,
-                           const void* w_gate, const void* w_up, const void* w_down, void* h_save, void* a_save,
-                           void* o_sorted, void* stream) {
+int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int max_expert_rows, int dtype, const int32_t* offsets,
+                           const void* x_sorted, const void* w_gate, const void* w_up, const void* w_down, void* h_save,
+                           void* a_save, void* o_sorted, void* stream) {
   const char* fn = "moe_grouped_swiglu_fwd";
   int rc = check_expert_dims(fn, H, F, E, dtype);
   if (rc || (rc = check_rows(fn, max_rows))) return rc;
+  REQUIRE(max_expert_rows >= 0, MOE_ERR_INVALID_ARGUMENT, "%s: max_expert_rows=%d is negative", fn, max_expert_rows);
   NONNULL(offsets);
   NONNULL(x_sorted);
   NONNULL(w_gate);
@@ -198,7 +200,7 @@ int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int dtype, const i
   hipStream_t s = as_stream(stream);
   auto run = [&](int mode) {
     return timed(kGemmKind[mode], s, [&] {
-      return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, s)
+      return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, max_expert_rows, s)
                                : moe::launch_row_gemm_f32(mode, g, max_rows, s);
     });
   };
@@ -275,7 +277,9 @@ int moe_grouped_bwd_dx(int T, int H, int F, int E, int k, int max_rows, int dtyp
     g.F = F;
     auto run = [&](int mode) {
       return timed(kGemmKind[mode], s, [&] {
-        return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, s)
+        // rows of one expert come from distinct pairs of distinct tokens when
+        // the routing picks distinct experts per token: T bounds them
+        return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, std::min(max_rows, T), s)
                                  : moe::launch_row_gemm_f32(mode, g, max_rows, s);
       });
     };

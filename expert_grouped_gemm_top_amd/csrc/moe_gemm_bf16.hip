@@ -42,6 +42,10 @@ namespace moe {
 
 namespace {
 
+#ifndef MOE_STREAM_SPLITK_MODES
+#define MOE_STREAM_SPLITK_MODES ((1 << kGemmGateUp) | (1 << kGemmDA))  // modes whose skinny-expert reduction is split
+#endif
+
 constexpr int kTileRows = 16;  // rows of one expert per wave tile of the streaming kernel (one MFMA row block)
 constexpr int kBigRows = kMidTileMinRows;  // experts with at least this many rows use an LDS-tiled kernel
 constexpr int kTBM = 128;      // LDS-tiled kernel: rows per workgroup tile
@@ -110,27 +114,40 @@ __host__ __device__ inline int row_gemm_blocks(int H, int F) {
   return MODE == kGemmGateUp ? (2 * F) / 128 : (MODE == kGemmDown ? H / 128 : (MODE == kGemmDA ? F / 64 : H / 64));
 }
 
+//
+// With a reduction split of 2 (g.stream_ksplit), a workgroup takes two
+// adjacent column blocks of one tile and each block's reduction is halved
+// between two waves; the upper half's partial sums are added to the lower
+// half's through LDS in a fixed order.  That doubles the waves streaming
+// weights when there are too few tiles to fill the chip.
 template <int MODE>
-__device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s_start, int* s_off, int* s_tmp) {
+__device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s_start, int* s_off, int* s_tmp,
+                                            f32x4* s_red) {
   constexpr bool NN = RowGemmShape<MODE>::kNN;
   build_tile_starts(g.offsets, g.E, kTileRows, s_start, s_off, s_tmp, 0, kBigRows);
 
   const int H = g.H, F = g.F;
   const int nblk = row_gemm_blocks<MODE>(H, F);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
-  // work item of this wave: (tile, column block); the four waves of a workgroup
-  // take adjacent column blocks of the same tile
-  const int item = wg * 4 + w;
+  const bool split = g.stream_ksplit == 2;
+  // work item of this wave: (tile, column block); the waves of a workgroup take
+  // adjacent column blocks of the same tile (with the split nblk is even, so
+  // both blocks of a workgroup fall on one tile)
+  const int item = split ? wg * 2 + (w & 1) : wg * 4 + w;
+  const int kpart = split ? (w >> 1) : 0;
   const TileSlot ts = lookup_tile(s_start, s_off, g.E, kTileRows, item / nblk);
-  if (ts.expert < 0) return;  // uniform across the wave; no block barrier follows
+  // uniform across the wave, and across the workgroup when split (before its barrier)
+  if (ts.expert < 0) return;
   const int nb = item % nblk;
   const int e = ts.expert;
   const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? H : (MODE == kGemmDown ? F : 2 * F);
+  const int Kp = split ? K / 2 : K;  // reduction length of this wave, from k_begin
+  const int k_begin = kpart * Kp;
 
   const bool a_ok = c < ts.rows;
   const uint16_t* __restrict__ A = (const uint16_t*)g.a;
   // rows past the tile read the tile's last row (always valid) and are zeroed at use
-  const uint16_t* a_row = A + (size_t)(ts.row_begin + (a_ok ? c : ts.rows - 1)) * K;
+  const uint16_t* a_row = A + (size_t)(ts.row_begin + (a_ok ? c : ts.rows - 1)) * K + k_begin;
 
   f32x4 acc[8];
 #pragma unroll
@@ -150,9 +167,9 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
       b_ptr = g.w0 + (size_t)e * F * H + nb * 128 + 8 * c;
       ldb = H;
     }
-    b_ptr += (size_t)(8 * gq) * ldb;
+    b_ptr += (size_t)(k_begin + 8 * gq) * ldb;
     const uint16_t* a_ptr = a_row + 8 * gq;
-    const int steps = K / 32, last = steps - 1;
+    const int steps = Kp / 32, last = steps - 1;
     auto load = [&](int s, u32x4* bq, u32x4& aq) {
       const uint16_t* bp = b_ptr + (size_t)s * 32 * ldb;
 #pragma unroll
@@ -200,9 +217,9 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
       Kw = F;
     }
     const uint16_t* a_ptr = a_row + 32 * gq;
-    const int stages = K / 128, last = stages - 1;
+    const int stages = Kp / 128, last = stages - 1;
     auto load = [&](int s, u32x4* bq, u32x4* aq) {
-      const int k0 = s * 128;
+      const int k0 = k_begin + s * 128;  // stages never straddle Kw (Kw % 128 == 0)
       const uint16_t* wp = (k0 < Kw) ? w_lo + k0 : w_hi + (k0 - Kw);
       wp += 32 * gq;
 #pragma unroll
@@ -210,7 +227,7 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
 #pragma unroll
         for (int q = 0; q < 4; ++q) bq[4 * jj + q] = *(const u32x4*)(wp + (size_t)jj * ldw + 8 * q);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) aq[q] = *(const u32x4*)(a_ptr + (size_t)k0 + 8 * q);
+      for (int q = 0; q < 4; ++q) aq[q] = *(const u32x4*)(a_ptr + (size_t)s * 128 + 8 * q);
     };
     auto compute = [&](const u32x4* bq, const u32x4* aq) {
 #pragma unroll
@@ -232,6 +249,20 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
       if (s + 1 < stages) compute(b1, a1);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  if (split) {
+    // upper reduction half -> LDS; the lower half adds it: acc(k < Kp) + acc(k >= Kp)
+    constexpr int NACC = NN ? 8 : 4;
+    f32x4* red = s_red + (w & 1) * NACC * kWave;
+    if (kpart == 1) {
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) red[j * kWave + l] = acc[j];
+    }
+    __syncthreads();
+    if (kpart == 1) return;
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) acc[j] = acc[j] + red[j * kWave + l];
   }
 
   // epilogue straight from registers: lane (c, gq) owns tile row c
@@ -576,7 +607,7 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, in
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kTBM * kTPitch];
   __shared__ __attribute__((aligned(16))) uint16_t s_b[2 * kTBN * kTPitch];
   if ((int)blockIdx.x < n_stream)
-    stream_gemm<MODE>(g, blockIdx.x, s_start, s_off, s_tmp);
+    stream_gemm<MODE>(g, blockIdx.x, s_start, s_off, s_tmp, reinterpret_cast<f32x4*>(s_a));
   else
     tile_gemm<MODE>(g, blockIdx.x - n_stream, s_start, s_off, s_tmp, s_a, s_b);
 }
@@ -689,14 +720,21 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(DwArgs g) {
 }  // namespace
 
 template <int MODE>
-hipError_t launch_row_gemm_mode(const RowGemmArgs& args, int max_rows, hipStream_t stream) {
+hipError_t launch_row_gemm_mode(const RowGemmArgs& args, int max_rows, int max_expert_rows, hipStream_t stream) {
   RowGemmArgs g = args;
   g.big_min_rows = big_gemm_min_rows(MODE, g.H, g.F);
+  if (max_expert_rows < g.big_min_rows) g.big_min_rows = kNoBigTiles;  // no launch of a kernel with no work
   const int64_t N = max_rows, E = g.E;
   // streaming kernel: experts with n_e < kBigRows, ceil(n_e / 16) tiles each
   const int64_t small_tiles = std::min<int64_t>((N + E * (kTileRows - 1)) / kTileRows,
                                                  E * ((kBigRows - 1 + kTileRows - 1) / kTileRows));
-  const int64_t n_stream = (small_tiles * row_gemm_blocks<MODE>(g.H, g.F) + 3) / 4;
+  // reduction split of the streaming kernel: needs whole K-steps (NN: 32,
+  // K-contiguous: 128) in each half
+  const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? g.H : (MODE == kGemmDown ? g.F : 2 * g.F);
+  const int kstep = RowGemmShape<MODE>::kNN ? 32 : 128;
+  const bool even_blocks = row_gemm_blocks<MODE>(g.H, g.F) % 2 == 0;
+  g.stream_ksplit = ((MOE_STREAM_SPLITK_MODES >> MODE) & 1) && K % (2 * kstep) == 0 && even_blocks ? 2 : 1;
+  const int64_t n_stream = (small_tiles * row_gemm_blocks<MODE>(g.H, g.F) * g.stream_ksplit + 3) / 4;
   // tiled kernel: experts with kBigRows <= n_e < g.big_min_rows, ceil(n_e / 128) tiles each
   const int64_t big_experts = std::min<int64_t>(E, N / kBigRows);
   const int64_t big_tiles = std::min<int64_t>((N + big_experts * (kTBM - 1)) / kTBM,
@@ -711,12 +749,13 @@ hipError_t launch_row_gemm_mode(const RowGemmArgs& args, int max_rows, hipStream
   return launch_big_gemm_bf16(MODE, g, max_rows, stream);
 }
 
-hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream) {
+hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, int max_expert_rows,
+                                hipStream_t stream) {
   switch (mode) {
-    case kGemmGateUp: return launch_row_gemm_mode<kGemmGateUp>(g, max_rows, stream);
-    case kGemmDown: return launch_row_gemm_mode<kGemmDown>(g, max_rows, stream);
-    case kGemmDA: return launch_row_gemm_mode<kGemmDA>(g, max_rows, stream);
-    default: return launch_row_gemm_mode<kGemmDX>(g, max_rows, stream);
+    case kGemmGateUp: return launch_row_gemm_mode<kGemmGateUp>(g, max_rows, max_expert_rows, stream);
+    case kGemmDown: return launch_row_gemm_mode<kGemmDown>(g, max_rows, max_expert_rows, stream);
+    case kGemmDA: return launch_row_gemm_mode<kGemmDA>(g, max_rows, max_expert_rows, stream);
+    default: return launch_row_gemm_mode<kGemmDX>(g, max_rows, max_expert_rows, stream);
   }
 }
 

@@ -33,7 +33,8 @@ struct RowGemmArgs {
   const uint16_t* h;
   uint16_t* out0;
   uint16_t* out1;
-  int big_min_rows;  // set by launch_row_gemm_bf16: experts from this row count take the 256-row kernel
+  int big_min_rows;   // set by launch_row_gemm_bf16: experts from this row count take the 256-row kernel
+  int stream_ksplit;  // set by launch_row_gemm_bf16: reduction split of the skinny-expert kernel (1 or 2)
 };
 
 struct DwArgs {
@@ -67,7 +68,10 @@ hipError_t launch_gather_rows(const int32_t* R_ptr, const int32_t* src, int max_
                               int a_bytes, const void* b_src, void* b_dst, int b_bytes, const void* c_src,
                               void* c_dst, int c_bytes, hipStream_t stream);
 
-hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
+// max_expert_rows bounds one expert's row count (a hint for kernel choice only:
+// experts above it are still computed, on the 128-row tiles)
+hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, int max_expert_rows,
+                                hipStream_t stream);
 hipError_t launch_dw_bf16(DwArgs g, hipStream_t stream);
 hipError_t launch_big_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
 // Row count from which an expert takes the 256-row kernel for this product and

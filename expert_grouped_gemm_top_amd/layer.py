@@ -64,7 +64,7 @@ class MoeLayerBuffers:
         moe.moe_dispatch(self.topk_idx, x, self.counts, self.offsets, self.perm, self.inv_perm, self.x_sorted,
                          self.ws, self.E, stream)
         moe.moe_grouped_swiglu_fwd(self.offsets, self.x_sorted, w_gate, w_up, w_down, self.h_save, self.a_save,
-                                   self.o_sorted, self.N, stream)
+                                   self.o_sorted, self.N, max_expert_rows=self.T, stream=stream)
         moe.moe_combine(self.o_sorted, self.inv_perm, self.topk_w, self.y, self.k, stream)
         return self.y
 

@@ -124,10 +124,15 @@ int moe_dispatch(int T, int H, int E, int k, int dtype, const int32_t* topk_idx,
  *   o_sorted[s] = a W_down[e]                                      (length H)
  * h_save[s] = [hg | hu] ([rows, 2F]) and a_save[s] = a ([rows, F]) are kept for
  * backward.  offsets [E+1] int32 (device); max_rows >= offsets[E] is a host
- * capacity (T*k) used only to size the launch; x_sorted [rows, H],
+ * capacity (T*k) used only to size the launch; max_expert_rows >= 0 is a host
+ * bound on one expert's row count used only to pick kernels (T for rows from
+ * moe_dispatch, since top-k picks distinct experts per token; max_rows when
+ * unknown): a bound below an actual count costs speed, never correctness,
+ * and results do not depend on it beyond rounding; x_sorted [rows, H],
  * w_gate/w_up [E, H, F], w_down [E, F, H] (device); h_save, a_save, o_sorted
  * (device, out).  Rows of empty experts: nothing. */
-int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int dtype, const int32_t* offsets,
+int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int max_expert_rows, int dtype,
+                           const int32_t* offsets,
                            const void* x_sorted, const void* w_gate, const void* w_up,
                            const void* w_down, void* h_save, void* a_save, void* o_sorted,
                            void* stream);
