@@ -92,8 +92,9 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 first, u32x4 second, f32x4 acc)
 // N-contiguous weights (GATEUP, DOWN): a wave covers 128 output columns; per
 // K-step of 32 a lane loads 8 rows x 16 B, so one load instruction reads 4 rows
 // x 256 contiguous bytes.  K-contiguous weights (DA, DX): a wave covers 64
-// output columns; per K-stage of 128 a lane loads 4 consecutive 16 B chunks of
-// each of its 4 weight rows, so every row is read in 256-byte runs.
+// output columns; per K-stage of 128 one load instruction again reads 4 rows x
+// 256 contiguous bytes, and the stage is turned into MFMA fragments through
+// LDS.
 template <int MODE>
 struct RowGemmShape;
 template <>
@@ -122,7 +123,7 @@ __host__ __device__ inline int row_gemm_blocks(int H, int F) {
 // weights when there are too few tiles to fill the chip.
 template <int MODE>
 __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s_start, int* s_off, int* s_tmp,
-                                            f32x4* s_red) {
+                                            unsigned char* lds) {
   constexpr bool NN = RowGemmShape<MODE>::kNN;
   build_tile_starts(g.offsets, g.E, kTileRows, s_start, s_off, s_tmp, 0, kBigRows);
 
@@ -199,42 +200,53 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    // B operand: weight rows n = col0 + 4c + jj (jj = 0..3), k chunks
-    // k0 + 32gq + 8q (q = 0..3) -- 64 contiguous bytes per lane and row
+    // K-contiguous weights, stage = 64 weight rows x 128 k.  One load
+    // instruction reads 4 rows x 256 contiguous bytes (16 lanes per row); the
+    // stage goes through this wave's 16 KiB of LDS (16-byte chunks XOR-swizzled
+    // by row & 15) and comes back as MFMA fragments: lane (c, gq) takes weight
+    // rows c + 16 jj, k chunks 4 gq + q, matching its activation chunks.
+    // LDS operations of one wave complete in order, so no barrier is needed.
+    const int lrow = l >> 4, lchunk = l & 15;
     const uint16_t* w_lo;  // rows for k in [0, Kw)
     const uint16_t* w_hi;  // DX only: rows for k in [F, 2F)
     size_t ldw;
     int Kw;
     if (MODE == kGemmDA) {
-      w_lo = g.w0 + (size_t)e * F * H + (size_t)(nb * 64 + 4 * c) * H;
+      w_lo = g.w0 + (size_t)e * F * H + (size_t)(nb * 64 + lrow) * H + 8 * lchunk;
       w_hi = w_lo;
       ldw = H;
       Kw = K;
     } else {
-      w_lo = g.w0 + (size_t)e * H * F + (size_t)(nb * 64 + 4 * c) * F;
-      w_hi = g.w1 + (size_t)e * H * F + (size_t)(nb * 64 + 4 * c) * F;
+      w_lo = g.w0 + (size_t)e * H * F + (size_t)(nb * 64 + lrow) * F + 8 * lchunk;
+      w_hi = g.w1 + (size_t)e * H * F + (size_t)(nb * 64 + lrow) * F + 8 * lchunk;
       ldw = F;
       Kw = F;
     }
+    unsigned char* xs = lds + w * 16384;
     const uint16_t* a_ptr = a_row + 32 * gq;
     const int stages = Kp / 128, last = stages - 1;
     auto load = [&](int s, u32x4* bq, u32x4* aq) {
       const int k0 = k_begin + s * 128;  // stages never straddle Kw (Kw % 128 == 0)
       const uint16_t* wp = (k0 < Kw) ? w_lo + k0 : w_hi + (k0 - Kw);
-      wp += 32 * gq;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bq[4 * jj + q] = *(const u32x4*)(wp + (size_t)jj * ldw + 8 * q);
+      for (int i = 0; i < 16; ++i) bq[i] = *(const u32x4*)(wp + (size_t)(4 * i) * ldw);
 #pragma unroll
       for (int q = 0; q < 4; ++q) aq[q] = *(const u32x4*)(a_ptr + (size_t)s * 128 + 8 * q);
     };
     auto compute = [&](const u32x4* bq, const u32x4* aq) {
 #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 4 * i + lrow;
+        *(u32x4*)(xs + row * 256 + 16 * (lchunk ^ (row & 15))) = bq[i];
+      }
+#pragma unroll
       for (int q = 0; q < 4; ++q) {
         const u32x4 av = a_ok ? aq[q] : zero4;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[jj] = mfma_bf16(bq[4 * jj + q], av, acc[jj]);
+        for (int jj = 0; jj < 4; ++jj) {
+          const u32x4 bv = *(const u32x4*)(xs + (c + 16 * jj) * 256 + 16 * ((4 * gq + q) ^ c));
+          acc[jj] = mfma_bf16(bv, av, acc[jj]);
+        }
       }
     };
     u32x4 b0[16], b1[16], a0[4], a1[4];
@@ -253,8 +265,9 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
 
   if (split) {
     // upper reduction half -> LDS; the lower half adds it: acc(k < Kp) + acc(k >= Kp)
+    // in the LDS of the upper-half wave (w = 2, 3), which only it has used
     constexpr int NACC = NN ? 8 : 4;
-    f32x4* red = s_red + (w & 1) * NACC * kWave;
+    f32x4* red = reinterpret_cast<f32x4*>(lds + (2 + (w & 1)) * 16384);
     if (kpart == 1) {
 #pragma unroll
       for (int j = 0; j < NACC; ++j) red[j * kWave + l] = acc[j];
@@ -302,46 +315,29 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
       *(u32x4*)(orow + 8 * r) = u32x4{pack_bf2(acc[0][r], acc[1][r]), pack_bf2(acc[2][r], acc[3][r]),
                                       pack_bf2(acc[4][r], acc[5][r]), pack_bf2(acc[6][r], acc[7][r])};
   } else {
-    // MFMA jj, register r: column 64 nb + 16 gq + 4 r + jj
-    float v[16];
+    // MFMA jj, register r: column 64 nb + 16 jj + 4 gq + r
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int jj = 0; jj < 4; ++jj) {
+      const int col = nb * 64 + 16 * jj + 4 * gq;
+      if (MODE == kGemmDA) {
+        // SwiGLU backward with the saved pre-activations hg, hu
+        const uint16_t* hrow = g.h + grow * 2 * F;
+        const u32x2 gw = *(const u32x2*)(hrow + col), uw = *(const u32x2*)(hrow + F + col);
+        float dg[4], du[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) v[4 * r + jj] = acc[jj][r];
-    const int col = nb * 64 + 16 * gq;
-    if (MODE == kGemmDA) {
-      // SwiGLU backward with the saved pre-activations hg, hu
-      const uint16_t* hrow = g.h + grow * 2 * F;
-      const u32x4 g0 = *(const u32x4*)(hrow + col), g1 = *(const u32x4*)(hrow + col + 8);
-      const u32x4 u0 = *(const u32x4*)(hrow + F + col), u1 = *(const u32x4*)(hrow + F + col + 8);
-      float dg[16], du[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t gw = (i < 8) ? g0[(i & 7) >> 1] : g1[(i & 7) >> 1];
-        const uint32_t uw = (i < 8) ? u0[(i & 7) >> 1] : u1[(i & 7) >> 1];
-        const float hgv = (i & 1) ? bf_hi(gw) : bf_lo(gw);
-        const float huv = (i & 1) ? bf_hi(uw) : bf_lo(uw);
-        const float sg = sigmoidf_fast(hgv);
-        dg[i] = v[i] * huv * sg * (1.0f + hgv * (1.0f - sg));
-        du[i] = v[i] * hgv * sg;
-      }
-      uint16_t* drow = g.out0 + grow * 2 * F;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float* G = dg + 8 * h;
-        const float* U = du + 8 * h;
-        *(u32x4*)(drow + col + 8 * h) =
-            u32x4{pack_bf2(G[0], G[1]), pack_bf2(G[2], G[3]), pack_bf2(G[4], G[5]), pack_bf2(G[6], G[7])};
-        *(u32x4*)(drow + F + col + 8 * h) =
-            u32x4{pack_bf2(U[0], U[1]), pack_bf2(U[2], U[3]), pack_bf2(U[4], U[5]), pack_bf2(U[6], U[7])};
-      }
-    } else {
-      uint16_t* orow = g.out0 + grow * H + col;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float* V = v + 8 * h;
-        *(u32x4*)(orow + 8 * h) =
-            u32x4{pack_bf2(V[0], V[1]), pack_bf2(V[2], V[3]), pack_bf2(V[4], V[5]), pack_bf2(V[6], V[7])};
+        for (int r = 0; r < 4; ++r) {
+          const float hgv = (r & 1) ? bf_hi(gw[r >> 1]) : bf_lo(gw[r >> 1]);
+          const float huv = (r & 1) ? bf_hi(uw[r >> 1]) : bf_lo(uw[r >> 1]);
+          const float sg = sigmoidf_fast(hgv);
+          dg[r] = acc[jj][r] * huv * sg * (1.0f + hgv * (1.0f - sg));
+          du[r] = acc[jj][r] * hgv * sg;
+        }
+        uint16_t* drow = g.out0 + grow * 2 * F;
+        *(u32x2*)(drow + col) = u32x2{pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3])};
+        *(u32x2*)(drow + F + col) = u32x2{pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3])};
+      } else {
+        *(u32x2*)(g.out0 + grow * H + col) =
+            u32x2{pack_bf2(acc[jj][0], acc[jj][1]), pack_bf2(acc[jj][2], acc[jj][3])};
       }
     }
   }
@@ -604,12 +600,14 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, int n_stream, int n_tile) {
   __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kTBM * kTPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[2 * kTBN * kTPitch];
+  // 64 KiB: the tiled kernel's double-buffered A and B tiles, or the streaming
+  // kernel's four per-wave 16 KiB areas
+  __shared__ __attribute__((aligned(16))) uint16_t s_ab[2 * kTBM * kTPitch + 2 * kTBN * kTPitch];
+  static_assert(sizeof(s_ab) == 4 * 16384, "streaming kernel: 16 KiB of LDS per wave");
   if ((int)blockIdx.x < n_stream)
-    stream_gemm<MODE>(g, blockIdx.x, s_start, s_off, s_tmp, reinterpret_cast<f32x4*>(s_a));
+    stream_gemm<MODE>(g, blockIdx.x, s_start, s_off, s_tmp, reinterpret_cast<unsigned char*>(s_ab));
   else
-    tile_gemm<MODE>(g, blockIdx.x - n_stream, s_start, s_off, s_tmp, s_a, s_b);
+    tile_gemm<MODE>(g, blockIdx.x - n_stream, s_start, s_off, s_tmp, s_ab, s_ab + 2 * kTBM * kTPitch);
 }
 
 // ---- dW GEMM ------------------------------------------------------------------
