@@ -42,8 +42,10 @@ namespace moe {
 
 namespace {
 
-#ifndef MOE_STREAM_SPLITK_MODES
-#define MOE_STREAM_SPLITK_MODES ((1 << kGemmGateUp) | (1 << kGemmDA))  // modes whose skinny-expert reduction is split
+// Reduction split of the skinny-expert kernel per product, 4 bits each
+// (GATEUP, DOWN, DA, DX from the low end): 1, 2 or 4 waves per column block.
+#ifndef MOE_STREAM_SPLITK
+#define MOE_STREAM_SPLITK 0x1212
 #endif
 
 constexpr int kTileRows = 16;  // rows of one expert per wave tile of the streaming kernel (one MFMA row block)
@@ -116,11 +118,11 @@ __host__ __device__ inline int row_gemm_blocks(int H, int F) {
 }
 
 //
-// With a reduction split of 2 (g.stream_ksplit), a workgroup takes two
-// adjacent column blocks of one tile and each block's reduction is halved
-// between two waves; the upper half's partial sums are added to the lower
-// half's through LDS in a fixed order.  That doubles the waves streaming
-// weights when there are too few tiles to fill the chip.
+// With a reduction split of S = 2 or 4 (g.stream_ksplit), a workgroup takes
+// 4 / S adjacent column blocks of one tile and each block's reduction is cut
+// into S parts run by S waves; the partial sums of parts 1.. are added to part
+// 0's through LDS in part order.  That multiplies the waves streaming weights
+// when there are too few tiles to fill the chip.
 template <int MODE>
 __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s_start, int* s_off, int* s_tmp,
                                             unsigned char* lds) {
@@ -130,19 +132,21 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   const int H = g.H, F = g.F;
   const int nblk = row_gemm_blocks<MODE>(H, F);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
-  const bool split = g.stream_ksplit == 2;
+  const int ks = g.stream_ksplit;  // 1, 2 or 4
+  const bool split = ks > 1;
+  const int cpw = 4 / ks;  // column blocks per workgroup
   // work item of this wave: (tile, column block); the waves of a workgroup take
-  // adjacent column blocks of the same tile (with the split nblk is even, so
-  // both blocks of a workgroup fall on one tile)
-  const int item = split ? wg * 2 + (w & 1) : wg * 4 + w;
-  const int kpart = split ? (w >> 1) : 0;
+  // adjacent column blocks of the same tile (when split, nblk is a multiple of
+  // cpw, so all blocks of a workgroup fall on one tile)
+  const int item = wg * cpw + (w % cpw);
+  const int kpart = w / cpw;
   const TileSlot ts = lookup_tile(s_start, s_off, g.E, kTileRows, item / nblk);
   // uniform across the wave, and across the workgroup when split (before its barrier)
   if (ts.expert < 0) return;
   const int nb = item % nblk;
   const int e = ts.expert;
   const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? H : (MODE == kGemmDown ? F : 2 * F);
-  const int Kp = split ? K / 2 : K;  // reduction length of this wave, from k_begin
+  const int Kp = K / ks;  // reduction length of this wave, from k_begin
   const int k_begin = kpart * Kp;
 
   const bool a_ok = c < ts.rows;
@@ -264,18 +268,21 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   }
 
   if (split) {
-    // upper reduction half -> LDS; the lower half adds it: acc(k < Kp) + acc(k >= Kp)
-    // in the LDS of the upper-half wave (w = 2, 3), which only it has used
+    // parts 1.. -> each into its own wave's LDS area (which only it has used);
+    // part 0 adds them in part order
     constexpr int NACC = NN ? 8 : 4;
-    f32x4* red = reinterpret_cast<f32x4*>(lds + (2 + (w & 1)) * 16384);
-    if (kpart == 1) {
+    if (kpart > 0) {
+      f32x4* red = reinterpret_cast<f32x4*>(lds + w * 16384);
 #pragma unroll
       for (int j = 0; j < NACC; ++j) red[j * kWave + l] = acc[j];
     }
     __syncthreads();
-    if (kpart == 1) return;
+    if (kpart > 0) return;
+    for (int p = 1; p < ks; ++p) {
+      const f32x4* red = reinterpret_cast<const f32x4*>(lds + (w + p * cpw) * 16384);
 #pragma unroll
-    for (int j = 0; j < NACC; ++j) acc[j] = acc[j] + red[j * kWave + l];
+      for (int j = 0; j < NACC; ++j) acc[j] = acc[j] + red[j * kWave + l];
+    }
   }
 
   // epilogue straight from registers: lane (c, gq) owns tile row c
@@ -730,8 +737,9 @@ hipError_t launch_row_gemm_mode(const RowGemmArgs& args, int max_rows, int max_e
   // K-contiguous: 128) in each half
   const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? g.H : (MODE == kGemmDown ? g.F : 2 * g.F);
   const int kstep = RowGemmShape<MODE>::kNN ? 32 : 128;
-  const bool even_blocks = row_gemm_blocks<MODE>(g.H, g.F) % 2 == 0;
-  g.stream_ksplit = ((MOE_STREAM_SPLITK_MODES >> MODE) & 1) && K % (2 * kstep) == 0 && even_blocks ? 2 : 1;
+  int ks = (MOE_STREAM_SPLITK >> (4 * MODE)) & 0xf;
+  while (ks > 1 && (K % (ks * kstep) != 0 || row_gemm_blocks<MODE>(g.H, g.F) % (4 / ks) != 0)) ks /= 2;
+  g.stream_ksplit = ks;
   const int64_t n_stream = (small_tiles * row_gemm_blocks<MODE>(g.H, g.F) * g.stream_ksplit + 3) / 4;
   // tiled kernel: experts with kBigRows <= n_e < g.big_min_rows, ceil(n_e / 128) tiles each
   const int64_t big_experts = std::min<int64_t>(E, N / kBigRows);

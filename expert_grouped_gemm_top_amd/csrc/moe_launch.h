@@ -34,7 +34,7 @@ struct RowGemmArgs {
   uint16_t* out0;
   uint16_t* out1;
   int big_min_rows;   // set by launch_row_gemm_bf16: experts from this row count take the 256-row kernel
-  int stream_ksplit;  // set by launch_row_gemm_bf16: reduction split of the skinny-expert kernel (1 or 2)
+  int stream_ksplit;  // set by launch_row_gemm_bf16: reduction split of the skinny-expert kernel (1, 2 or 4)
 };
 
 struct DwArgs {
