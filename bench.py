@@ -68,10 +68,15 @@ TRAFFIC_FILE = {K_GATEUP: "gemm_gateup", K_DOWN: "gemm_down", K_DA: "gemm_da", K
 
 
 def sources_digest(kernel):
+    """sha256 of the kernel's sources with comments and blank space removed
+    (an edit of a comment does not change the kernel)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "expert_grouped_gemm_top_amd", "csrc", name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(ROOT, "expert_grouped_gemm_top_amd", "csrc", name)) as f:
+            code = re.sub(r"/\*.*?\*/", " ", f.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        code = " ".join(code.split())
+        h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 

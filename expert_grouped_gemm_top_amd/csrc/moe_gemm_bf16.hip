@@ -1,5 +1,6 @@
 // moe_gemm_bf16.hip -- ragged grouped GEMMs of the SwiGLU experts in bf16 on
-// gfx950 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// gfx950 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulate): the
+// skinny-expert and mid-size regimes of the row GEMMs, and the dW GEMM.
 //
 // Expert forward, backward dx and dW (npu-train issue #14, sections Proposal
 // and Scope), run as variable-size grouped GEMMs over each expert's own row
@@ -10,21 +11,17 @@
 //   DOWN    [n_e,F] x W_down[e]        (W [F,H], N-contiguous)  -> o
 //   DA      [n_e,H] x W_down[e]^T      (W [F,H], K-contiguous)  -> dh=[dHg|dHu] (SwiGLU backward)
 //   DX      [n_e,2F] x [W_gate|W_up][e]^T (K-contiguous)        -> dX
-// Each workgroup owns one 32-row tile of one expert (found on the device from
-// the offsets, see find_row_tile) and one block of output columns; its four
-// waves split K four ways, stream operands straight from global memory into
-// MFMA registers (no LDS round trip: at the routed row counts of these layers
-// the weights are read once and are the traffic that bounds the kernel), and
-// reduce their fp32 partial tiles through LDS before the fused epilogue.
-//
-// Operand mapping inside a wave (lane l: c = l % 16, g = l / 16):
-//   A (rows, K-contiguous): lane loads 8 consecutive k (k0 + 8g ..) of row c.
-//   B columns are split into 8 interleaved sub-tiles: MFMA number jj covers
-//   columns 8c + jj (c = 0..15).  N-contiguous weights: the lane loads rows
-//   k0 + 8g + (0..7) x columns 8c .. 8c+7 (16 B each) and transposes the 8x8
-//   bf16 block in registers; K-contiguous weights: one 16 B load per column.
-//   The MFMA runs with B as its first operand, so lane (c, g) ends up holding
-//   row c and columns 32g + (0..31) of the tile: contiguous output segments.
+// One launch covers two regimes, both scheduled on the device from the
+// offsets (build_tile_starts / lookup_tile):
+//   * experts with fewer than 48 rows: every wave streams one 16-row tile x one
+//     column block straight from memory (the weights are the traffic), with
+//     an optional split of K between waves of a workgroup;
+//   * experts with 48 .. big_min_rows rows: 128 x 128 workgroup tiles staged
+//     through double-buffered, swizzled LDS.
+// Experts with more rows run in the 256-row kernel of moe_gemm_big.hip.
+// In every case the MFMA takes the weights as its first operand, so a lane
+// ends up holding one output row and contiguous columns, and the epilogue
+// (SwiGLU forward or backward) is applied from registers.
 //
 // dW GEMM (K = the expert's rows, ragged):
 //   dW_gate|dW_up [H, 2F] = x_rows^T [dHg|dHu],  dW_down [F, H] = a_rows^T dO_rows
