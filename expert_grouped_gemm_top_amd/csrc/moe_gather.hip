@@ -10,6 +10,8 @@
 // Every thread moves 8 elements (16 B of bf16, 32 B of fp32) per step; a token
 // row is read once and its k expert rows are gathered with full-row coalesced
 // loads.  Sums run in fp32 in ascending j and are rounded once.
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -42,83 +44,103 @@ struct Vec8<uint16_t> {
   }
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(int Tn, int H, int k, const T* __restrict__ rows,
+// The k pair slots of a token are handled with KP >= k compile-time slots
+// (KP a power of two); every row load is issued before any of them is used.
+// Slots past k and skipped pairs (inv < 0) load a harmless in-bounds address
+// (the token's own row of another tensor) and are masked out by a select, so
+// the loads need no branches and stay in flight together.
+
+// One thread per (token, 16-byte chunk of the row).  HAS_W: router weights
+// given (else every weight is 1).
+template <typename T, int KP, bool HAS_W>
+__global__ __launch_bounds__(128) void combine_kernel(int Tn, int H, int k, const T* __restrict__ rows,
                                                       const int32_t* __restrict__ inv, const float* __restrict__ w,
                                                       T* __restrict__ out) {
   const int chunks = H / 8;
-  for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
-    int src[kMaxTopK];
-    float wt[kMaxTopK];
+  const int64_t items = (int64_t)Tn * chunks;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(it / chunks), c = (int)(it % chunks);
+    int src[KP];
+    float wt[KP];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      src[j] = (j < k) ? inv[(size_t)t * k + j] : -1;
-      wt[j] = (j < k && w != nullptr) ? w[(size_t)t * k + j] : 1.0f;
+    for (int j = 0; j < KP; ++j) {
+      const size_t p = (size_t)t * k + (j < k ? j : k - 1);  // in bounds: loads need no branch
+      const int32_t iv = inv[p];
+      src[j] = (j < k) ? iv : -1;
+      wt[j] = HAS_W ? w[p] : 1.0f;
     }
-    for (int c = threadIdx.x; c < chunks; c += 256) {
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    T* orow = out + (size_t)t * H + c * 8;
+    float v[KP][8];
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k && src[j] >= 0) {
-          float v[8];
-          Vec8<T>::load(rows + (size_t)src[j] * H + c * 8, v);
+    for (int j = 0; j < KP; ++j)
+      Vec8<T>::load(src[j] >= 0 ? rows + (size_t)src[j] * H + c * 8 : (const T*)orow, v[j]);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += wt[j] * v[i];
-        }
-      }
-      Vec8<T>::store(out + (size_t)t * H + c * 8, acc);
-    }
+    for (int j = 0; j < KP; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = (src[j] >= 0) ? acc[i] + wt[j] * v[j][i] : acc[i];
+    Vec8<T>::store(orow, acc);
   }
 }
 
-// One block per token.  dg needs a block-wide dot product per pair.
-template <typename T>
+// One block per token (dg needs a block-wide dot product per pair).  DG: dg is
+// wanted (o_sorted and inv_all are then valid; a pair without a row reads row 0
+// and is masked).
+template <typename T, int KP, bool DG>
 __global__ __launch_bounds__(256) void grad_rows_kernel(int Tn, int H, int k, const T* __restrict__ dy,
                                                         const float* __restrict__ w, const int32_t* __restrict__ inv,
                                                         T* __restrict__ dO_rows, const int32_t* __restrict__ inv_all,
                                                         const T* __restrict__ o_sorted, float* __restrict__ dg) {
-  __shared__ float s_part[4][kMaxTopK];
+  __shared__ float s_part[4][KP];
   const int chunks = H / 8;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
-    int dst[kMaxTopK], osrc[kMaxTopK];
-    float wt[kMaxTopK], dot[kMaxTopK];
+    // lane j of every wave fetches slot j's indices (one load per array, all
+    // in flight together); the slots are then broadcast from those lanes
+    const size_t pl = (size_t)t * k + (lane < k ? lane : k - 1);
+    const int32_t inv_l = inv[pl];
+    const float w_l = w[pl];
+    const int32_t ia_l = DG ? inv_all[pl] : -1;
+    int dst[KP], osrc[KP];
+    float wt[KP], dot[KP];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      const size_t p = (size_t)t * k + j;
-      dst[j] = (j < k) ? inv[p] : -1;
-      wt[j] = (j < k) ? w[p] : 0.0f;
-      osrc[j] = (j < k && dg != nullptr) ? inv_all[p] : -1;
+    for (int j = 0; j < KP; ++j) {
+      dst[j] = (j < k) ? __builtin_amdgcn_readlane(inv_l, j) : -1;
+      wt[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), j));
+      osrc[j] = (DG && j < k) ? __builtin_amdgcn_readlane(ia_l, j) : -1;
       dot[j] = 0.0f;
     }
+    const T* dyrow = dy + (size_t)t * H;
     for (int c = tid; c < chunks; c += 256) {
       float g[8];
-      Vec8<T>::load(dy + (size_t)t * H + c * 8, g);
+      Vec8<T>::load(dyrow + c * 8, g);
+      float o[KP][8];
+      if constexpr (DG) {
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k && dst[j] >= 0) {
+        for (int j = 0; j < KP; ++j)
+          Vec8<T>::load(o_sorted + (size_t)(osrc[j] >= 0 ? osrc[j] : 0) * H + c * 8, o[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        if (dst[j] >= 0) {
           float v[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) v[i] = wt[j] * g[i];
           Vec8<T>::store(dO_rows + (size_t)dst[j] * H + c * 8, v);
         }
-        if (j < k && osrc[j] >= 0) {
-          float o[8];
-          Vec8<T>::load(o_sorted + (size_t)osrc[j] * H + c * 8, o);
+        if constexpr (DG) {
           float s = 0.0f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) s += g[i] * o[i];
-          dot[j] += s;
+          for (int i = 0; i < 8; ++i) s += g[i] * o[j][i];
+          dot[j] += (osrc[j] >= 0) ? s : 0.0f;
         }
       }
     }
-    if (dg != nullptr) {
+    if constexpr (DG) {
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k) {
-          const float s = wave_sum(dot[j]);
-          if (lane == 0) s_part[wv][j] = s;
-        }
+      for (int j = 0; j < KP; ++j) {
+        const float s = wave_sum(dot[j]);
+        if (lane == 0) s_part[wv][j] = s;
       }
       __syncthreads();
       if (tid < k) dg[(size_t)t * k + tid] = s_part[0][tid] + s_part[1][tid] + s_part[2][tid] + s_part[3][tid];
@@ -149,16 +171,64 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restr
 
 inline int token_grid(int T) { return T < 16384 ? T : 16384; }
 
+
+template <typename T, int KP>
+void launch_combine_kp(int T_, int H, int k, const void* rows, const int32_t* inv, const float* w, void* out,
+                       hipStream_t stream) {
+  const int64_t items = (int64_t)T_ * (H / 8);
+  const int64_t blocks = std::min<int64_t>((items + 127) / 128, 65536);
+  if (w != nullptr)
+    hipLaunchKernelGGL((combine_kernel<T, KP, true>), dim3((unsigned)blocks), dim3(128), 0, stream, T_, H, k,
+                       (const T*)rows, inv, w, (T*)out);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, KP, false>), dim3((unsigned)blocks), dim3(128), 0, stream, T_, H, k,
+                       (const T*)rows, inv, w, (T*)out);
+}
+
+template <typename T, int KP>
+void launch_grad_rows_kp(int T_, int H, int k, const void* dy, const float* w, const int32_t* inv, void* dO_rows,
+                         const int32_t* inv_all, const void* o_sorted, float* dg, hipStream_t stream) {
+  if (dg != nullptr)
+    hipLaunchKernelGGL((grad_rows_kernel<T, KP, true>), dim3(token_grid(T_)), dim3(256), 0, stream, T_, H, k,
+                       (const T*)dy, w, inv, (T*)dO_rows, inv_all, (const T*)o_sorted, dg);
+  else
+    hipLaunchKernelGGL((grad_rows_kernel<T, KP, false>), dim3(token_grid(T_)), dim3(256), 0, stream, T_, H, k,
+                       (const T*)dy, w, inv, (T*)dO_rows, inv_all, (const T*)o_sorted, dg);
+}
+
+// k -> the smallest power-of-two slot count KP >= k (k <= 16)
+template <typename T, template <typename, int> class L, typename... A>
+void dispatch_kp(int k, A... a) {
+  if (k <= 1) L<T, 1>::run(a...);
+  else if (k <= 2) L<T, 2>::run(a...);
+  else if (k <= 4) L<T, 4>::run(a...);
+  else if (k <= 8) L<T, 8>::run(a...);
+  else L<T, 16>::run(a...);
+}
+
+template <typename T, int KP>
+struct CombineL {
+  static void run(int T_, int H, int k, const void* rows, const int32_t* inv, const float* w, void* out,
+                  hipStream_t s) {
+    launch_combine_kp<T, KP>(T_, H, k, rows, inv, w, out, s);
+  }
+};
+template <typename T, int KP>
+struct GradRowsL {
+  static void run(int T_, int H, int k, const void* dy, const float* w, const int32_t* inv, void* dO_rows,
+                  const int32_t* inv_all, const void* o_sorted, float* dg, hipStream_t s) {
+    launch_grad_rows_kp<T, KP>(T_, H, k, dy, w, inv, dO_rows, inv_all, o_sorted, dg, s);
+  }
+};
+
 }  // namespace
 
 hipError_t launch_combine(int T, int H, int k, int esize, const void* rows, const int32_t* inv, const float* w,
                           void* out, hipStream_t stream) {
   if (esize == 4)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, k,
-                       (const float*)rows, inv, w, (float*)out);
+    dispatch_kp<float, CombineL>(k, T, H, k, rows, inv, w, out, stream);
   else
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, k,
-                       (const uint16_t*)rows, inv, w, (uint16_t*)out);
+    dispatch_kp<uint16_t, CombineL>(k, T, H, k, rows, inv, w, out, stream);
   return hipGetLastError();
 }
 
@@ -166,11 +236,9 @@ hipError_t launch_grad_rows(int T, int H, int k, int esize, const void* dy, cons
                             void* dO_rows, const int32_t* inv_all, const void* o_sorted, float* dg,
                             hipStream_t stream) {
   if (esize == 4)
-    hipLaunchKernelGGL(grad_rows_kernel<float>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, k,
-                       (const float*)dy, w, inv, (float*)dO_rows, inv_all, (const float*)o_sorted, dg);
+    dispatch_kp<float, GradRowsL>(k, T, H, k, dy, w, inv, dO_rows, inv_all, o_sorted, dg, stream);
   else
-    hipLaunchKernelGGL(grad_rows_kernel<uint16_t>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, k,
-                       (const uint16_t*)dy, w, inv, (uint16_t*)dO_rows, inv_all, (const uint16_t*)o_sorted, dg);
+    dispatch_kp<uint16_t, GradRowsL>(k, T, H, k, dy, w, inv, dO_rows, inv_all, o_sorted, dg, stream);
   return hipGetLastError();
 }
 

@@ -11,67 +11,71 @@ namespace moe {
 
 namespace {
 
-constexpr int kPerLane = kMaxExperts / kWave;  // logits held per lane (E <= 256)
-
 // (va, ia) ranks before (vb, ib)?
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// One wavefront per token; lane l holds the logits of experts l + 64 i
+// (i < SLOTS = ceil(E / 64)).  Every lane computes the rank of each of its
+// logits under the order above by comparing it with all E logits of the token
+// (read back from LDS as broadcasts); the ranks are distinct, and a logit of
+// rank r < k is the token's r-th selection.  The weights are the softmax over
+// the k selected logits, shifted by the largest one.
+template <int SLOTS>
 __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k, const float* __restrict__ logits,
                                                          int32_t* __restrict__ idx, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) float s_l[4][kMaxExperts];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wave exits together
+  if (t >= T) return;  // whole wave exits; only this wave's LDS row is used below
   const float* lt = logits + (size_t)t * E;
-  float v[kPerLane];
-  bool live[kPerLane];
+  float v[SLOTS];
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
-    const int e = lane + i * kWave;
-    live[i] = e < E;
-    v[i] = live[i] ? lt[e] : 0.0f;
+  for (int i = 0; i < SLOTS; ++i) v[i] = lt[min(lane + 64 * i, E - 1)];  // in bounds, no branch
+  const int E4 = (E + 3) & ~3;
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const int e = lane + 64 * i;
+    // entries E..E4-1 are -inf: they never rank before a finite logit
+    if (e < E4) s_l[wv][e] = (e < E) ? v[i] : -__builtin_inff();
   }
-  float sel_v = 0.0f;  // lane j (< k) keeps the j-th selected logit
-  int sel_e = 0;
-  float top = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    // lane-local best among the experts not taken yet
-    float bv = 0.0f;
-    int be = 0x7fffffff;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the wave's LDS writes before its reads
+  int rank[SLOTS];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      const int e = lane + i * kWave;
-      if (live[i] && (be == 0x7fffffff || ranks_before(v[i], e, bv, be))) {
-        bv = v[i];
-        be = e;
-      }
-    }
-    // wave arg-max under the same order (butterfly: every lane ends with the winner)
+  for (int i = 0; i < SLOTS; ++i) rank[i] = 0;
+  for (int j = 0; j < E4; j += 4) {
+    const f32x4 q = *(const f32x4*)&s_l[wv][j];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      if (oe != 0x7fffffff && (be == 0x7fffffff || ranks_before(ov, oe, bv, be))) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (j == 0) top = bv;
-    if (lane == j) {
-      sel_v = bv;
-      sel_e = be;
-    }
-    // retire the winner in its owning lane
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i)
-      if (lane + i * kWave == be) live[i] = false;
+      for (int i = 0; i < SLOTS; ++i) rank[i] += ranks_before(q[u], j + u, v[i], lane + 64 * i) ? 1 : 0;
   }
-  const float ex = (lane < k) ? expf(sel_v - top) : 0.0f;
-  const float denom = wave_sum(ex);
-  if (lane < k) {
-    idx[(size_t)t * k + lane] = sel_e;
-    w[(size_t)t * k + lane] = ex / denom;
+  float top = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i)
+    if (lane + 64 * i < E) top = fmaxf(top, v[i]);
+  top = wave_max(top);
+  float ex[SLOTS], part = 0.0f;
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const bool sel = lane + 64 * i < E && rank[i] < k;
+    ex[i] = sel ? expf(v[i] - top) : 0.0f;
+    part += ex[i];
+  }
+  const float denom = wave_sum(part);
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    if (lane + 64 * i < E && rank[i] < k) {
+      idx[(size_t)t * k + rank[i]] = lane + 64 * i;
+      w[(size_t)t * k + rank[i]] = ex[i] / denom;
+    }
   }
 }
 
@@ -79,8 +83,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k, co
 
 hipError_t launch_route_topk(int T, int E, int k, const float* logits, int32_t* idx, float* w,
                              hipStream_t stream) {
-  const int blocks = (T + 3) / 4;
-  hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(256), 0, stream, T, E, k, logits, idx, w);
+  const dim3 grid((T + 3) / 4), block(256);
+  switch ((E + 63) / 64) {
+    case 1: hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
+    case 2: hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
+    case 3: hipLaunchKernelGGL(route_topk_kernel<3>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
+    default: hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
+  }
   return hipGetLastError();
 }
 

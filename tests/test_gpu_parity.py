@@ -143,7 +143,8 @@ def _gpu_route(logits, k):
     return idx.cpu().numpy(), w.cpu().numpy()
 
 
-@pytest.mark.parametrize("T,E,k", [(64, 256, 16), (33, 256, 1), (17, 8, 8), (5, 1, 1), (300, 128, 8), (7, 65, 3)])
+@pytest.mark.parametrize("T,E,k", [(64, 256, 16), (33, 256, 1), (17, 8, 8), (5, 1, 1), (300, 128, 8), (7, 65, 3),
+                                   (9, 190, 5), (12, 7, 7)])
 def test_route_edge_cases(T, E, k):
     rng = np.random.default_rng(T * E + k)
     cases = [rng.standard_normal((T, E)).astype(np.float32),
