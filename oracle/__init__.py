@@ -71,6 +71,21 @@ def router_logits(x, Wr):
     return out
 
 
+def router_backward(x, Wr, idx, w, dg):
+    """Router backward with the selection fixed: dlogits [T,E], dWr [H,E] and
+    the router's share of dx [T,H], from dg = dL/dw [T,k]."""
+    x, Wr, w, dg = _f64(x), _f64(Wr), _f64(w), _f64(dg)
+    idx = _i32(idx)
+    T, H = x.shape
+    E = Wr.shape[1]
+    k = idx.shape[1]
+    dl = np.empty((T, E), np.float64)
+    dWr = np.empty((H, E), np.float64)
+    dxr = np.empty((T, H), np.float64)
+    _load().oracle_router_backward(T, H, E, k, _p(x), _p(Wr), _p(idx), _p(w), _p(dg), _p(dl), _p(dWr), _p(dxr))
+    return dl, dWr, dxr
+
+
 def route_topk(logits, k):
     """Top-k by (logit desc, index asc); softmax over the selected logits."""
     logits = _f64(logits)

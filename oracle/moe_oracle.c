@@ -22,6 +22,8 @@
  *    fine-tuning): issue #14, sections Proposal and Scope;
  *  - saved forward activations reused by backward: npu-train pull request #44,
  *    section Changes (HostMLP keep_graph);
+ *  - the router's logits and its backward with the selection held fixed
+ *    (issue #14, sections Proposal and Done when);
  *  - retention quotas, per-pair selection within quotas, physical compaction and
  *    a backward restricted to the retained token-expert pairs: LRMoE
  *    (arXiv:2610.37720), abstract.
@@ -41,9 +43,8 @@
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
 /* ------------------------------------------------------------------------- */
-/* Router logits  l[t,e] = sum_h x[t,h] * Wr[h,e]  (used to build the inputs of
- * the routing step for the tiny fp32 layer; the router itself lies before the
- * expert path).                                                              */
+/* Router logits  l[t,e] = sum_h x[t,h] * Wr[h,e]  (the router forward; also
+ * builds the routing inputs of the tiny fp32 layer).                         */
 void oracle_router_logits(int T, int H, int E, const double* x, const double* Wr, double* logits) {
 #pragma omp parallel for schedule(static)
   for (int t = 0; t < T; ++t)
@@ -51,6 +52,45 @@ void oracle_router_logits(int T, int H, int E, const double* x, const double* Wr
       double s = 0.0;
       for (int h = 0; h < H; ++h) s += x[(size_t)t * H + h] * Wr[(size_t)h * E + e];
       logits[(size_t)t * E + e] = s;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Router backward with the selection held fixed (issue #14, Proposal: routing
+ * precedes dispatch; Done when: the device path matches the host path in
+ * outputs and gradients).  The weights are the softmax over the k selected
+ * logits (the reading of oracle_route_topk), so with g_j = dL/dw[t,j] the chain
+ * rule through that softmax gives
+ *     dl[t, idx_j] = w_j * (g_j - sum_i w_i g_i),   dl[t, e] = 0 otherwise,
+ * and through l = x Wr:
+ *     dWr[h,e]      = sum_t x[t,h] * dl[t,e]
+ *     dx_router[t,h] = sum_e dl[t,e] * Wr[h,e].
+ * Each output is one plain sum in index order.                               */
+void oracle_router_backward(int T, int H, int E, int k, const double* x, const double* Wr, const int32_t* idx,
+                            const double* w, const double* dg, double* dlogits, double* dWr, double* dx_router) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    double s = 0.0;
+    for (int j = 0; j < k; ++j) s += w[(size_t)t * k + j] * dg[(size_t)t * k + j];
+    for (int e = 0; e < E; ++e) dlogits[(size_t)t * E + e] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const size_t p = (size_t)t * k + j;
+      dlogits[(size_t)t * E + idx[p]] = w[p] * (dg[p] - s);
+    }
+  }
+#pragma omp parallel for schedule(static)
+  for (int h = 0; h < H; ++h)
+    for (int e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int t = 0; t < T; ++t) s += x[(size_t)t * H + h] * dlogits[(size_t)t * E + e];
+      dWr[(size_t)h * E + e] = s;
+    }
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t)
+    for (int h = 0; h < H; ++h) {
+      double s = 0.0;
+      for (int e = 0; e < E; ++e) s += dlogits[(size_t)t * E + e] * Wr[(size_t)h * E + e];
+      dx_router[(size_t)t * H + h] = s;
     }
 }
 

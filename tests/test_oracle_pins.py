@@ -403,3 +403,85 @@ def test_masked_backward_against_autograd(tiny):
     (y * torch.tensor(d["dy"])).sum().backward()
     for got, ref in ((dx, X.grad), (dg, wt.grad), (dW[0], Wt[0].grad), (dW[1], Wt[1].grad), (dW[2], Wt[2].grad)):
         np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- router backward
+def _router_loss(x, Wr, idx, dg):
+    """L = sum_t sum_j softmax(l[t, idx_t])_j * dg[t, j] with the selection fixed,
+    written directly with numpy (shares nothing with the oracle's backward)."""
+    l = x @ Wr
+    sel = np.take_along_axis(l, idx.astype(np.int64), axis=1)
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return float(((ex / ex.sum(axis=1, keepdims=True)) * dg).sum())
+
+
+def _router_case(tiny, seed=5):
+    x, Wr = tiny["x"], tiny["W_r"]
+    idx, _ = oracle.route_topk(x @ Wr, TINY.k)
+    sel = np.take_along_axis(x @ Wr, idx.astype(np.int64), axis=1)
+    w = torch.softmax(torch.tensor(sel), dim=1).numpy()  # weights of the same double logits
+    dg = np.random.default_rng(seed).standard_normal(idx.shape)
+    return x, Wr, idx, w, dg
+
+
+def test_router_backward_against_autograd(tiny):
+    x, Wr, idx, w, dg = _router_case(tiny)
+    dl, dWr, dxr = oracle.router_backward(x, Wr, idx, w, dg)
+    xt = torch.tensor(x, requires_grad=True)
+    Wt = torch.tensor(Wr, requires_grad=True)
+    l = xt @ Wt
+    l.retain_grad()
+    wt = torch.softmax(torch.gather(l, 1, torch.tensor(idx, dtype=torch.int64)), dim=1)
+    (wt * torch.tensor(dg)).sum().backward()
+    for name, mine, ref in (("dlogits", dl, l.grad), ("dW_r", dWr, Wt.grad), ("dx", dxr, xt.grad)):
+        ref = ref.numpy()
+        assert np.abs(mine - ref).max() <= 1e-13 * np.abs(ref).max(), name
+
+
+def test_router_backward_finite_differences(tiny):
+    x, Wr, idx, w, dg = _router_case(tiny, seed=11)
+    dl, dWr, dxr = oracle.router_backward(x, Wr, idx, w, dg)
+    rng = np.random.default_rng(3)
+    h = 1e-6
+    for _ in range(40):
+        i, e = rng.integers(Wr.shape[0]), rng.integers(Wr.shape[1])
+        Wp, Wm = Wr.copy(), Wr.copy()
+        Wp[i, e] += h
+        Wm[i, e] -= h
+        fd = (_router_loss(x, Wp, idx, dg) - _router_loss(x, Wm, idx, dg)) / (2 * h)
+        assert abs(fd - dWr[i, e]) <= 1e-7 * max(1.0, abs(dWr).max()), (i, e)
+    for _ in range(40):
+        t, c = rng.integers(x.shape[0]), rng.integers(x.shape[1])
+        xp, xm = x.copy(), x.copy()
+        xp[t, c] += h
+        xm[t, c] -= h
+        fd = (_router_loss(xp, Wr, idx, dg) - _router_loss(xm, Wr, idx, dg)) / (2 * h)
+        assert abs(fd - dxr[t, c]) <= 1e-7 * max(1.0, abs(dxr).max()), (t, c)
+
+
+def test_router_backward_closed_form_and_invariants(tiny):
+    # one token, logits (2, 0, 1), k = 2: selection (0, 2), w = (e, 1) / (e + 1);
+    # dg = (1, 0) gives dl = (w0 w1, 0, -w0 w1) with w0 w1 = e / (e + 1)^2
+    x = np.eye(3)[:1]
+    Wr = np.array([[2.0, 0.0, 1.0], [0, 0, 0], [0, 0, 0]])
+    idx = np.array([[0, 2]], np.int32)
+    w = np.array([[math.e / (math.e + 1), 1 / (math.e + 1)]])
+    dl, dWr, dxr = oracle.router_backward(x, Wr, idx, w, np.array([[1.0, 0.0]]))
+    q = math.e / (math.e + 1) ** 2
+    np.testing.assert_allclose(dl, [[q, 0.0, -q]], rtol=1e-15, atol=1e-16)
+    np.testing.assert_allclose(dWr[0], [q, 0.0, -q], rtol=1e-15, atol=1e-16)  # x = e_0
+    np.testing.assert_allclose(dxr, [[2 * q - q, 0.0, 0.0]], rtol=1e-15, atol=1e-16)  # dl . Wr[h, :]
+    # every token's dlogits sum to zero; k = 1 gives exact zeros
+    x, Wr, idx, w, dg = _router_case(tiny)
+    dl, _, _ = oracle.router_backward(x, Wr, idx, w, dg)
+    assert np.abs(dl.sum(axis=1)).max() <= 1e-15 * np.abs(dl).max() * dl.shape[1]
+    idx1 = idx[:, :1]
+    dl1, dW1, dx1 = oracle.router_backward(x, Wr, idx1, np.ones((x.shape[0], 1)), dg[:, :1])
+    assert not dl1.any() and not dW1.any() and not dx1.any()
+
+
+def test_router_logits_against_library_matmul(tiny):
+    x, Wr = tiny["x"], tiny["W_r"]
+    l = oracle.router_logits(x, Wr)
+    ref = np.matmul(x, Wr)
+    assert np.abs(l - ref).max() <= 1e-14 * np.abs(ref).max()
