@@ -35,10 +35,12 @@ PEAK_F32_TFLOPS = 157.3
 
 # kernel ids of include/moe.h (moe_kernel)
 K_GATEUP, K_DOWN, K_COMBINE, K_GRAD_ROWS, K_DA, K_DX, K_DW, K_DISPATCH_ROWS = 2, 3, 4, 5, 6, 7, 8, 1
+K_ROUTER_FWD, K_ROUTER_DW = 10, 11
 KERNEL_NAMES = {K_GATEUP: "row_gemm_bf16_kernel<GATEUP>", K_DOWN: "row_gemm_bf16_kernel<DOWN>",
                 K_DA: "row_gemm_bf16_kernel<DA>", K_DX: "row_gemm_bf16_kernel<DX>", K_DW: "dw_bf16_kernel",
                 K_DISPATCH_ROWS: "dispatch_rows_kernel", K_GRAD_ROWS: "grad_rows_kernel",
-                K_COMBINE: "combine_kernel"}
+                K_COMBINE: "combine_kernel", K_ROUTER_FWD: "router_gemm_kernel<logits>",
+                K_ROUTER_DW: "router_bwd (dlogits, dW_r, dx)"}
 
 
 def parse():
@@ -49,6 +51,8 @@ def parse():
     p.add_argument("--workload", default="qwen3_lora_t128")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens of the CPU-oracle sample (0: auto)")
+    p.add_argument("--router", action="store_true",
+                   help="run the router in front of the path (logits = x W_r, drawn W_r) and its backward after dx")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after the timed steps, run one plain elementwise copy of this many MiB (read and write "
                         "each) so that HBM byte counters can be calibrated against a kernel of known traffic")
@@ -112,6 +116,11 @@ def algorithmic(wl, counts, kept_counts=None):
         K_DA: (H * F * b * Ea_b + R * H * b + 2 * R * 2 * F * b, 2.0 * H * F * R),
         K_DX: (2 * H * F * b * Ea_b + R * 2 * F * b + R * H * b, 4.0 * H * F * R),
         K_DW: (R * (2 * H + 3 * F) * b + 3 * H * F * wl.E * b, 6.0 * H * F * R),
+        # router: x and W_r in, fp32 logits out; backward reads x, W_r, dx and
+        # writes dlogits, dW_r, dx
+        K_ROUTER_FWD: (T * H * b + H * wl.E * b + 4 * T * wl.E, 2.0 * T * H * wl.E),
+        K_ROUTER_DW: (2 * T * H * b + H * wl.E * b + 8 * T * wl.E + H * wl.E * b + T * H * b + 12 * T * k,
+                      4.0 * T * H * wl.E),
     }
 
 
@@ -162,18 +171,21 @@ def main():
     dev = torch.device("cuda:0")
     t = {n: torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in ("x", "W_gate", "W_up", "W_down", "dy")}
     logits = torch.from_numpy(d["logits"]).to(dev)
-    L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho, dw=wl.dw, dg=True)
+    L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho, dw=wl.dw, dg=True,
+                        router=args.router)
+    w_r = torch.from_numpy(W.router_weights(wl, seed=0)).to(dev).to(torch.bfloat16) if args.router else None
     stream = torch.cuda.current_stream()
 
     def step():
-        L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], stream)
-        L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream)
+        L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], stream, w_r=w_r)
+        L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream, w_r=w_r)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     gemm_kernels = [K_GATEUP, K_DOWN, K_DA, K_DX] + ([K_DW] if wl.dw else [])
+    profiled = gemm_kernels + ([K_ROUTER_FWD, K_ROUTER_DW] if args.router else [])
     lib = moe.lib()
     lib.moe_profile_kernel.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
 
@@ -201,7 +213,7 @@ def main():
         return dt, {kk: float(np.mean([a.elapsed_time(b) for a, b in ev[kk]])) for kk in kinds}
 
     # untimed pass: every GEMM's duration, to find the dominant kernel
-    _, kernel_ms = run_steps(max(3, min(args.steps, 10)), gemm_kernels)
+    _, kernel_ms = run_steps(max(3, min(args.steps, 10)), profiled)
     dom = max(gemm_kernels, key=lambda kk: kernel_ms[kk])
     # timed steps: only the dominant kernel is bracketed by events
     elapsed, dom_ms = run_steps(args.steps, [dom])
@@ -232,13 +244,21 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "F": wl.F, "E": wl.E, "k": wl.k,
-                   "pass": "fwd+dx+dg" + ("+dW" if wl.dw else "") + (f"+compact(rho={wl.rho})" if wl.rho else ""),
+                   "pass": ("router+" if args.router else "") + "fwd+dx+dg" + ("+dW" if wl.dw else "")
+                           + (f"+compact(rho={wl.rho})" if wl.rho else "") + ("+router_bwd" if args.router else ""),
                    "experts_with_rows": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max())},
         "tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
         "mfma_frac_of_step": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "kernel_us": {KERNEL_NAMES[kk]: kernel_ms[kk] * 1e3 for kk in gemm_kernels},
+        "kernel_us": {KERNEL_NAMES[kk]: kernel_ms[kk] * 1e3 for kk in profiled},
         "roofline": roof,
     }
+    if args.router:
+        # router kernels run on the fp32 vector ALUs (roofline: fp32 vector peak)
+        out["router"] = {KERNEL_NAMES[kk]: {"us": kernel_ms[kk] * 1e3,
+                                            "TFLOP/s": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12,
+                                            "frac_fp32_alu": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
+                                            "GB/s": alg[kk][0] / (kernel_ms[kk] * 1e-3) / 1e9}
+                         for kk in (K_ROUTER_FWD, K_ROUTER_DW)}
     if args.copy_probe_mib > 0:
         # one read + one write of copy_probe_mib MiB each, outside the timed steps
         src = torch.ones(args.copy_probe_mib << 19, dtype=torch.bfloat16, device=dev)

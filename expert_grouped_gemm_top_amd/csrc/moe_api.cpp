@@ -103,6 +103,14 @@ int check_rows(const char* fn, int max_rows) {
   return MOE_OK;
 }
 
+int check_router_workspace(const char* fn, int T, int H, int E, const void* ws, size_t ws_bytes) {
+  const size_t need = moe::router_workspace_bytes(T, H, E);
+  REQUIRE(ws_bytes >= need, MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+  REQUIRE(need == 0 || ws != nullptr, MOE_ERR_INVALID_ARGUMENT, "%s: workspace must not be NULL", fn);
+  REQUIRE(((uintptr_t)ws & 15) == 0, MOE_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,7 +128,7 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
   const char* fn = "moe_profile_kernel";
@@ -130,6 +138,27 @@ int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
   g_armed[kernel].start = reinterpret_cast<hipEvent_t>(start_event);
   g_armed[kernel].stop = reinterpret_cast<hipEvent_t>(stop_event);
   return MOE_OK;
+}
+
+size_t moe_router_workspace_bytes(int T, int H, int E) {
+  if (T < 1 || H < 1 || E < 1) return 0;
+  return moe::router_workspace_bytes(T, H, E);
+}
+
+int moe_router_fwd(int T, int H, int E, int dtype, const void* x, const void* w_r, float* logits, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_router_fwd";
+  int rc = check_routing_dims(fn, T, E, 1);
+  if (rc || (rc = check_dtype(fn, dtype)) || (rc = check_row_width(fn, "H", H))) return rc;
+  REQUIRE((int64_t)T * H < ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "%s: x too large", fn);
+  NONNULL(x);
+  NONNULL(w_r);
+  NONNULL(logits);
+  if ((rc = check_router_workspace(fn, T, H, E, workspace, workspace_bytes))) return rc;
+  hipStream_t s = as_stream(stream);
+  return hip_status(timed(MOE_K_ROUTER_FWD, s,
+                          [&] { return moe::launch_router_fwd(T, H, E, esize_of(dtype), x, w_r, logits, workspace, s); }),
+                    fn);
 }
 
 int moe_route_topk(int T, int E, int k, const float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
@@ -331,6 +360,31 @@ int moe_grouped_bwd_dw(int H, int F, int E, int max_rows, int dtype, const int32
   return hip_status(
       timed(MOE_K_GEMM_DW, s, [&] { return dtype == MOE_BF16 ? moe::launch_dw_bf16(g, s) : moe::launch_dw_f32(g, s); }),
       fn);
+}
+
+int moe_router_bwd(int T, int H, int E, int k, int dtype, const void* x, const void* w_r, const int32_t* topk_idx,
+                   const float* topk_w, const float* dg, float* dlogits, void* dw_r, void* dx, int dx_accumulate,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_router_bwd";
+  int rc = check_routing_dims(fn, T, E, k);
+  if (rc || (rc = check_dtype(fn, dtype)) || (rc = check_row_width(fn, "H", H))) return rc;
+  REQUIRE((int64_t)T * H < ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "%s: x too large", fn);
+  NONNULL(x);
+  NONNULL(w_r);
+  NONNULL(topk_idx);
+  NONNULL(topk_w);
+  NONNULL(dg);
+  NONNULL(dlogits);
+  NONNULL(dw_r);
+  NONNULL(dx);
+  if ((rc = check_router_workspace(fn, T, H, E, workspace, workspace_bytes))) return rc;
+  hipStream_t s = as_stream(stream);
+  return hip_status(timed(MOE_K_ROUTER_DW, s,
+                          [&] {
+                            return moe::launch_router_bwd(T, H, E, k, esize_of(dtype), x, w_r, topk_idx, topk_w, dg,
+                                                          dlogits, dw_r, dx, dx_accumulate != 0, workspace, s);
+                          }),
+                    fn);
 }
 
 int64_t moe_quota_cap(int T, int E, int k, double rho) {

@@ -80,6 +80,13 @@ int big_gemm_min_rows(int mode, int H, int F);
 hipError_t launch_row_gemm_f32(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
 hipError_t launch_dw_f32(DwArgs g, hipStream_t stream);
 
+size_t router_workspace_bytes(int T, int H, int E);
+hipError_t launch_router_fwd(int T, int H, int E, int esize, const void* x, const void* w_r, float* logits, void* ws,
+                             hipStream_t stream);
+hipError_t launch_router_bwd(int T, int H, int E, int k, int esize, const void* x, const void* w_r,
+                             const int32_t* idx, const float* w, const float* dg, float* dlogits, void* dw_r,
+                             void* dx, bool dx_accumulate, void* ws, hipStream_t stream);
+
 hipError_t launch_fill_i32(int32_t* a, int64_t n, int32_t v, hipStream_t stream);
 hipError_t launch_compact(int64_t N, int E, int cap, const int32_t* counts, const int32_t* offsets, const int32_t* perm,
                           const float* score, int32_t* kept_counts, int32_t* kept_offsets, int32_t* kept_perm,

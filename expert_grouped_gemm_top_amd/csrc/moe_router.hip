@@ -1,0 +1,224 @@
+// moe_router.hip -- the router in front of the expert path: logits = x W_r, and
+// its backward with the top-k selection held fixed.
+//
+// Routing precedes dispatch (npu-train issue #14, section Proposal), and the
+// device path has to match the host path in gradients as well as outputs
+// (issue #14, section Done when).  With the weights the softmax over the k
+// selected logits, g_j = dL/dw[t,j] and s_t = sum_j w[t,j] g_j:
+//     dlogits[t, idx_j] = w_j (g_j - s_t),  dlogits[t, e] = 0 otherwise,
+//     dW_r = x^T dlogits,   dx += dlogits W_r^T.
+//
+// The three products are small next to the experts' (E columns against k * 3F),
+// so they run on one tiled fp32 kernel: 64 x 64 output tiles, reduction depth
+// 16 per LDS stage, 4 x 4 outputs per thread, every operand converted to fp32
+// on its way into LDS.  Two of them have few outputs and a long reduction
+// (logits: T x E over H; dW_r: H x E over T), so the reduction is cut into S
+// slices run by separate workgroups that write fp32 partial tiles to the
+// caller's workspace; a second kernel adds the S partials of each output in
+// slice order and rounds once.  Every output is thus reduced in one fixed
+// order (deterministic, no atomics).
+#include <algorithm>
+
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRBM = 64, kRBN = 64, kRBK = 16;
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf2f(v); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return (uint16_t)f2bf(v); }
+
+// C[M,N] (+)= sum_k A(m,k) B(k,n).  A(m,k) = a[m*lda + k] when A_KC (k
+// contiguous), else a[k*lda + m]; B(k,n) = b[n*ldb + k] when B_KC, else
+// b[k*ldb + n].  C is row-major with leading dimension N; ACC adds the product
+// to C's current contents (one rounding of the sum).  With slices > 1,
+// workgroup z reduces k in [z*kslice, (z+1)*kslice) and writes its fp32 partial
+// tile to part + z*M*N instead (C, ACC unused).
+template <typename TA, typename TB, typename TC, bool A_KC, bool B_KC, bool ACC>
+__global__ __launch_bounds__(256) void router_gemm_kernel(int M, int N, int K, const TA* __restrict__ a, int lda,
+                                                          const TB* __restrict__ b, int ldb, TC* __restrict__ c,
+                                                          int kslice, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float s_a[kRBK][kRBM];
+  __shared__ __attribute__((aligned(16))) float s_b[kRBK][kRBN];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.x * kRBM, n0 = blockIdx.y * kRBN;
+  const int kb0 = blockIdx.z * kslice, kb1 = min(K, kb0 + kslice);
+  float acc[4][4] = {};
+  for (int k0 = kb0; k0 < kb1; k0 += kRBK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;  // element of the 64 x 16 tile
+      // walk the contiguous index fastest so that neighbouring threads read
+      // neighbouring addresses
+      const int mm = A_KC ? q / kRBK : q % kRBM, kk = A_KC ? q % kRBK : q / kRBM;
+      const int m = m0 + mm, k = k0 + kk;
+      float v = 0.0f;
+      if (m < M && k < kb1) v = to_f32<TA>(A_KC ? a[(size_t)m * lda + k] : a[(size_t)k * lda + m]);
+      s_a[kk][mm] = v;
+      const int nn = B_KC ? q / kRBK : q % kRBN, kb = B_KC ? q % kRBK : q / kRBN;
+      const int n = n0 + nn, kq = k0 + kb;
+      float u = 0.0f;
+      if (n < N && kq < kb1) u = to_f32<TB>(B_KC ? b[(size_t)n * ldb + kq] : b[(size_t)kq * ldb + n]);
+      s_b[kb][nn] = u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kRBK; ++kk) {
+      const f32x4 av = *(const f32x4*)&s_a[kk][4 * ty];
+      const f32x4 bv = *(const f32x4*)&s_b[kk][4 * tx];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 4 * ty + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 4 * tx + j;
+      if (n >= N) continue;
+      if (part != nullptr) {
+        part[((size_t)blockIdx.z * M + m) * N + n] = acc[i][j];
+      } else {
+        TC* p = c + (size_t)m * N + n;
+        const float v = ACC ? to_f32<TC>(*p) + acc[i][j] : acc[i][j];
+        *p = from_f32<TC>(v);
+      }
+    }
+  }
+}
+
+// c[i] = sum_{z < slices} part[z*MN + i], z ascending, rounded once.
+template <typename TC>
+__global__ __launch_bounds__(256) void router_sum_slices_kernel(int64_t MN, int slices, const float* __restrict__ part,
+                                                                TC* __restrict__ c) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += (int64_t)gridDim.x * 256) {
+    float v = 0.0f;
+    for (int z = 0; z < slices; ++z) v += part[z * MN + i];
+    c[i] = from_f32<TC>(v);
+  }
+}
+
+// One wavefront per token: s = sum_j w_j g_j (wave tree), then every lane
+// writes its experts' entries of the token's dlogits row exactly once.
+__global__ __launch_bounds__(256) void router_dlogits_kernel(int T, int E, int k, const int32_t* __restrict__ idx,
+                                                             const float* __restrict__ w, const float* __restrict__ dg,
+                                                             float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave
+  const size_t p = (size_t)t * k + (lane < k ? lane : k - 1);
+  const int32_t e_l = idx[p];
+  const float w_l = w[p], g_l = dg[p];
+  const float s = wave_sum(lane < k ? w_l * g_l : 0.0f);
+  const float d_l = w_l * (g_l - s);
+  for (int e = lane; e < E; e += kWave) {
+    float v = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e_l, j);
+      const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d_l), j));
+      if (ej == e) v = dj;
+    }
+    dl[(size_t)t * E + e] = v;
+  }
+}
+
+// Reduction slices of an M x N x K product: enough workgroups to cover the
+// chip (about kTargetGroups), each slice a multiple of the LDS depth.
+constexpr int64_t kTargetGroups = 512;
+constexpr int kMinSlice = 128;
+
+int64_t slice_count(int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + kRBM - 1) / kRBM) * ((N + kRBN - 1) / kRBN);
+  int64_t s = (kTargetGroups + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, (K + kMinSlice - 1) / kMinSlice);
+  return std::max<int64_t>(s, 1);
+}
+
+int slice_length(int K, int64_t slices) {
+  const int64_t per = (K + slices - 1) / slices;
+  return (int)((per + kRBK - 1) / kRBK * kRBK);
+}
+
+size_t split_bytes(int M, int N, int K) {
+  const int64_t s = slice_count(M, N, K);
+  return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
+}
+
+// Plain launch (one slice) or the sliced reduction through `ws`.
+template <typename TA, typename TB, typename TC, bool A_KC, bool B_KC, bool ACC>
+hipError_t gemm(int M, int N, int K, const void* a, int lda, const void* b, int ldb, void* c, float* ws,
+                bool may_split, hipStream_t stream) {
+  const int64_t slices = may_split ? slice_count(M, N, K) : 1;
+  const int kslice = slices > 1 ? slice_length(K, slices) : K;
+  const int64_t used = (K + kslice - 1) / kslice;  // slices that hold some k
+  const dim3 grid((M + kRBM - 1) / kRBM, (N + kRBN - 1) / kRBN, (unsigned)(slices > 1 ? used : 1));
+  hipLaunchKernelGGL((router_gemm_kernel<TA, TB, TC, A_KC, B_KC, ACC>), grid, dim3(256), 0, stream, M, N, K,
+                     (const TA*)a, lda, (const TB*)b, ldb, (TC*)c, kslice, slices > 1 ? ws : nullptr);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || slices == 1) return err;
+  const int64_t MN = (int64_t)M * N;
+  const int64_t blocks = std::min<int64_t>((MN + 255) / 256, 4096);
+  hipLaunchKernelGGL((router_sum_slices_kernel<TC>), dim3((unsigned)blocks), dim3(256), 0, stream, MN, (int)used,
+                     (const float*)ws, (TC*)c);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t router_bwd_typed(int T_, int H, int E, int k, const void* x, const void* w_r, const int32_t* idx,
+                            const float* w, const float* dg, float* dl, void* dw_r, void* dx, bool dx_acc,
+                            float* ws, hipStream_t stream) {
+  hipLaunchKernelGGL(router_dlogits_kernel, dim3((T_ + 3) / 4), dim3(256), 0, stream, T_, E, k, idx, w, dg, dl);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // dW_r [H,E] = x^T dl: A(h,t) = x[t*H + h], B(t,e) = dl[t*E + e]; reduction over T
+  err = gemm<T, float, T, false, false, false>(H, E, T_, x, H, dl, E, dw_r, ws, true, stream);
+  if (err != hipSuccess) return err;
+  // dx [T,H] (+)= dl W_r^T: A(t,e) = dl[t*E + e], B(e,h) = w_r[h*E + e]; reduction over E only
+  if (dx_acc) return gemm<float, T, T, true, true, true>(T_, H, E, dl, E, w_r, E, dx, nullptr, false, stream);
+  return gemm<float, T, T, true, true, false>(T_, H, E, dl, E, w_r, E, dx, nullptr, false, stream);
+}
+
+}  // namespace
+
+size_t router_workspace_bytes(int T, int H, int E) {
+  return std::max(split_bytes(T, E, H), split_bytes(H, E, T));
+}
+
+hipError_t launch_router_fwd(int T, int H, int E, int esize, const void* x, const void* w_r, float* logits, void* ws,
+                             hipStream_t stream) {
+  // logits [T,E] = x W_r: A(t,h) = x[t*H + h], B(h,e) = w_r[h*E + e]; reduction over H
+  if (esize == 4)
+    return gemm<float, float, float, true, false, false>(T, E, H, x, H, w_r, E, logits, (float*)ws, true, stream);
+  return gemm<uint16_t, uint16_t, float, true, false, false>(T, E, H, x, H, w_r, E, logits, (float*)ws, true, stream);
+}
+
+hipError_t launch_router_bwd(int T, int H, int E, int k, int esize, const void* x, const void* w_r,
+                             const int32_t* idx, const float* w, const float* dg, float* dlogits, void* dw_r,
+                             void* dx, bool dx_accumulate, void* ws, hipStream_t stream) {
+  if (esize == 4)
+    return router_bwd_typed<float>(T, H, E, k, x, w_r, idx, w, dg, dlogits, dw_r, dx, dx_accumulate, (float*)ws,
+                                   stream);
+  return router_bwd_typed<uint16_t>(T, H, E, k, x, w_r, idx, w, dg, dlogits, dw_r, dx, dx_accumulate, (float*)ws,
+                                    stream);
+}
+
+}  // namespace moe

@@ -2,9 +2,10 @@
 
 ``MoeLayerBuffers`` owns every device buffer of the path (torch allocations,
 sized once from the host capacities) and ``forward`` / ``backward`` enqueue the
-library calls in order on one stream -- route, dispatch, grouped SwiGLU
-forward, combine; then optionally compaction, backward dx (+ dg) and dW.  No
-step here computes anything itself: every value comes from libmoe's kernels.
+library calls in order on one stream -- (router logits,) route, dispatch,
+grouped SwiGLU forward, combine; then optionally compaction, backward dx (+ dg),
+dW and the router's backward.  No step here computes anything itself: every
+value comes from libmoe's kernels.
 """
 from __future__ import annotations
 
@@ -14,7 +15,8 @@ from . import moe
 
 
 class MoeLayerBuffers:
-    def __init__(self, T, H, F, E, k, dtype=torch.bfloat16, device="cuda", rho=None, dw=True, dg=True):
+    def __init__(self, T, H, F, E, k, dtype=torch.bfloat16, device="cuda", rho=None, dw=True, dg=True,
+                 router=False):
         self.T, self.H, self.F, self.E, self.k = T, H, F, E, k
         self.N = N = T * k
         self.dtype, self.rho, self.dw, self.want_dg = dtype, rho, dw, dg
@@ -57,9 +59,22 @@ class MoeLayerBuffers:
             self.dw_gate = em(E, H, F)
             self.dw_up = em(E, H, F)
             self.dw_down = em(E, F, H)
+        self.router = router
+        if router:  # logits = x W_r in front of routing; its backward needs dg
+            assert dg, "the router backward needs dg"
+            self.logits = em(T, E, dt=f32)
+            self.dlogits = em(T, E, dt=f32)
+            self.dw_r = em(H, E)
+            self.router_ws = em(max(moe.moe_router_workspace_bytes(T, H, E), 16), dt=torch.uint8)
 
     # ------------------------------------------------------------------ forward
-    def forward(self, logits, x, w_gate, w_up, w_down, stream=None):
+    def forward(self, logits, x, w_gate, w_up, w_down, stream=None, w_r=None):
+        """With w_r (a layer built with router=True) the logits are x W_r and
+        the `logits` argument is ignored."""
+        if w_r is not None:
+            moe.moe_router_fwd(x, w_r, self.logits, self.router_ws, stream)
+            logits = self.logits
+            self._x = x
         moe.moe_route_topk(logits, self.topk_idx, self.topk_w, self.k, stream)
         moe.moe_dispatch(self.topk_idx, x, self.counts, self.offsets, self.perm, self.inv_perm, self.x_sorted,
                          self.ws, self.E, stream)
@@ -75,10 +90,11 @@ class MoeLayerBuffers:
                               self.x_sorted, self.a_save if self.dw else None, self.h_save, self.x_kept,
                               self.a_kept if self.dw else None, self.h_kept, stream)
 
-    def backward(self, dy, w_gate, w_up, w_down, score=None, stream=None):
+    def backward(self, dy, w_gate, w_up, w_down, score=None, stream=None, w_r=None):
         """dx (+ dg) and, for full fine-tuning, dW.  With a quota ratio the
         backward runs on the compacted retained pairs (score defaults to the
-        routing weights)."""
+        routing weights).  With w_r, the router's backward follows: dlogits,
+        dw_r, and its share added to dx."""
         if self.rho is not None:
             self.compact(self.topk_w.view(-1) if score is None else score, stream)
             offsets, inv, x_rows, a_rows, h_rows = (self.kept_offsets, self.kept_inv, self.x_kept, self.a_kept,
@@ -91,4 +107,7 @@ class MoeLayerBuffers:
         if self.dw:
             moe.moe_grouped_bwd_dw(offsets, x_rows, a_rows, self.dO, self.dh, self.dw_gate, self.dw_up,
                                    self.dw_down, self.R, stream)
+        if w_r is not None:
+            moe.moe_router_bwd(self._x, w_r, self.topk_idx, self.topk_w, self.dg, self.dlogits, self.dw_r, self.dx,
+                               True, self.router_ws, stream)
         return self.dx

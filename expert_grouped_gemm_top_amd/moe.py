@@ -29,7 +29,10 @@ _SIGS = {
     "moe_status_string": ([_i], ctypes.c_char_p),
     "moe_last_error": ([], ctypes.c_char_p),
     "moe_abi_version": ([], _i),
+    "moe_router_workspace_bytes": ([_i, _i, _i], _sz),
+    "moe_router_fwd": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_route_topk": ([_i, _i, _i, _vp, _vp, _vp, _vp], _i),
+    "moe_router_bwd": ([_i, _i, _i, _i, _i] + [_vp] * 8 + [_i, _vp, _sz, _vp], _i),
     "moe_dispatch_workspace_bytes": ([_i, _i, _i], _sz),
     "moe_dispatch": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_grouped_swiglu_fwd": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i),
@@ -109,6 +112,38 @@ def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
 
 def moe_quota_cap(T: int, E: int, k: int, rho: float) -> int:
     return int(lib().moe_quota_cap(T, E, k, float(rho)))
+
+
+def moe_router_workspace_bytes(T: int, H: int, E: int) -> int:
+    return int(lib().moe_router_workspace_bytes(T, H, E))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def moe_router_fwd(x, w_r, logits, workspace=None, stream=None):
+    T, H = x.shape
+    E = w_r.shape[1]
+    d = x.dtype
+    ws, ws_bytes = _ws(workspace)
+    _check(lib().moe_router_fwd(T, H, E, _dt(x), _ptr(x, "x", d, T * H), _ptr(w_r, "w_r", d, H * E),
+                                _ptr(logits, "logits", F32, T * E), ws, ws_bytes, _stream(stream)))
+
+
+def moe_router_bwd(x, w_r, topk_idx, topk_w, dg, dlogits, dw_r, dx, accumulate: bool, workspace=None, stream=None):
+    T, H = x.shape
+    E = w_r.shape[1]
+    k = topk_idx.shape[1]
+    d = x.dtype
+    ws, ws_bytes = _ws(workspace)
+    _check(lib().moe_router_bwd(T, H, E, k, _dt(x), _ptr(x, "x", d, T * H), _ptr(w_r, "w_r", d, H * E),
+                                _ptr(topk_idx, "topk_idx", I32, T * k), _ptr(topk_w, "topk_w", F32, T * k),
+                                _ptr(dg, "dg", F32, T * k), _ptr(dlogits, "dlogits", F32, T * E),
+                                _ptr(dw_r, "dw_r", d, H * E), _ptr(dx, "dx", d, T * H), 1 if accumulate else 0,
+                                ws, ws_bytes, _stream(stream)))
 
 
 def moe_route_topk(logits, topk_idx, topk_w, k: int, stream=None):

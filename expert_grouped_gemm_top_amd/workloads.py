@@ -99,6 +99,13 @@ def expert_weights(wl: Workload, name: str, experts=None, seed: int = 0) -> np.n
     return round_bf16(out) if wl.dtype == "bf16" else out
 
 
+def router_weights(wl: Workload, seed: int = 0) -> np.ndarray:
+    """W_r [H,E] = 0.02 N(0,1), the same draw as a "wr" workload's router (for
+    running the router in front of a workload whose logits are drawn)."""
+    rnd = round_bf16 if wl.dtype == "bf16" else (lambda a: a)
+    return rnd(np.float32(0.02) * _normal((wl.H, wl.E), seed, _TAGS["W_r"]))
+
+
 def generate(wl: Workload, seed: int = 0, weights: bool = True) -> dict:
     """Draw the workload's tensors: x [T,H], W_r [H,E] (router "wr") or logits
     [T,E], W_gate, W_up [E,H,F], W_down [E,F,H] (unless ``weights`` is False),

@@ -7,6 +7,7 @@
  * and Scope; npu-train pull request #44, section Changes; LRMoE,
  * arXiv:2610.37720, abstract):
  *
+ *   moe_router_fwd          router logits = x W_r
  *   moe_route_topk          router logits -> top-k experts and weights per token
  *   moe_dispatch            token-expert pairs -> rows contiguous per expert
  *   moe_grouped_swiglu_fwd  SwiGLU expert MLP over every expert's rows (ragged
@@ -17,6 +18,8 @@
  *   moe_grouped_bwd_dx      input gradient (experts frozen) + routing-weight
  *                           gradient, over all or only the retained pairs
  *   moe_grouped_bwd_dw      expert weight gradients (full fine-tuning)
+ *   moe_router_bwd          router gradients (logits, W_r, the router's share
+ *                           of dx) from the routing-weight gradient
  *
  * Conventions for every call:
  *  - Pointers marked (device) are device pointers owned by the caller; the
@@ -62,7 +65,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 const char* moe_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);
-/* ABI version, currently 1. */
+/* ABI version, currently 2. */
 int moe_abi_version(void);
 
 /* Kernels that moe_profile_kernel can bracket with events. */
@@ -77,7 +80,9 @@ typedef enum moe_kernel {
   MOE_K_GEMM_DX = 7,       /* dX GEMM of moe_grouped_bwd_dx */
   MOE_K_GEMM_DW = 8,       /* moe_grouped_bwd_dw */
   MOE_K_COMPACT = 9,       /* the selection kernel of moe_compact_pairs */
-  MOE_K_COUNT = 10
+  MOE_K_ROUTER_FWD = 10,   /* moe_router_fwd */
+  MOE_K_ROUTER_DW = 11,    /* the dW_r GEMM of moe_router_bwd */
+  MOE_K_COUNT = 12
 } moe_kernel;
 
 /* Profiling hook.  Arms a one-shot request on the calling thread: the next
@@ -87,6 +92,20 @@ typedef enum moe_kernel {
  * hipEvent_t created by the caller; NULL events disarm.  Several kernels may be
  * armed at once.  Results of the calls are unaffected. */
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event);
+
+/* Workspace (device bytes) that moe_router_fwd and moe_router_bwd need for T
+ * tokens, hidden size H and E experts: fp32 partial sums of the long
+ * reductions (at most ~8.5 MB; 0 when no reduction is split).  Host-only. */
+size_t moe_router_workspace_bytes(int T, int H, int E);
+
+/* Router logits (issue #14, Proposal: routing precedes dispatch):
+ *   logits[t,e] = sum_h x[t,h] W_r[h,e]
+ * accumulated in fp32 in one fixed order.  x [T, H] and w_r [H, E] of `dtype`
+ * (device); logits [T, E] fp32 (device, out); workspace (device) of at least
+ * moe_router_workspace_bytes(T, H, E) bytes (may be NULL when that is 0).
+ * 1 <= E <= 256; H a multiple of 8. */
+int moe_router_fwd(int T, int H, int E, int dtype, const void* x, const void* w_r, float* logits, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* Top-k routing (issue #14, Evidence and Proposal: each token is routed to k
  * of E experts).  For token t the experts are ranked by logit descending, equal
@@ -184,6 +203,22 @@ int moe_grouped_bwd_dw(int H, int F, int E, int max_rows, int dtype, const int32
                        const void* x_rows, const void* a_rows, const void* dO_rows,
                        const void* dh_rows, void* dw_gate, void* dw_up, void* dw_down,
                        void* stream);
+
+/* Router backward with the selection held fixed (issue #14, Proposal and Done
+ * when: the gradients of the device path match the host path's).  The weights
+ * being the softmax over the k selected logits, with g = dg (dL/dtopk_w, from
+ * moe_grouped_bwd_dx) and s_t = sum_j topk_w[t,j] g[t,j]:
+ *   dlogits[t, topk_idx[t,j]] = topk_w[t,j] (g[t,j] - s_t), other entries 0
+ *   dw_r = x^T dlogits                       [H, E], overwritten
+ *   dx   = dlogits w_r^T  (+ dx if dx_accumulate != 0)   [T, H]
+ * all accumulated in fp32 and rounded once to `dtype`.  x [T, H], w_r [H, E]
+ * of `dtype` (device); topk_idx [T, k] int32 (device, distinct experts per
+ * token, as moe_route_topk gives); topk_w, dg [T, k] fp32 (device); dlogits
+ * [T, E] fp32 (device, out); dw_r [H, E] and dx [T, H] of `dtype` (device;
+ * dx read too when accumulating); workspace as for moe_router_fwd. */
+int moe_router_bwd(int T, int H, int E, int k, int dtype, const void* x, const void* w_r, const int32_t* topk_idx,
+                   const float* topk_w, const float* dg, float* dlogits, void* dw_r, void* dx, int dx_accumulate,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Quota cap used by moe_compact_pairs: ceil(rho * T * k / E) (integer
  * arithmetic when rho == 1, else evaluated in double).  Host-only. */

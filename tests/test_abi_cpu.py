@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(LIB)
     missing = [n for n in declared_functions() if not hasattr(raw, n)]
     assert not missing, missing
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def _err(lib):
@@ -113,3 +113,23 @@ def test_compaction_validation_and_quota(lib):
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_router_calls_validation(lib):
+    f = lib.moe_router_fwd
+    ws = lib.moe_router_workspace_bytes(128, 2048, 128)
+    assert ws > 0 and lib.moe_router_workspace_bytes(64, 128, 8) == 0
+    assert f(0, 128, 8, 1, P, P, P, P, 0, NULL) == 1
+    assert f(64, 100, 8, 1, P, P, P, P, 0, NULL) == 2 and "multiple of 8" in _err(lib)
+    assert f(64, 128, 300, 1, P, P, P, P, 0, NULL) == 2
+    assert f(64, 128, 8, 5, P, P, P, P, 0, NULL) == 1 and "dtype" in _err(lib)
+    assert f(64, 128, 8, 1, P, NULL, P, P, 0, NULL) == 1 and "w_r" in _err(lib)
+    assert f(128, 2048, 128, 1, P, P, P, P, ws - 1, NULL) == 3 and "workspace" in _err(lib)
+    b = lib.moe_router_bwd
+    args = [64, 128, 8, 2, 1] + [P] * 8 + [0, P, 1 << 30, NULL]
+    bad = list(args); bad[3] = 9
+    assert b(*bad) == 1 and "exceeds E" in _err(lib)
+    bad = list(args); bad[9] = NULL
+    assert b(*bad) == 1 and "dg must" in _err(lib)
+    bad = list(args); bad[12] = NULL
+    assert b(*bad) == 1 and "dx must" in _err(lib)
