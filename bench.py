@@ -62,11 +62,11 @@ def parse():
 # Sources whose code decides the HBM traffic of each kernel; a stored counter
 # reading only counts while these files are unchanged.
 KERNEL_SOURCES = {
-    K_GATEUP: ("moe_gemm_bf16.hip", "moe_gemm_big.hip", "moe_common.h", "moe_launch.h"),
-    K_DOWN: ("moe_gemm_bf16.hip", "moe_gemm_big.hip", "moe_common.h", "moe_launch.h"),
-    K_DA: ("moe_gemm_bf16.hip", "moe_gemm_big.hip", "moe_common.h", "moe_launch.h"),
-    K_DX: ("moe_gemm_bf16.hip", "moe_gemm_big.hip", "moe_common.h", "moe_launch.h"),
-    K_DW: ("moe_gemm_bf16.hip", "moe_common.h", "moe_launch.h"),
+    K_GATEUP: ("moe_gemm_bf16.hip", "moe_gemm_big.hip", "moe_lds32.h", "moe_common.h", "moe_launch.h"),
+    K_DOWN: ("moe_gemm_bf16.hip", "moe_gemm_big.hip", "moe_lds32.h", "moe_common.h", "moe_launch.h"),
+    K_DA: ("moe_gemm_bf16.hip", "moe_gemm_big.hip", "moe_lds32.h", "moe_common.h", "moe_launch.h"),
+    K_DX: ("moe_gemm_bf16.hip", "moe_gemm_big.hip", "moe_lds32.h", "moe_common.h", "moe_launch.h"),
+    K_DW: ("moe_gemm_dw.hip", "moe_lds32.h", "moe_common.h", "moe_launch.h"),
 }
 TRAFFIC_FILE = {K_GATEUP: "gemm_gateup", K_DOWN: "gemm_down", K_DA: "gemm_da", K_DX: "gemm_dx", K_DW: "gemm_dw"}
 

@@ -763,6 +763,10 @@ hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, in
 }
 
 hipError_t launch_dw_bf16(DwArgs g, hipStream_t stream) {
+#ifndef MOE_DW_BIG
+#define MOE_DW_BIG 1
+#endif
+  if (MOE_DW_BIG) return launch_dw_big_bf16(g, stream);
   g.tiles_job1 = (g.H / 128) * ((2 * g.F) / 128);
   g.tiles_per_expert = g.tiles_job1 + (g.F / 128) * (g.H / 128);
   const int64_t blocks = (int64_t)g.E * g.tiles_per_expert;

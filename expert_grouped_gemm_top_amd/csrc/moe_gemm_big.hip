@@ -24,42 +24,11 @@
 
 #include "moe_common.h"
 #include "moe_launch.h"
+#include "moe_lds32.h"
 
 namespace moe {
 
 namespace {
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// D = first x second + D on the 32x32x16 bf16 matrix core.  Lane l supplies
-// row (first) / column (second) l % 32 and k-group l / 32 (8 consecutive k);
-// register r of lane l is D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
-__device__ __forceinline__ f32x16 mfma32(u32x4 first, u32x4 second, f32x16 acc) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, first), __builtin_bit_cast(bf16x8, second),
-                                                  acc, 0, 0, 0);
-}
-
-// 16 B from global straight into LDS at lds_base + 16 * lane.
-__device__ __forceinline__ void g2lds(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
-}
-
-// Workgroup barrier without the memory fence of __syncthreads(): the fence
-// would make the compiler wait for every outstanding global load (including
-// the stages still meant to be in flight).  LDS data written by the direct
-// loads is made complete explicitly with wait_vmcnt before this barrier; the
-// asm clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // s_waitcnt vmcnt(N); expcnt and lgkmcnt left unconstrained
-  static_assert(N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
-}
 
 template <int MODE>
 struct BigShape {
@@ -78,9 +47,6 @@ template <int CPR>
 __device__ __forceinline__ int kc_swz(int row, int chunk) {
   return CPR == 4 ? (chunk ^ ((row >> 1) & 3)) : (chunk ^ (row & 7));
 }
-// k row of an N-contiguous tile -> XOR on the 16-byte chunk index (keeps the
-// 4-chunk groups one transpose read covers aligned)
-__device__ __forceinline__ int nn_swz(int k) { return 4 * (k & 3); }
 
 // Tile of BM rows x BN columns, reduction depth BK per stage, NW waves laid out
 // WM x (NW / WM); STAGES stages resident in LDS; WPC workgroups per CU.
@@ -242,22 +208,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (NN) {
-        // 16-lane group G = l / 16 reads k rows 16 sub + 8 (G >> 1) + 4 h + (r >> 2)
-        // and columns TN wn + 32 j + 16 (G & 1) + 4 (r & 3) .. + 3, r = l % 16
-        const int G = l >> 4, r = l & 15;
-        const int col = TN * wn + 32 * j + 16 * (G & 1) + 4 * (r & 3);
-        v4i16 part[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k = 16 * sub + 8 * (G >> 1) + 4 * h + (r >> 2);
-          const int chunk = (col >> 3) ^ nn_swz(k);
-          part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(sb + k * (BN * 2) + 16 * chunk + 2 * (col & 7)));
-        }
-        fr.b[j] = u32x4{(uint32_t)(uint16_t)part[0][0] | ((uint32_t)(uint16_t)part[0][1] << 16),
-                        (uint32_t)(uint16_t)part[0][2] | ((uint32_t)(uint16_t)part[0][3] << 16),
-                        (uint32_t)(uint16_t)part[1][0] | ((uint32_t)(uint16_t)part[1][1] << 16),
-                        (uint32_t)(uint16_t)part[1][2] | ((uint32_t)(uint16_t)part[1][3] << 16)};
+        fr.b[j] = tr_frag32(sb, BN * 2, sub, TN * wn + 32 * j);
       } else {
         const int row = TN * wn + 32 * j + l32;
         fr.b[j] = *(const u32x4*)(sb + row * (2 * BK) + 16 * kc_swz<CPR>(row, 2 * sub + hk));

@@ -73,6 +73,7 @@ hipError_t launch_gather_rows(const int32_t* R_ptr, const int32_t* src, int max_
 hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, int max_expert_rows,
                                 hipStream_t stream);
 hipError_t launch_dw_bf16(DwArgs g, hipStream_t stream);
+hipError_t launch_dw_big_bf16(const DwArgs& g, hipStream_t stream);
 hipError_t launch_big_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
 // Row count from which an expert takes the 256-row kernel for this product and
 // shape; kNoBigTiles where that kernel does not apply.
