@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens of the CPU-oracle sample (0: auto)")
     p.add_argument("--router", action="store_true",
                    help="run the router in front of the path (logits = x W_r, drawn W_r) and its backward after dx")
+    p.add_argument("--no-keep-graph", action="store_true",
+                   help="recompute path: the forward keeps no pre-activations, the backward recomputes them")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after the timed steps, run one plain elementwise copy of this many MiB (read and write "
                         "each) so that HBM byte counters can be calibrated against a kernel of known traffic")
@@ -172,7 +174,7 @@ def main():
     t = {n: torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in ("x", "W_gate", "W_up", "W_down", "dy")}
     logits = torch.from_numpy(d["logits"]).to(dev)
     L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho, dw=wl.dw, dg=True,
-                        router=args.router)
+                        router=args.router, keep_graph=not args.no_keep_graph)
     w_r = torch.from_numpy(W.router_weights(wl, seed=0)).to(dev).to(torch.bfloat16) if args.router else None
     stream = torch.cuda.current_stream()
 
@@ -245,7 +247,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "F": wl.F, "E": wl.E, "k": wl.k,
                    "pass": ("router+" if args.router else "") + "fwd+dx+dg" + ("+dW" if wl.dw else "")
-                           + (f"+compact(rho={wl.rho})" if wl.rho else "") + ("+router_bwd" if args.router else ""),
+                           + (f"+compact(rho={wl.rho})" if wl.rho else "") + ("+router_bwd" if args.router else "")
+                           + ("+recompute_h" if args.no_keep_graph else ""),
                    "experts_with_rows": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max())},
         "tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
         "mfma_frac_of_step": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

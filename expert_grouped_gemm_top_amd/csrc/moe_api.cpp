@@ -217,7 +217,6 @@ int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int max_expert_row
   NONNULL(w_gate);
   NONNULL(w_up);
   NONNULL(w_down);
-  NONNULL(h_save);
   NONNULL(a_save);
   NONNULL(o_sorted);
   if (max_rows == 0) return MOE_OK;
@@ -245,6 +244,39 @@ int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int max_expert_row
   g.out0 = (uint16_t*)o_sorted;
   g.out1 = nullptr;
   return hip_status(run(moe::kGemmDown), fn);
+}
+
+int moe_grouped_swiglu_recompute(int H, int F, int E, int max_rows, int max_expert_rows, int dtype,
+                                 const int32_t* offsets, const void* x_rows, const void* w_gate, const void* w_up,
+                                 void* h_rows, void* a_rows, void* stream) {
+  const char* fn = "moe_grouped_swiglu_recompute";
+  int rc = check_expert_dims(fn, H, F, E, dtype);
+  if (rc || (rc = check_rows(fn, max_rows))) return rc;
+  REQUIRE(max_expert_rows >= 0, MOE_ERR_INVALID_ARGUMENT, "%s: max_expert_rows=%d is negative", fn, max_expert_rows);
+  NONNULL(offsets);
+  NONNULL(x_rows);
+  NONNULL(w_gate);
+  NONNULL(w_up);
+  NONNULL(h_rows);
+  if (max_rows == 0) return MOE_OK;
+  moe::RowGemmArgs g{};
+  g.offsets = offsets;
+  g.E = E;
+  g.H = H;
+  g.F = F;
+  g.a = (const uint16_t*)x_rows;
+  g.w0 = (const uint16_t*)w_gate;
+  g.w1 = (const uint16_t*)w_up;
+  g.out0 = (uint16_t*)h_rows;
+  g.out1 = (uint16_t*)a_rows;
+  hipStream_t s = as_stream(stream);
+  return hip_status(timed(MOE_K_GEMM_GATEUP, s,
+                          [&] {
+                            return dtype == MOE_BF16
+                                       ? moe::launch_row_gemm_bf16(moe::kGemmGateUp, g, max_rows, max_expert_rows, s)
+                                       : moe::launch_row_gemm_f32(moe::kGemmGateUp, g, max_rows, s);
+                          }),
+                    fn);
 }
 
 int moe_combine(int T, int H, int k, int dtype, const void* rows, const int32_t* inv, const float* topk_w, void* out,

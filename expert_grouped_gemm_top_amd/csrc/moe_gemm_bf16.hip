@@ -306,10 +306,15 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
       const float* G = hg + 8 * h;
       const float* U = hu + 8 * h;
       const float* V = av + 8 * h;
-      *(u32x4*)(hrow + f + 8 * h) = u32x4{pack_bf2(G[0], G[1]), pack_bf2(G[2], G[3]), pack_bf2(G[4], G[5]), pack_bf2(G[6], G[7])};
-      *(u32x4*)(hrow + F + f + 8 * h) =
-          u32x4{pack_bf2(U[0], U[1]), pack_bf2(U[2], U[3]), pack_bf2(U[4], U[5]), pack_bf2(U[6], U[7])};
-      *(u32x4*)(arow + f + 8 * h) = u32x4{pack_bf2(V[0], V[1]), pack_bf2(V[2], V[3]), pack_bf2(V[4], V[5]), pack_bf2(V[6], V[7])};
+      if (g.out0 != nullptr) {
+        *(u32x4*)(hrow + f + 8 * h) =
+            u32x4{pack_bf2(G[0], G[1]), pack_bf2(G[2], G[3]), pack_bf2(G[4], G[5]), pack_bf2(G[6], G[7])};
+        *(u32x4*)(hrow + F + f + 8 * h) =
+            u32x4{pack_bf2(U[0], U[1]), pack_bf2(U[2], U[3]), pack_bf2(U[4], U[5]), pack_bf2(U[6], U[7])};
+      }
+      if (g.out1 != nullptr)
+        *(u32x4*)(arow + f + 8 * h) =
+            u32x4{pack_bf2(V[0], V[1]), pack_bf2(V[2], V[3]), pack_bf2(V[4], V[5]), pack_bf2(V[6], V[7])};
     }
   } else if (MODE == kGemmDown) {
     // MFMA jj, register r: column 128 nb + 32 gq + 8 r + jj
@@ -546,12 +551,16 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
 #pragma unroll
       for (int i = 0; i < 8; ++i) av[i] = hg[i] * sigmoidf_fast(hg[i]) * hu[i];
       const int f = nb * 64 + 32 * wn + 8 * gq;
-      uint16_t* hrow = g.out0 + grow * 2 * F;
-      *(u32x4*)(hrow + f) = u32x4{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3]), pack_bf2(hg[4], hg[5]), pack_bf2(hg[6], hg[7])};
-      *(u32x4*)(hrow + F + f) =
-          u32x4{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3]), pack_bf2(hu[4], hu[5]), pack_bf2(hu[6], hu[7])};
-      *(u32x4*)(g.out1 + grow * F + f) =
-          u32x4{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3]), pack_bf2(av[4], av[5]), pack_bf2(av[6], av[7])};
+      if (g.out0 != nullptr) {
+        uint16_t* hrow = g.out0 + grow * 2 * F;
+        *(u32x4*)(hrow + f) =
+            u32x4{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3]), pack_bf2(hg[4], hg[5]), pack_bf2(hg[6], hg[7])};
+        *(u32x4*)(hrow + F + f) =
+            u32x4{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3]), pack_bf2(hu[4], hu[5]), pack_bf2(hu[6], hu[7])};
+      }
+      if (g.out1 != nullptr)
+        *(u32x4*)(g.out1 + grow * F + f) =
+            u32x4{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3]), pack_bf2(av[4], av[5]), pack_bf2(av[6], av[7])};
     } else {
       // column 128 nb + 64 wn + 16 gq + 4 r + jb
       float v[16];

@@ -310,9 +310,11 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
             hu[e2] = acc[i][j][8 * p + 4 + e2];
             av[e2] = hg[e2] * sigmoidf_fast(hg[e2]) * hu[e2];
           }
-          *(u32x2*)(hrow + f) = u32x2{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3])};
-          *(u32x2*)(hrow + F + f) = u32x2{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3])};
-          *(u32x2*)(g.out1 + grow * F + f) = u32x2{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3])};
+          if (g.out0 != nullptr) {
+            *(u32x2*)(hrow + f) = u32x2{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3])};
+            *(u32x2*)(hrow + F + f) = u32x2{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3])};
+          }
+          if (g.out1 != nullptr) *(u32x2*)(g.out1 + grow * F + f) = u32x2{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3])};
         }
       } else {
         const int width = (MODE == kGemmDA) ? 2 * F : H;

@@ -66,10 +66,12 @@ __global__ __launch_bounds__(256) void row_gemm_f32_kernel(RowGemmArgs g) {
   }
   if (!ok) return;
   if (MODE == kGemmGateUp) {
-    float* h = (float*)g.out0 + (size_t)row * 2 * F;
-    h[col] = s0;
-    h[F + col] = s1;
-    ((float*)g.out1)[(size_t)row * F + col] = s0 / (1.0f + expf(-s0)) * s1;
+    if (g.out0 != nullptr) {
+      float* h = (float*)g.out0 + (size_t)row * 2 * F;
+      h[col] = s0;
+      h[F + col] = s1;
+    }
+    if (g.out1 != nullptr) ((float*)g.out1)[(size_t)row * F + col] = s0 / (1.0f + expf(-s0)) * s1;
   } else if (MODE == kGemmDA) {
     const float* h = (const float*)g.h + (size_t)row * 2 * F;
     const float hg = h[col], hu = h[F + col];

@@ -16,8 +16,12 @@ from . import moe
 
 class MoeLayerBuffers:
     def __init__(self, T, H, F, E, k, dtype=torch.bfloat16, device="cuda", rho=None, dw=True, dg=True,
-                 router=False):
+                 router=False, keep_graph=True):
+        """keep_graph=False: the forward keeps no pre-activations [hg|hu]; the
+        backward recomputes them from the saved rows (the recompute path that
+        pull request #44 keeps behind keep_graph=False)."""
         self.T, self.H, self.F, self.E, self.k = T, H, F, E, k
+        self.keep_graph = keep_graph
         self.N = N = T * k
         self.dtype, self.rho, self.dw, self.want_dg = dtype, rho, dw, dg
         dev = torch.device(device)
@@ -78,17 +82,19 @@ class MoeLayerBuffers:
         moe.moe_route_topk(logits, self.topk_idx, self.topk_w, self.k, stream)
         moe.moe_dispatch(self.topk_idx, x, self.counts, self.offsets, self.perm, self.inv_perm, self.x_sorted,
                          self.ws, self.E, stream)
-        moe.moe_grouped_swiglu_fwd(self.offsets, self.x_sorted, w_gate, w_up, w_down, self.h_save, self.a_save,
-                                   self.o_sorted, self.N, max_expert_rows=self.T, stream=stream)
+        moe.moe_grouped_swiglu_fwd(self.offsets, self.x_sorted, w_gate, w_up, w_down,
+                                   self.h_save if self.keep_graph else None, self.a_save, self.o_sorted, self.N,
+                                   max_expert_rows=self.T, stream=stream)
         moe.moe_combine(self.o_sorted, self.inv_perm, self.topk_w, self.y, self.k, stream)
         return self.y
 
     # ----------------------------------------------------------------- backward
     def compact(self, score, stream=None):
+        kg = self.keep_graph
         moe.moe_compact_pairs(self.counts, self.offsets, self.perm, score, self.rho, self.kept_counts,
                               self.kept_offsets, self.kept_perm, self.kept_src, self.kept_inv, self.T, self.k,
-                              self.x_sorted, self.a_save if self.dw else None, self.h_save, self.x_kept,
-                              self.a_kept if self.dw else None, self.h_kept, stream)
+                              self.x_sorted, self.a_save if self.dw else None, self.h_save if kg else None,
+                              self.x_kept, self.a_kept if self.dw else None, self.h_kept if kg else None, stream)
 
     def backward(self, dy, w_gate, w_up, w_down, score=None, stream=None, w_r=None):
         """dx (+ dg) and, for full fine-tuning, dW.  With a quota ratio the
@@ -101,6 +107,9 @@ class MoeLayerBuffers:
                                                     self.h_kept)
         else:
             offsets, inv, x_rows, a_rows, h_rows = self.offsets, self.inv_perm, self.x_sorted, self.a_save, self.h_save
+        if not self.keep_graph:  # recompute [hg | hu] of the backward's rows
+            moe.moe_grouped_swiglu_recompute(offsets, x_rows, w_gate, w_up, h_rows, None, self.R,
+                                             max_expert_rows=self.T, stream=stream)
         moe.moe_grouped_bwd_dx(offsets, inv, dy, self.topk_w, h_rows, w_gate, w_up, w_down, self.dO, self.dh,
                                self.dX, self.dx, self.R, inv_all=self.inv_perm if self.want_dg else None,
                                o_sorted=self.o_sorted if self.want_dg else None, dg=self.dg, stream=stream)

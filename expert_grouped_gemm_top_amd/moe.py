@@ -36,6 +36,7 @@ _SIGS = {
     "moe_dispatch_workspace_bytes": ([_i, _i, _i], _sz),
     "moe_dispatch": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_grouped_swiglu_fwd": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i),
+    "moe_grouped_swiglu_recompute": ([_i, _i, _i, _i, _i, _i] + [_vp] * 7, _i),
     "moe_combine": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
     "moe_grouped_bwd_dx": ([_i, _i, _i, _i, _i, _i, _i] + [_vp] * 16, _i),
     "moe_grouped_bwd_dw": ([_i, _i, _i, _i, _i] + [_vp] * 9, _i),
@@ -177,8 +178,19 @@ def moe_grouped_swiglu_fwd(offsets, x_sorted, w_gate, w_up, w_down, h_save, a_sa
     _check(lib().moe_grouped_swiglu_fwd(
         H, F, E, R, R if max_expert_rows is None else max_expert_rows, dt, _ptr(offsets, "offsets", I32, E + 1), _ptr(x_sorted, "x_sorted", d, R * H),
         _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F), _ptr(w_down, "w_down", d, E * F * H),
-        _ptr(h_save, "h_save", d, R * 2 * F), _ptr(a_save, "a_save", d, R * F), _ptr(o_sorted, "o_sorted", d, R * H),
-        _stream(stream)))
+        _ptr(h_save, "h_save", d, R * 2 * F, allow_none=True), _ptr(a_save, "a_save", d, R * F),
+        _ptr(o_sorted, "o_sorted", d, R * H), _stream(stream)))
+
+
+def moe_grouped_swiglu_recompute(offsets, x_rows, w_gate, w_up, h_rows, a_rows, max_rows: int,
+                                 max_expert_rows: int | None = None, stream=None):
+    E, H, F = w_gate.shape
+    dt, d = _dt(w_gate), w_gate.dtype
+    R = max_rows
+    _check(lib().moe_grouped_swiglu_recompute(
+        H, F, E, R, R if max_expert_rows is None else max_expert_rows, dt, _ptr(offsets, "offsets", I32, E + 1),
+        _ptr(x_rows, "x_rows", d, R * H), _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F),
+        _ptr(h_rows, "h_rows", d, R * 2 * F), _ptr(a_rows, "a_rows", d, R * F, allow_none=True), _stream(stream)))
 
 
 def moe_combine(rows, inv, topk_w, out, k: int, stream=None):

@@ -12,6 +12,8 @@
  *   moe_dispatch            token-expert pairs -> rows contiguous per expert
  *   moe_grouped_swiglu_fwd  SwiGLU expert MLP over every expert's rows (ragged
  *                           grouped GEMM); keeps the activations backward needs
+ *   moe_grouped_swiglu_recompute  the forward's pre-activations again, for a
+ *                           forward that did not keep them
  *   moe_combine             router-weighted sum of each token's expert rows
  *   moe_compact_pairs       keep at most a quota of pairs per expert and gather
  *                           their rows into smaller contiguous buffers
@@ -149,12 +151,28 @@ int moe_dispatch(int T, int H, int E, int k, int dtype, const int32_t* topk_idx,
  * unknown): a bound below an actual count costs speed, never correctness,
  * and results do not depend on it beyond rounding; x_sorted [rows, H],
  * w_gate/w_up [E, H, F], w_down [E, F, H] (device); h_save, a_save, o_sorted
- * (device, out).  Rows of empty experts: nothing. */
+ * (device, out).  h_save may be NULL: the forward then keeps no pre-activations
+ * and the backward recomputes them with moe_grouped_swiglu_recompute (pull
+ * request #44, Changes and Compatibility and limits: keep_graph=False restores
+ * the recompute path).  Rows of empty experts: nothing. */
 int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int max_expert_rows, int dtype,
                            const int32_t* offsets,
                            const void* x_sorted, const void* w_gate, const void* w_up,
                            const void* w_down, void* h_save, void* a_save, void* o_sorted,
                            void* stream);
+
+/* The gate/up half of the expert forward over given rows, for the recompute
+ * path (pull request #44, Background and Changes: without kept activations
+ * the backward first recomputes the forward):
+ *   h_rows[s] = [x_rows[s] W_gate[e] | x_rows[s] W_up[e]],  a_rows[s] = silu(hg) * hu
+ * for the rows s of every expert e in offsets.  With the same offsets and row
+ * capacities as a moe_grouped_swiglu_fwd call it gives that call's h_save and
+ * a_save bit for bit.  Arguments as in moe_grouped_swiglu_fwd; x_rows [rows,
+ * H] (device); h_rows [rows, 2F] (device, out); a_rows [rows, F] (device,
+ * out) or NULL. */
+int moe_grouped_swiglu_recompute(int H, int F, int E, int max_rows, int max_expert_rows, int dtype,
+                                 const int32_t* offsets, const void* x_rows, const void* w_gate, const void* w_up,
+                                 void* h_rows, void* a_rows, void* stream);
 
 /* Router-weighted combine (issue #14, Proposal: results scattered back):
  *   out[t] = sum_{j = 0..k-1, inv[t*k+j] >= 0} w[t,j] * rows[inv[t*k+j]]

@@ -32,7 +32,9 @@ def _full_compare(wl, d, L, rho=None, score=None):
     xs = np32(L.x_sorted)
     assert np.array_equal(xs, d["x"][perm // wl.k]), "x_sorted is not an exact row copy"
     y, it = oracle.forward(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"], intermediates=True)
-    assert_close("h_save", np32(L.h_save), np.concatenate([it["hg"], it["hu"]], 1)[perm], tol)
+    h_ref = np.concatenate([it["hg"], it["hu"]], 1)  # pair-indexed
+    if L.keep_graph:  # without it the forward keeps no pre-activations
+        assert_close("h_save", np32(L.h_save), h_ref[perm], tol)
     assert_close("a_save", np32(L.a_save), it["a"][perm], tol)
     assert_close("o_sorted", np32(L.o_sorted), it["o"][perm], tol)
     assert_close("y", np32(L.y), y, tol)
@@ -46,7 +48,10 @@ def _full_compare(wl, d, L, rho=None, score=None):
         assert np.array_equal(L.kept_perm.cpu().numpy()[:R], c["perm"]), "kept_perm"
         assert np.array_equal(L.kept_src.cpu().numpy()[:R], c["src"]), "kept_src"
         assert np.array_equal(np32(L.x_kept)[:R], xs[c["src"]]), "x_kept"
-        assert np.array_equal(np32(L.h_kept)[:R], np32(L.h_save)[c["src"]]), "h_kept"
+        if L.keep_graph:
+            assert np.array_equal(np32(L.h_kept)[:R], np32(L.h_save)[c["src"]]), "h_kept"
+        else:  # recomputed over the kept rows
+            assert_close("h_kept", np32(L.h_kept)[:R], h_ref[c["perm"]], tol)
         if wl.dw:
             assert np.array_equal(np32(L.a_kept)[:R], np32(L.a_save)[c["src"]]), "a_kept"
         retained = c["retained"]
@@ -118,6 +123,33 @@ def test_compaction_with_large_quota_is_bitwise_the_dense_backward():
     assert torch.equal(L1.kept_inv, L0.inv_perm) and torch.equal(L1.kept_offsets, L0.offsets)
     for n in ("dx", "dg", "dw_gate", "dw_up", "dw_down"):
         assert torch.equal(getattr(L0, n), getattr(L1, n)), n
+
+
+# the recompute path (keep_graph=False) against the kept-activation path: the
+# same kernels on the same rows, so every output is bitwise equal
+@pytest.mark.parametrize("wl", [
+    W.custom("bf16_recompute", T=300, H=256, F=256, E=16, k=4, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_recompute_big", T=700, H=256, F=256, E=4, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("fp32_recompute", T=90, H=64, F=40, E=6, k=3, dtype="f32", skew=True, dw=True),
+], ids=lambda w: w.name)
+def test_recompute_path_is_bitwise_the_kept_path(wl):
+    d = W.generate(wl, seed=6)
+    logits = logits_of(wl, d)
+    kept = run_gpu(wl, d, logits)
+    rec = run_gpu(wl, d, logits, keep_graph=False)
+    for n in ("y", "h_save", "a_save", "o_sorted", "dO", "dh", "dX", "dx", "dg", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(getattr(kept, n), getattr(rec, n)), n
+
+
+def test_recompute_path_compacted_matches_oracle():
+    rho = 0.5
+    wl = W.custom("bf16_compact_recompute", T=256, H=256, F=128, E=8, k=2, dtype="bf16", skew=True, dw=True, rho=rho)
+    d = W.generate(wl, seed=2)
+    logits = logits_of(wl, d)
+    _, w = oracle.route_topk(logits, wl.k)
+    score = w.reshape(-1).astype(np.float32)
+    L = run_gpu(wl, d, logits, rho=rho, score=score, keep_graph=False)
+    _full_compare(wl, d, L, rho=rho, score=score)
 
 
 def test_deterministic_bitwise():
