@@ -39,6 +39,8 @@ def _load():
         build()
         _lib = ctypes.CDLL(_LIB)
         _lib.oracle_quota_cap.restype = ctypes.c_int64
+        _lib.oracle_quota_cap_for_budget.restype = ctypes.c_int64
+        _lib.oracle_quota_cap_for_budget.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double]
         _lib.oracle_compact.restype = ctypes.c_int64
         _lib.oracle_dispatch.restype = ctypes.c_int
         _lib.oracle_num_threads.restype = ctypes.c_int
@@ -113,6 +115,23 @@ def dispatch(idx, E):
 
 def quota_cap(T, E, k, rho):
     return int(_load().oracle_quota_cap(T, E, k, ctypes.c_double(rho)))
+
+
+def pair_scores(a_pairs, dy, w):
+    """score[p] = w[p] * ||a_p|| * ||dy_t||: the Frobenius norm of pair p's
+    rank-one term in dW_down.  a_pairs [N, F] pair-indexed, dy [T, H], w [T, k]."""
+    a_pairs, dy, w = _f64(a_pairs), _f64(dy), _f64(w)
+    T, H = dy.shape
+    k = w.shape[1]
+    F = a_pairs.shape[1]
+    out = np.empty(T * k, np.float64)
+    _load().oracle_pair_scores(T, H, F, k, _p(a_pairs), _p(dy), _p(w), _p(out))
+    return out
+
+
+def quota_cap_for_budget(T, H, F, E, k, elem_bytes, with_dw, keep_graph, budget_bytes):
+    return int(_load().oracle_quota_cap_for_budget(T, H, F, E, k, elem_bytes, int(bool(with_dw)),
+                                                   int(bool(keep_graph)), float(budget_bytes)))
 
 
 def compact(T, E, k, counts, offsets, perm, score, rho):

@@ -151,6 +151,45 @@ int oracle_dispatch(int T, int E, int k, const int32_t* idx, int32_t* counts, in
 }
 
 /* ------------------------------------------------------------------------- */
+/* Pair scores for the quota selection (LRMoE abstract: retention guided by
+ * each pair's contribution to the expert update).  The pages leave the metric
+ * open; the one taken here is available before any backward GEMM: the
+ * Frobenius norm of pair p's rank-one term in dW_down,
+ *     score_p = || a_p (w_p dy_t)^T ||_F = w_p * ||a_p||_2 * ||dy_t||_2,
+ * with a_p the pair's SwiGLU activation [F] and t its token.                 */
+void oracle_pair_scores(int T, int H, int F, int k, const double* a_pairs, const double* dy, const double* w,
+                        double* score) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    double sdy = 0.0;
+    for (int h = 0; h < H; ++h) sdy += dy[(size_t)t * H + h] * dy[(size_t)t * H + h];
+    for (int j = 0; j < k; ++j) {
+      const size_t p = (size_t)t * k + j;
+      double sa = 0.0;
+      for (int f = 0; f < F; ++f) sa += a_pairs[p * F + f] * a_pairs[p * F + f];
+      score[p] = w[p] * sqrt(sa) * sqrt(sdy);
+    }
+  }
+}
+
+/* Quota from a memory budget (LRMoE abstract: quotas planned from the memory a
+ * node has for backward work).  A retained row holds dO [H], dh [2F], dX [H] and
+ * the compacted copy of x [H], plus h [2F] when the forward's pre-activations
+ * are kept and a [F] when dW is computed, each of elem_bytes.  The cap is the
+ * largest per-expert quota whose worst case (every expert at its cap) fits:
+ *     cap = floor(budget / (E * row_bytes)),  at most ceil(T k / E);
+ * -1 when not even one row per expert fits.                                 */
+int64_t oracle_quota_cap_for_budget(int T, int H, int F, int E, int k, int elem_bytes, int with_dw, int keep_graph,
+                                    double budget_bytes) {
+  const double row_bytes = (double)elem_bytes * (3.0 * H + 2.0 * F + (keep_graph ? 2.0 * F : 0.0) +
+                                                 (with_dw ? (double)F : 0.0));
+  const double cap = floor(budget_bytes / ((double)E * row_bytes));
+  if (cap < 1.0) return -1;
+  const int64_t most = ((int64_t)T * k + E - 1) / E;
+  return cap < (double)most ? (int64_t)cap : most;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Retention quota (LRMoE abstract: quotas planned during forward).  The
  * per-expert quota is q_e = min(count_e, cap) with cap = ceil(rho * T * k / E);
  * rho = 1 is evaluated in integers.                                          */

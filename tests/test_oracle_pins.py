@@ -485,3 +485,28 @@ def test_router_logits_against_library_matmul(tiny):
     l = oracle.router_logits(x, Wr)
     ref = np.matmul(x, Wr)
     assert np.abs(l - ref).max() <= 1e-14 * np.abs(ref).max()
+
+
+# ----------------------------------------------------------------------------- quota metric and budget
+def test_pair_scores_are_rank_one_frobenius_norms(tiny):
+    x, idx, w = tiny["x"], tiny["idx"], tiny["w"]
+    _, it = oracle.forward(x, idx, w, tiny["W_gate"], tiny["W_up"], tiny["W_down"], intermediates=True)
+    dy = tiny["dy"]
+    s = oracle.pair_scores(it["a"], dy, w)
+    T, k = idx.shape
+    for p in range(0, T * k, 7):  # brute force: build the outer product and take its norm
+        t, j = divmod(p, k)
+        outer = np.outer(it["a"][p], w[t, j] * dy[t])
+        assert abs(s[p] - np.sqrt((outer ** 2).sum())) <= 1e-13 * s[p]
+
+
+def test_quota_cap_for_budget_closed_forms():
+    # row bytes (bf16, H=2048, F=768): 2 * (3*2048 + 2*768 [+ 2*768 kept h] [+ 768 dW])
+    rb = 2 * (3 * 2048 + 2 * 768 + 2 * 768 + 768)
+    assert oracle.quota_cap_for_budget(16384, 2048, 768, 128, 8, 2, True, True, 128 * rb * 1000) == 1000
+    assert oracle.quota_cap_for_budget(16384, 2048, 768, 128, 8, 2, True, True, 128 * rb * 1000 - 1) == 999
+    rb2 = 2 * (3 * 2048 + 2 * 768)  # no kept h, no dW
+    assert oracle.quota_cap_for_budget(16384, 2048, 768, 128, 8, 2, False, False, 128 * rb2 * 7) == 7
+    # capped at ceil(T k / E); -1 when one row per expert does not fit
+    assert oracle.quota_cap_for_budget(100, 64, 32, 8, 2, 4, True, True, 1e12) == 25
+    assert oracle.quota_cap_for_budget(100, 64, 32, 8, 2, 4, True, True, 8 * 4 * (192 + 160) - 1) == -1
