@@ -55,6 +55,11 @@ def parse():
                    help="run the router in front of the path (logits = x W_r, drawn W_r) and its backward after dx")
     p.add_argument("--no-keep-graph", action="store_true",
                    help="recompute path: the forward keeps no pre-activations, the backward recomputes them")
+    p.add_argument("--metric-score", action="store_true",
+                   help="compacted workloads: rank pairs by the norm of their rank-one dW_down term instead of the "
+                        "routing weight")
+    p.add_argument("--budget-mib", type=int, default=0,
+                   help="compacted workloads: quota from this memory budget for the backward's rows instead of rho")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after the timed steps, run one plain elementwise copy of this many MiB (read and write "
                         "each) so that HBM byte counters can be calibrated against a kernel of known traffic")
@@ -173,14 +178,20 @@ def main():
     dev = torch.device("cuda:0")
     t = {n: torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in ("x", "W_gate", "W_up", "W_down", "dy")}
     logits = torch.from_numpy(d["logits"]).to(dev)
-    L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho, dw=wl.dw, dg=True,
-                        router=args.router, keep_graph=not args.no_keep_graph)
+    quota_cap = None
+    if args.budget_mib > 0 and wl.rho is not None:
+        quota_cap = moe.moe_quota_cap_for_budget(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, wl.dw,
+                                                 not args.no_keep_graph, args.budget_mib << 20)
+        assert quota_cap >= 1, "the budget does not hold one row per expert"
+    L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho if quota_cap is None else None,
+                        dw=wl.dw, dg=True, router=args.router, keep_graph=not args.no_keep_graph, quota_cap=quota_cap)
+    score = "metric" if args.metric_score else None
     w_r = torch.from_numpy(W.router_weights(wl, seed=0)).to(dev).to(torch.bfloat16) if args.router else None
     stream = torch.cuda.current_stream()
 
     def step():
         L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], stream, w_r=w_r)
-        L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream, w_r=w_r)
+        L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream, w_r=w_r, score=score)
 
     for _ in range(args.warmup):
         step()
@@ -223,7 +234,7 @@ def main():
     tokens_per_s = wl.T * args.steps / elapsed
 
     counts = L.counts.cpu().numpy()
-    kept = L.kept_counts.cpu().numpy() if wl.rho is not None else None
+    kept = L.kept_counts.cpu().numpy() if L.compacted else None
     alg = algorithmic(wl, counts, kept)
     step_flops = sum(alg[kk][1] for kk in gemm_kernels)
     byts, flops = alg[dom]
@@ -247,8 +258,11 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "F": wl.F, "E": wl.E, "k": wl.k,
                    "pass": ("router+" if args.router else "") + "fwd+dx+dg" + ("+dW" if wl.dw else "")
-                           + (f"+compact(rho={wl.rho})" if wl.rho else "") + ("+router_bwd" if args.router else "")
-                           + ("+recompute_h" if args.no_keep_graph else ""),
+                           + (f"+compact(rho={wl.rho})" if wl.rho and not quota_cap else "")
+                           + ("+router_bwd" if args.router else "")
+                           + ("+recompute_h" if args.no_keep_graph else "")
+                           + ("+metric_score" if args.metric_score else "")
+                           + (f"+budget({args.budget_mib} MiB: cap {quota_cap})" if quota_cap else ""),
                    "experts_with_rows": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max())},
         "tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
         "mfma_frac_of_step": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

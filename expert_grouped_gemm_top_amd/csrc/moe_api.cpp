@@ -419,6 +419,49 @@ int moe_router_bwd(int T, int H, int E, int k, int dtype, const void* x, const v
                     fn);
 }
 
+int moe_compact_pairs(int T, int H, int F, int E, int k, int dtype, double rho, const int32_t* counts,
+                      const int32_t* offsets, const int32_t* perm, const float* score, int32_t* kept_counts,
+                      int32_t* kept_offsets, int32_t* kept_perm, int32_t* kept_src, int32_t* kept_inv,
+                      const void* x_sorted, const void* a_save, const void* h_save, void* x_kept, void* a_kept,
+                      void* h_kept, void* stream) {
+  const char* fn = "moe_compact_pairs";
+  REQUIRE(rho > 0.0 && std::isfinite(rho), MOE_ERR_INVALID_ARGUMENT, "%s: rho=%g must be positive and finite", fn,
+          rho);
+  int rc = check_routing_dims(fn, T, E, k);
+  if (rc) return rc;
+  const int64_t cap64 = moe_quota_cap(T, E, k, rho);
+  return moe_compact_pairs_cap(T, H, F, E, k, dtype, (int)std::min<int64_t>(cap64, (int64_t)T * k), counts, offsets,
+                               perm, score, kept_counts, kept_offsets, kept_perm, kept_src, kept_inv, x_sorted, a_save,
+                               h_save, x_kept, a_kept, h_kept, stream);
+}
+
+int64_t moe_quota_cap_for_budget(int T, int H, int F, int E, int k, int dtype, int with_dw, int keep_graph,
+                                 size_t budget_bytes) {
+  if (T < 1 || H < 1 || F < 1 || E < 1 || k < 1 || (dtype != MOE_F32 && dtype != MOE_BF16)) return -1;
+  const int64_t eb = dtype == MOE_F32 ? 4 : 2;
+  const int64_t row_bytes = eb * (3 * (int64_t)H + 2 * (int64_t)F + (keep_graph ? 2 * (int64_t)F : 0) +
+                                  (with_dw ? (int64_t)F : 0));
+  const int64_t cap = (int64_t)(budget_bytes / (uint64_t)(E * row_bytes));
+  if (cap < 1) return -1;
+  const int64_t most = ((int64_t)T * k + E - 1) / E;
+  return cap < most ? cap : most;
+}
+
+int moe_pair_scores(int T, int H, int F, int k, int dtype, const int32_t* inv_perm, const float* topk_w,
+                    const void* a_save, const void* dy, float* score, void* stream) {
+  const char* fn = "moe_pair_scores";
+  int rc = check_routing_dims(fn, T, k, k);
+  if (rc || (rc = check_dtype(fn, dtype)) || (rc = check_row_width(fn, "H", H)) || (rc = check_row_width(fn, "F", F)))
+    return rc;
+  NONNULL(inv_perm);
+  NONNULL(topk_w);
+  NONNULL(a_save);
+  NONNULL(dy);
+  NONNULL(score);
+  hipStream_t s = as_stream(stream);
+  return hip_status(moe::launch_pair_scores(T, H, F, k, esize_of(dtype), inv_perm, topk_w, a_save, dy, score, s), fn);
+}
+
 int64_t moe_quota_cap(int T, int E, int k, double rho) {
   if (T < 1 || E < 1 || k < 1 || !(rho > 0.0) || !std::isfinite(rho)) return -1;
   if (rho == 1.0) return ((int64_t)T * k + E - 1) / E;
@@ -427,16 +470,15 @@ int64_t moe_quota_cap(int T, int E, int k, double rho) {
   return (int64_t)(c < n ? c : n);
 }
 
-int moe_compact_pairs(int T, int H, int F, int E, int k, int dtype, double rho, const int32_t* counts,
-                      const int32_t* offsets, const int32_t* perm, const float* score, int32_t* kept_counts,
-                      int32_t* kept_offsets, int32_t* kept_perm, int32_t* kept_src, int32_t* kept_inv,
-                      const void* x_sorted, const void* a_save, const void* h_save, void* x_kept, void* a_kept,
-                      void* h_kept, void* stream) {
-  const char* fn = "moe_compact_pairs";
+int moe_compact_pairs_cap(int T, int H, int F, int E, int k, int dtype, int cap, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* perm, const float* score, int32_t* kept_counts,
+                          int32_t* kept_offsets, int32_t* kept_perm, int32_t* kept_src, int32_t* kept_inv,
+                          const void* x_sorted, const void* a_save, const void* h_save, void* x_kept, void* a_kept,
+                          void* h_kept, void* stream) {
+  const char* fn = "moe_compact_pairs_cap";
   int rc = check_routing_dims(fn, T, E, k);
   if (rc || (rc = check_dtype(fn, dtype))) return rc;
-  REQUIRE(rho > 0.0 && std::isfinite(rho), MOE_ERR_INVALID_ARGUMENT, "%s: rho=%g must be positive and finite", fn,
-          rho);
+  REQUIRE(cap >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: quota cap=%d must be >= 1", fn, cap);
   NONNULL(counts);
   NONNULL(offsets);
   NONNULL(perm);
@@ -452,8 +494,7 @@ int moe_compact_pairs(int T, int H, int F, int E, int k, int dtype, double rho, 
   if (x_sorted && (rc = check_row_width(fn, "H", H))) return rc;
   if ((a_save || h_save) && (rc = check_row_width(fn, "F", F))) return rc;
   const int64_t N = (int64_t)T * k;
-  const int64_t cap64 = moe_quota_cap(T, E, k, rho);
-  const int cap = (int)(cap64 < N ? cap64 : N);
+  if ((int64_t)cap > N) cap = (int)N;
   hipStream_t s = as_stream(stream);
   if ((rc = hip_status(moe::launch_fill_i32(kept_inv, N, -1, s), fn))) return rc;
   if ((rc = hip_status(timed(MOE_K_COMPACT, s,

@@ -149,6 +149,50 @@ __global__ __launch_bounds__(256) void grad_rows_kernel(int Tn, int H, int k, co
   }
 }
 
+// Pair scores for the quota selection: score[p] = w[p] * ||a_p|| * ||dy_t||,
+// the Frobenius norm of pair p's rank-one term in dW_down (a_p = the pair's
+// row of a_save, found through inv_perm; a pair without a row scores 0).  One
+// block per token; sums of squares in fp32, reduced in a fixed order.
+template <typename T>
+__global__ __launch_bounds__(256) void pair_scores_kernel(int Tn, int H, int F, int k, const int32_t* __restrict__ inv,
+                                                          const float* __restrict__ w, const T* __restrict__ a_rows,
+                                                          const T* __restrict__ dy, float* __restrict__ score) {
+  __shared__ float s_part[4];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  auto block_sum = [&](float v) {
+    v = wave_sum(v);
+    if (lane == 0) s_part[wv] = v;
+    __syncthreads();
+    const float r = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+    __syncthreads();
+    return r;
+  };
+  for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
+    float q = 0.0f;
+    for (int c = tid; c < H / 8; c += 256) {
+      float v[8];
+      Vec8<T>::load(dy + (size_t)t * H + c * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q += v[i] * v[i];
+    }
+    const float ndy = sqrtf(block_sum(q));
+    for (int j = 0; j < k; ++j) {
+      const size_t p = (size_t)t * k + j;
+      const int r = inv[p];
+      float sa = 0.0f;
+      if (r >= 0)
+        for (int c = tid; c < F / 8; c += 256) {
+          float v[8];
+          Vec8<T>::load(a_rows + (size_t)r * F + c * 8, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sa += v[i] * v[i];
+        }
+      const float na = sqrtf(block_sum(sa));
+      if (tid == 0) score[p] = (r >= 0) ? w[p] * na * ndy : 0.0f;
+    }
+  }
+}
+
 // Row r < R = kept_offsets[E]: copy 16-byte chunks of up to three row sources.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restrict__ R_ptr,
                                                           const int32_t* __restrict__ src, int max_rows,
@@ -239,6 +283,17 @@ hipError_t launch_grad_rows(int T, int H, int k, int esize, const void* dy, cons
     dispatch_kp<float, GradRowsL>(k, T, H, k, dy, w, inv, dO_rows, inv_all, o_sorted, dg, stream);
   else
     dispatch_kp<uint16_t, GradRowsL>(k, T, H, k, dy, w, inv, dO_rows, inv_all, o_sorted, dg, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_scores(int T, int H, int F, int k, int esize, const int32_t* inv, const float* w,
+                              const void* a_rows, const void* dy, float* score, hipStream_t stream) {
+  if (esize == 4)
+    hipLaunchKernelGGL(pair_scores_kernel<float>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, F, k, inv, w,
+                       (const float*)a_rows, (const float*)dy, score);
+  else
+    hipLaunchKernelGGL(pair_scores_kernel<uint16_t>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, F, k, inv, w,
+                       (const uint16_t*)a_rows, (const uint16_t*)dy, score);
   return hipGetLastError();
 }
 

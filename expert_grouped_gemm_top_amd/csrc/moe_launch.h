@@ -64,6 +64,8 @@ hipError_t launch_combine(int T, int H, int k, int esize, const void* rows, cons
 hipError_t launch_grad_rows(int T, int H, int k, int esize, const void* dy, const float* w, const int32_t* inv,
                             void* dO_rows, const int32_t* inv_all, const void* o_sorted, float* dg,
                             hipStream_t stream);
+hipError_t launch_pair_scores(int T, int H, int F, int k, int esize, const int32_t* inv, const float* w,
+                              const void* a_rows, const void* dy, float* score, hipStream_t stream);
 hipError_t launch_gather_rows(const int32_t* R_ptr, const int32_t* src, int max_rows, const void* a_src, void* a_dst,
                               int a_bytes, const void* b_src, void* b_dst, int b_bytes, const void* c_src,
                               void* c_dst, int c_bytes, hipStream_t stream);

@@ -16,10 +16,13 @@ from . import moe
 
 class MoeLayerBuffers:
     def __init__(self, T, H, F, E, k, dtype=torch.bfloat16, device="cuda", rho=None, dw=True, dg=True,
-                 router=False, keep_graph=True):
-        """keep_graph=False: the forward keeps no pre-activations [hg|hu]; the
-        backward recomputes them from the saved rows (the recompute path that
-        pull request #44 keeps behind keep_graph=False)."""
+                 router=False, keep_graph=True, quota_cap=None):
+        """rho: quota ratio of the compacted backward (None: no compaction);
+        quota_cap: the per-expert quota directly (e.g. from
+        moe.moe_quota_cap_for_budget), instead of rho.  keep_graph=False: the
+        forward keeps no pre-activations [hg|hu]; the backward recomputes them
+        from the saved rows (the recompute path that pull request #44 keeps
+        behind keep_graph=False)."""
         self.T, self.H, self.F, self.E, self.k = T, H, F, E, k
         self.keep_graph = keep_graph
         self.N = N = T * k
@@ -40,8 +43,10 @@ class MoeLayerBuffers:
         self.a_save = em(N, F)
         self.o_sorted = em(N, H)
         self.y = em(T, H)
-        if rho is not None:
-            cap = moe.moe_quota_cap(T, E, k, rho)
+        self.quota_cap = quota_cap
+        self.compacted = rho is not None or quota_cap is not None
+        if self.compacted:
+            cap = moe.moe_quota_cap(T, E, k, rho) if quota_cap is None else quota_cap
             self.R = min(N, E * cap)
             self.kept_counts = em(E, dt=i32)
             self.kept_offsets = em(E + 1, dt=i32)
@@ -51,6 +56,7 @@ class MoeLayerBuffers:
             self.x_kept = em(self.R, H)
             self.a_kept = em(self.R, F)
             self.h_kept = em(self.R, 2 * F)
+            self.score = em(N, dt=f32)
         else:
             self.R = N
         R = self.R
@@ -91,17 +97,23 @@ class MoeLayerBuffers:
     # ----------------------------------------------------------------- backward
     def compact(self, score, stream=None):
         kg = self.keep_graph
-        moe.moe_compact_pairs(self.counts, self.offsets, self.perm, score, self.rho, self.kept_counts,
+        moe.moe_compact_pairs(self.counts, self.offsets, self.perm, score, self.rho or 1.0, self.kept_counts,
                               self.kept_offsets, self.kept_perm, self.kept_src, self.kept_inv, self.T, self.k,
                               self.x_sorted, self.a_save if self.dw else None, self.h_save if kg else None,
-                              self.x_kept, self.a_kept if self.dw else None, self.h_kept if kg else None, stream)
+                              self.x_kept, self.a_kept if self.dw else None, self.h_kept if kg else None, stream,
+                              cap=self.quota_cap)
 
     def backward(self, dy, w_gate, w_up, w_down, score=None, stream=None, w_r=None):
-        """dx (+ dg) and, for full fine-tuning, dW.  With a quota ratio the
-        backward runs on the compacted retained pairs (score defaults to the
-        routing weights).  With w_r, the router's backward follows: dlogits,
-        dw_r, and its share added to dx."""
-        if self.rho is not None:
+        """dx (+ dg) and, for full fine-tuning, dW.  With a quota the backward
+        runs on the compacted retained pairs; score: a pair-indexed fp32 tensor,
+        None (the routing weights) or "metric" (moe_pair_scores: the norm of
+        each pair's rank-one dW_down term).  With w_r, the router's backward
+        follows: dlogits, dw_r, and its share added to dx."""
+        if self.compacted:
+            if isinstance(score, str):
+                assert score == "metric", score
+                moe.moe_pair_scores(self.inv_perm, self.topk_w, self.a_save, dy, self.score, stream)
+                score = self.score
             self.compact(self.topk_w.view(-1) if score is None else score, stream)
             offsets, inv, x_rows, a_rows, h_rows = (self.kept_offsets, self.kept_inv, self.x_kept, self.a_kept,
                                                     self.h_kept)

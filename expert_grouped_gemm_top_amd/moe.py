@@ -42,6 +42,9 @@ _SIGS = {
     "moe_grouped_bwd_dw": ([_i, _i, _i, _i, _i] + [_vp] * 9, _i),
     "moe_quota_cap": ([_i, _i, _i, _d], _i64),
     "moe_compact_pairs": ([_i, _i, _i, _i, _i, _i, _d] + [_vp] * 16, _i),
+    "moe_compact_pairs_cap": ([_i, _i, _i, _i, _i, _i, _i] + [_vp] * 16, _i),
+    "moe_quota_cap_for_budget": ([_i, _i, _i, _i, _i, _i, _i, _i, _sz], _i64),
+    "moe_pair_scores": ([_i, _i, _i, _i, _i] + [_vp] * 6, _i),
 }
 
 
@@ -230,19 +233,40 @@ def moe_grouped_bwd_dw(offsets, x_rows, a_rows, dO_rows, dh_rows, dw_gate, dw_up
         _ptr(dw_down, "dw_down", d, E * F * H), _stream(stream)))
 
 
-def moe_compact_pairs(counts, offsets, perm, score, rho: float, kept_counts, kept_offsets, kept_perm, kept_src,
+def moe_quota_cap_for_budget(T: int, H: int, F: int, E: int, k: int, dtype, with_dw: bool, keep_graph: bool,
+                             budget_bytes: int) -> int:
+    dt = MOE_F32 if dtype == torch.float32 else MOE_BF16
+    return int(lib().moe_quota_cap_for_budget(T, H, F, E, k, dt, int(bool(with_dw)), int(bool(keep_graph)),
+                                              int(budget_bytes)))
+
+
+def moe_pair_scores(inv_perm, topk_w, a_save, dy, score, stream=None):
+    T, H = dy.shape
+    k = topk_w.shape[1]
+    F = a_save.shape[1]
+    d = dy.dtype
+    _check(lib().moe_pair_scores(T, H, F, k, _dt(dy), _ptr(inv_perm, "inv_perm", I32, T * k),
+                                 _ptr(topk_w, "topk_w", F32, T * k), _ptr(a_save, "a_save", d, None),
+                                 _ptr(dy, "dy", d, T * H), _ptr(score, "score", F32, T * k), _stream(stream)))
+
+
+def moe_compact_pairs(counts, offsets, perm, score, rho, kept_counts, kept_offsets, kept_perm, kept_src,
                       kept_inv, T: int, k: int, x_sorted=None, a_save=None, h_save=None, x_kept=None, a_kept=None,
-                      h_kept=None, stream=None):
+                      h_kept=None, stream=None, cap=None):
+    """Quota from rho (moe_compact_pairs) or, when cap is given, that quota
+    directly (moe_compact_pairs_cap; rho is then ignored)."""
     E = counts.shape[0]
     N = T * k
     ref = next((t for t in (x_sorted, a_save, h_save) if t is not None), None)
     d = ref.dtype if ref is not None else torch.bfloat16
     H = x_sorted.shape[1] if x_sorted is not None else 8
     F = a_save.shape[1] if a_save is not None else (h_save.shape[1] // 2 if h_save is not None else 8)
-    cap = moe_quota_cap(T, E, k, rho)
-    R = min(N, E * cap) if cap > 0 else 0
-    _check(lib().moe_compact_pairs(
-        T, H, F, E, k, MOE_F32 if d == torch.float32 else MOE_BF16, float(rho), _ptr(counts, "counts", I32, E),
+    q = moe_quota_cap(T, E, k, rho) if cap is None else int(cap)
+    R = min(N, E * q) if q > 0 else 0
+    call = lib().moe_compact_pairs if cap is None else lib().moe_compact_pairs_cap
+    _check(call(
+        T, H, F, E, k, MOE_F32 if d == torch.float32 else MOE_BF16, float(rho) if cap is None else q,
+        _ptr(counts, "counts", I32, E),
         _ptr(offsets, "offsets", I32, E + 1), _ptr(perm, "perm", I32, N), _ptr(score, "score", F32, N),
         _ptr(kept_counts, "kept_counts", I32, E), _ptr(kept_offsets, "kept_offsets", I32, E + 1),
         _ptr(kept_perm, "kept_perm", I32, R), _ptr(kept_src, "kept_src", I32, R), _ptr(kept_inv, "kept_inv", I32, N),

@@ -19,6 +19,7 @@
  *                           their rows into smaller contiguous buffers
  *   moe_grouped_bwd_dx      input gradient (experts frozen) + routing-weight
  *                           gradient, over all or only the retained pairs
+ *   moe_pair_scores         per-pair scores for the quota selection
  *   moe_grouped_bwd_dw      expert weight gradients (full fine-tuning)
  *   moe_router_bwd          router gradients (logits, W_r, the router's share
  *                           of dx) from the routing-weight gradient
@@ -261,6 +262,38 @@ int moe_compact_pairs(int T, int H, int F, int E, int k, int dtype, double rho,
                       int32_t* kept_perm, int32_t* kept_src, int32_t* kept_inv,
                       const void* x_sorted, const void* a_save, const void* h_save, void* x_kept,
                       void* a_kept, void* h_kept, void* stream);
+
+/* The same selection and compaction with the per-expert quota given directly
+ * (cap >= 1; a cap above T*k means no pair is dropped), e.g. from
+ * moe_quota_cap_for_budget. */
+int moe_compact_pairs_cap(int T, int H, int F, int E, int k, int dtype, int cap,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                      const float* score, int32_t* kept_counts, int32_t* kept_offsets,
+                      int32_t* kept_perm, int32_t* kept_src, int32_t* kept_inv,
+                      const void* x_sorted, const void* a_save, const void* h_save, void* x_kept,
+                      void* a_kept, void* h_kept, void* stream);
+
+/* Quota cap from a memory budget for the backward's per-row buffers (LRMoE
+ * abstract: quotas planned from the memory a node can spend).  A retained row
+ * holds dO [H], dh [2F], dX [H] and its compacted x [H], plus h [2F] when
+ * keep_graph and a [F] when with_dw, all of `dtype`; the cap is the largest
+ * per-expert quota whose worst case (every expert at its cap) fits:
+ *   floor(budget_bytes / (E * row_bytes)), at most ceil(T k / E);
+ * -1 when not even one row per expert fits or an argument is invalid.
+ * Host-only. */
+int64_t moe_quota_cap_for_budget(int T, int H, int F, int E, int k, int dtype, int with_dw, int keep_graph,
+                                 size_t budget_bytes);
+
+/* Pair scores for the quota selection (LRMoE abstract: retention by each
+ * pair's contribution to the expert update; the pages leave the metric open).
+ * The metric here is known before any backward GEMM: the Frobenius norm of
+ * pair p's rank-one term in dW_down,
+ *   score[p] = topk_w[p] * ||a_save[inv_perm[p]]||_2 * ||dy[p / k]||_2
+ * (0 for a pair without a row), sums of squares in fp32.  inv_perm [T*k] int32,
+ * topk_w [T*k] fp32, a_save [*, F], dy [T, H] of `dtype` (device); score
+ * [T*k] fp32 (device, out). */
+int moe_pair_scores(int T, int H, int F, int k, int dtype, const int32_t* inv_perm, const float* topk_w,
+                    const void* a_save, const void* dy, float* score, void* stream);
 
 #ifdef __cplusplus
 }

@@ -133,3 +133,20 @@ def test_router_calls_validation(lib):
     assert b(*bad) == 1 and "dg must" in _err(lib)
     bad = list(args); bad[12] = NULL
     assert b(*bad) == 1 and "dx must" in _err(lib)
+
+
+def test_quota_metric_calls(lib):
+    import oracle
+    for args in ((16384, 2048, 768, 128, 8, 1, 1, 1, 1 << 30), (100, 64, 32, 8, 2, 0, 1, 1, 10 ** 12),
+                 (4096, 2048, 768, 128, 8, 1, 0, 0, 123456789), (100, 64, 32, 8, 2, 0, 1, 1, 11263)):
+        T, H, F, E, k, dt, dw, kg, budget = args
+        assert lib.moe_quota_cap_for_budget(*args) == oracle.quota_cap_for_budget(
+            T, H, F, E, k, 4 if dt == 0 else 2, dw, kg, budget)
+    assert lib.moe_quota_cap_for_budget(16, 64, 32, 8, 2, 7, 1, 1, 1 << 20) == -1
+    c = lib.moe_compact_pairs_cap
+    args = [16384, 2048, 768, 128, 8, 1, 1024] + [P] * 15 + [NULL]
+    bad = list(args); bad[6] = 0
+    assert c(*bad) == 1 and "cap" in _err(lib)
+    s = lib.moe_pair_scores
+    assert s(64, 128, 64, 2, 1, P, P, P, P, NULL, NULL) == 1 and "score" in _err(lib)
+    assert s(64, 100, 64, 2, 1, P, P, P, P, P, NULL) == 2

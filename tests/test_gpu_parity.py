@@ -11,8 +11,9 @@ import torch
 
 import oracle
 from expert_grouped_gemm_top_amd import workloads as W
+from expert_grouped_gemm_top_amd.layer import MoeLayerBuffers
 from moe_cases import (TOL, assert_close, dw_queries, gpu_dw_entries, logits_of, note, np32, oracle_dw_sample,
-                       oracle_tokens, run_gpu)
+                       oracle_tokens, run_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -274,3 +275,60 @@ def test_full_size_layer(name):
             assert_close(name, got[sel], ref[sel], tol)
         for e in np.nonzero(kc == 0)[0]:
             assert not L.dw_gate[e].any() and not L.dw_up[e].any() and not L.dw_down[e].any(), f"expert {e} not zero"
+
+
+# ----------------------------------------------------------------------------- quota metric and budget
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pair_scores_match_oracle(dtype):
+    from expert_grouped_gemm_top_amd import moe
+    wl = W.custom("scores_" + dtype, T=120, H=256 if dtype == "bf16" else 64, F=128 if dtype == "bf16" else 40,
+                  E=8, k=2, dtype=dtype, skew=True, dw=False)
+    d = W.generate(wl, seed=7)
+    logits = logits_of(wl, d)
+    L = run_gpu(wl, d, logits)
+    t = to_dev(wl, d)
+    score = torch.empty(wl.N, dtype=torch.float32, device="cuda")
+    moe.moe_pair_scores(L.inv_perm, L.topk_w, L.a_save, t["dy"], score)
+    torch.cuda.synchronize()
+    idx, w = oracle.route_topk(logits, wl.k)
+    _, it = oracle.forward(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"], intermediates=True)
+    ref = oracle.pair_scores(it["a"], d["dy"], w)
+    assert_close("score", score.cpu().numpy(), ref, TOL[dtype])
+
+
+def test_budget_quota_with_metric_scores():
+    """Compaction with the quota from a memory budget and the pairs ranked by
+    the metric: kept counts are min(n_e, cap); each expert keeps its top-cap
+    pairs by the GPU's own scores (ties to the lower pair id); where the
+    oracle's scores separate the cap boundary by more than the tolerance, the
+    kept set is the oracle's."""
+    from expert_grouped_gemm_top_amd import moe
+    wl = W.custom("bf16_budget", T=256, H=256, F=128, E=8, k=2, dtype="bf16", skew=True, dw=True)
+    d = W.generate(wl, seed=8)
+    logits = logits_of(wl, d)
+    budget = 40 * wl.E * 2 * (3 * wl.H + 2 * wl.F + 2 * wl.F + wl.F)  # room for 40 rows per expert
+    cap = moe.moe_quota_cap_for_budget(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, True, True, budget)
+    assert cap == 40
+    t = to_dev(wl, d)
+    L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, "cuda", dw=True, quota_cap=cap)
+    L.forward(torch.from_numpy(logits).cuda(), t["x"], t["W_gate"], t["W_up"], t["W_down"])
+    L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], score="metric")
+    torch.cuda.synchronize()
+    counts = L.counts.cpu().numpy()
+    assert np.array_equal(L.kept_counts.cpu().numpy(), np.minimum(counts, cap))
+    sc = L.score.cpu().numpy()
+    perm = L.perm.cpu().numpy()
+    offs = L.offsets.cpu().numpy()
+    kinv = L.kept_inv.cpu().numpy()
+    idx, w = oracle.route_topk(logits, wl.k)
+    _, it = oracle.forward(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"], intermediates=True)
+    ref = oracle.pair_scores(it["a"], d["dy"], w)
+    for e in range(wl.E):
+        pairs = perm[offs[e]:offs[e + 1]]
+        order = sorted(pairs, key=lambda p: (-sc[p], p))
+        assert set(order[:cap]) == set(p for p in pairs if kinv[p] >= 0), e
+        if len(pairs) > cap:
+            r = sorted(ref[pairs], reverse=True)
+            if r[cap - 1] - r[cap] > 2e-2 * r[0]:  # unambiguous boundary
+                top = set(sorted(pairs, key=lambda p: (-ref[p], p))[:cap])
+                assert top == set(p for p in pairs if kinv[p] >= 0), e
