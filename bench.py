@@ -55,6 +55,8 @@ def parse():
                    help="run the router in front of the path (logits = x W_r, drawn W_r) and its backward after dx")
     p.add_argument("--no-keep-graph", action="store_true",
                    help="recompute path: the forward keeps no pre-activations, the backward recomputes them")
+    p.add_argument("--forward-only", action="store_true",
+                   help="time the forward alone (route, dispatch, expert GEMMs, combine), e.g. for decode batches")
     p.add_argument("--metric-score", action="store_true",
                    help="compacted workloads: rank pairs by the norm of their rank-one dW_down term instead of the "
                         "routing weight")
@@ -191,14 +193,16 @@ def main():
 
     def step():
         L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], stream, w_r=w_r)
-        L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream, w_r=w_r, score=score)
+        if not args.forward_only:
+            L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream, w_r=w_r, score=score)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    gemm_kernels = [K_GATEUP, K_DOWN, K_DA, K_DX] + ([K_DW] if wl.dw else [])
-    profiled = gemm_kernels + ([K_ROUTER_FWD, K_ROUTER_DW] if args.router else [])
+    gemm_kernels = [K_GATEUP, K_DOWN] + ([] if args.forward_only else [K_DA, K_DX] + ([K_DW] if wl.dw else []))
+    router_kernels = ([K_ROUTER_FWD] + ([] if args.forward_only else [K_ROUTER_DW])) if args.router else []
+    profiled = gemm_kernels + router_kernels
     lib = moe.lib()
     lib.moe_profile_kernel.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
 
@@ -257,7 +261,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "F": wl.F, "E": wl.E, "k": wl.k,
-                   "pass": ("router+" if args.router else "") + "fwd+dx+dg" + ("+dW" if wl.dw else "")
+                   "pass": ("router+" if args.router else "") + ("fwd" if args.forward_only else "fwd+dx+dg")
+                           + ("+dW" if wl.dw and not args.forward_only else "")
                            + (f"+compact(rho={wl.rho})" if wl.rho and not quota_cap else "")
                            + ("+router_bwd" if args.router else "")
                            + ("+recompute_h" if args.no_keep_graph else "")
@@ -275,7 +280,7 @@ def main():
                                             "TFLOP/s": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12,
                                             "frac_fp32_alu": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
                                             "GB/s": alg[kk][0] / (kernel_ms[kk] * 1e-3) / 1e9}
-                         for kk in (K_ROUTER_FWD, K_ROUTER_DW)}
+                         for kk in router_kernels}
     if args.copy_probe_mib > 0:
         # one read + one write of copy_probe_mib MiB each, outside the timed steps
         src = torch.ones(args.copy_probe_mib << 19, dtype=torch.bfloat16, device=dev)

@@ -45,6 +45,7 @@ namespace {
 #define MOE_STREAM_SPLITK 0x1212
 #endif
 
+constexpr int kFewRows = 128;  // below this many rows in all, the streaming kernel splits K four ways
 constexpr int kTileRows = 16;  // rows of one expert per wave tile of the streaming kernel (one MFMA row block)
 constexpr int kBigRows = kMidTileMinRows;  // experts with at least this many rows use an LDS-tiled kernel
 constexpr int kTBM = 128;      // LDS-tiled kernel: rows per workgroup tile
@@ -743,7 +744,9 @@ hipError_t launch_row_gemm_mode(const RowGemmArgs& args, int max_rows, int max_e
   // K-contiguous: 128) in each half
   const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? g.H : (MODE == kGemmDown ? g.F : 2 * g.F);
   const int kstep = RowGemmShape<MODE>::kNN ? 32 : 128;
-  int ks = (MOE_STREAM_SPLITK >> (4 * MODE)) & 0xf;
+  // decode-sized batches (a handful of rows in all) have too few tiles to keep
+  // the chip's memory busy: split every product four ways
+  int ks = N < kFewRows ? 4 : (MOE_STREAM_SPLITK >> (4 * MODE)) & 0xf;
   while (ks > 1 && (K % (ks * kstep) != 0 || row_gemm_blocks<MODE>(g.H, g.F) % (4 / ks) != 0)) ks /= 2;
   g.stream_ksplit = ks;
   const int64_t n_stream = (small_tiles * row_gemm_blocks<MODE>(g.H, g.F) * g.stream_ksplit + 3) / 4;

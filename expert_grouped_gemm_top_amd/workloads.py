@@ -16,6 +16,7 @@ pages train Qwen3-30B-A3B and name GLM4.5-106B-A12B in the LRMoE abstract):
   qwen3_ft_t4096       T=4096,  H=2048, F=768,  E=128, k=8, bf16, skewed logits
   glm45air_t8192       T=8192,  H=4096, F=1408, E=128, k=8, bf16, skewed logits
   qwen3_compact_t16384 T=16384, H=2048, F=768,  E=128, k=8, bf16, skewed, quota rho=1
+  qwen3_decode_t1/_t8  T=1 / 8, H=2048, F=768,  E=128, k=8, bf16, N(0,1) logits
 Skew: logits += b_e with b_e = 1.2*ln(1/rank_e), rank_e = e+1 (expert 0 is the
 hottest), added in float32.  "N(0, s)" means standard deviation s.
 """
@@ -52,6 +53,10 @@ WORKLOADS = {
     "qwen3_ft_t4096": Workload("qwen3_ft_t4096", 4096, 2048, 768, 128, 8, "bf16", "logits", True, True, None),
     "glm45air_t8192": Workload("glm45air_t8192", 8192, 4096, 1408, 128, 8, "bf16", "logits", True, True, None),
     "qwen3_compact_t16384": Workload("qwen3_compact_t16384", 16384, 2048, 768, 128, 8, "bf16", "logits", True, True, 1.0),
+    # decode-sized batches: every routed expert has one or a few rows, so the
+    # layer streams k (or up to T*k) experts' weights per step
+    "qwen3_decode_t1": Workload("qwen3_decode_t1", 1, 2048, 768, 128, 8, "bf16", "logits", False, False, None),
+    "qwen3_decode_t8": Workload("qwen3_decode_t8", 8, 2048, 768, 128, 8, "bf16", "logits", False, False, None),
 }
 
 

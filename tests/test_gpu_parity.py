@@ -218,7 +218,8 @@ def test_dispatch_edge_cases(T, E, k, skew):
 
 
 # ----------------------------------------------------------------------------- full-size layers (sampled)
-FULL = ["qwen3_lora_t128", "qwen3_ft_t4096", "glm45air_t8192", "qwen3_compact_t16384"]
+FULL = ["qwen3_lora_t128", "qwen3_ft_t4096", "glm45air_t8192", "qwen3_compact_t16384", "qwen3_decode_t1",
+        "qwen3_decode_t8"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -248,7 +249,8 @@ def test_full_size_layer(name):
         rows_of_pair = c["inv"]
     rng = np.random.default_rng(123)
     hot = np.nonzero(idx.reshape(-1) == int(np.argmax(counts)))[0] // wl.k
-    tokens = np.unique(np.concatenate([rng.choice(wl.T, 6, replace=False), hot[:2], [0, wl.T - 1]])).astype(np.int32)
+    tokens = np.unique(np.concatenate([rng.choice(wl.T, min(6, wl.T), replace=False), hot[:2],
+                                       [0, wl.T - 1]])).astype(np.int32)
     note(f"oracle on {len(tokens)} sampled tokens")
     y, dx, dg, it, bt = oracle_tokens(wl, d, idx, w, tokens, retained=retained)
     tt = torch.from_numpy(tokens).long().cuda()
