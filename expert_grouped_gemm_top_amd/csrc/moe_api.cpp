@@ -111,6 +111,52 @@ int check_router_workspace(const char* fn, int T, int H, int E, const void* ws, 
   return MOE_OK;
 }
 
+// The expert forward; with perm, row s of the gate/up product reads
+// x[perm[s] / k] (gathered on load) instead of x_sorted[s].
+int swiglu_fwd(const char* fn, int H, int F, int E, int max_rows, int max_expert_rows, int dtype, const int32_t* offsets,
+               const void* x_rows, const int32_t* perm, int k, const void* w_gate, const void* w_up, const void* w_down,
+               void* h_save, void* a_save, void* o_sorted, void* stream) {
+  int rc = check_expert_dims(fn, H, F, E, dtype);
+  if (rc || (rc = check_rows(fn, max_rows))) return rc;
+  REQUIRE(max_expert_rows >= 0, MOE_ERR_INVALID_ARGUMENT, "%s: max_expert_rows=%d is negative", fn, max_expert_rows);
+  NONNULL(offsets);
+  REQUIRE(x_rows != nullptr, MOE_ERR_INVALID_ARGUMENT, "%s: %s must not be NULL", fn, perm ? "x" : "x_sorted");
+  NONNULL(w_gate);
+  NONNULL(w_up);
+  NONNULL(w_down);
+  NONNULL(a_save);
+  NONNULL(o_sorted);
+  if (max_rows == 0) return MOE_OK;
+  moe::RowGemmArgs g{};
+  g.offsets = offsets;
+  g.E = E;
+  g.H = H;
+  g.F = F;
+  hipStream_t s = as_stream(stream);
+  auto run = [&](int mode) {
+    return timed(kGemmKind[mode], s, [&] {
+      return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, max_expert_rows, s)
+                               : moe::launch_row_gemm_f32(mode, g, max_rows, s);
+    });
+  };
+  g.a = (const uint16_t*)x_rows;
+  g.a_map = perm;
+  g.a_div = k;
+  g.w0 = (const uint16_t*)w_gate;
+  g.w1 = (const uint16_t*)w_up;
+  g.out0 = (uint16_t*)h_save;
+  g.out1 = (uint16_t*)a_save;
+  if ((rc = hip_status(run(moe::kGemmGateUp), fn))) return rc;
+  g.a = (const uint16_t*)a_save;
+  g.a_map = nullptr;
+  g.a_div = 1;
+  g.w0 = (const uint16_t*)w_down;
+  g.w1 = nullptr;
+  g.out0 = (uint16_t*)o_sorted;
+  g.out1 = nullptr;
+  return hip_status(run(moe::kGemmDown), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,42 +254,19 @@ int moe_dispatch(int T, int H, int E, int k, int dtype, const int32_t* topk_idx,
 int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int max_expert_rows, int dtype, const int32_t* offsets,
                            const void* x_sorted, const void* w_gate, const void* w_up, const void* w_down, void* h_save,
                            void* a_save, void* o_sorted, void* stream) {
-  const char* fn = "moe_grouped_swiglu_fwd";
-  int rc = check_expert_dims(fn, H, F, E, dtype);
-  if (rc || (rc = check_rows(fn, max_rows))) return rc;
-  REQUIRE(max_expert_rows >= 0, MOE_ERR_INVALID_ARGUMENT, "%s: max_expert_rows=%d is negative", fn, max_expert_rows);
-  NONNULL(offsets);
-  NONNULL(x_sorted);
-  NONNULL(w_gate);
-  NONNULL(w_up);
-  NONNULL(w_down);
-  NONNULL(a_save);
-  NONNULL(o_sorted);
-  if (max_rows == 0) return MOE_OK;
-  moe::RowGemmArgs g{};
-  g.offsets = offsets;
-  g.E = E;
-  g.H = H;
-  g.F = F;
-  hipStream_t s = as_stream(stream);
-  auto run = [&](int mode) {
-    return timed(kGemmKind[mode], s, [&] {
-      return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, max_expert_rows, s)
-                               : moe::launch_row_gemm_f32(mode, g, max_rows, s);
-    });
-  };
-  g.a = (const uint16_t*)x_sorted;
-  g.w0 = (const uint16_t*)w_gate;
-  g.w1 = (const uint16_t*)w_up;
-  g.out0 = (uint16_t*)h_save;
-  g.out1 = (uint16_t*)a_save;
-  if ((rc = hip_status(run(moe::kGemmGateUp), fn))) return rc;
-  g.a = (const uint16_t*)a_save;
-  g.w0 = (const uint16_t*)w_down;
-  g.w1 = nullptr;
-  g.out0 = (uint16_t*)o_sorted;
-  g.out1 = nullptr;
-  return hip_status(run(moe::kGemmDown), fn);
+  return swiglu_fwd("moe_grouped_swiglu_fwd", H, F, E, max_rows, max_expert_rows, dtype, offsets, x_sorted, nullptr, 1,
+                    w_gate, w_up, w_down, h_save, a_save, o_sorted, stream);
+}
+
+int moe_grouped_swiglu_fwd_gather(int H, int F, int E, int k, int max_rows, int max_expert_rows, int dtype,
+                                  const int32_t* offsets, const void* x, const int32_t* perm, const void* w_gate,
+                                  const void* w_up, const void* w_down, void* h_save, void* a_save, void* o_sorted,
+                                  void* stream) {
+  const char* fn = "moe_grouped_swiglu_fwd_gather";
+  REQUIRE(k >= 1 && k <= 16, MOE_ERR_INVALID_ARGUMENT, "%s: k=%d must be in 1..16", fn, k);
+  NONNULL(perm);
+  return swiglu_fwd(fn, H, F, E, max_rows, max_expert_rows, dtype, offsets, x, perm, k, w_gate, w_up, w_down, h_save,
+                    a_save, o_sorted, stream);
 }
 
 int moe_grouped_swiglu_recompute(int H, int F, int E, int max_rows, int max_expert_rows, int dtype,

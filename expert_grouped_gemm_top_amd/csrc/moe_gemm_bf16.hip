@@ -150,7 +150,7 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   const bool a_ok = c < ts.rows;
   const uint16_t* __restrict__ A = (const uint16_t*)g.a;
   // rows past the tile read the tile's last row (always valid) and are zeroed at use
-  const uint16_t* a_row = A + (size_t)(ts.row_begin + (a_ok ? c : ts.rows - 1)) * K + k_begin;
+  const uint16_t* a_row = A + a_row_of(g, ts.row_begin + (a_ok ? c : ts.rows - 1)) * K + k_begin;
 
   f32x4 acc[8];
 #pragma unroll
@@ -409,7 +409,7 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
   for (int i = 0; i < 4; ++i) {
     const int ch = tid + 256 * i, row = ch >> 3, kc = ch & 7;
     a_ok[i] = row < ts.rows;
-    a_src[i] = A + (size_t)(ts.row_begin + (a_ok[i] ? row : ts.rows - 1)) * K + 8 * kc;
+    a_src[i] = A + a_row_of(g, ts.row_begin + (a_ok[i] ? row : ts.rows - 1)) * K + 8 * kc;
     a_dst[i] = row * kTPitch + 8 * (kc ^ (row & 7));
   }
   // B, N-contiguous: thread -> 8 k-rows (8 kb .. 8 kb + 7) x 4 columns of one matrix

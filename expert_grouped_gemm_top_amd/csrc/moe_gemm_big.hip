@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
     const int row = (64 / CPR) * (A_INS * w + i) + l / CPR;
     const int chunk = kc_swz<CPR>(row, l % CPR);  // LDS position l % CPR holds this chunk
     const int r = row < ts.rows ? row : ts.rows - 1;
-    a_src[i] = g.a + (size_t)(ts.row_begin + r) * K + 8 * chunk;
+    a_src[i] = g.a + a_row_of(g, ts.row_begin + r) * K + 8 * chunk;
   }
   const uint16_t* b_src[B_INS];
   const uint16_t* b_hi[B_INS];  // DX: the same rows in W_up for k >= F

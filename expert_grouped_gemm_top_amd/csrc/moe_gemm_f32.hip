@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void row_gemm_f32_kernel(RowGemmArgs g) {
   const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? H : (MODE == kGemmDown ? F : 2 * F);
   const int col = blockIdx.y * 256 + tid;
   const bool ok = col < ncols;
-  const float* A = (const float*)g.a + (size_t)row * K;
+  const float* A = (const float*)g.a + a_row_of(g, row) * K;
   const float* w0 = (const float*)g.w0;
   const float* w1 = (const float*)g.w1;
   float s0 = 0.0f, s1 = 0.0f;

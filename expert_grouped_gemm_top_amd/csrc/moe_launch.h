@@ -33,6 +33,8 @@ struct RowGemmArgs {
   const uint16_t* h;
   uint16_t* out0;
   uint16_t* out1;
+  const int32_t* a_map;  // when set, row s of `a` is a[a_map[s] / a_div] (rows gathered on load)
+  int a_div;
   int big_min_rows;   // set by launch_row_gemm_bf16: experts from this row count take the 256-row kernel
   int stream_ksplit;  // set by launch_row_gemm_bf16: reduction split of the skinny-expert kernel (1, 2 or 4)
 };
@@ -50,6 +52,11 @@ struct DwArgs {
   int tiles_job1;      // filled by the launcher
   int tiles_per_expert;
 };
+
+// Source row of operand row s of a row GEMM.
+__device__ __forceinline__ int64_t a_row_of(const RowGemmArgs& g, int s) {
+  return g.a_map != nullptr ? (int64_t)(g.a_map[s] / g.a_div) : (int64_t)s;
+}
 
 hipError_t launch_route_topk(int T, int E, int k, const float* logits, int32_t* idx, float* w, hipStream_t stream);
 

@@ -16,13 +16,16 @@ from . import moe
 
 class MoeLayerBuffers:
     def __init__(self, T, H, F, E, k, dtype=torch.bfloat16, device="cuda", rho=None, dw=True, dg=True,
-                 router=False, keep_graph=True, quota_cap=None):
+                 router=False, keep_graph=True, quota_cap=None, gather_rows=None):
         """rho: quota ratio of the compacted backward (None: no compaction);
         quota_cap: the per-expert quota directly (e.g. from
         moe.moe_quota_cap_for_budget), instead of rho.  keep_graph=False: the
         forward keeps no pre-activations [hg|hu]; the backward recomputes them
         from the saved rows (the recompute path that pull request #44 keeps
-        behind keep_graph=False)."""
+        behind keep_graph=False).  gather_rows: the forward reads x rows
+        through perm instead of a materialized x_sorted (moe_dispatch then
+        skips its row copy); None picks it whenever nothing later needs
+        x_sorted (no dW, no compaction, pre-activations kept)."""
         self.T, self.H, self.F, self.E, self.k = T, H, F, E, k
         self.keep_graph = keep_graph
         self.N = N = T * k
@@ -45,6 +48,9 @@ class MoeLayerBuffers:
         self.y = em(T, H)
         self.quota_cap = quota_cap
         self.compacted = rho is not None or quota_cap is not None
+        eligible = not dw and not self.compacted and keep_graph
+        self.gather_rows = eligible if gather_rows is None else bool(gather_rows)
+        assert eligible or not self.gather_rows, "dW, compaction and recompute read x_sorted"
         if self.compacted:
             cap = moe.moe_quota_cap(T, E, k, rho) if quota_cap is None else quota_cap
             self.R = min(N, E * cap)
@@ -86,11 +92,17 @@ class MoeLayerBuffers:
             logits = self.logits
             self._x = x
         moe.moe_route_topk(logits, self.topk_idx, self.topk_w, self.k, stream)
-        moe.moe_dispatch(self.topk_idx, x, self.counts, self.offsets, self.perm, self.inv_perm, self.x_sorted,
-                         self.ws, self.E, stream)
-        moe.moe_grouped_swiglu_fwd(self.offsets, self.x_sorted, w_gate, w_up, w_down,
-                                   self.h_save if self.keep_graph else None, self.a_save, self.o_sorted, self.N,
-                                   max_expert_rows=self.T, stream=stream)
+        g = self.gather_rows  # index-only dispatch: the forward gathers x rows itself
+        moe.moe_dispatch(self.topk_idx, None if g else x, self.counts, self.offsets, self.perm, self.inv_perm,
+                         None if g else self.x_sorted, self.ws, self.E, stream)
+        if self.gather_rows:
+            moe.moe_grouped_swiglu_fwd_gather(self.offsets, x, self.perm, w_gate, w_up, w_down, self.h_save,
+                                              self.a_save, self.o_sorted, self.k, self.N, max_expert_rows=self.T,
+                                              stream=stream)
+        else:
+            moe.moe_grouped_swiglu_fwd(self.offsets, self.x_sorted, w_gate, w_up, w_down,
+                                       self.h_save if self.keep_graph else None, self.a_save, self.o_sorted, self.N,
+                                       max_expert_rows=self.T, stream=stream)
         moe.moe_combine(self.o_sorted, self.inv_perm, self.topk_w, self.y, self.k, stream)
         return self.y
 

@@ -36,6 +36,7 @@ _SIGS = {
     "moe_dispatch_workspace_bytes": ([_i, _i, _i], _sz),
     "moe_dispatch": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_grouped_swiglu_fwd": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i),
+    "moe_grouped_swiglu_fwd_gather": ([_i] * 7 + [_vp] * 10, _i),
     "moe_grouped_swiglu_recompute": ([_i, _i, _i, _i, _i, _i] + [_vp] * 7, _i),
     "moe_combine": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
     "moe_grouped_bwd_dx": ([_i, _i, _i, _i, _i, _i, _i] + [_vp] * 16, _i),
@@ -181,6 +182,20 @@ def moe_grouped_swiglu_fwd(offsets, x_sorted, w_gate, w_up, w_down, h_save, a_sa
     _check(lib().moe_grouped_swiglu_fwd(
         H, F, E, R, R if max_expert_rows is None else max_expert_rows, dt, _ptr(offsets, "offsets", I32, E + 1), _ptr(x_sorted, "x_sorted", d, R * H),
         _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F), _ptr(w_down, "w_down", d, E * F * H),
+        _ptr(h_save, "h_save", d, R * 2 * F, allow_none=True), _ptr(a_save, "a_save", d, R * F),
+        _ptr(o_sorted, "o_sorted", d, R * H), _stream(stream)))
+
+
+def moe_grouped_swiglu_fwd_gather(offsets, x, perm, w_gate, w_up, w_down, h_save, a_save, o_sorted, k: int,
+                                  max_rows: int, max_expert_rows: int | None = None, stream=None):
+    E, H, F = w_gate.shape
+    dt, d = _dt(w_gate), w_gate.dtype
+    R = max_rows
+    T = x.shape[0]
+    _check(lib().moe_grouped_swiglu_fwd_gather(
+        H, F, E, k, R, R if max_expert_rows is None else max_expert_rows, dt, _ptr(offsets, "offsets", I32, E + 1),
+        _ptr(x, "x", d, T * H), _ptr(perm, "perm", I32, R), _ptr(w_gate, "w_gate", d, E * H * F),
+        _ptr(w_up, "w_up", d, E * H * F), _ptr(w_down, "w_down", d, E * F * H),
         _ptr(h_save, "h_save", d, R * 2 * F, allow_none=True), _ptr(a_save, "a_save", d, R * F),
         _ptr(o_sorted, "o_sorted", d, R * H), _stream(stream)))
 

@@ -12,6 +12,7 @@
  *   moe_dispatch            token-expert pairs -> rows contiguous per expert
  *   moe_grouped_swiglu_fwd  SwiGLU expert MLP over every expert's rows (ragged
  *                           grouped GEMM); keeps the activations backward needs
+ *   moe_grouped_swiglu_fwd_gather  the same with the rows gathered on load
  *   moe_grouped_swiglu_recompute  the forward's pre-activations again, for a
  *                           forward that did not keep them
  *   moe_combine             router-weighted sum of each token's expert rows
@@ -161,6 +162,16 @@ int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int max_expert_row
                            const void* x_sorted, const void* w_gate, const void* w_up,
                            const void* w_down, void* h_save, void* a_save, void* o_sorted,
                            void* stream);
+
+/* The expert forward with the gate/up product's rows gathered on load: row s
+ * of expert e's rows reads x[perm[s] / k] instead of a materialized x_sorted[s]
+ * (so moe_dispatch can skip its row copy: x_sorted = NULL there).  Everything
+ * else as moe_grouped_swiglu_fwd, whose outputs it reproduces bit for bit.
+ * x [T, H] (device); perm [T*k] int32 from moe_dispatch (device). */
+int moe_grouped_swiglu_fwd_gather(int H, int F, int E, int k, int max_rows, int max_expert_rows, int dtype,
+                                  const int32_t* offsets, const void* x, const int32_t* perm, const void* w_gate,
+                                  const void* w_up, const void* w_down, void* h_save, void* a_save, void* o_sorted,
+                                  void* stream);
 
 /* The gate/up half of the expert forward over given rows, for the recompute
  * path (pull request #44, Background and Changes: without kept activations

@@ -30,8 +30,9 @@ def _full_compare(wl, d, L, rho=None, score=None):
     assert np.array_equal(L.offsets.cpu().numpy(), offsets), "offsets"
     assert np.array_equal(L.perm.cpu().numpy(), perm), "perm"
     assert np.array_equal(L.inv_perm.cpu().numpy(), inv), "inv_perm"
-    xs = np32(L.x_sorted)
-    assert np.array_equal(xs, d["x"][perm // wl.k]), "x_sorted is not an exact row copy"
+    xs = d["x"][perm // wl.k]
+    if not L.gather_rows:  # gathered on load: dispatch writes no x_sorted
+        assert np.array_equal(np32(L.x_sorted), xs), "x_sorted is not an exact row copy"
     y, it = oracle.forward(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"], intermediates=True)
     h_ref = np.concatenate([it["hg"], it["hu"]], 1)  # pair-indexed
     if L.keep_graph:  # without it the forward keeps no pre-activations
@@ -151,6 +152,28 @@ def test_recompute_path_compacted_matches_oracle():
     score = w.reshape(-1).astype(np.float32)
     L = run_gpu(wl, d, logits, rho=rho, score=score, keep_graph=False)
     _full_compare(wl, d, L, rho=rho, score=score)
+
+
+@pytest.mark.parametrize("wl", [
+    W.custom("bf16_gather", T=300, H=256, F=256, E=16, k=4, dtype="bf16", skew=True, dw=False),
+    W.custom("bf16_gather_big", T=700, H=256, F=256, E=4, k=2, dtype="bf16", skew=True, dw=False),
+    W.custom("fp32_gather", T=90, H=64, F=40, E=6, k=3, dtype="f32", skew=True, dw=False),
+], ids=lambda w: w.name)
+def test_gather_on_load_is_bitwise_the_materialized_path(wl):
+    from expert_grouped_gemm_top_amd.layer import MoeLayerBuffers
+    d = W.generate(wl, seed=9)
+    logits = torch.from_numpy(logits_of(wl, d)).cuda()
+    t = to_dev(wl, d)
+    out = []
+    for gather in (False, True):
+        L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, t["x"].dtype, "cuda", dw=False, gather_rows=gather)
+        L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"])
+        L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"])
+        out.append(L)
+    torch.cuda.synchronize()
+    assert out[1].gather_rows and not out[0].gather_rows
+    for n in ("h_save", "a_save", "o_sorted", "y", "dx", "dg"):
+        assert torch.equal(getattr(out[0], n), getattr(out[1], n)), n
 
 
 def test_deterministic_bitwise():
