@@ -108,8 +108,10 @@ def measured_traffic(kernel, workload):
     return int(m_b.group(1))
 
 
-def algorithmic(wl, counts, kept_counts=None):
-    """Per-kernel algorithmic bytes and flops (real rows only, no padding)."""
+def algorithmic(wl, counts, kept_counts=None, gathered=False):
+    """Per-kernel algorithmic bytes and flops (real rows only, no padding).
+    gathered: the gate/up product reads token rows [T,H] through perm instead of
+    the materialized x_sorted [N,H]."""
     b = 2 if wl.dtype == "bf16" else 4
     H, F, T, k = wl.H, wl.F, wl.T, wl.k
     N = wl.N
@@ -118,7 +120,8 @@ def algorithmic(wl, counts, kept_counts=None):
     Ea_b = int((kept_counts > 0).sum()) if kept_counts is not None else Ea
     return {
         K_DISPATCH_ROWS: (T * H * b + N * H * b + 4 * N, 0.0),
-        K_GATEUP: (2 * H * F * b * Ea + N * H * b + N * 2 * F * b + N * F * b, 4.0 * H * F * N),
+        K_GATEUP: (2 * H * F * b * Ea + (T * H * b + 4 * N if gathered else N * H * b) + N * 2 * F * b + N * F * b,
+                   4.0 * H * F * N),
         K_DOWN: (H * F * b * Ea + N * F * b + N * H * b, 2.0 * H * F * N),
         K_COMBINE: (N * H * b + 8 * N + T * H * b, 0.0),
         K_GRAD_ROWS: (T * H * b + R * H * b + 8 * N + N * H * b, 0.0),
@@ -239,7 +242,7 @@ def main():
 
     counts = L.counts.cpu().numpy()
     kept = L.kept_counts.cpu().numpy() if L.compacted else None
-    alg = algorithmic(wl, counts, kept)
+    alg = algorithmic(wl, counts, kept, gathered=L.gather_rows)
     step_flops = sum(alg[kk][1] for kk in gemm_kernels)
     byts, flops = alg[dom]
     ai = flops / byts
