@@ -135,8 +135,10 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   const int cpw = 4 / ks;  // column blocks per workgroup
   // work item of this wave: (tile, column block); the waves of a workgroup take
   // adjacent column blocks of the same tile (when split, nblk is a multiple of
-  // cpw, so all blocks of a workgroup fall on one tile)
-  const int item = wg * cpw + (w % cpw);
+  // cpw, so all blocks of a workgroup fall on one tile).  Workgroups are taken
+  // in XCD order, so a tile's activation rows are fetched into one L2.
+  const int real_wgs = (s_start[g.E] * nblk + cpw - 1) / cpw;
+  const int item = xcd_item(wg, real_wgs) * cpw + (w % cpw);
   const int kpart = w / cpw;
   const TileSlot ts = lookup_tile(s_start, s_off, g.E, kTileRows, item / nblk);
   // uniform across the wave, and across the workgroup when split (before its barrier)
