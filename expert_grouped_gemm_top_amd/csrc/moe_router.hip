@@ -9,8 +9,8 @@
 //     dW_r = x^T dlogits,   dx += dlogits W_r^T.
 //
 // The three products are small next to the experts' (E columns against k * 3F),
-// so they run on one tiled fp32 kernel: 64 x 64 output tiles, reduction depth
-// 16 per LDS stage, 4 x 4 outputs per thread, every operand converted to fp32
+// so they run on one tiled fp32 kernel: 128 x 128 output tiles, reduction depth
+// 16 per LDS stage, 8 x 8 outputs per thread, every operand converted to fp32
 // on its way into LDS.  Two of them have few outputs and a long reduction
 // (logits: T x E over H; dW_r: H x E over T), so the reduction is cut into S
 // slices run by separate workgroups that write fp32 partial tiles to the
@@ -26,7 +26,8 @@ namespace moe {
 
 namespace {
 
-constexpr int kRBM = 64, kRBN = 64, kRBK = 16;
+constexpr int kRBK = 16;  // LDS depth
+// Output tiles are TILE x TILE (64 or 128), TILE / 16 x TILE / 16 outputs per thread.
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T v);
@@ -48,20 +49,24 @@ __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return (uint16
 // to C's current contents (one rounding of the sum).  With slices > 1,
 // workgroup z reduces k in [z*kslice, (z+1)*kslice) and writes its fp32 partial
 // tile to part + z*M*N instead (C, ACC unused).
-template <typename TA, typename TB, typename TC, bool A_KC, bool B_KC, bool ACC>
+template <int TILE, typename TA, typename TB, typename TC, bool A_KC, bool B_KC, bool ACC>
 __global__ __launch_bounds__(256) void router_gemm_kernel(int M, int N, int K, const TA* __restrict__ a, int lda,
                                                           const TB* __restrict__ b, int ldb, TC* __restrict__ c,
                                                           int kslice, float* __restrict__ part) {
+  constexpr int kRBM = TILE, kRBN = TILE, TPT = TILE / 16;
   __shared__ __attribute__((aligned(16))) float s_a[kRBK][kRBM];
   __shared__ __attribute__((aligned(16))) float s_b[kRBK][kRBN];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int m0 = blockIdx.x * kRBM, n0 = blockIdx.y * kRBN;
   const int kb0 = blockIdx.z * kslice, kb1 = min(K, kb0 + kslice);
-  float acc[4][4] = {};
+  // thread (tx, ty) owns rows 64 (i / 4) + 4 ty + i % 4 and columns
+  // 64 (j / 4) + 4 tx + j % 4 (i, j < TPT): its LDS reads are float4s that
+  // neighbouring threads take from neighbouring addresses
+  float acc[TPT][TPT] = {};
   for (int k0 = kb0; k0 < kb1; k0 += kRBK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i;  // element of the 64 x 16 tile
+    for (int i = 0; i < kRBM * kRBK / 256; ++i) {
+      const int q = tid + 256 * i;  // element of the 128 x 16 tile
       // walk the contiguous index fastest so that neighbouring threads read
       // neighbouring addresses
       const int mm = A_KC ? q / kRBK : q % kRBM, kk = A_KC ? q % kRBK : q / kRBM;
@@ -78,22 +83,31 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(int M, int N, int K, c
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kRBK; ++kk) {
-      const f32x4 av = *(const f32x4*)&s_a[kk][4 * ty];
-      const f32x4 bv = *(const f32x4*)&s_b[kk][4 * tx];
+      float av[TPT], bv[TPT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int h = 0; h < TPT / 4; ++h) {
+        const f32x4 a4 = *(const f32x4*)&s_a[kk][64 * h + 4 * ty];
+        const f32x4 b4 = *(const f32x4*)&s_b[kk][64 * h + 4 * tx];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        for (int u = 0; u < 4; ++u) {
+          av[4 * h + u] = a4[u];
+          bv[4 * h + u] = b4[u];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TPT; ++i)
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 4 * ty + i;
+  for (int i = 0; i < TPT; ++i) {
+    const int m = m0 + 64 * (i / 4) + 4 * ty + i % 4;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + 4 * tx + j;
+    for (int j = 0; j < TPT; ++j) {
+      const int n = n0 + 64 * (j / 4) + 4 * tx + j % 4;
       if (n >= N) continue;
       if (part != nullptr) {
         part[((size_t)blockIdx.z * M + m) * N + n] = acc[i][j];
@@ -146,11 +160,24 @@ __global__ __launch_bounds__(256) void router_dlogits_kernel(int T, int E, int k
 constexpr int64_t kTargetGroups = 512;
 constexpr int kMinSlice = 128;
 
-int64_t slice_count(int M, int N, int K) {
-  const int64_t tiles = (int64_t)((M + kRBM - 1) / kRBM) * ((N + kRBN - 1) / kRBN);
+int64_t slices_for(int64_t tiles, int K, bool may_split) {
+  if (!may_split) return 1;
   int64_t s = (kTargetGroups + tiles - 1) / tiles;
   s = std::min<int64_t>(s, (K + kMinSlice - 1) / kMinSlice);
   return std::max<int64_t>(s, 1);
+}
+
+// 128 x 128 tiles when they (with their reduction slices) give enough
+// workgroups to cover the chip, else 64 x 64
+int tile_of(int M, int N, int K, bool may_split) {
+  const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  return t128 * slices_for(t128, K, may_split) >= 256 ? 128 : 64;
+}
+
+int64_t slice_count(int M, int N, int K, bool may_split = true) {
+  const int tile = tile_of(M, N, K, may_split);
+  const int64_t tiles = (int64_t)((M + tile - 1) / tile) * ((N + tile - 1) / tile);
+  return slices_for(tiles, K, may_split);
 }
 
 int slice_length(int K, int64_t slices) {
@@ -167,12 +194,18 @@ size_t split_bytes(int M, int N, int K) {
 template <typename TA, typename TB, typename TC, bool A_KC, bool B_KC, bool ACC>
 hipError_t gemm(int M, int N, int K, const void* a, int lda, const void* b, int ldb, void* c, float* ws,
                 bool may_split, hipStream_t stream) {
-  const int64_t slices = may_split ? slice_count(M, N, K) : 1;
+  const int64_t slices = slice_count(M, N, K, may_split);
   const int kslice = slices > 1 ? slice_length(K, slices) : K;
   const int64_t used = (K + kslice - 1) / kslice;  // slices that hold some k
-  const dim3 grid((M + kRBM - 1) / kRBM, (N + kRBN - 1) / kRBN, (unsigned)(slices > 1 ? used : 1));
-  hipLaunchKernelGGL((router_gemm_kernel<TA, TB, TC, A_KC, B_KC, ACC>), grid, dim3(256), 0, stream, M, N, K,
-                     (const TA*)a, lda, (const TB*)b, ldb, (TC*)c, kslice, slices > 1 ? ws : nullptr);
+  const int tile = tile_of(M, N, K, may_split);
+  const dim3 grid((M + tile - 1) / tile, (N + tile - 1) / tile, (unsigned)(slices > 1 ? used : 1));
+  float* part = slices > 1 ? ws : nullptr;
+  if (tile == 128)
+    hipLaunchKernelGGL((router_gemm_kernel<128, TA, TB, TC, A_KC, B_KC, ACC>), grid, dim3(256), 0, stream, M, N, K,
+                       (const TA*)a, lda, (const TB*)b, ldb, (TC*)c, kslice, part);
+  else
+    hipLaunchKernelGGL((router_gemm_kernel<64, TA, TB, TC, A_KC, B_KC, ACC>), grid, dim3(256), 0, stream, M, N, K,
+                       (const TA*)a, lda, (const TB*)b, ldb, (TC*)c, kslice, part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || slices == 1) return err;
   const int64_t MN = (int64_t)M * N;
