@@ -1,6 +1,6 @@
 // moe_gemm_bf16.hip -- ragged grouped GEMMs of the SwiGLU experts in bf16 on
 // gfx950 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulate): the
-// skinny-expert and mid-size regimes of the row GEMMs, and the dW GEMM.
+// skinny-expert and mid-size regimes of the row GEMMs.
 //
 // Expert forward, backward dx and dW (npu-train issue #14, sections Proposal
 // and Scope), run as variable-size grouped GEMMs over each expert's own row
@@ -22,14 +22,7 @@
 // In every case the MFMA takes the weights as its first operand, so a lane
 // ends up holding one output row and contiguous columns, and the epilogue
 // (SwiGLU forward or backward) is applied from registers.
-//
-// dW GEMM (K = the expert's rows, ragged):
-//   dW_gate|dW_up [H, 2F] = x_rows^T [dHg|dHu],  dW_down [F, H] = a_rows^T dO_rows
-// Workgroup = one 128x128 output tile of one expert; both operands are
-// row-major over the reduced index, so each lane loads 8 rows x 4 columns and
-// transposes them in registers.  The reduction runs in a fixed order over all
-// of the expert's rows (deterministic, no atomics); an empty expert stores
-// exact zeros.
+
 #include <algorithm>
 
 #include "moe_common.h"
@@ -626,111 +619,6 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, in
     tile_gemm<MODE>(g, blockIdx.x - n_stream, s_start, s_off, s_tmp, s_ab, s_ab + 2 * kTBM * kTPitch);
 }
 
-// ---- dW GEMM ------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void dw_bf16_kernel(DwArgs g) {
-  const int e = blockIdx.x / g.tiles_per_expert;
-  const int t = blockIdx.x - e * g.tiles_per_expert;
-  const int H = g.H, F = g.F;
-  const int row0 = g.offsets[e];
-  const int n_e = g.offsets[e + 1] - row0;
-  const uint16_t *P, *Q;
-  int ldp, ldq, mt, nt;
-  uint16_t* out;
-  int ldo, out_col0;
-  if (t < g.tiles_job1) {  // [dW_gate | dW_up] = x^T [dHg | dHu]
-    const int ntn = (2 * F) / 128;
-    mt = t / ntn;
-    nt = t - mt * ntn;
-    P = g.x; ldp = H;
-    Q = g.dh; ldq = 2 * F;
-    const bool up = nt * 128 >= F;
-    out = (up ? g.dwu : g.dwg) + (size_t)e * H * F;
-    ldo = F;
-    out_col0 = up ? -F : 0;
-  } else {                 // dW_down = a^T dO
-    const int tt = t - g.tiles_job1;
-    const int ntn = H / 128;
-    mt = tt / ntn;
-    nt = tt - mt * ntn;
-    P = g.a; ldp = F;
-    Q = g.dO; ldq = H;
-    out = g.dwd + (size_t)e * F * H;
-    ldo = H;
-    out_col0 = 0;
-  }
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
-  const int mb = mt * 128 + (w & 1) * 64;
-  const int nb = nt * 128 + (w >> 1) * 64;
-  const uint16_t* p_base = P + (size_t)row0 * ldp + mb + 4 * c;
-  const uint16_t* q_base = Q + (size_t)row0 * ldq + nb + 4 * c;
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int steps = (n_e + 31) / 32;
-  // Unconditional loads (rows past n_e read the expert's last row and are
-  // zeroed by a select), so the load pipeline keeps a counted depth.
-  auto load = [&](int s, u32x2* pq, u32x2* qq) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int rr = 32 * s + 8 * gq + r;
-      const int rc = rr < n_e ? rr : n_e - 1;
-      pq[r] = *(const u32x2*)(p_base + (size_t)rc * ldp);
-      qq[r] = *(const u32x2*)(q_base + (size_t)rc * ldq);
-    }
-  };
-  auto compute = [&](int s, const u32x2* pq_in, const u32x2* qq_in) {
-    u32x2 pq[8], qq[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const bool ok = 32 * s + 8 * gq + r < n_e;
-      const u32x2 z = {0u, 0u};
-      pq[r] = ok ? pq_in[r] : z;
-      qq[r] = ok ? qq_in[r] : z;
-    }
-    u32x4 pf[4], qf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pf[j] = column_of_8x4(pq, j);
-      qf[j] = column_of_8x4(qq, j);
-    }
-#pragma unroll
-    for (int ja = 0; ja < 4; ++ja)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) acc[ja][jb] = mfma_bf16(qf[jb], pf[ja], acc[ja][jb]);
-  };
-
-  if (steps > 0) {
-    u32x2 pA[8], qA[8], pB[8], qB[8];
-    load(0, pA, qA);
-    for (int s = 0; s < steps; s += 2) {
-      load(min(s + 1, steps - 1), pB, qB);
-      compute(s, pA, qA);
-      load(min(s + 2, steps - 1), pA, qA);
-      if (s + 1 < steps) compute(s + 1, pB, qB);
-    }
-  }
-
-  // lane (c, gq) holds rows mb + 4c + ja and columns nb + 16gq + 4r + jb
-#pragma unroll
-  for (int ja = 0; ja < 4; ++ja) {
-    uint16_t* orow = out + (size_t)(mb + 4 * c + ja) * ldo + nb + 16 * gq + out_col0;
-    u32x4 lo, hi;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      lo[2 * r] = pack_bf2(acc[ja][0][r], acc[ja][1][r]);
-      lo[2 * r + 1] = pack_bf2(acc[ja][2][r], acc[ja][3][r]);
-      hi[2 * r] = pack_bf2(acc[ja][0][r + 2], acc[ja][1][r + 2]);
-      hi[2 * r + 1] = pack_bf2(acc[ja][2][r + 2], acc[ja][3][r + 2]);
-    }
-    *(u32x4*)orow = lo;
-    *(u32x4*)(orow + 8) = hi;
-  }
-}
-
 }  // namespace
 
 template <int MODE>
@@ -776,16 +664,5 @@ hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, in
   }
 }
 
-hipError_t launch_dw_bf16(DwArgs g, hipStream_t stream) {
-#ifndef MOE_DW_BIG
-#define MOE_DW_BIG 1
-#endif
-  if (MOE_DW_BIG) return launch_dw_big_bf16(g, stream);
-  g.tiles_job1 = (g.H / 128) * ((2 * g.F) / 128);
-  g.tiles_per_expert = g.tiles_job1 + (g.F / 128) * (g.H / 128);
-  const int64_t blocks = (int64_t)g.E * g.tiles_per_expert;
-  hipLaunchKernelGGL(dw_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g);
-  return hipGetLastError();
-}
 
 }  // namespace moe

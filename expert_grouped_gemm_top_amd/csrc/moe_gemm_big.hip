@@ -1,9 +1,9 @@
 // moe_gemm_big.hip -- row GEMMs of the SwiGLU experts for experts with many
 // rows (>= 256), where the grouped GEMM is bound by the matrix cores.
 //
-// Same four products as the other row GEMMs (expert forward and backward dx:
-// npu-train issue #14, sections Proposal and Scope; variable-size grouped GEMMs:
-// LRMoE abstract), tiled for gfx950:
+// Gate/up, down and dX, the products of the other row GEMMs but dA (expert
+// forward and backward dx: npu-train issue #14, sections Proposal and Scope;
+// variable-size grouped GEMMs: LRMoE abstract), tiled for gfx950:
 //   * workgroup tile BM rows x BN columns, waves laid out WM x (NW / WM), each
 //     wave a grid of 32 x 32 blocks on v_mfma_f32_32x32x16_bf16
 //     (on gfx950 it sustains ~2.4 PFLOP/s where the 16x16x32 form stops near
@@ -32,12 +32,14 @@ namespace {
 
 template <int MODE>
 struct BigShape {
+  // the product with the transposed down projection (dA) stays on 128-row tiles
+  static_assert(MODE != kGemmDA, "no 256-row dA kernel");
   static constexpr bool kNN = (MODE == kGemmGateUp || MODE == kGemmDown);
 };
 
 template <int MODE>
 __host__ __device__ inline int big_out_cols(int H, int F) {
-  return MODE == kGemmGateUp ? 2 * F : (MODE == kGemmDA ? F : H);
+  return MODE == kGemmGateUp ? 2 * F : H;
 }
 
 // K-contiguous tile rows of BK elements (CPR 16-byte chunks): swizzled chunk
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
   const int nb = within / gm;
   const TileSlot ts = lookup_tile(s_start, s_off, g.E, BM, s_start[lo] + mt);
   const int e = ts.expert;
-  const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? H : (MODE == kGemmDown ? F : 2 * F);
+  const int K = MODE == kGemmGateUp ? H : (MODE == kGemmDown ? F : 2 * F);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wm = w % WM, wn = w / WM;
   const int l32 = l & 31, hk = l >> 5;  // MFMA row/column and k-group of this lane
@@ -161,13 +163,9 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
       const int row = (64 / CPR) * (B_INS * w + i) + l / CPR;  // output column within the tile
       const int chunk = kc_swz<CPR>(row, l % CPR);
       const int n = nb * BN + row;
-      if (MODE == kGemmDA) {
-        b_src[i] = g.w0 + (size_t)e * F * H + (size_t)n * H + 8 * chunk;
-        b_hi[i] = b_src[i];
-      } else {  // DX: k < F from W_gate, k >= F from W_up
-        b_src[i] = g.w0 + (size_t)e * H * F + (size_t)n * F + 8 * chunk;
-        b_hi[i] = g.w1 + (size_t)e * H * F + (size_t)n * F + 8 * chunk;
-      }
+      // DX: k < F from W_gate, k >= F from W_up
+      b_src[i] = g.w0 + (size_t)e * H * F + (size_t)n * F + 8 * chunk;
+      b_hi[i] = g.w1 + (size_t)e * H * F + (size_t)n * F + 8 * chunk;
     }
   }
 
@@ -317,31 +315,12 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
           if (g.out1 != nullptr) *(u32x2*)(g.out1 + grow * F + f) = u32x2{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3])};
         }
       } else {
-        const int width = (MODE == kGemmDA) ? 2 * F : H;
-        uint16_t* orow = g.out0 + grow * width;
+        uint16_t* orow = g.out0 + grow * H;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = nb * BN + TN * wn + 32 * j + 8 * q + 4 * hk;
-          if (MODE == kGemmDA) {
-            const uint16_t* hrow = g.h + grow * 2 * F;
-            const u32x2 gw = *(const u32x2*)(hrow + col), uw = *(const u32x2*)(hrow + F + col);
-            float dgv[4], duv[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              const uint32_t gg = gw[e2 >> 1], uu = uw[e2 >> 1];
-              const float hgv = (e2 & 1) ? bf_hi(gg) : bf_lo(gg);
-              const float huv = (e2 & 1) ? bf_hi(uu) : bf_lo(uu);
-              const float sg = sigmoidf_fast(hgv);
-              const float dA = acc[i][j][4 * q + e2];
-              dgv[e2] = dA * huv * sg * (1.0f + hgv * (1.0f - sg));
-              duv[e2] = dA * hgv * sg;
-            }
-            *(u32x2*)(orow + col) = u32x2{pack_bf2(dgv[0], dgv[1]), pack_bf2(dgv[2], dgv[3])};
-            *(u32x2*)(orow + F + col) = u32x2{pack_bf2(duv[0], duv[1]), pack_bf2(duv[2], duv[3])};
-          } else {
-            *(u32x2*)(orow + col) = u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                          pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-          }
+          *(u32x2*)(orow + col) = u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                        pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
         }
       }
     }
@@ -355,9 +334,8 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
 template <int MODE, int BM, int BN, int BK, int NW, int WM, int STAGES, int WPC>
 struct BigCfg {
   static int min_rows(int H, int F) {
-    // The product with the transposed down projection (DA) measured faster on
-    // 128-row tiles at every row count; the others need whole column blocks.
-    if (MODE == kGemmDA || big_out_cols<MODE>(H, F) % BN != 0) return kNoBigTiles;
+    // whole column blocks only
+    if (big_out_cols<MODE>(H, F) % BN != 0) return kNoBigTiles;
     return kBigTileMinRows;
   }
 

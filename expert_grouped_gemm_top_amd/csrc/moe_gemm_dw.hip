@@ -53,7 +53,7 @@ __host__ __device__ inline DwShape dw_shape(int H, int F) {
   return s;
 }
 
-__global__ __launch_bounds__(64 * kDwWaves, 1) void dw_big_kernel(DwArgs g) {
+__global__ __launch_bounds__(64 * kDwWaves, 1) void dw_bf16_kernel(DwArgs g) {
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_expert;
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(64 * kDwWaves, 1) void dw_big_kernel(DwArgs g) {
 
 }  // namespace
 
-hipError_t launch_dw_big_bf16(const DwArgs& g, hipStream_t stream) {
+hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream) {
   const DwShape sh = dw_shape(g.H, g.F);
   const int64_t blocks = (int64_t)g.E * sh.tiles;
   const size_t lds = (size_t)kDwStages * kDwStageBytes;
@@ -200,11 +200,11 @@ hipError_t launch_dw_big_bf16(const DwArgs& g, hipStream_t stream) {
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    err = hipFuncSetAttribute((const void*)dw_big_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    err = hipFuncSetAttribute((const void*)dw_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     if (dev >= 0 && dev < 64) attr_set[dev] = true;
   }
-  hipLaunchKernelGGL(dw_big_kernel, dim3((unsigned)blocks), dim3(64 * kDwWaves), lds, stream, g);
+  hipLaunchKernelGGL(dw_bf16_kernel, dim3((unsigned)blocks), dim3(64 * kDwWaves), lds, stream, g);
   return hipGetLastError();
 }
 

@@ -49,8 +49,6 @@ struct DwArgs {
   uint16_t* dwg;       // [E,H,F]
   uint16_t* dwu;       // [E,H,F]
   uint16_t* dwd;       // [E,F,H]
-  int tiles_job1;      // filled by the launcher
-  int tiles_per_expert;
 };
 
 // Source row of operand row s of a row GEMM.
@@ -81,8 +79,7 @@ hipError_t launch_gather_rows(const int32_t* R_ptr, const int32_t* src, int max_
 // experts above it are still computed, on the 128-row tiles)
 hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, int max_expert_rows,
                                 hipStream_t stream);
-hipError_t launch_dw_bf16(DwArgs g, hipStream_t stream);
-hipError_t launch_dw_big_bf16(const DwArgs& g, hipStream_t stream);
+hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream);
 hipError_t launch_big_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
 // Row count from which an expert takes the 256-row kernel for this product and
 // shape; kNoBigTiles where that kernel does not apply.
