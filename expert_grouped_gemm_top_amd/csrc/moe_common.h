@@ -96,7 +96,7 @@ __device__ __forceinline__ void build_tile_starts(const int32_t* __restrict__ of
                                                   int* s_start, int* s_off, int* s_tmp, int min_rows = 0,
                                                   int max_rows = 0x7fffffff) {
   const int tid = threadIdx.x;
-  if (tid <= E) s_off[tid] = offsets[tid];
+  for (int i = tid; i <= E; i += 256) s_off[i] = offsets[i];  // E + 1 entries: 257 at E = 256
   __syncthreads();
   int n_tiles = 0;
   if (tid < E) {

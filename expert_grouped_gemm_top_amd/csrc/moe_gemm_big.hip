@@ -73,13 +73,12 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
 
   // schedule (the builder needs 256 threads; larger workgroups run it on the first 256)
+  static_assert(NW == 4 || 64 * NW > kMaxExperts, "every offsets entry has a thread");
   if (NW == 4) {
     build_tile_starts(g.offsets, g.E, BM, s_start, s_off, s_tmp, kMinRows);
   } else {
     const bool first = threadIdx.x < 256;
-    if (first) {
-      if (threadIdx.x <= g.E) s_off[threadIdx.x] = g.offsets[threadIdx.x];
-    }
+    if (threadIdx.x <= g.E) s_off[threadIdx.x] = g.offsets[threadIdx.x];  // 64 NW >= 512 > E threads
     __syncthreads();
     int n_tiles = 0;
     if (first && threadIdx.x < g.E) {

@@ -64,6 +64,7 @@ __global__ __launch_bounds__(64 * kDwWaves, 1) void dw_bf16_kernel(DwArgs g) {
 
   // ---- which expert: rank of this workgroup's expert in decreasing row count
   const int rank = blockIdx.x / sh.tiles, t = blockIdx.x - rank * sh.tiles;
+  static_assert(64 * kDwWaves > kMaxExperts, "every offsets entry has a thread");
   if (tid <= E) s_off[tid] = g.offsets[tid];
   __syncthreads();
   if (tid < E) {

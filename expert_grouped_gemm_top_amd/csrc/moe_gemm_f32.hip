@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void row_gemm_f32_kernel(RowGemmArgs g) {
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ float s_a[64];
   const int tid = threadIdx.x;
-  if (tid <= g.E) s_off[tid] = g.offsets[tid];
+  for (int i = tid; i <= g.E; i += 256) s_off[i] = g.offsets[i];  // E + 1 entries: 257 at E = 256
   __syncthreads();
   const int row = blockIdx.x;
   if (row >= s_off[g.E]) return;

@@ -95,6 +95,7 @@ SMALL_BF16 = [
     # experts past 256 rows (256-row tiles with ragged tails), 128-row tiles, and the streaming path together
     W.custom("bf16_big_tiles", T=700, H=256, F=256, E=4, k=2, dtype="bf16", skew=True, dw=True),
     W.custom("bf16_big_tiles_f384", T=600, H=384, F=384, E=6, k=1, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_e256_k16", T=64, H=128, F=128, E=256, k=16, dtype="bf16", skew=True, dw=True),
 ]
 
 
@@ -357,3 +358,24 @@ def test_budget_quota_with_metric_scores():
             if r[cap - 1] - r[cap] > 2e-2 * r[0]:  # unambiguous boundary
                 top = set(sorted(pairs, key=lambda p: (-ref[p], p))[:cap])
                 assert top == set(p for p in pairs if kinv[p] >= 0), e
+
+
+# ----------------------------------------------------------------------------- row-count regime boundaries
+def test_row_count_regime_boundaries():
+    """Experts with row counts on both sides of every kernel-regime boundary
+    (16-row tiles, 48: LDS tiles, 256: 256-row tiles), empty and one-row
+    experts, through the whole layer with dW: routing is steered by one-hot
+    logits so every expert gets exactly its count."""
+    counts = np.array([47, 48, 255, 256, 257, 0, 1, 16, 17, 300])
+    E = len(counts)
+    T = int(counts.sum())
+    wl = W.custom("bf16_regimes", T=T, H=256, F=256, E=E, k=1, dtype="bf16", skew=False, dw=True)
+    d = W.generate(wl, seed=10)
+    owner = np.repeat(np.arange(E), counts)
+    np.random.default_rng(10).shuffle(owner)  # tokens of one expert are not contiguous
+    logits = d["logits"].copy()
+    logits[np.arange(T), owner] = 50.0
+    d["logits"] = logits
+    L = run_gpu(wl, d, logits)
+    assert np.array_equal(L.counts.cpu().numpy(), counts)
+    _full_compare(wl, d, L)
