@@ -4,15 +4,19 @@
 //   [dW_gate | dW_up][e] (H x 2F) = x_rows^T [dHg | dHu]   over the rows of e
 //   dW_down[e]           (F x H)  = a_rows^T dO_rows
 //
-// Workgroup = one 256 x 256 output tile of one expert, eight waves of 128 x 64.
-// Both operands are row-major over the reduced index (the expert's rows), so
-// both land in LDS as [64 rows][256 columns] stages through direct
-// global->LDS loads (two stages in flight) and both MFMA fragments come from
-// the transposing LDS read.  Rows past the expert's last one are loaded from
-// its last row and zeroed in LDS before use.  Every output is reduced in row
-// order by one workgroup (deterministic, no atomics); an expert without rows
-// stores exact zeros.  Workgroups take experts in order of decreasing row
-// count, so the longest reductions start first.
+// Workgroup = one BM x BN output tile of one expert, waves of 128 x 64.  Both
+// operands are row-major over the reduced index (the expert's rows), so both
+// land in LDS as [BK rows][tile columns] stages through direct global->LDS
+// loads and both MFMA fragments come from the transposing LDS read.  Rows past
+// the expert's last one are loaded from its last row and zeroed in LDS before
+// use.  Every output is reduced in row order by one workgroup (deterministic,
+// no atomics); an expert without rows stores exact zeros.
+//
+// Work order: workgroups take experts in order of decreasing row count, so the
+// longest reductions start first; the tiles of one expert are dealt to the 8
+// XCDs in contiguous runs (tiles next to each other share an operand block,
+// which then stays in that XCD's L2).  The output tile is staged through LDS
+// so that every store is a full 16-byte lane of a contiguous row segment.
 #include <algorithm>
 
 #include "moe_common.h"
@@ -23,18 +27,33 @@ namespace moe {
 
 namespace {
 
-constexpr int kDwBM = 256, kDwBN = 256, kDwBK = 64;  // tile rows (of dW), columns, rows reduced per stage
-constexpr int kDwWaves = 8, kDwWM = 2;               // waves, waves along the tile rows
-constexpr int kDwTM = kDwBM / kDwWM;                 // 128 tile rows per wave
-constexpr int kDwTN = kDwBN / (kDwWaves / kDwWM);    // 64 tile columns per wave
-constexpr int kDwMI = kDwTM / 32, kDwNJ = kDwTN / 32;
-constexpr int kDwPitch = kDwBM * 2;                    // bytes per reduced row of a stage tile
-constexpr int kDwTileBytes = kDwBK * kDwPitch;         // 32 KiB per operand and stage
-constexpr int kDwStageBytes = 2 * kDwTileBytes;
-constexpr int kDwStages = 2;
-constexpr int kDwIns = kDwTileBytes / 1024 / kDwWaves;  // direct loads per wave, operand and stage
-static_assert(kDwBM == kDwBN, "one stage layout for both operands");
-static_assert(kDwIns * 1024 * kDwWaves == kDwTileBytes, "loads cover the tile");
+#ifndef MOE_DW_CFG
+#define MOE_DW_CFG 256, 8, 64, 2, 1
+#endif
+#ifndef MOE_DW_SCHED
+#define MOE_DW_SCHED 1
+#endif
+
+template <int BN_, int WAVES_, int BK_, int STAGES_, int OCC_>
+struct DwCfg {
+  static constexpr int BM = 256, BN = BN_, BK = BK_, WAVES = WAVES_, STAGES = STAGES_, OCC = OCC_;
+  static constexpr int WM = 2;                       // waves along the tile rows
+  static constexpr int TM = BM / WM;                 // 128 tile rows per wave
+  static constexpr int TN = BN / (WAVES / WM);       // tile columns per wave
+  static constexpr int MI = TM / 32, NJ = TN / 32;
+  static constexpr int PITCH_P = 2 * BM, PITCH_Q = 2 * BN;  // bytes per reduced row of a stage tile
+  static constexpr int TILE_P = BK * PITCH_P, TILE_Q = BK * PITCH_Q;
+  static constexpr int STAGE_BYTES = TILE_P + TILE_Q;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int INS_P = TILE_P / 1024 / WAVES, INS_Q = TILE_Q / 1024 / WAVES;  // direct loads per wave
+  static constexpr int INS = INS_P + INS_Q;
+  static_assert(TN == 64 && TM == 128, "waves of 128 x 64");
+  static_assert(INS_P * 1024 * WAVES == TILE_P && INS_Q * 1024 * WAVES == TILE_Q, "loads cover the tiles");
+  static_assert(STAGES >= 2 && STAGES <= 4 && 2 * INS < 64, "waits cover up to two stages issued ahead");
+  static_assert(BM * BN * 2 <= LDS_BYTES, "the output tile fits the stage buffers");
+  static_assert(64 * WAVES >= kMaxExperts, "every expert has a thread in the ranking");
+};
+using Cfg = DwCfg<MOE_DW_CFG>;
 
 struct DwShape {
   int nt1, tiles1;  // gate/up: column tiles, all tiles
@@ -44,38 +63,87 @@ struct DwShape {
 
 __host__ __device__ inline DwShape dw_shape(int H, int F) {
   DwShape s;
-  const int mt1 = (H + kDwBM - 1) / kDwBM;
-  s.nt1 = (2 * F + kDwBN - 1) / kDwBN;
+  const int mt1 = (H + Cfg::BM - 1) / Cfg::BM;
+  s.nt1 = (2 * F + Cfg::BN - 1) / Cfg::BN;
   s.tiles1 = mt1 * s.nt1;
-  const int mt2 = (F + kDwBM - 1) / kDwBM;
-  s.nt2 = (H + kDwBN - 1) / kDwBN;
+  const int mt2 = (F + Cfg::BM - 1) / Cfg::BM;
+  s.nt2 = (H + Cfg::BN - 1) / Cfg::BN;
   s.tiles = s.tiles1 + mt2 * s.nt2;
   return s;
 }
 
-__global__ __launch_bounds__(64 * kDwWaves, 1) void dw_bf16_kernel(DwArgs g) {
+// Workgroups per expert: the tiles rounded up to a multiple of the 8 XCDs.
+__host__ __device__ inline int dw_slots(const DwShape& s) { return (s.tiles + 7) & ~7; }
+
+// 16-byte direct loads of one operand's stage tile, `cpr` chunks per reduced
+// row; LDS position p of row k holds the chunk p ^ nn_swz(k).
+template <int INS_N>
+struct DwLoader {
+  const uint16_t* col[INS_N];
+  int krow[INS_N];
+  __device__ void init(const uint16_t* base, int c0, int ncols, int cpr, int w, int l) {
+#pragma unroll
+    for (int i = 0; i < INS_N; ++i) {
+      const int k = (64 / cpr) * (INS_N * w + i) + l / cpr;
+      const int c = c0 + 8 * ((l % cpr) ^ nn_swz(k));
+      krow[i] = k;
+      col[i] = base + (c < ncols ? c : 0);  // chunks past the matrix edge read column 0 (never stored)
+    }
+  }
+  __device__ void issue(int s, int n_e, int ld, unsigned char* tile, int w) const {
+#pragma unroll
+    for (int i = 0; i < INS_N; ++i) {
+      int r = s * Cfg::BK + krow[i];
+      r = r < n_e ? r : n_e - 1;  // past the expert's rows: its last row, zeroed before use
+      g2lds(col[i] + (size_t)r * ld, tile + 1024 * (INS_N * w + i));
+    }
+  }
+};
+
+__global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwArgs g) {
   __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_rank[kMaxExperts];
   __shared__ int s_expert;
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l32 = l & 31, hk = l >> 5;
-  const int wm = w % kDwWM, wn = w / kDwWM;
+  const int wm = w % Cfg::WM, wn = w / Cfg::WM;
   const int H = g.H, F = g.F, E = g.E;
   const DwShape sh = dw_shape(H, F);
 
-  // ---- which expert: rank of this workgroup's expert in decreasing row count
-  const int rank = blockIdx.x / sh.tiles, t = blockIdx.x - rank * sh.tiles;
-  static_assert(64 * kDwWaves > kMaxExperts, "every offsets entry has a thread");
-  if (tid <= E) s_off[tid] = g.offsets[tid];
+  // ---- work item: expert rank and tile.  Workgroup b runs on XCD b % 8; the
+  // j-th slot of XCD x within an expert's run of workgroups takes tile
+  // x * slots / 8 + j.
+  const int slots = dw_slots(sh);
+  const int rank = blockIdx.x / slots, traw = blockIdx.x - rank * slots;
+  const int t = (traw & 7) * (slots >> 3) + (traw >> 3);
+  if (t >= sh.tiles) return;
+
+  // ---- which expert has that rank in decreasing row count (ties: lower id
+  // first).  Each expert's rank is summed from `parts` threads' partial counts.
+  for (int i = tid; i <= E; i += 64 * Cfg::WAVES) s_off[i] = g.offsets[i];
   __syncthreads();
   if (tid < E) {
-    const int n = s_off[tid + 1] - s_off[tid];
-    int r = 0;
-    for (int e2 = 0; e2 < E; ++e2) {
-      const int n2 = s_off[e2 + 1] - s_off[e2];
-      r += (n2 > n || (n2 == n && e2 < tid)) ? 1 : 0;
-    }
-    if (r == rank) s_expert = tid;
+    s_cnt[tid] = s_off[tid + 1] - s_off[tid];
+    s_rank[tid] = 0;
   }
+  __syncthreads();
+  {
+    const int parts = (64 * Cfg::WAVES) / E;
+    if (tid < parts * E) {
+      const int ee = tid % E, part = tid / E;
+      const int n = s_cnt[ee];
+      const int lo = part * E / parts, hi = (part + 1) * E / parts;
+      int r = 0;
+      for (int e2 = lo; e2 < hi; ++e2) {
+        const int n2 = s_cnt[e2];
+        r += (n2 > n || (n2 == n && e2 < ee)) ? 1 : 0;
+      }
+      atomicAdd(&s_rank[ee], r);
+    }
+  }
+  __syncthreads();
+  if (tid < E && s_rank[tid] == rank) s_expert = tid;
   __syncthreads();
   const int e = s_expert;
   const int row0 = s_off[e], n_e = s_off[e + 1] - row0;
@@ -95,97 +163,133 @@ __global__ __launch_bounds__(64 * kDwWaves, 1) void dw_bf16_kernel(DwArgs g) {
     P = g.a; ldp = F; M = F;
     Q = g.dO; ldq = H; N = H;
   }
-  const int m0 = mt * kDwBM, n0 = nt * kDwBN;
+  const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN;
 
-  // ---- loader: instruction i of wave w fills reduced rows 2 (kDwIns w + i) + hk
-  // of a stage; LDS position l32 of a row holds the 8-column chunk
-  // l32 ^ nn_swz(row).  Chunks past the matrix edge read column 0 (their
-  // results are never stored).
-  const uint16_t* p_col[kDwIns];
-  const uint16_t* q_col[kDwIns];
-  int krow[kDwIns];
-#pragma unroll
-  for (int i = 0; i < kDwIns; ++i) {
-    const int k = 2 * (kDwIns * w + i) + hk;
-    const int ch = l32 ^ nn_swz(k);
-    const int pc = m0 + 8 * ch, qc = n0 + 8 * ch;
-    krow[i] = k;
-    p_col[i] = P + (size_t)row0 * ldp + (pc < M ? pc : 0);
-    q_col[i] = Q + (size_t)row0 * ldq + (qc < N ? qc : 0);
-  }
+  DwLoader<Cfg::INS_P> lp;
+  DwLoader<Cfg::INS_Q> lq;
+  lp.init(P + (size_t)row0 * ldp, m0, M, Cfg::PITCH_P / 16, w, l);
+  lq.init(Q + (size_t)row0 * ldq, n0, N, Cfg::PITCH_Q / 16, w, l);
   auto issue = [&](int s) {
-    unsigned char* st = s_dyn + (s % kDwStages) * kDwStageBytes;
-#pragma unroll
-    for (int i = 0; i < kDwIns; ++i) {
-      int r = s * kDwBK + krow[i];
-      r = r < n_e ? r : n_e - 1;  // past the expert's rows: its last row, zeroed before use
-      g2lds(p_col[i] + (size_t)r * ldp, st + 1024 * (kDwIns * w + i));
-      g2lds(q_col[i] + (size_t)r * ldq, st + kDwTileBytes + 1024 * (kDwIns * w + i));
-    }
+    unsigned char* st = s_dyn + (s % Cfg::STAGES) * Cfg::STAGE_BYTES;
+    lp.issue(s, n_e, ldp, st, w);
+    lq.issue(s, n_e, ldq, st + Cfg::TILE_P, w);
   };
 
-  f32x16 acc[kDwMI][kDwNJ];
+  f32x16 acc[Cfg::MI][Cfg::NJ];
 #pragma unroll
-  for (int i = 0; i < kDwMI; ++i)
+  for (int i = 0; i < Cfg::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < kDwNJ; ++j)
+    for (int j = 0; j < Cfg::NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int s) {
-    const unsigned char* st = s_dyn + (s % kDwStages) * kDwStageBytes;
+  struct Frags {
+    u32x4 a[Cfg::MI];
+    u32x4 b[Cfg::NJ];
+  };
+  auto read_frags = [&](const unsigned char* st, int sub, Frags& fr) {
 #pragma unroll
-    for (int sub = 0; sub < kDwBK / 16; ++sub) {
-      u32x4 fa[kDwMI], fb[kDwNJ];
+    for (int i = 0; i < Cfg::MI; ++i) fr.a[i] = tr_frag32(st, Cfg::PITCH_P, sub, Cfg::TM * wm + 32 * i);
 #pragma unroll
-      for (int i = 0; i < kDwMI; ++i) fa[i] = tr_frag32(st, kDwPitch, sub, kDwTM * wm + 32 * i);
+    for (int j = 0; j < Cfg::NJ; ++j) fr.b[j] = tr_frag32(st + Cfg::TILE_P, Cfg::PITCH_Q, sub, Cfg::TN * wn + 32 * j);
+  };
+  auto mfmas = [&](const Frags& fr) {
 #pragma unroll
-      for (int j = 0; j < kDwNJ; ++j) fb[j] = tr_frag32(st + kDwTileBytes, kDwPitch, sub, kDwTN * wn + 32 * j);
+    for (int j = 0; j < Cfg::NJ; ++j)
 #pragma unroll
-      for (int j = 0; j < kDwNJ; ++j)
+      for (int i = 0; i < Cfg::MI; ++i) acc[i][j] = mfma32(fr.b[j], fr.a[i], acc[i][j]);
+  };
+  // one sub-step's MFMAs with the next sub-step's fragment reads woven in
+  auto mfmas_interleaved = [&](const Frags& cur, const unsigned char* st, int next_sub, Frags& nxt) {
+    __builtin_amdgcn_s_setprio(1);
+    if (next_sub >= 0) read_frags(st, next_sub, nxt);
+    mfmas(cur);
 #pragma unroll
-        for (int i = 0; i < kDwMI; ++i) acc[i][j] = mfma32(fb[j], fa[i], acc[i][j]);
+    for (int q = 0; q < Cfg::MI * Cfg::NJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads (one transposed fragment)
     }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute = [&](int s) {
+    const unsigned char* st = s_dyn + (s % Cfg::STAGES) * Cfg::STAGE_BYTES;
+    constexpr int SUBS = Cfg::BK / 16;
+#if MOE_DW_SCHED
+    Frags f0, f1;
+    read_frags(st, 0, f0);
+#pragma unroll
+    for (int u = 0; u < SUBS; u += 2) {
+      mfmas_interleaved(f0, st, u + 1 < SUBS ? u + 1 : -1, f1);
+      if (u + 1 < SUBS) mfmas_interleaved(f1, st, u + 2 < SUBS ? u + 2 : -1, f0);
+    }
+#else
+#pragma unroll
+    for (int sub = 0; sub < SUBS; ++sub) {
+      Frags f;
+      read_frags(st, sub, f);
+      mfmas(f);
+    }
+#endif
   };
 
-  const int steps = (n_e + kDwBK - 1) / kDwBK;
-  if (steps > 0) issue(0);
+  const int steps = (n_e + Cfg::BK - 1) / Cfg::BK;
+#pragma unroll
+  for (int s = 0; s < Cfg::STAGES - 1; ++s)
+    if (s < steps) issue(s);
   for (int s = 0; s < steps; ++s) {
-    wait_vmcnt<0>();  // this wave's loads of stage s (the only stage in flight)
+    // stage s has landed once at most (stages issued after it) x INS loads remain
+    const int ahead = min(Cfg::STAGES - 2, steps - 1 - s);
+    if (ahead >= 2) wait_vmcnt<2 * Cfg::INS>();
+    else if (ahead == 1) wait_vmcnt<Cfg::INS>();
+    else wait_vmcnt<0>();
     barrier_no_fence();
-    if (s + 1 < steps) issue(s + 1);
-    const int valid = n_e - s * kDwBK;
-    if (valid < kDwBK) {
+    if (s + Cfg::STAGES - 1 < steps) issue(s + Cfg::STAGES - 1);
+    const int valid = n_e - s * Cfg::BK;
+    if (valid < Cfg::BK) {
       // last stage: zero the rows past the expert's end in both operand tiles
-      unsigned char* st = s_dyn + (s % kDwStages) * kDwStageBytes;
-      for (int c = tid; c < 2 * kDwBK * (kDwPitch / 16); c += 64 * kDwWaves) {
-        const int op = c / (kDwBK * (kDwPitch / 16));
-        const int rr = (c / (kDwPitch / 16)) % kDwBK;
-        if (rr >= valid) *(u32x4*)(st + op * kDwTileBytes + rr * kDwPitch + 16 * (c % (kDwPitch / 16))) = u32x4{0, 0, 0, 0};
+      unsigned char* st = s_dyn + (s % Cfg::STAGES) * Cfg::STAGE_BYTES;
+      for (int c = tid; c < Cfg::STAGE_BYTES / 16; c += 64 * Cfg::WAVES) {
+        const bool in_q = c >= Cfg::TILE_P / 16;
+        const int rr = in_q ? (c - Cfg::TILE_P / 16) / (Cfg::PITCH_Q / 16) : c / (Cfg::PITCH_P / 16);
+        if (rr >= valid) *(u32x4*)(st + 16 * c) = u32x4{0, 0, 0, 0};
       }
       __syncthreads();
     }
     compute(s);
   }
 
-  // ---- epilogue.  acc[i][j] register r -> tile row kDwTM wm + 32 i + l32,
-  // tile column kDwTN wn + 32 j + 8 q + 4 hk + (0..3) with q = r / 4.
+  // ---- epilogue, staged through LDS.  acc[i][j] register r -> tile row
+  // TM wm + 32 i + l32, tile column TN wn + 32 j + 8 q + 4 hk + (0..3) with
+  // q = r / 4.  LDS row m holds the tile row, its 16-byte chunk c at position
+  // c ^ (m % CPR).
+  constexpr int CPR = Cfg::BN / 8;
+  __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
-  for (int i = 0; i < kDwMI; ++i) {
-    const int m = m0 + kDwTM * wm + 32 * i + l32;
-    if (m >= M) continue;
+  for (int i = 0; i < Cfg::MI; ++i) {
+    const int m = Cfg::TM * wm + 32 * i + l32;
 #pragma unroll
-    for (int j = 0; j < kDwNJ; ++j)
+    for (int j = 0; j < Cfg::NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + kDwTN * wn + 32 * j + 8 * q + 4 * hk;
-        if (n >= N) continue;
-        uint16_t* dst;
-        if (t < sh.tiles1) dst = (n < F) ? g.dwg + ((size_t)e * H + m) * F + n : g.dwu + ((size_t)e * H + m) * F + (n - F);
-        else dst = g.dwd + ((size_t)e * F + m) * H + n;
-        *(u32x2*)dst = u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                             pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+        const int c = (Cfg::TN * wn + 32 * j + 8 * q) >> 3;
+        *(u32x2*)(s_dyn + m * (2 * Cfg::BN) + 16 * (c ^ (m % CPR)) + 8 * hk) =
+            u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]), pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
       }
+  }
+  __syncthreads();
+  constexpr int kRowsPerWave = Cfg::BM / Cfg::WAVES, kRowsPerIns = 64 / CPR;
+#pragma unroll
+  for (int it = 0; it < kRowsPerWave / kRowsPerIns; ++it) {
+    const int m = kRowsPerWave * w + kRowsPerIns * it + l / CPR, c = l % CPR;
+    const int gm = m0 + m, gn = n0 + 8 * c;
+    if (gm < M && gn < N) {
+      const u32x4 v = *(const u32x4*)(s_dyn + m * (2 * Cfg::BN) + 16 * (c ^ (m % CPR)));
+      uint16_t* dst;
+      if (t < sh.tiles1) dst = (gn < F) ? g.dwg + ((size_t)e * H + gm) * F + gn : g.dwu + ((size_t)e * H + gm) * F + (gn - F);
+      else dst = g.dwd + ((size_t)e * F + gm) * H + gn;
+      *(u32x4*)dst = v;
+    }
   }
 }
 
@@ -193,8 +297,8 @@ __global__ __launch_bounds__(64 * kDwWaves, 1) void dw_bf16_kernel(DwArgs g) {
 
 hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream) {
   const DwShape sh = dw_shape(g.H, g.F);
-  const int64_t blocks = (int64_t)g.E * sh.tiles;
-  const size_t lds = (size_t)kDwStages * kDwStageBytes;
+  const int64_t blocks = (int64_t)g.E * dw_slots(sh);
+  const size_t lds = (size_t)Cfg::LDS_BYTES;
   // dynamic LDS above 64 KiB must be allowed explicitly, once per device
   static bool attr_set[64] = {};
   int dev = 0;
@@ -205,7 +309,7 @@ hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream) {
     if (err != hipSuccess) return err;
     if (dev >= 0 && dev < 64) attr_set[dev] = true;
   }
-  hipLaunchKernelGGL(dw_bf16_kernel, dim3((unsigned)blocks), dim3(64 * kDwWaves), lds, stream, g);
+  hipLaunchKernelGGL(dw_bf16_kernel, dim3((unsigned)blocks), dim3(64 * Cfg::WAVES), lds, stream, g);
   return hipGetLastError();
 }
 
