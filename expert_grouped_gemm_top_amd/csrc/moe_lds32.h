@@ -21,9 +21,25 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 first, u32x4 second, f32x16 acc) 
                                                   acc, 0, 0, 0);
 }
 
-// 16 B from global straight into LDS at lds_base + 16 * lane.
+// 16 B from global straight into LDS at lds_base + 16 * lane (lds_base
+// wave-uniform).
+// Issued as inline assembly so that the compiler does not see an LDS write in
+// flight: it would otherwise wait for every outstanding direct load before the
+// next LDS read, whichever buffer that read touches, and no stage could load
+// while another is computed.  Completion is the caller's business (wait_vmcnt
+// and a barrier before the stage is read).
 __device__ __forceinline__ void g2lds(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+  // m0 carries the LDS address; its previous value is restored for the compiler
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
