@@ -10,6 +10,9 @@
 // 8-pass MSB-first radix select (256-bin LDS histograms; the counts do not
 // depend on the order of the LDS atomics).  A block prefix scan over the
 // expert's pairs in sorted order then writes the kept pairs in ascending p.
+// Up to kLdsPairs pairs, the expert's pair ids and score keys are gathered
+// into LDS once (eight independent loads per thread in flight) and every pass
+// runs out of LDS; larger experts re-read them from memory in each pass.
 // kept_offsets follows from the counts alone (q_e depends only on n_e), so
 // every workgroup computes its own base with one block scan.
 #include "moe_common.h"
@@ -19,11 +22,42 @@ namespace moe {
 
 namespace {
 
+constexpr int kLdsPairs = 16384;  // pairs whose id and score key fit the workgroup's LDS (128 KiB)
+constexpr int kUnroll = 8;        // independent loads per thread in flight
+
+// Score -> unsigned key with the same order (-0 ranks equal to +0).
+__device__ __forceinline__ uint32_t score_key(float score) {
+  if (score == 0.0f) score = 0.0f;
+  const uint32_t u = __float_as_uint(score);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __device__ __forceinline__ uint64_t pair_key(float score, int32_t p) {
-  if (score == 0.0f) score = 0.0f;  // -0 ranks equal to +0
-  uint32_t u = __float_as_uint(score);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)p);
+  return ((uint64_t)score_key(score) << 32) | (uint32_t)(~(uint32_t)p);
+}
+
+__device__ __forceinline__ uint64_t lds_key(const uint32_t* s_khi, const int32_t* s_p, int i) {
+  return ((uint64_t)s_khi[i] << 32) | (uint32_t)(~(uint32_t)s_p[i]);
+}
+
+// The key threshold from a 256-bin histogram pass: thread t looks at bin
+// 255 - t; the keys in higher bins are an exclusive scan.  Updates the prefix
+// class and the rank still to find within it.
+__device__ __forceinline__ void radix_pick(const int* s_hist, int* s_tmp, int* s_pick, int shift, uint64_t& prefix,
+                                           uint64_t& mask, int& remaining) {
+  const int tid = threadIdx.x;
+  const int cnt = s_hist[255 - tid];
+  int tot;
+  const int above = block256_exclusive_scan(cnt, s_tmp, tot);
+  if (above < remaining && remaining <= above + cnt) {
+    s_pick[0] = 255 - tid;
+    s_pick[1] = remaining - above;
+  }
+  __syncthreads();
+  prefix |= (uint64_t)s_pick[0] << shift;
+  mask |= (uint64_t)0xffu << shift;
+  remaining = s_pick[1];
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ a, int64_t n, int32_t v) {
@@ -42,6 +76,7 @@ __global__ __launch_bounds__(256) void compact_select_kernel(int E, int cap, con
   __shared__ int s_tmp[4];
   __shared__ int s_hist[256];
   __shared__ int s_pick[2];
+  extern __shared__ __attribute__((aligned(16))) uint32_t s_pairs[];  // [kLdsPairs] keys, then [kLdsPairs] ids
   const int e = blockIdx.x, tid = threadIdx.x;
   // kept base of this expert: exclusive scan of min(n_e', cap)
   const int qv = (tid < E) ? min(counts[tid], cap) : 0;
@@ -60,11 +95,80 @@ __global__ __launch_bounds__(256) void compact_select_kernel(int E, int cap, con
   const int q = min(n, cap);
   __syncthreads();
   if (q == n) {
-    for (int i = tid; i < n; i += 256) {
-      const int32_t p = perm[off + i];
-      kept_perm[kbase + i] = p;
-      kept_src[kbase + i] = off + i;
-      kept_inv[p] = kbase + i;
+    for (int i0 = 0; i0 < n; i0 += 256 * kUnroll) {
+      int32_t pv[kUnroll];
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int i = i0 + 256 * j + tid;
+        pv[j] = i < n ? perm[off + i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int i = i0 + 256 * j + tid;
+        if (i < n) {
+          kept_perm[kbase + i] = pv[j];
+          kept_src[kbase + i] = off + i;
+          kept_inv[pv[j]] = kbase + i;
+        }
+      }
+    }
+    return;
+  }
+  if (n <= kLdsPairs) {
+    uint32_t* s_khi = s_pairs;
+    int32_t* s_p = reinterpret_cast<int32_t*>(s_pairs + kLdsPairs);
+    for (int i0 = 0; i0 < n; i0 += 256 * kUnroll) {
+      int32_t pv[kUnroll];
+      float sv[kUnroll];
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int i = i0 + 256 * j + tid;
+        pv[j] = i < n ? perm[off + i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int i = i0 + 256 * j + tid;
+        sv[j] = i < n ? score[pv[j]] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int i = i0 + 256 * j + tid;
+        if (i < n) {
+          s_p[i] = pv[j];
+          s_khi[i] = score_key(sv[j]);
+        }
+      }
+    }
+    __syncthreads();
+    uint64_t prefix = 0, mask = 0;
+    int remaining = q;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      s_hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += 256) {
+        const uint64_t key = lds_key(s_khi, s_p, i);
+        if ((key & mask) == prefix) atomicAdd(&s_hist[(int)((key >> shift) & 0xffu)], 1);
+      }
+      __syncthreads();
+      radix_pick(s_hist, s_tmp, s_pick, shift, prefix, mask, remaining);
+    }
+    // kept pairs in ascending order: thread t takes the contiguous chunk
+    // [t c, (t + 1) c) and its place follows from a scan of the chunk counts
+    const int c = (n + 255) / 256, i_lo = min(n, tid * c), i_hi = min(n, i_lo + c);
+    int cnt = 0;
+    for (int i = i_lo; i < i_hi; ++i) cnt += lds_key(s_khi, s_p, i) >= prefix ? 1 : 0;
+    int tot;
+    int pos = kbase + block256_exclusive_scan(cnt, s_tmp, tot);
+    for (int i = i_lo; i < i_hi; ++i) {
+      const int32_t p = s_p[i];
+      if (lds_key(s_khi, s_p, i) >= prefix) {
+        kept_perm[pos] = p;
+        kept_src[pos] = off + i;
+        kept_inv[p] = pos;
+        ++pos;
+      } else {
+        kept_inv[p] = -1;
+      }
     }
     return;
   }
@@ -80,19 +184,7 @@ __global__ __launch_bounds__(256) void compact_select_kernel(int E, int cap, con
       if ((key & mask) == prefix) atomicAdd(&s_hist[(int)((key >> shift) & 0xffu)], 1);
     }
     __syncthreads();
-    // thread t looks at bin 255 - t; count of keys in higher bins = exclusive scan
-    const int cnt = s_hist[255 - tid];
-    int tot;
-    const int above = block256_exclusive_scan(cnt, s_tmp, tot);
-    if (above < remaining && remaining <= above + cnt) {
-      s_pick[0] = 255 - tid;
-      s_pick[1] = remaining - above;
-    }
-    __syncthreads();
-    prefix |= (uint64_t)s_pick[0] << shift;
-    mask |= (uint64_t)0xffu << shift;
-    remaining = s_pick[1];
-    __syncthreads();
+    radix_pick(s_hist, s_tmp, s_pick, shift, prefix, mask, remaining);
   }
   const uint64_t thr = prefix;  // the q-th largest key; keep key >= thr
   int run = 0;
@@ -132,7 +224,18 @@ hipError_t launch_compact(int64_t N, int E, int cap, const int32_t* counts, cons
                           const float* score, int32_t* kept_counts, int32_t* kept_offsets, int32_t* kept_perm,
                           int32_t* kept_src, int32_t* kept_inv, hipStream_t stream) {
   (void)N;
-  hipLaunchKernelGGL(compact_select_kernel, dim3(E), dim3(256), 0, stream, E, cap, counts, offsets, perm, score,
+  const size_t lds = 2 * kLdsPairs * sizeof(uint32_t);
+  // dynamic LDS above 64 KiB must be allowed explicitly, once per device
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    err = hipFuncSetAttribute((const void*)compact_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    if (dev >= 0 && dev < 64) attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL(compact_select_kernel, dim3(E), dim3(256), lds, stream, E, cap, counts, offsets, perm, score,
                      kept_counts, kept_offsets, kept_perm, kept_src, kept_inv);
   return hipGetLastError();
 }

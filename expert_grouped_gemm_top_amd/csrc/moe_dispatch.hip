@@ -9,6 +9,7 @@
 // Kernels (all on the caller's stream):
 //   hist  per block of 1024 pairs: expert histogram in LDS     (order-free LDS atomics)
 //   scan  one block: offsets = exclusive scan of counts, and every block's base
+//         (the blocks split into ranges summed by separate threads)
 //   rank  per block: stable rank of each pair among equal experts, from
 //         ballots on the bits of the expert id and popcounts below the lane,
 //         plus per-wave running bases in LDS; writes perm and inv_perm
@@ -49,27 +50,64 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(int64_t N, int E, co
   if (tid < E) ws_hist[(size_t)blockIdx.x * E + tid] = s_cnt[tid];
 }
 
-// One block; thread e walks the blocks in order.  ws_base[b][e] = offsets[e] +
-// pairs of expert e in blocks before b.
+// One block.  ws_base[b][e] = offsets[e] + pairs of expert e in blocks before
+// b.  The blocks are split into `parts` ranges (parts x E <= 256 threads);
+// thread (part, e) sums its range, the part sums and the expert totals are
+// scanned in LDS, then the thread writes its range's running bases.  Loads
+// are issued kUnroll at a time so that their latencies overlap.
+constexpr int kScanUnroll = 8;
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(int nblocks, int E, const int32_t* __restrict__ ws_hist,
                                                             int32_t* __restrict__ ws_base, int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets) {
   __shared__ int s_tmp[4];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E)
-    for (int b = 0; b < nblocks; ++b) {
-      ws_base[(size_t)b * E + e] = run;
-      run += ws_hist[(size_t)b * E + e];
+  __shared__ int s_part[4][kMaxExperts];
+  const int tid = threadIdx.x;
+  const int parts = min(4, 256 / E);
+  const bool active = tid < parts * E;
+  const int e = active ? tid % E : 0, part = active ? tid / E : 0;
+  const int lo = (int)((int64_t)part * nblocks / parts), hi = (int)((int64_t)(part + 1) * nblocks / parts);
+  int sum = 0;
+  if (active)
+    for (int b0 = lo; b0 < hi; b0 += kScanUnroll) {
+      int v[kScanUnroll];
+#pragma unroll
+      for (int j = 0; j < kScanUnroll; ++j) v[j] = (b0 + j < hi) ? ws_hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanUnroll; ++j) sum += v[j];
     }
+  if (active) s_part[part][e] = sum;
+  __syncthreads();
+  int tot = 0;
+  if (tid < E)
+    for (int q = 0; q < parts; ++q) tot += s_part[q][tid];
   int total;
-  const int off = block256_exclusive_scan(e < E ? run : 0, s_tmp, total);
-  if (e < E) {
-    counts[e] = run;
-    offsets[e] = off;
-    for (int b = 0; b < nblocks; ++b) ws_base[(size_t)b * E + e] += off;
+  const int off = block256_exclusive_scan(tid < E ? tot : 0, s_tmp, total);
+  if (tid < E) {
+    counts[tid] = tot;
+    offsets[tid] = off;
+    int run = off;
+    for (int q = 0; q < parts; ++q) {  // part sums -> part bases
+      const int c = s_part[q][tid];
+      s_part[q][tid] = run;
+      run += c;
+    }
   }
-  if (e == 0) offsets[E] = total;
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  if (active) {
+    int run = s_part[part][e];
+    for (int b0 = lo; b0 < hi; b0 += kScanUnroll) {
+      int v[kScanUnroll];
+#pragma unroll
+      for (int j = 0; j < kScanUnroll; ++j) v[j] = (b0 + j < hi) ? ws_hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanUnroll; ++j)
+        if (b0 + j < hi) {
+          ws_base[(size_t)(b0 + j) * E + e] = run;
+          run += v[j];
+        }
+    }
+  }
 }
 
 // FUSED: this is the only block; counts/offsets are produced here.

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle
+from expert_grouped_gemm_top_amd import moe
 from expert_grouped_gemm_top_amd import workloads as W
 from expert_grouped_gemm_top_amd.layer import MoeLayerBuffers
 from moe_cases import (TOL, assert_close, dw_queries, gpu_dw_entries, logits_of, note, np32, oracle_dw_sample,
@@ -127,6 +128,44 @@ def test_compaction_with_large_quota_is_bitwise_the_dense_backward():
     assert torch.equal(L1.kept_inv, L0.inv_perm) and torch.equal(L1.kept_offsets, L0.offsets)
     for n in ("dx", "dg", "dw_gate", "dw_up", "dw_down"):
         assert torch.equal(getattr(L0, n), getattr(L1, n)), n
+
+
+# Selection alone (index arrays, no row copies) on experts large enough for
+# each of the selection kernel's three paths: every pair kept (copy), pairs
+# gathered into LDS (up to 16384 pairs), and pairs re-read from memory in
+# every radix pass (more than that).  Scores carry many ties, both zeros and
+# negative values, so the tie order (lower pair first) and the key mapping of
+# the sign are exercised.  Index and count arrays come from the oracle.
+@pytest.mark.parametrize("sizes,k,rho", [((18000, 5000, 1000), 1, 0.5), ((3000, 9000, 11000, 2), 2, 0.3)])
+def test_compaction_selection_paths(sizes, k, rho):
+    E = len(sizes)
+    N = sum(sizes)
+    assert N % k == 0
+    T = N // k
+    rng = np.random.default_rng(N + E)
+    experts = np.repeat(np.arange(E, dtype=np.int32), sizes)
+    rng.shuffle(experts)
+    idx = experts.reshape(T, k)
+    counts, offsets, perm, inv = oracle.dispatch(idx, E)
+    score = (rng.integers(-20, 40, N) / 20.0).astype(np.float32)
+    score[rng.random(N) < 0.05] = -0.0
+    note(f"compaction selection sizes={sizes} k={k} rho={rho}")
+    c = oracle.compact(T, E, k, counts, offsets, perm, score, rho)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    R = c["R"]
+    R_cap = min(N, E * moe.moe_quota_cap(T, E, k, rho))  # capacity of the kept arrays
+    kc = torch.empty(E, dtype=torch.int32, device="cuda")
+    ko = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    kp = torch.empty(R_cap, dtype=torch.int32, device="cuda")
+    ks = torch.empty(R_cap, dtype=torch.int32, device="cuda")
+    ki = torch.empty(N, dtype=torch.int32, device="cuda")
+    moe.moe_compact_pairs(dev(counts), dev(offsets), dev(perm), dev(score), rho, kc, ko, kp, ks, ki, T, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), c["counts"])
+    assert np.array_equal(ko.cpu().numpy(), c["offsets"])
+    assert np.array_equal(kp.cpu().numpy()[:R], c["perm"])
+    assert np.array_equal(ks.cpu().numpy()[:R], c["src"])
+    assert np.array_equal(ki.cpu().numpy(), c["inv"])
 
 
 # the recompute path (keep_graph=False) against the kept-activation path: the
