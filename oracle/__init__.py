@@ -44,6 +44,14 @@ def _load():
         _lib.oracle_compact.restype = ctypes.c_int64
         _lib.oracle_dispatch.restype = ctypes.c_int
         _lib.oracle_num_threads.restype = ctypes.c_int
+        _lib.oracle_e4m3_decode.restype = ctypes.c_double
+        _lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        _lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        _lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        _lib.oracle_fp8_scale_exp.restype = ctypes.c_int
+        _lib.oracle_fp8_scale_exp.argtypes = [ctypes.c_double]
+        _lib.oracle_quantize_fp8.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     return _lib
 
 
@@ -235,3 +243,45 @@ def dw_entries(x, idx, w, Wg, Wu, Wd, dy, q_e, q_mat, q_r, q_c, retained=None):
     _load().oracle_dw_entries(T, H, F, E, k, _p(x), _p(idx), _p(w), _p(Wg), _p(Wu), _p(Wd), _p(dy),
                               _p(ret), len(q_e), _p(q_e), _p(q_mat), _p(q_r), _p(q_c), _p(out))
     return out
+
+
+def e4m3_decode(codes):
+    """Values of OCP E4M3 codes (uint8 array) as float64."""
+    c = np.asarray(codes, dtype=np.uint8)
+    L = _load()
+    return np.array([L.oracle_e4m3_decode(int(v)) for v in c.reshape(-1)], dtype=np.float64).reshape(c.shape)
+
+
+def e4m3_encode(values):
+    """OCP E4M3 codes of float64 values (round to nearest even, saturating)."""
+    v = _f64(values)
+    L = _load()
+    return np.array([L.oracle_e4m3_encode(float(x)) for x in v.reshape(-1)], dtype=np.uint8).reshape(v.shape)
+
+
+def fp8_scale_exp(amax: float) -> int:
+    """log2 of the smallest power-of-two scale s with amax <= 448 s."""
+    return int(_load().oracle_fp8_scale_exp(float(amax)))
+
+
+def quantize_fp8(w0, w1=None):
+    """Per-expert fp8 storage of w0 [E, ...] (and w1 of the same E, sharing the
+    scale): returns (q0, q1 or None, scale [E])."""
+    a0 = _f64(w0)
+    E = a0.shape[0]
+    n0 = a0.size // E
+    a1 = None if w1 is None else _f64(w1)
+    n1 = 0 if a1 is None else a1.size // E
+    q0 = np.empty(a0.shape, np.uint8)
+    q1 = None if a1 is None else np.empty(a1.shape, np.uint8)
+    scale = np.empty(E, np.float64)
+    _load().oracle_quantize_fp8(E, n0, _p(a0), n1, _p(a1), _p(q0), _p(q1), _p(scale))
+    return q0, q1, scale
+
+
+def dequantize_fp8(q, scale):
+    """w = E4M3 value x scale[e] (exact in float64)."""
+    table = e4m3_decode(np.arange(256, dtype=np.uint8))
+    q = np.asarray(q, dtype=np.uint8)
+    s = np.asarray(scale, dtype=np.float64).reshape((-1,) + (1,) * (q.ndim - 1))
+    return table[q] * s

@@ -508,6 +508,77 @@ void oracle_dw_entries(int T, int H, int F, int E, int k, const double* x, const
   }
 }
 
+/* ------------------------------------------------------------------------- */
+/* fp8 storage of frozen expert weights.  The experts are frozen in the LoRA
+ * step (issue #14, Scope) and their weights stay resident on the device
+ * (issue #14, Proposal), so they can be stored once in 8 bits.  The pages fix
+ * no format; the element format is OCP 8-bit floating point E4M3 ("E4M3FN":
+ * 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+ * infinities, S.1111.111 = NaN, largest finite 448), and each expert keeps one
+ * power-of-two scale shared by its W_gate and W_up (and one for W_down).
+ *
+ * Decoding is the format's definition. */
+double oracle_e4m3_decode(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Encoding: round to nearest, ties to the even mantissa, values beyond 448 in
+ * magnitude saturate to 448, NaN to S.1111.111.  Every step below is exact in
+ * double for the inputs it receives, so rint() alone decides the rounding. */
+uint8_t oracle_e4m3_encode(double v) {
+  if (isnan(v)) return 0x7F;
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) {  /* subnormal range: multiples of 2^-9 (8 * 2^-9 is the smallest normal) */
+    const int q = (int)rint(ldexp(a, 9));
+    return sign | (uint8_t)q;
+  }
+  int e2;
+  const double f = frexp(a, &e2); /* a = f 2^e2, f in [0.5, 1) */
+  int e = e2 - 1;                   /* a = (2 f) 2^e, 2 f in [1, 2) */
+  int m = (int)rint((2.0 * f - 1.0) * 8.0);
+  if (m == 8) {
+    m = 0;
+    ++e;
+  }
+  const int code = ((e + 7) << 3) | m;
+  return sign | (uint8_t)(code > 0x7E ? 0x7E : code);
+}
+
+/* The scale of one expert: the smallest power of two s with amax <= 448 s,
+ * amax the largest magnitude over the expert's matrices (s = 1 when all are
+ * zero).  Returns log2(s). */
+int oracle_fp8_scale_exp(double amax) {
+  if (!(amax > 0.0)) return 0;
+  int k;
+  (void)frexp(amax, &k);
+  k -= 9; /* a start near the answer (448 is just under 2^9); the loops make it exact */
+  while (448.0 * ldexp(1.0, k) < amax) ++k;
+  while (448.0 * ldexp(1.0, k - 1) >= amax) --k;
+  return k;
+}
+
+/* Quantize E experts' matrices: w0 [E][n0] and optionally w1 [E][n1] share
+ * one scale per expert; q = E4M3(w / s), scale[e] = s. */
+void oracle_quantize_fp8(int E, int64_t n0, const double* w0, int64_t n1, const double* w1, uint8_t* q0, uint8_t* q1,
+                         double* scale) {
+  for (int e = 0; e < E; ++e) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < n0; ++i) amax = fmax(amax, fabs(w0[(size_t)e * n0 + i]));
+    if (w1)
+      for (int64_t i = 0; i < n1; ++i) amax = fmax(amax, fabs(w1[(size_t)e * n1 + i]));
+    const int k = oracle_fp8_scale_exp(amax);
+    scale[e] = ldexp(1.0, k);
+    for (int64_t i = 0; i < n0; ++i) q0[(size_t)e * n0 + i] = oracle_e4m3_encode(ldexp(w0[(size_t)e * n0 + i], -k));
+    if (w1)
+      for (int64_t i = 0; i < n1; ++i) q1[(size_t)e * n1 + i] = oracle_e4m3_encode(ldexp(w1[(size_t)e * n1 + i], -k));
+  }
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

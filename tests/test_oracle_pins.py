@@ -510,3 +510,74 @@ def test_quota_cap_for_budget_closed_forms():
     # capped at ceil(T k / E); -1 when one row per expert does not fit
     assert oracle.quota_cap_for_budget(100, 64, 32, 8, 2, 4, True, True, 1e12) == 25
     assert oracle.quota_cap_for_budget(100, 64, 32, 8, 2, 4, True, True, 8 * 4 * (192 + 160) - 1) == -1
+
+
+# ----------------------------------------------------------------------------- fp8 (OCP E4M3) weight storage
+def test_e4m3_values_of_the_format():
+    # codes fixed by the format: bias 7, 3 mantissa bits, subnormal step 2^-9,
+    # largest finite 448 = 1.75 * 2^8, S.1111.111 = NaN, no infinities
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0, 0x39: 1.125,
+             0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0x80: -0.0, 0xC0: -2.0, 0xFE: -448.0}
+    for c, v in table.items():
+        got = float(oracle.e4m3_decode(np.array([c], np.uint8))[0])
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), hex(c)
+        assert int(oracle.e4m3_encode(np.array([v]))[0]) == c, hex(c)
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    finite = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(finite) > 0) and len(finite) == 127  # 0 and 126 positive values, increasing
+
+
+def test_e4m3_encode_is_nearest_with_ties_to_even_bruteforce():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    rng = np.random.default_rng(5)
+    srt = np.sort(vals)
+    xs = np.concatenate([rng.uniform(-448, 448, 3000), rng.uniform(-0.05, 0.05, 3000),
+                         (srt[:-1] + srt[1:]) / 2.0])  # every midpoint between neighbours: a tie
+    enc = oracle.e4m3_encode(xs)
+    got = oracle.e4m3_decode(enc)
+    for x, g, c in zip(xs, got, enc):
+        d = np.abs(vals - x)
+        best = d.min()
+        assert abs(g - x) == best, (x, g)
+        cands = codes[d == best]
+        if len(cands) > 1 and not (len(set(vals[d == best])) == 1):  # a tie between two values
+            assert c & 1 == 0, (x, hex(c))  # the even mantissa wins
+
+
+def test_e4m3_round_trip_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(oracle.e4m3_encode(oracle.e4m3_decode(codes)), codes)
+    assert list(oracle.e4m3_encode(np.array([464.0, 1e9, -500.0]))) == [0x7E, 0x7E, 0xFE]
+
+
+def test_fp8_scale_closed_forms():
+    for j in (-20, -8, 0, 3):
+        assert oracle.fp8_scale_exp(448.0 * 2.0 ** j) == j
+        assert oracle.fp8_scale_exp(np.nextafter(448.0 * 2.0 ** j, np.inf)) == j + 1
+    rng = np.random.default_rng(6)
+    for amax in rng.uniform(1e-6, 1e3, 200):
+        k = oracle.fp8_scale_exp(amax)
+        assert amax <= 448.0 * 2.0 ** k and amax > 448.0 * 2.0 ** (k - 1)
+    assert oracle.fp8_scale_exp(0.0) == 0
+
+
+def test_quantize_fp8_shared_scale_and_error_bound():
+    rng = np.random.default_rng(7)
+    E = 3
+    w0 = W.round_bf16((0.02 * rng.standard_normal((E, 64, 48))).astype(np.float32))
+    w1 = W.round_bf16((0.05 * rng.standard_normal((E, 64, 48))).astype(np.float32))
+    q0, q1, s = oracle.quantize_fp8(w0, w1)
+    for e in range(E):
+        amax = max(np.abs(w0[e]).max(), np.abs(w1[e]).max())
+        assert s[e] == 2.0 ** oracle.fp8_scale_exp(amax)  # one scale for both matrices
+    for w, q in ((w0, q0), (w1, q1)):
+        d = oracle.dequantize_fp8(q, s)
+        # round to nearest: error <= half a step; the step is 2^-3 of the binade (normals) or 2^-9 s
+        step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(w) / s[:, None, None], 2.0 ** -6))) - 3),
+                          2.0 ** -9) * s[:, None, None]
+        assert np.all(np.abs(d - w) <= step / 2 + 0.0)
+    # values already on the fp8 grid come back exactly
+    grid = oracle.e4m3_decode(np.arange(0, 0x7F, 5, dtype=np.uint8))[None, :, None] * np.ones((1, 1, 2))
+    qg, _, sg = oracle.quantize_fp8(grid * 2.0 ** -4)
+    assert sg[0] == 2.0 ** -4 and np.array_equal(oracle.dequantize_fp8(qg, sg), grid * 2.0 ** -4)
