@@ -113,9 +113,12 @@ int check_router_workspace(const char* fn, int T, int H, int E, const void* ws, 
 
 // The expert forward; with perm, row s of the gate/up product reads
 // x[perm[s] / k] (gathered on load) instead of x_sorted[s].
+// s_gu / s_down non-NULL: the weights are fp8 (E4M3) with those per-expert scales.
 int swiglu_fwd(const char* fn, int H, int F, int E, int max_rows, int max_expert_rows, int dtype, const int32_t* offsets,
                const void* x_rows, const int32_t* perm, int k, const void* w_gate, const void* w_up, const void* w_down,
-               void* h_save, void* a_save, void* o_sorted, void* stream) {
+               void* h_save, void* a_save, void* o_sorted, void* stream, const float* s_gu = nullptr,
+               const float* s_down = nullptr) {
+  const bool w8 = s_gu != nullptr;
   int rc = check_expert_dims(fn, H, F, E, dtype);
   if (rc || (rc = check_rows(fn, max_rows))) return rc;
   REQUIRE(max_expert_rows >= 0, MOE_ERR_INVALID_ARGUMENT, "%s: max_expert_rows=%d is negative", fn, max_expert_rows);
@@ -135,6 +138,7 @@ int swiglu_fwd(const char* fn, int H, int F, int E, int max_rows, int max_expert
   hipStream_t s = as_stream(stream);
   auto run = [&](int mode) {
     return timed(kGemmKind[mode], s, [&] {
+      if (w8) return moe::launch_row_gemm_fp8w(mode, g, max_rows, s);
       return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, max_expert_rows, s)
                                : moe::launch_row_gemm_f32(mode, g, max_rows, s);
     });
@@ -146,6 +150,7 @@ int swiglu_fwd(const char* fn, int H, int F, int E, int max_rows, int max_expert
   g.w1 = (const uint16_t*)w_up;
   g.out0 = (uint16_t*)h_save;
   g.out1 = (uint16_t*)a_save;
+  g.wscale = s_gu;
   if ((rc = hip_status(run(moe::kGemmGateUp), fn))) return rc;
   g.a = (const uint16_t*)a_save;
   g.a_map = nullptr;
@@ -154,7 +159,89 @@ int swiglu_fwd(const char* fn, int H, int F, int E, int max_rows, int max_expert
   g.w1 = nullptr;
   g.out0 = (uint16_t*)o_sorted;
   g.out1 = nullptr;
+  g.wscale = s_down;
   return hip_status(run(moe::kGemmDown), fn);
+}
+
+// fp8 weights of one call: present, 8-byte aligned (the kernels load 8 bytes at
+// a time), scales present.
+int check_fp8_weights(const char* fn, const void* wq_gate, const void* wq_up, const void* wq_down, const float* s_gu,
+                      const float* s_down) {
+  NONNULL(wq_gate);
+  NONNULL(wq_up);
+  NONNULL(wq_down);
+  NONNULL(s_gu);
+  NONNULL(s_down);
+  REQUIRE(((uintptr_t)wq_gate | (uintptr_t)wq_up | (uintptr_t)wq_down) % 8 == 0, MOE_ERR_INVALID_ARGUMENT,
+          "%s: fp8 weights must be 8-byte aligned", fn);
+  return MOE_OK;
+}
+
+int bwd_dx(const char* fn, int T, int H, int F, int E, int k, int max_rows, int dtype, const int32_t* offsets,
+           const int32_t* inv, const void* dy, const float* topk_w, const void* h_rows, const void* w_gate,
+           const void* w_up, const void* w_down, const int32_t* inv_all, const void* o_sorted, float* dg,
+           void* dO_rows, void* dh_rows, void* dX_rows, void* dx, void* stream, const float* s_gu,
+           const float* s_down) {
+  const bool w8 = s_gu != nullptr;
+  int rc = check_routing_dims(fn, T, E, k);
+  if (rc || (rc = check_expert_dims(fn, H, F, E, dtype)) || (rc = check_rows(fn, max_rows))) return rc;
+  REQUIRE(max_rows <= T * k, MOE_ERR_INVALID_ARGUMENT, "%s: max_rows=%d exceeds T*k=%d", fn, max_rows, T * k);
+  NONNULL(offsets);
+  NONNULL(inv);
+  NONNULL(dy);
+  NONNULL(topk_w);
+  NONNULL(h_rows);
+  NONNULL(w_gate);
+  NONNULL(w_up);
+  NONNULL(w_down);
+  NONNULL(dO_rows);
+  NONNULL(dh_rows);
+  NONNULL(dX_rows);
+  NONNULL(dx);
+  if (dg != nullptr) {
+    NONNULL(inv_all);
+    NONNULL(o_sorted);
+  }
+  hipStream_t s = as_stream(stream);
+  const int es = esize_of(dtype);
+  if ((rc = hip_status(timed(MOE_K_GRAD_ROWS, s,
+                             [&] {
+                               return moe::launch_grad_rows(T, H, k, es, dy, topk_w, inv, dO_rows, inv_all, o_sorted,
+                                                            dg, s);
+                             }),
+                       fn)))
+    return rc;
+  if (max_rows > 0) {
+    moe::RowGemmArgs g{};
+    g.offsets = offsets;
+    g.E = E;
+    g.H = H;
+    g.F = F;
+    auto run = [&](int mode) {
+      return timed(kGemmKind[mode], s, [&] {
+        // rows of one expert come from distinct pairs of distinct tokens when
+        // the routing picks distinct experts per token: T bounds them
+        if (w8) return moe::launch_row_gemm_fp8w(mode, g, max_rows, s);
+        return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, std::min(max_rows, T), s)
+                                 : moe::launch_row_gemm_f32(mode, g, max_rows, s);
+      });
+    };
+    g.a = (const uint16_t*)dO_rows;
+    g.w0 = (const uint16_t*)w_down;
+    g.h = (const uint16_t*)h_rows;
+    g.out0 = (uint16_t*)dh_rows;
+    g.wscale = s_down;
+    if ((rc = hip_status(run(moe::kGemmDA), fn))) return rc;
+    g.a = (const uint16_t*)dh_rows;
+    g.w0 = (const uint16_t*)w_gate;
+    g.w1 = (const uint16_t*)w_up;
+    g.h = nullptr;
+    g.out0 = (uint16_t*)dX_rows;
+    g.wscale = s_gu;
+    if ((rc = hip_status(run(moe::kGemmDX), fn))) return rc;
+  }
+  return hip_status(timed(MOE_K_COMBINE, s, [&] { return moe::launch_combine(T, H, k, es, dX_rows, inv, nullptr, dx, s); }),
+                    fn);
 }
 
 }  // namespace
@@ -174,7 +261,7 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int moe_abi_version(void) { return 2; }
+int moe_abi_version(void) { return 3; }
 
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
   const char* fn = "moe_profile_kernel";
@@ -258,6 +345,42 @@ int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int max_expert_row
                     w_gate, w_up, w_down, h_save, a_save, o_sorted, stream);
 }
 
+int moe_grouped_swiglu_fwd_fp8w(int H, int F, int E, int k, int max_rows, const int32_t* offsets, const void* x_rows,
+                                const int32_t* perm, const uint8_t* wq_gate, const uint8_t* wq_up,
+                                const uint8_t* wq_down, const float* s_gu, const float* s_down, void* h_save,
+                                void* a_save, void* o_sorted, void* stream) {
+  const char* fn = "moe_grouped_swiglu_fwd_fp8w";
+  REQUIRE(perm == nullptr || (k >= 1 && k <= 16), MOE_ERR_INVALID_ARGUMENT, "%s: k=%d must be in 1..16", fn, k);
+  const int rc = check_fp8_weights(fn, wq_gate, wq_up, wq_down, s_gu, s_down);
+  if (rc) return rc;
+  return swiglu_fwd(fn, H, F, E, max_rows, max_rows, MOE_BF16, offsets, x_rows, perm, perm ? k : 1, wq_gate, wq_up,
+                    wq_down, h_save, a_save, o_sorted, stream, s_gu, s_down);
+}
+
+int moe_quantize_weights_fp8(int E, int64_t n0, int64_t n1, const void* w0, const void* w1, uint8_t* q0, uint8_t* q1,
+                             float* scale, void* stream) {
+  const char* fn = "moe_quantize_weights_fp8";
+  REQUIRE(E >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: E=%d must be >= 1", fn, E);
+  REQUIRE(n0 >= 8 && n0 % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: n0=%lld must be a positive multiple of 8", fn,
+          (long long)n0);
+  NONNULL(w0);
+  NONNULL(q0);
+  NONNULL(scale);
+  REQUIRE((w1 == nullptr) == (q1 == nullptr), MOE_ERR_INVALID_ARGUMENT, "%s: w1 and q1 must both be given or both be NULL",
+          fn);
+  if (w1 != nullptr)
+    REQUIRE(n1 >= 8 && n1 % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: n1=%lld must be a positive multiple of 8", fn,
+            (long long)n1);
+  else
+    REQUIRE(n1 == 0, MOE_ERR_INVALID_ARGUMENT, "%s: n1=%lld must be 0 without w1", fn, (long long)n1);
+  REQUIRE(((uintptr_t)w0 | (uintptr_t)w1) % 16 == 0 && ((uintptr_t)q0 | (uintptr_t)q1) % 8 == 0,
+          MOE_ERR_INVALID_ARGUMENT, "%s: w0/w1 must be 16-byte and q0/q1 8-byte aligned", fn);
+  REQUIRE((int64_t)E * (n0 > n1 ? n0 : n1) < ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "%s: matrices too large", fn);
+  hipStream_t s = as_stream(stream);
+  return hip_status(moe::launch_quantize_fp8(E, n0, n1, (const uint16_t*)w0, (const uint16_t*)w1, q0, q1, scale, s),
+                    fn);
+}
+
 int moe_grouped_swiglu_fwd_gather(int H, int F, int E, int k, int max_rows, int max_expert_rows, int dtype,
                                   const int32_t* offsets, const void* x, const int32_t* perm, const void* w_gate,
                                   const void* w_up, const void* w_down, void* h_save, void* a_save, void* o_sorted,
@@ -324,63 +447,20 @@ int moe_grouped_bwd_dx(int T, int H, int F, int E, int k, int max_rows, int dtyp
                        const void* w_gate, const void* w_up, const void* w_down, const int32_t* inv_all,
                        const void* o_sorted, float* dg, void* dO_rows, void* dh_rows, void* dX_rows, void* dx,
                        void* stream) {
-  const char* fn = "moe_grouped_bwd_dx";
-  int rc = check_routing_dims(fn, T, E, k);
-  if (rc || (rc = check_expert_dims(fn, H, F, E, dtype)) || (rc = check_rows(fn, max_rows))) return rc;
-  REQUIRE(max_rows <= T * k, MOE_ERR_INVALID_ARGUMENT, "%s: max_rows=%d exceeds T*k=%d", fn, max_rows, T * k);
-  NONNULL(offsets);
-  NONNULL(inv);
-  NONNULL(dy);
-  NONNULL(topk_w);
-  NONNULL(h_rows);
-  NONNULL(w_gate);
-  NONNULL(w_up);
-  NONNULL(w_down);
-  NONNULL(dO_rows);
-  NONNULL(dh_rows);
-  NONNULL(dX_rows);
-  NONNULL(dx);
-  if (dg != nullptr) {
-    NONNULL(inv_all);
-    NONNULL(o_sorted);
-  }
-  hipStream_t s = as_stream(stream);
-  const int es = esize_of(dtype);
-  if ((rc = hip_status(timed(MOE_K_GRAD_ROWS, s,
-                             [&] {
-                               return moe::launch_grad_rows(T, H, k, es, dy, topk_w, inv, dO_rows, inv_all, o_sorted,
-                                                            dg, s);
-                             }),
-                       fn)))
-    return rc;
-  if (max_rows > 0) {
-    moe::RowGemmArgs g{};
-    g.offsets = offsets;
-    g.E = E;
-    g.H = H;
-    g.F = F;
-    auto run = [&](int mode) {
-      return timed(kGemmKind[mode], s, [&] {
-        // rows of one expert come from distinct pairs of distinct tokens when
-        // the routing picks distinct experts per token: T bounds them
-        return dtype == MOE_BF16 ? moe::launch_row_gemm_bf16(mode, g, max_rows, std::min(max_rows, T), s)
-                                 : moe::launch_row_gemm_f32(mode, g, max_rows, s);
-      });
-    };
-    g.a = (const uint16_t*)dO_rows;
-    g.w0 = (const uint16_t*)w_down;
-    g.h = (const uint16_t*)h_rows;
-    g.out0 = (uint16_t*)dh_rows;
-    if ((rc = hip_status(run(moe::kGemmDA), fn))) return rc;
-    g.a = (const uint16_t*)dh_rows;
-    g.w0 = (const uint16_t*)w_gate;
-    g.w1 = (const uint16_t*)w_up;
-    g.h = nullptr;
-    g.out0 = (uint16_t*)dX_rows;
-    if ((rc = hip_status(run(moe::kGemmDX), fn))) return rc;
-  }
-  return hip_status(timed(MOE_K_COMBINE, s, [&] { return moe::launch_combine(T, H, k, es, dX_rows, inv, nullptr, dx, s); }),
-                    fn);
+  return bwd_dx("moe_grouped_bwd_dx", T, H, F, E, k, max_rows, dtype, offsets, inv, dy, topk_w, h_rows, w_gate, w_up,
+                w_down, inv_all, o_sorted, dg, dO_rows, dh_rows, dX_rows, dx, stream, nullptr, nullptr);
+}
+
+int moe_grouped_bwd_dx_fp8w(int T, int H, int F, int E, int k, int max_rows, const int32_t* offsets,
+                            const int32_t* inv, const void* dy, const float* topk_w, const void* h_rows,
+                            const uint8_t* wq_gate, const uint8_t* wq_up, const uint8_t* wq_down, const float* s_gu,
+                            const float* s_down, const int32_t* inv_all, const void* o_sorted, float* dg,
+                            void* dO_rows, void* dh_rows, void* dX_rows, void* dx, void* stream) {
+  const char* fn = "moe_grouped_bwd_dx_fp8w";
+  const int rc = check_fp8_weights(fn, wq_gate, wq_up, wq_down, s_gu, s_down);
+  if (rc) return rc;
+  return bwd_dx(fn, T, H, F, E, k, max_rows, MOE_BF16, offsets, inv, dy, topk_w, h_rows, wq_gate, wq_up, wq_down,
+                inv_all, o_sorted, dg, dO_rows, dh_rows, dX_rows, dx, stream, s_gu, s_down);
 }
 
 int moe_grouped_bwd_dw(int H, int F, int E, int max_rows, int dtype, const int32_t* offsets, const void* x_rows,

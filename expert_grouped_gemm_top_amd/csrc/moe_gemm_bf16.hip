@@ -81,6 +81,37 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 first, u32x4 second, f32x4 acc)
                                                   acc, 0, 0, 0);
 }
 
+// 8 fp8 (E4M3) weights -> 8 bf16, exactly (an E4M3 value has at most 4
+// significant bits): the hardware conversion to fp32, then the upper half of
+// each fp32.  Element order is kept: byte b of the input is element b.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 q) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[h], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[h], true);
+    r[2 * h] = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
+    r[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+  }
+  return r;
+}
+
+// Weight element and 8-element load of the streaming kernel: bf16, or fp8
+// bytes widened to bf16 just before use.
+template <bool W8>
+struct WeightFmt {
+  using Elem = uint16_t;
+  using Vec = u32x4;
+  static __device__ __forceinline__ u32x4 widen(u32x4 v) { return v; }
+};
+template <>
+struct WeightFmt<true> {
+  using Elem = uint8_t;
+  using Vec = u32x2;
+  static __device__ __forceinline__ u32x4 widen(u32x2 v) { return fp8x8_to_bf16(v); }
+};
+
 // ---- row GEMMs --------------------------------------------------------------
 // N-contiguous weights (GATEUP, DOWN): a wave covers 128 output columns; per
 // K-step of 32 a lane loads 8 rows x 16 B, so one load instruction reads 4 rows
@@ -114,11 +145,18 @@ __host__ __device__ inline int row_gemm_blocks(int H, int F) {
 // into S parts run by S waves; the partial sums of parts 1.. are added to part
 // 0's through LDS in part order.  That multiplies the waves streaming weights
 // when there are too few tiles to fill the chip.
-template <int MODE>
+//
+// W8: the weights are fp8 (E4M3) bytes, widened to bf16 in registers right
+// before the MFMA, and the products of expert e are scaled by g.wscale[e]; the
+// kernel then takes every expert, whatever its row count.
+template <int MODE, bool W8>
 __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s_start, int* s_off, int* s_tmp,
                                             unsigned char* lds) {
   constexpr bool NN = RowGemmShape<MODE>::kNN;
-  build_tile_starts(g.offsets, g.E, kTileRows, s_start, s_off, s_tmp, 0, kBigRows);
+  using WF = WeightFmt<W8>;
+  using WE = typename WF::Elem;
+  using WV = typename WF::Vec;
+  build_tile_starts(g.offsets, g.E, kTileRows, s_start, s_off, s_tmp, 0, W8 ? kNoBigTiles : kBigRows);
 
   const int H = g.H, F = g.F;
   const int nblk = row_gemm_blocks<MODE>(H, F);
@@ -154,32 +192,36 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
 
   if constexpr (NN) {
     // B operand: lane c reads columns [col, col+8) of rows k0 + 8gq + (0..7)
-    const uint16_t* b_ptr;
+    const WE* b_ptr;
     size_t ldb;
     if (MODE == kGemmGateUp) {
       // even lanes read W_gate, odd lanes W_up, at the same 8 features f
-      const uint16_t* W = (c & 1) ? g.w1 : g.w0;
+      const WE* W = (const WE*)((c & 1) ? g.w1 : g.w0);
       b_ptr = W + (size_t)e * H * F + nb * 64 + 8 * (c >> 1);
       ldb = F;
     } else {
-      b_ptr = g.w0 + (size_t)e * F * H + nb * 128 + 8 * c;
+      b_ptr = (const WE*)g.w0 + (size_t)e * F * H + nb * 128 + 8 * c;
       ldb = H;
     }
     b_ptr += (size_t)(k_begin + 8 * gq) * ldb;
     const uint16_t* a_ptr = a_row + 8 * gq;
     const int steps = Kp / 32, last = steps - 1;
-    auto load = [&](int s, u32x4* bq, u32x4& aq) {
-      const uint16_t* bp = b_ptr + (size_t)s * 32 * ldb;
+    auto load = [&](int s, WV* bq, u32x4& aq) {
+      const WE* bp = b_ptr + (size_t)s * 32 * ldb;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) bq[r] = *(const u32x4*)(bp + (size_t)r * ldb);
+      for (int r = 0; r < 8; ++r) bq[r] = *(const WV*)(bp + (size_t)r * ldb);
       aq = *(const u32x4*)(a_ptr + (size_t)s * 32);
     };
-    auto compute = [&](const u32x4* bq, const u32x4& aq) {
+    auto compute = [&](const WV* bq, const u32x4& aq) {
       const u32x4 av = a_ok ? aq : zero4;
+      u32x4 bw[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) acc[jj] = mfma_bf16(column_of_8x8(bq, jj), av, acc[jj]);
+      for (int r = 0; r < 8; ++r) bw[r] = WF::widen(bq[r]);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) acc[jj] = mfma_bf16(column_of_8x8(bw, jj), av, acc[jj]);
     };
-    u32x4 b0[8], b1[8], b2[8], a0, a1, a2;
+    WV b0[8], b1[8], b2[8];
+    u32x4 a0, a1, a2;
     load(0, b0, a0);
     load(min(1, last), b1, a1);
     for (int s = 0; s < steps; s += 3) {
@@ -204,37 +246,37 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
     // rows c + 16 jj, k chunks 4 gq + q, matching its activation chunks.
     // LDS operations of one wave complete in order, so no barrier is needed.
     const int lrow = l >> 4, lchunk = l & 15;
-    const uint16_t* w_lo;  // rows for k in [0, Kw)
-    const uint16_t* w_hi;  // DX only: rows for k in [F, 2F)
+    const WE* w_lo;  // rows for k in [0, Kw)
+    const WE* w_hi;  // DX only: rows for k in [F, 2F)
     size_t ldw;
     int Kw;
     if (MODE == kGemmDA) {
-      w_lo = g.w0 + (size_t)e * F * H + (size_t)(nb * 64 + lrow) * H + 8 * lchunk;
+      w_lo = (const WE*)g.w0 + (size_t)e * F * H + (size_t)(nb * 64 + lrow) * H + 8 * lchunk;
       w_hi = w_lo;
       ldw = H;
       Kw = K;
     } else {
-      w_lo = g.w0 + (size_t)e * H * F + (size_t)(nb * 64 + lrow) * F + 8 * lchunk;
-      w_hi = g.w1 + (size_t)e * H * F + (size_t)(nb * 64 + lrow) * F + 8 * lchunk;
+      w_lo = (const WE*)g.w0 + (size_t)e * H * F + (size_t)(nb * 64 + lrow) * F + 8 * lchunk;
+      w_hi = (const WE*)g.w1 + (size_t)e * H * F + (size_t)(nb * 64 + lrow) * F + 8 * lchunk;
       ldw = F;
       Kw = F;
     }
     unsigned char* xs = lds + w * 16384;
     const uint16_t* a_ptr = a_row + 32 * gq;
     const int stages = Kp / 128, last = stages - 1;
-    auto load = [&](int s, u32x4* bq, u32x4* aq) {
+    auto load = [&](int s, WV* bq, u32x4* aq) {
       const int k0 = k_begin + s * 128;  // stages never straddle Kw (Kw % 128 == 0)
-      const uint16_t* wp = (k0 < Kw) ? w_lo + k0 : w_hi + (k0 - Kw);
+      const WE* wp = (k0 < Kw) ? w_lo + k0 : w_hi + (k0 - Kw);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) bq[i] = *(const u32x4*)(wp + (size_t)(4 * i) * ldw);
+      for (int i = 0; i < 16; ++i) bq[i] = *(const WV*)(wp + (size_t)(4 * i) * ldw);
 #pragma unroll
       for (int q = 0; q < 4; ++q) aq[q] = *(const u32x4*)(a_ptr + (size_t)s * 128 + 8 * q);
     };
-    auto compute = [&](const u32x4* bq, const u32x4* aq) {
+    auto compute = [&](const WV* bq, const u32x4* aq) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 4 * i + lrow;
-        *(u32x4*)(xs + row * 256 + 16 * (lchunk ^ (row & 15))) = bq[i];
+        *(u32x4*)(xs + row * 256 + 16 * (lchunk ^ (row & 15))) = WF::widen(bq[i]);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -246,7 +288,8 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
         }
       }
     };
-    u32x4 b0[16], b1[16], a0[4], a1[4];
+    WV b0[16], b1[16];
+    u32x4 a0[4], a1[4];
     load(0, b0, a0);
     for (int s = 0; s < stages; s += 2) {
       load(min(s + 1, last), b1, a1);
@@ -276,6 +319,13 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
 #pragma unroll
       for (int j = 0; j < NACC; ++j) acc[j] = acc[j] + red[j * kWave + l];
     }
+  }
+
+  if constexpr (W8) {  // the weights' scale: a power of two, so the product is exact
+    constexpr int NACC = NN ? 8 : 4;
+    const float sc = g.wscale[e];
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) acc[j] = acc[j] * sc;
   }
 
   // epilogue straight from registers: lane (c, gq) owns tile row c
@@ -614,12 +664,55 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, in
   __shared__ __attribute__((aligned(16))) uint16_t s_ab[2 * kTBM * kTPitch + 2 * kTBN * kTPitch];
   static_assert(sizeof(s_ab) == 4 * 16384, "streaming kernel: 16 KiB of LDS per wave");
   if ((int)blockIdx.x < n_stream)
-    stream_gemm<MODE>(g, blockIdx.x, s_start, s_off, s_tmp, reinterpret_cast<unsigned char*>(s_ab));
+    stream_gemm<MODE, false>(g, blockIdx.x, s_start, s_off, s_tmp, reinterpret_cast<unsigned char*>(s_ab));
   else
     tile_gemm<MODE>(g, blockIdx.x - n_stream, s_start, s_off, s_tmp, s_ab, s_ab + 2 * kTBM * kTPitch);
 }
 
+// fp8 weights: every expert on the streaming kernel (one wave per 16-row tile
+// and column block), so weight bytes are read once per 16 rows.
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void row_gemm_fp8w_kernel(RowGemmArgs g) {
+  __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
+  __shared__ __attribute__((aligned(16))) unsigned char s_lds[4 * 16384];  // 16 KiB per wave
+  stream_gemm<MODE, true>(g, blockIdx.x, s_start, s_off, s_tmp, s_lds);
+}
+
+// Reduction split of the streaming kernel for this product and row count.
+template <int MODE>
+int stream_split(const RowGemmArgs& g, int64_t N) {
+  const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? g.H : (MODE == kGemmDown ? g.F : 2 * g.F);
+  const int kstep = RowGemmShape<MODE>::kNN ? 32 : 128;  // whole K-steps in each part
+  // decode-sized batches (a handful of rows in all) have too few tiles to keep
+  // the chip's memory busy: split every product four ways
+  int ks = N < kFewRows ? 4 : (MOE_STREAM_SPLITK >> (4 * MODE)) & 0xf;
+  while (ks > 1 && (K % (ks * kstep) != 0 || row_gemm_blocks<MODE>(g.H, g.F) % (4 / ks) != 0)) ks /= 2;
+  return ks;
+}
+
 }  // namespace
+
+template <int MODE>
+hipError_t launch_row_gemm_fp8w_mode(const RowGemmArgs& args, int max_rows, hipStream_t stream) {
+  RowGemmArgs g = args;
+  g.big_min_rows = kNoBigTiles;
+  const int64_t N = max_rows, E = g.E;
+  const int64_t tiles = (N + E * (kTileRows - 1)) / kTileRows;
+  g.stream_ksplit = stream_split<MODE>(g, N);
+  const int64_t grid = (tiles * row_gemm_blocks<MODE>(g.H, g.F) * g.stream_ksplit + 3) / 4;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_gemm_fp8w_kernel<MODE>, dim3((unsigned)grid), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_gemm_fp8w(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream) {
+  switch (mode) {
+    case kGemmGateUp: return launch_row_gemm_fp8w_mode<kGemmGateUp>(g, max_rows, stream);
+    case kGemmDown: return launch_row_gemm_fp8w_mode<kGemmDown>(g, max_rows, stream);
+    case kGemmDA: return launch_row_gemm_fp8w_mode<kGemmDA>(g, max_rows, stream);
+    default: return launch_row_gemm_fp8w_mode<kGemmDX>(g, max_rows, stream);
+  }
+}
 
 template <int MODE>
 hipError_t launch_row_gemm_mode(const RowGemmArgs& args, int max_rows, int max_expert_rows, hipStream_t stream) {
@@ -630,15 +723,7 @@ hipError_t launch_row_gemm_mode(const RowGemmArgs& args, int max_rows, int max_e
   // streaming kernel: experts with n_e < kBigRows, ceil(n_e / 16) tiles each
   const int64_t small_tiles = std::min<int64_t>((N + E * (kTileRows - 1)) / kTileRows,
                                                  E * ((kBigRows - 1 + kTileRows - 1) / kTileRows));
-  // reduction split of the streaming kernel: needs whole K-steps (NN: 32,
-  // K-contiguous: 128) in each half
-  const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? g.H : (MODE == kGemmDown ? g.F : 2 * g.F);
-  const int kstep = RowGemmShape<MODE>::kNN ? 32 : 128;
-  // decode-sized batches (a handful of rows in all) have too few tiles to keep
-  // the chip's memory busy: split every product four ways
-  int ks = N < kFewRows ? 4 : (MOE_STREAM_SPLITK >> (4 * MODE)) & 0xf;
-  while (ks > 1 && (K % (ks * kstep) != 0 || row_gemm_blocks<MODE>(g.H, g.F) % (4 / ks) != 0)) ks /= 2;
-  g.stream_ksplit = ks;
+  g.stream_ksplit = stream_split<MODE>(g, N);
   const int64_t n_stream = (small_tiles * row_gemm_blocks<MODE>(g.H, g.F) * g.stream_ksplit + 3) / 4;
   // tiled kernel: experts with kBigRows <= n_e < g.big_min_rows, ceil(n_e / 128) tiles each
   const int64_t big_experts = std::min<int64_t>(E, N / kBigRows);

@@ -37,6 +37,10 @@ struct RowGemmArgs {
   int a_div;
   int big_min_rows;   // set by launch_row_gemm_bf16: experts from this row count take the 256-row kernel
   int stream_ksplit;  // set by launch_row_gemm_bf16: reduction split of the skinny-expert kernel (1, 2 or 4)
+  // fp8 weights (launch_row_gemm_fp8w): w0 / w1 point at E4M3 bytes, and every
+  // product of expert e is multiplied by wscale[e] (the scale of the weights
+  // it reads)
+  const float* wscale;
 };
 
 struct DwArgs {
@@ -80,6 +84,13 @@ hipError_t launch_gather_rows(const int32_t* R_ptr, const int32_t* src, int max_
 hipError_t launch_row_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, int max_expert_rows,
                                 hipStream_t stream);
 hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream);
+// Row GEMMs with fp8 (E4M3) weights and bf16 activations: every expert, whatever
+// its row count, on the streaming kernel.
+hipError_t launch_row_gemm_fp8w(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
+// Per-expert fp8 storage of w0 [E][n0] and w1 [E][n1] (w1 may be NULL) with one
+// power-of-two scale per expert.
+hipError_t launch_quantize_fp8(int E, int64_t n0, int64_t n1, const uint16_t* w0, const uint16_t* w1, uint8_t* q0,
+                               uint8_t* q1, float* scale, hipStream_t stream);
 hipError_t launch_big_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
 // Row count from which an expert takes the 256-row kernel for this product and
 // shape; kNoBigTiles where that kernel does not apply.

@@ -84,9 +84,10 @@ class MoeLayerBuffers:
             self.router_ws = em(max(moe.moe_router_workspace_bytes(T, H, E), 16), dt=torch.uint8)
 
     # ------------------------------------------------------------------ forward
-    def forward(self, logits, x, w_gate, w_up, w_down, stream=None, w_r=None):
+    def forward(self, logits, x, w_gate, w_up, w_down, stream=None, w_r=None, wq=None):
         """With w_r (a layer built with router=True) the logits are x W_r and
-        the `logits` argument is ignored."""
+        the `logits` argument is ignored.  With wq (moe.Fp8Weights of the same
+        frozen weights) the expert GEMMs read the fp8 copy."""
         if w_r is not None:
             moe.moe_router_fwd(x, w_r, self.logits, self.router_ws, stream)
             logits = self.logits
@@ -95,7 +96,12 @@ class MoeLayerBuffers:
         g = self.gather_rows  # index-only dispatch: the forward gathers x rows itself
         moe.moe_dispatch(self.topk_idx, None if g else x, self.counts, self.offsets, self.perm, self.inv_perm,
                          None if g else self.x_sorted, self.ws, self.E, stream)
-        if self.gather_rows:
+        if wq is not None:
+            assert self.keep_graph, "the fp8 path keeps the pre-activations"
+            moe.moe_grouped_swiglu_fwd_fp8w(self.offsets, x if g else self.x_sorted, wq, self.h_save, self.a_save,
+                                            self.o_sorted, self.N, perm=self.perm if g else None, k=self.k,
+                                            stream=stream)
+        elif self.gather_rows:
             moe.moe_grouped_swiglu_fwd_gather(self.offsets, x, self.perm, w_gate, w_up, w_down, self.h_save,
                                               self.a_save, self.o_sorted, self.k, self.N, max_expert_rows=self.T,
                                               stream=stream)
@@ -115,7 +121,7 @@ class MoeLayerBuffers:
                               self.x_kept, self.a_kept if self.dw else None, self.h_kept if kg else None, stream,
                               cap=self.quota_cap)
 
-    def backward(self, dy, w_gate, w_up, w_down, score=None, stream=None, w_r=None):
+    def backward(self, dy, w_gate, w_up, w_down, score=None, stream=None, w_r=None, wq=None):
         """dx (+ dg) and, for full fine-tuning, dW.  With a quota the backward
         runs on the compacted retained pairs; score: a pair-indexed fp32 tensor,
         None (the routing weights) or "metric" (moe_pair_scores: the norm of
@@ -134,9 +140,15 @@ class MoeLayerBuffers:
         if not self.keep_graph:  # recompute [hg | hu] of the backward's rows
             moe.moe_grouped_swiglu_recompute(offsets, x_rows, w_gate, w_up, h_rows, None, self.R,
                                              max_expert_rows=self.T, stream=stream)
-        moe.moe_grouped_bwd_dx(offsets, inv, dy, self.topk_w, h_rows, w_gate, w_up, w_down, self.dO, self.dh,
-                               self.dX, self.dx, self.R, inv_all=self.inv_perm if self.want_dg else None,
-                               o_sorted=self.o_sorted if self.want_dg else None, dg=self.dg, stream=stream)
+        extra = dict(inv_all=self.inv_perm if self.want_dg else None, o_sorted=self.o_sorted if self.want_dg else None,
+                     dg=self.dg, stream=stream)
+        if wq is not None:  # frozen fp8 weights: no weight gradient
+            assert not self.dw, "fp8 weights are frozen: no dW"
+            moe.moe_grouped_bwd_dx_fp8w(offsets, inv, dy, self.topk_w, h_rows, wq, self.dO, self.dh, self.dX,
+                                        self.dx, self.R, **extra)
+        else:
+            moe.moe_grouped_bwd_dx(offsets, inv, dy, self.topk_w, h_rows, w_gate, w_up, w_down, self.dO, self.dh,
+                                   self.dX, self.dx, self.R, **extra)
         if self.dw:
             moe.moe_grouped_bwd_dw(offsets, x_rows, a_rows, self.dO, self.dh, self.dw_gate, self.dw_up,
                                    self.dw_down, self.R, stream)

@@ -46,6 +46,9 @@ _SIGS = {
     "moe_compact_pairs_cap": ([_i, _i, _i, _i, _i, _i, _i] + [_vp] * 16, _i),
     "moe_quota_cap_for_budget": ([_i, _i, _i, _i, _i, _i, _i, _i, _sz], _i64),
     "moe_pair_scores": ([_i, _i, _i, _i, _i] + [_vp] * 6, _i),
+    "moe_quantize_weights_fp8": ([_i, _i64, _i64] + [_vp] * 6, _i),
+    "moe_grouped_swiglu_fwd_fp8w": ([_i] * 5 + [_vp] * 12, _i),
+    "moe_grouped_bwd_dx_fp8w": ([_i] * 6 + [_vp] * 18, _i),
 }
 
 
@@ -184,6 +187,69 @@ def moe_grouped_swiglu_fwd(offsets, x_sorted, w_gate, w_up, w_down, h_save, a_sa
         _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F), _ptr(w_down, "w_down", d, E * F * H),
         _ptr(h_save, "h_save", d, R * 2 * F, allow_none=True), _ptr(a_save, "a_save", d, R * F),
         _ptr(o_sorted, "o_sorted", d, R * H), _stream(stream)))
+
+
+class Fp8Weights:
+    """Frozen expert weights stored once in fp8 (E4M3) by moe_quantize_weights_fp8:
+    codes q_gate/q_up [E,H,F], q_down [E,F,H] (uint8) and per-expert fp32 scales
+    s_gu (shared by W_gate and W_up) and s_down [E]."""
+
+    def __init__(self, w_gate, w_up, w_down, stream=None):
+        E, H, F = w_gate.shape
+        if w_gate.dtype != torch.bfloat16:
+            raise MoeError("fp8 storage is made from bf16 weights")
+        dev = w_gate.device
+        self.E, self.H, self.F = E, H, F
+        self.q_gate = torch.empty(E, H, F, dtype=torch.uint8, device=dev)
+        self.q_up = torch.empty(E, H, F, dtype=torch.uint8, device=dev)
+        self.q_down = torch.empty(E, F, H, dtype=torch.uint8, device=dev)
+        self.s_gu = torch.empty(E, dtype=F32, device=dev)
+        self.s_down = torch.empty(E, dtype=F32, device=dev)
+        moe_quantize_weights_fp8(w_gate, w_up, self.q_gate, self.q_up, self.s_gu, stream)
+        moe_quantize_weights_fp8(w_down, None, self.q_down, None, self.s_down, stream)
+
+
+def moe_quantize_weights_fp8(w0, w1, q0, q1, scale, stream=None):
+    E = w0.shape[0]
+    n0 = w0.numel() // E
+    n1 = 0 if w1 is None else w1.numel() // E
+    U8 = torch.uint8
+    _check(lib().moe_quantize_weights_fp8(
+        E, n0, n1, _ptr(w0, "w0", torch.bfloat16, E * n0), _ptr(w1, "w1", torch.bfloat16, E * n1, allow_none=True),
+        _ptr(q0, "q0", U8, E * n0), _ptr(q1, "q1", U8, E * n1, allow_none=w1 is None), _ptr(scale, "scale", F32, E),
+        _stream(stream)))
+
+
+def moe_grouped_swiglu_fwd_fp8w(offsets, x_rows, wq: Fp8Weights, h_save, a_save, o_sorted, max_rows: int,
+                                perm=None, k: int = 1, stream=None):
+    """x_rows: x_sorted, or with perm the token matrix x [T, H] (rows gathered on load)."""
+    E, H, F = wq.E, wq.H, wq.F
+    d, U8, R = torch.bfloat16, torch.uint8, max_rows
+    _check(lib().moe_grouped_swiglu_fwd_fp8w(
+        H, F, E, k, R, _ptr(offsets, "offsets", I32, E + 1),
+        _ptr(x_rows, "x_rows", d, (R // k) * H if perm is not None else R * H),
+        _ptr(perm, "perm", I32, R, allow_none=True),
+        _ptr(wq.q_gate, "q_gate", U8, E * H * F), _ptr(wq.q_up, "q_up", U8, E * H * F),
+        _ptr(wq.q_down, "q_down", U8, E * F * H), _ptr(wq.s_gu, "s_gu", F32, E), _ptr(wq.s_down, "s_down", F32, E),
+        _ptr(h_save, "h_save", d, R * 2 * F, allow_none=True), _ptr(a_save, "a_save", d, R * F),
+        _ptr(o_sorted, "o_sorted", d, R * H), _stream(stream)))
+
+
+def moe_grouped_bwd_dx_fp8w(offsets, inv, dy, topk_w, h_rows, wq: Fp8Weights, dO_rows, dh_rows, dX_rows, dx,
+                            max_rows: int, inv_all=None, o_sorted=None, dg=None, stream=None):
+    T, H = dy.shape
+    E, F = wq.E, wq.F
+    k = topk_w.shape[1]
+    d, U8, R, N = torch.bfloat16, torch.uint8, max_rows, T * k
+    _check(lib().moe_grouped_bwd_dx_fp8w(
+        T, H, F, E, k, R, _ptr(offsets, "offsets", I32, E + 1), _ptr(inv, "inv", I32, N),
+        _ptr(dy, "dy", d, T * H), _ptr(topk_w, "topk_w", F32, N), _ptr(h_rows, "h_rows", d, R * 2 * F),
+        _ptr(wq.q_gate, "q_gate", U8, E * H * F), _ptr(wq.q_up, "q_up", U8, E * H * F),
+        _ptr(wq.q_down, "q_down", U8, E * F * H), _ptr(wq.s_gu, "s_gu", F32, E), _ptr(wq.s_down, "s_down", F32, E),
+        _ptr(inv_all, "inv_all", I32, N, allow_none=dg is None),
+        _ptr(o_sorted, "o_sorted", d, N * H, allow_none=dg is None), _ptr(dg, "dg", F32, N, allow_none=True),
+        _ptr(dO_rows, "dO_rows", d, R * H), _ptr(dh_rows, "dh_rows", d, R * 2 * F), _ptr(dX_rows, "dX_rows", d, R * H),
+        _ptr(dx, "dx", d, T * H), _stream(stream)))
 
 
 def moe_grouped_swiglu_fwd_gather(offsets, x, perm, w_gate, w_up, w_down, h_save, a_save, o_sorted, k: int,

@@ -24,6 +24,9 @@
  *   moe_grouped_bwd_dw      expert weight gradients (full fine-tuning)
  *   moe_router_bwd          router gradients (logits, W_r, the router's share
  *                           of dx) from the routing-weight gradient
+ *   moe_quantize_weights_fp8, moe_grouped_swiglu_fwd_fp8w,
+ *   moe_grouped_bwd_dx_fp8w frozen expert weights stored once in fp8 (E4M3),
+ *                           and the forward and dx backward reading them
  *
  * Conventions for every call:
  *  - Pointers marked (device) are device pointers owned by the caller; the
@@ -69,7 +72,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 const char* moe_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);
-/* ABI version, currently 2. */
+/* ABI version, currently 3. */
 int moe_abi_version(void);
 
 /* Kernels that moe_profile_kernel can bracket with events. */
@@ -220,6 +223,51 @@ int moe_grouped_bwd_dx(int T, int H, int F, int E, int k, int max_rows, int dtyp
                        const void* w_up, const void* w_down, const int32_t* inv_all,
                        const void* o_sorted, float* dg, void* dO_rows, void* dh_rows,
                        void* dX_rows, void* dx, void* stream);
+
+/* ---- fp8 storage of frozen expert weights --------------------------------
+ * In the LoRA step the experts are frozen (issue #14, Scope) and their weights
+ * stay resident on the device (issue #14, Proposal), so they can be stored once
+ * in 8 bits; the GEMMs then read half the weight bytes, which is what bounds
+ * them when experts have few rows.  Element format: OCP 8-bit floating point
+ * E4M3 (bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN,
+ * largest finite 448).  Every expert has one power-of-two scale s: the
+ * smallest with amax <= 448 s over all of that expert's matrices quantized
+ * together (W_gate and W_up share one scale; W_down has its own).  The stored
+ * code is E4M3(w / s), rounded to nearest with ties to the even mantissa
+ * (w / s is exact); the weight the GEMMs use is decode(code) * s, exactly. */
+
+/* Quantize E experts' bf16 matrices w0 [E][n0] and, when given, w1 [E][n1]
+ * with one scale per expert shared by both: q0 [E][n0], q1 [E][n1] uint8
+ * codes and scale [E] fp32 (device, out).  n0, n1 multiples of 8 (n1 = 0 and
+ * w1 = q1 = NULL for a single matrix); w0/w1 16-byte aligned, q0/q1 8-byte
+ * aligned (device).  One workgroup per expert; run once per set of weights. */
+int moe_quantize_weights_fp8(int E, int64_t n0, int64_t n1, const void* w0, const void* w1, uint8_t* q0,
+                             uint8_t* q1, float* scale, void* stream);
+
+/* moe_grouped_swiglu_fwd with fp8 weights: wq_gate/wq_up [E, H, F] and
+ * wq_down [E, F, H] E4M3 codes (device, 8-byte aligned) with per-expert scales
+ * s_gu (of W_gate and W_up) and s_down [E] fp32 (device), as written by
+ * moe_quantize_weights_fp8.  Activations and outputs are bf16.  perm = NULL:
+ * x_rows is x_sorted [rows, H]; otherwise x_rows is x [T, H] and row s reads
+ * x[perm[s] / k] (as moe_grouped_swiglu_fwd_gather).  Every expert, whatever
+ * its row count, runs on the weight-streaming kernel (16-row tiles), the
+ * regime where the weight bytes bound the GEMM.  The products are exactly
+ * those of moe_grouped_swiglu_fwd on the decoded weights decode(q) * s, up to
+ * the order of the fp32 sums. */
+int moe_grouped_swiglu_fwd_fp8w(int H, int F, int E, int k, int max_rows, const int32_t* offsets,
+                                const void* x_rows, const int32_t* perm, const uint8_t* wq_gate,
+                                const uint8_t* wq_up, const uint8_t* wq_down, const float* s_gu,
+                                const float* s_down, void* h_save, void* a_save, void* o_sorted,
+                                void* stream);
+
+/* moe_grouped_bwd_dx with fp8 weights (arguments as there, dtype bf16, and the
+ * weights as in moe_grouped_swiglu_fwd_fp8w). */
+int moe_grouped_bwd_dx_fp8w(int T, int H, int F, int E, int k, int max_rows, const int32_t* offsets,
+                            const int32_t* inv, const void* dy, const float* topk_w, const void* h_rows,
+                            const uint8_t* wq_gate, const uint8_t* wq_up, const uint8_t* wq_down,
+                            const float* s_gu, const float* s_down, const int32_t* inv_all,
+                            const void* o_sorted, float* dg, void* dO_rows, void* dh_rows, void* dX_rows,
+                            void* dx, void* stream);
 
 /* Expert weight gradients (issue #14, Scope: dW for full fine-tuning), over the
  * rows r of each expert e (all pairs or the retained ones):

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(LIB)
     missing = [n for n in declared_functions() if not hasattr(raw, n)]
     assert not missing, missing
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def _err(lib):
@@ -150,3 +150,30 @@ def test_quota_metric_calls(lib):
     s = lib.moe_pair_scores
     assert s(64, 128, 64, 2, 1, P, P, P, P, NULL, NULL) == 1 and "score" in _err(lib)
     assert s(64, 100, 64, 2, 1, P, P, P, P, P, NULL) == 2
+
+
+def test_fp8_weight_calls_validation(lib):
+    A = ctypes.c_void_p(64)  # aligned dummies
+    q = lib.moe_quantize_weights_fp8
+    assert q(0, 64, 0, A, NULL, A, NULL, A, NULL) == 1
+    assert q(4, 60, 0, A, NULL, A, NULL, A, NULL) == 2 and "multiple of 8" in _err(lib)
+    assert q(4, 64, 64, A, NULL, A, NULL, A, NULL) == 1 and "n1" in _err(lib)
+    assert q(4, 64, 64, A, A, A, NULL, A, NULL) == 1 and "both" in _err(lib)
+    assert q(4, 64, 0, ctypes.c_void_p(72), NULL, A, NULL, A, NULL) == 1 and "aligned" in _err(lib)
+    assert q(4, 64, 0, A, NULL, A, NULL, NULL, NULL) == 1 and "scale" in _err(lib)
+    f = lib.moe_grouped_swiglu_fwd_fp8w
+    ok = [2048, 768, 128, 8, 1024, A, A, NULL, A, A, A, A, A, A, A, A, NULL]
+    bad = list(ok); bad[11] = NULL
+    assert f(*bad) == 1 and "s_gu" in _err(lib)
+    bad = list(ok); bad[8] = ctypes.c_void_p(68)
+    assert f(*bad) == 1 and "aligned" in _err(lib)
+    bad = list(ok); bad[1] = 700
+    assert f(*bad) == 2
+    bad = list(ok); bad[7] = A; bad[3] = 0
+    assert f(*bad) == 1 and "k=" in _err(lib)
+    d = lib.moe_grouped_bwd_dx_fp8w
+    ok = [128, 2048, 768, 128, 8, 1024] + [A] * 17 + [NULL]
+    bad = list(ok); bad[15] = NULL
+    assert d(*bad) == 1 and "s_down" in _err(lib)
+    bad = list(ok); bad[5] = 2000
+    assert d(*bad) == 1 and "max_rows" in _err(lib)
