@@ -62,6 +62,9 @@ def parse():
                         "routing weight")
     p.add_argument("--budget-mib", type=int, default=0,
                    help="compacted workloads: quota from this memory budget for the backward's rows instead of rho")
+    p.add_argument("--fp8-weights", action="store_true",
+                   help="frozen expert weights stored once in fp8 (E4M3, one power-of-two scale per expert) and read "
+                        "by the GEMMs (LoRA and forward-only workloads; not the headline configuration)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after the timed steps, run one plain elementwise copy of this many MiB (read and write "
                         "each) so that HBM byte counters can be calibrated against a kernel of known traffic")
@@ -108,11 +111,13 @@ def measured_traffic(kernel, workload):
     return int(m_b.group(1))
 
 
-def algorithmic(wl, counts, kept_counts=None, gathered=False):
+def algorithmic(wl, counts, kept_counts=None, gathered=False, weight_bytes=None):
     """Per-kernel algorithmic bytes and flops (real rows only, no padding).
     gathered: the gate/up product reads token rows [T,H] through perm instead of
-    the materialized x_sorted [N,H]."""
+    the materialized x_sorted [N,H].  weight_bytes: bytes per expert-weight
+    element when it differs from the activations' (1 for fp8 weights)."""
     b = 2 if wl.dtype == "bf16" else 4
+    wb = b if weight_bytes is None else weight_bytes
     H, F, T, k = wl.H, wl.F, wl.T, wl.k
     N = wl.N
     Ea = int((counts > 0).sum())
@@ -120,13 +125,13 @@ def algorithmic(wl, counts, kept_counts=None, gathered=False):
     Ea_b = int((kept_counts > 0).sum()) if kept_counts is not None else Ea
     return {
         K_DISPATCH_ROWS: (T * H * b + N * H * b + 4 * N, 0.0),
-        K_GATEUP: (2 * H * F * b * Ea + (T * H * b + 4 * N if gathered else N * H * b) + N * 2 * F * b + N * F * b,
+        K_GATEUP: (2 * H * F * wb * Ea + (T * H * b + 4 * N if gathered else N * H * b) + N * 2 * F * b + N * F * b,
                    4.0 * H * F * N),
-        K_DOWN: (H * F * b * Ea + N * F * b + N * H * b, 2.0 * H * F * N),
+        K_DOWN: (H * F * wb * Ea + N * F * b + N * H * b, 2.0 * H * F * N),
         K_COMBINE: (N * H * b + 8 * N + T * H * b, 0.0),
         K_GRAD_ROWS: (T * H * b + R * H * b + 8 * N + N * H * b, 0.0),
-        K_DA: (H * F * b * Ea_b + R * H * b + 2 * R * 2 * F * b, 2.0 * H * F * R),
-        K_DX: (2 * H * F * b * Ea_b + R * 2 * F * b + R * H * b, 4.0 * H * F * R),
+        K_DA: (H * F * wb * Ea_b + R * H * b + 2 * R * 2 * F * b, 2.0 * H * F * R),
+        K_DX: (2 * H * F * wb * Ea_b + R * 2 * F * b + R * H * b, 4.0 * H * F * R),
         K_DW: (R * (2 * H + 3 * F) * b + 3 * H * F * wl.E * b, 6.0 * H * F * R),
         # router: x and W_r in, fp32 logits out; backward reads x, W_r, dx and
         # writes dlogits, dW_r, dx
@@ -191,13 +196,18 @@ def main():
     L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho if quota_cap is None else None,
                         dw=wl.dw, dg=True, router=args.router, keep_graph=not args.no_keep_graph, quota_cap=quota_cap)
     score = "metric" if args.metric_score else None
+    wq = None
+    if args.fp8_weights:
+        assert not wl.dw and wl.rho is None and not args.no_keep_graph, \
+            "fp8 weights are frozen: LoRA or forward-only workloads, pre-activations kept"
+        wq = moe.Fp8Weights(t["W_gate"], t["W_up"], t["W_down"])  # once, before any timing
     w_r = torch.from_numpy(W.router_weights(wl, seed=0)).to(dev).to(torch.bfloat16) if args.router else None
     stream = torch.cuda.current_stream()
 
     def step():
-        L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], stream, w_r=w_r)
+        L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], stream, w_r=w_r, wq=wq)
         if not args.forward_only:
-            L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream, w_r=w_r, score=score)
+            L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream, w_r=w_r, score=score, wq=wq)
 
     for _ in range(args.warmup):
         step()
@@ -242,7 +252,7 @@ def main():
 
     counts = L.counts.cpu().numpy()
     kept = L.kept_counts.cpu().numpy() if L.compacted else None
-    alg = algorithmic(wl, counts, kept, gathered=L.gather_rows)
+    alg = algorithmic(wl, counts, kept, gathered=L.gather_rows, weight_bytes=1 if wq is not None else None)
     step_flops = sum(alg[kk][1] for kk in gemm_kernels)
     byts, flops = alg[dom]
     ai = flops / byts
@@ -253,7 +263,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": byts / sec / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom, wl.name)
+    # the stored counter readings are of the bf16-weight kernels
+    roof["traffic"] = None if wq is not None else measured_traffic(dom, wl.name)
     roof["kernel"] = KERNEL_NAMES[dom]
     roof["kernel_us"] = dom_ms[dom] * 1e3
     roof["algorithmic_bytes"] = byts
@@ -270,7 +281,10 @@ def main():
                            + ("+router_bwd" if args.router else "")
                            + ("+recompute_h" if args.no_keep_graph else "")
                            + ("+metric_score" if args.metric_score else "")
-                           + (f"+budget({args.budget_mib} MiB: cap {quota_cap})" if quota_cap else ""),
+                           + (f"+budget({args.budget_mib} MiB: cap {quota_cap})" if quota_cap else "")
+                           + ("+fp8_weights" if wq is not None else ""),
+                   "weights": "fp8 E4M3 (per-expert power-of-two scale), widened to bf16" if wq is not None
+                              else "bf16",
                    "experts_with_rows": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max())},
         "tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
         "mfma_frac_of_step": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
