@@ -83,6 +83,13 @@ int check_row_width(const char* fn, const char* name, int v) {
   return MOE_OK;
 }
 
+// An optional row map (rows gathered on load): its divisor when present.
+int check_row_map(const char* fn, const char* name, const int32_t* map, int div) {
+  if (map != nullptr)
+    REQUIRE(div >= 1 && div <= 16, MOE_ERR_INVALID_ARGUMENT, "%s: %s divisor %d must be in 1..16", fn, name, div);
+  return MOE_OK;
+}
+
 int check_expert_dims(const char* fn, int H, int F, int E, int dtype) {
   int rc = check_dtype(fn, dtype);
   if (rc) return rc;
@@ -178,7 +185,8 @@ int check_fp8_weights(const char* fn, const void* wq_gate, const void* wq_up, co
 }
 
 int bwd_dx(const char* fn, int T, int H, int F, int E, int k, int max_rows, int dtype, const int32_t* offsets,
-           const int32_t* inv, const void* dy, const float* topk_w, const void* h_rows, const void* w_gate,
+           const int32_t* inv, const void* dy, const float* topk_w, const void* h_rows, const int32_t* h_src,
+           const void* w_gate,
            const void* w_up, const void* w_down, const int32_t* inv_all, const void* o_sorted, float* dg,
            void* dO_rows, void* dh_rows, void* dX_rows, void* dx, void* stream, const float* s_gu,
            const float* s_down) {
@@ -229,6 +237,7 @@ int bwd_dx(const char* fn, int T, int H, int F, int E, int k, int max_rows, int 
     g.a = (const uint16_t*)dO_rows;
     g.w0 = (const uint16_t*)w_down;
     g.h = (const uint16_t*)h_rows;
+    g.h_map = h_src;
     g.out0 = (uint16_t*)dh_rows;
     g.wscale = s_down;
     if ((rc = hip_status(run(moe::kGemmDA), fn))) return rc;
@@ -236,6 +245,7 @@ int bwd_dx(const char* fn, int T, int H, int F, int E, int k, int max_rows, int 
     g.w0 = (const uint16_t*)w_gate;
     g.w1 = (const uint16_t*)w_up;
     g.h = nullptr;
+    g.h_map = nullptr;
     g.out0 = (uint16_t*)dX_rows;
     g.wscale = s_gu;
     if ((rc = hip_status(run(moe::kGemmDX), fn))) return rc;
@@ -261,7 +271,7 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int moe_abi_version(void) { return 3; }
+int moe_abi_version(void) { return 4; }
 
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
   const char* fn = "moe_profile_kernel";
@@ -393,11 +403,11 @@ int moe_grouped_swiglu_fwd_gather(int H, int F, int E, int k, int max_rows, int 
 }
 
 int moe_grouped_swiglu_recompute(int H, int F, int E, int max_rows, int max_expert_rows, int dtype,
-                                 const int32_t* offsets, const void* x_rows, const void* w_gate, const void* w_up,
-                                 void* h_rows, void* a_rows, void* stream) {
+                                 const int32_t* offsets, const void* x_rows, const int32_t* x_src, int x_div,
+                                 const void* w_gate, const void* w_up, void* h_rows, void* a_rows, void* stream) {
   const char* fn = "moe_grouped_swiglu_recompute";
   int rc = check_expert_dims(fn, H, F, E, dtype);
-  if (rc || (rc = check_rows(fn, max_rows))) return rc;
+  if (rc || (rc = check_rows(fn, max_rows)) || (rc = check_row_map(fn, "x_src", x_src, x_div))) return rc;
   REQUIRE(max_expert_rows >= 0, MOE_ERR_INVALID_ARGUMENT, "%s: max_expert_rows=%d is negative", fn, max_expert_rows);
   NONNULL(offsets);
   NONNULL(x_rows);
@@ -411,6 +421,8 @@ int moe_grouped_swiglu_recompute(int H, int F, int E, int max_rows, int max_expe
   g.H = H;
   g.F = F;
   g.a = (const uint16_t*)x_rows;
+  g.a_map = x_src;
+  g.a_div = x_src ? x_div : 1;
   g.w0 = (const uint16_t*)w_gate;
   g.w1 = (const uint16_t*)w_up;
   g.out0 = (uint16_t*)h_rows;
@@ -444,31 +456,32 @@ int moe_combine(int T, int H, int k, int dtype, const void* rows, const int32_t*
 
 int moe_grouped_bwd_dx(int T, int H, int F, int E, int k, int max_rows, int dtype, const int32_t* offsets,
                        const int32_t* inv, const void* dy, const float* topk_w, const void* h_rows,
-                       const void* w_gate, const void* w_up, const void* w_down, const int32_t* inv_all,
-                       const void* o_sorted, float* dg, void* dO_rows, void* dh_rows, void* dX_rows, void* dx,
-                       void* stream) {
-  return bwd_dx("moe_grouped_bwd_dx", T, H, F, E, k, max_rows, dtype, offsets, inv, dy, topk_w, h_rows, w_gate, w_up,
-                w_down, inv_all, o_sorted, dg, dO_rows, dh_rows, dX_rows, dx, stream, nullptr, nullptr);
+                       const int32_t* h_src, const void* w_gate, const void* w_up, const void* w_down,
+                       const int32_t* inv_all, const void* o_sorted, float* dg, void* dO_rows, void* dh_rows,
+                       void* dX_rows, void* dx, void* stream) {
+  return bwd_dx("moe_grouped_bwd_dx", T, H, F, E, k, max_rows, dtype, offsets, inv, dy, topk_w, h_rows, h_src, w_gate,
+                w_up, w_down, inv_all, o_sorted, dg, dO_rows, dh_rows, dX_rows, dx, stream, nullptr, nullptr);
 }
 
 int moe_grouped_bwd_dx_fp8w(int T, int H, int F, int E, int k, int max_rows, const int32_t* offsets,
                             const int32_t* inv, const void* dy, const float* topk_w, const void* h_rows,
-                            const uint8_t* wq_gate, const uint8_t* wq_up, const uint8_t* wq_down, const float* s_gu,
+                            const int32_t* h_src, const uint8_t* wq_gate, const uint8_t* wq_up, const uint8_t* wq_down, const float* s_gu,
                             const float* s_down, const int32_t* inv_all, const void* o_sorted, float* dg,
                             void* dO_rows, void* dh_rows, void* dX_rows, void* dx, void* stream) {
   const char* fn = "moe_grouped_bwd_dx_fp8w";
   const int rc = check_fp8_weights(fn, wq_gate, wq_up, wq_down, s_gu, s_down);
   if (rc) return rc;
-  return bwd_dx(fn, T, H, F, E, k, max_rows, MOE_BF16, offsets, inv, dy, topk_w, h_rows, wq_gate, wq_up, wq_down,
-                inv_all, o_sorted, dg, dO_rows, dh_rows, dX_rows, dx, stream, s_gu, s_down);
+  return bwd_dx(fn, T, H, F, E, k, max_rows, MOE_BF16, offsets, inv, dy, topk_w, h_rows, h_src, wq_gate, wq_up,
+                wq_down, inv_all, o_sorted, dg, dO_rows, dh_rows, dX_rows, dx, stream, s_gu, s_down);
 }
 
 int moe_grouped_bwd_dw(int H, int F, int E, int max_rows, int dtype, const int32_t* offsets, const void* x_rows,
-                       const void* a_rows, const void* dO_rows, const void* dh_rows, void* dw_gate, void* dw_up,
-                       void* dw_down, void* stream) {
+                       const int32_t* x_src, int x_div, const void* a_rows, const int32_t* a_src,
+                       const void* dO_rows, const void* dh_rows, void* dw_gate, void* dw_up, void* dw_down,
+                       void* stream) {
   const char* fn = "moe_grouped_bwd_dw";
   int rc = check_expert_dims(fn, H, F, E, dtype);
-  if (rc || (rc = check_rows(fn, max_rows))) return rc;
+  if (rc || (rc = check_rows(fn, max_rows)) || (rc = check_row_map(fn, "x_src", x_src, x_div))) return rc;
   NONNULL(offsets);
   NONNULL(dw_gate);
   NONNULL(dw_up);
@@ -485,7 +498,10 @@ int moe_grouped_bwd_dw(int H, int F, int E, int max_rows, int dtype, const int32
   g.H = H;
   g.F = F;
   g.x = (const uint16_t*)x_rows;
+  g.x_map = x_src;
+  g.x_div = x_src ? x_div : 1;
   g.a = (const uint16_t*)a_rows;
+  g.a_map = a_src;
   g.dO = (const uint16_t*)dO_rows;
   g.dh = (const uint16_t*)dh_rows;
   g.dwg = (uint16_t*)dw_gate;

@@ -376,7 +376,7 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
       const int col = nb * 64 + 16 * jj + 4 * gq;
       if (MODE == kGemmDA) {
         // SwiGLU backward with the saved pre-activations hg, hu
-        const uint16_t* hrow = g.h + grow * 2 * F;
+        const uint16_t* hrow = g.h + h_row_of(g, grow) * 2 * F;
         const u32x2 gw = *(const u32x2*)(hrow + col), uw = *(const u32x2*)(hrow + F + col);
         float dg[4], du[4];
 #pragma unroll
@@ -616,7 +616,7 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
         for (int jb = 0; jb < 4; ++jb) v[4 * r + jb] = acc[ia][jb][r];
       const int col = nb * kTBN + 64 * wn + 16 * gq;
       if (MODE == kGemmDA) {
-        const uint16_t* hrow = g.h + grow * 2 * F;
+        const uint16_t* hrow = g.h + h_row_of(g, grow) * 2 * F;
         const u32x4 g0 = *(const u32x4*)(hrow + col), g1 = *(const u32x4*)(hrow + col + 8);
         const u32x4 u0 = *(const u32x4*)(hrow + F + col), u1 = *(const u32x4*)(hrow + F + col + 8);
         float dgv[16], duv[16];

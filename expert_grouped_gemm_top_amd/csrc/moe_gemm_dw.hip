@@ -18,6 +18,7 @@
 // which then stays in that XCD's L2).  The output tile is staged through LDS
 // so that every store is a full 16-byte lane of a contiguous row segment.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_common.h"
 #include "moe_launch.h"
@@ -76,7 +77,9 @@ __host__ __device__ inline DwShape dw_shape(int H, int F) {
 __host__ __device__ inline int dw_slots(const DwShape& s) { return (s.tiles + 7) & ~7; }
 
 // 16-byte direct loads of one operand's stage tile, `cpr` chunks per reduced
-// row; LDS position p of row k holds the chunk p ^ nn_swz(k).
+// row; LDS position p of row k holds the chunk p ^ nn_swz(k).  Row r of the
+// expert is row row0 + r of the operand, or, with a row map, row
+// map[row0 + r] / div (rows gathered on load).
 template <int INS_N>
 struct DwLoader {
   const uint16_t* col[INS_N];
@@ -90,13 +93,29 @@ struct DwLoader {
       col[i] = base + (c < ncols ? c : 0);  // chunks past the matrix edge read column 0 (never stored)
     }
   }
-  __device__ void issue(int s, int n_e, int ld, unsigned char* tile, int w) const {
+  __device__ void issue(int s, int row0, int n_e, int ld, unsigned char* tile, int w) const {
 #pragma unroll
     for (int i = 0; i < INS_N; ++i) {
       int r = s * Cfg::BK + krow[i];
       r = r < n_e ? r : n_e - 1;  // past the expert's rows: its last row, zeroed before use
-      g2lds(col[i] + (size_t)r * ld, tile + 1024 * (INS_N * w + i));
+      g2lds(col[i] + (size_t)(row0 + r) * ld, tile + 1024 * (INS_N * w + i));
     }
+  }
+  // Mapped rows: the map entries of this lane's loads of stage s, read one
+  // stage ahead of their use (ordinary loads that land while the previous
+  // stage computes; nothing reads them before the next issue, which follows
+  // the two-stage wait, so no wait is spent on them).
+  __device__ void rows_of(int s, int row0, int n_e, const int32_t* map, int* pent) const {
+#pragma unroll
+    for (int i = 0; i < INS_N; ++i) {
+      int r = s * Cfg::BK + krow[i];
+      r = r < n_e ? r : n_e - 1;
+      pent[i] = map[row0 + r];
+    }
+  }
+  __device__ void issue_rows(const int* pent, int div, int ld, unsigned char* tile, int w) const {
+#pragma unroll
+    for (int i = 0; i < INS_N; ++i) g2lds(col[i] + (size_t)(pent[i] / div) * ld, tile + 1024 * (INS_N * w + i));
   }
 };
 
@@ -150,29 +169,41 @@ __global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwAr
 
   // ---- the product this tile belongs to
   const uint16_t *P, *Q;
-  int ldp, ldq, M, N, mt, nt;
+  const int32_t* pmap;  // gathered rows of the left operand, or NULL
+  int ldp, ldq, M, N, mt, nt, pdiv;
   if (t < sh.tiles1) {  // [dW_gate | dW_up] = x^T [dHg | dHu]
     mt = t / sh.nt1;
     nt = t - mt * sh.nt1;
     P = g.x; ldp = H; M = H;
+    pmap = g.x_map; pdiv = g.x_div;
     Q = g.dh; ldq = 2 * F; N = 2 * F;
   } else {              // dW_down = a^T dO
     const int tt = t - sh.tiles1;
     mt = tt / sh.nt2;
     nt = tt - mt * sh.nt2;
     P = g.a; ldp = F; M = F;
+    pmap = g.a_map; pdiv = 1;
     Q = g.dO; ldq = H; N = H;
   }
   const int m0 = mt * Cfg::BM, n0 = nt * Cfg::BN;
 
   DwLoader<Cfg::INS_P> lp;
   DwLoader<Cfg::INS_Q> lq;
-  lp.init(P + (size_t)row0 * ldp, m0, M, Cfg::PITCH_P / 16, w, l);
-  lq.init(Q + (size_t)row0 * ldq, n0, N, Cfg::PITCH_Q / 16, w, l);
-  auto issue = [&](int s) {
+  lp.init(P, m0, M, Cfg::PITCH_P / 16, w, l);
+  lq.init(Q, n0, N, Cfg::PITCH_Q / 16, w, l);
+  static_assert(Cfg::STAGES == 2, "mapped rows are read one stage ahead, inside the two-stage wait");
+  int pent[Cfg::INS_P];  // map entries of the next stage to issue
+  // MAPPED is a compile-time switch so that the two pipelines are separate
+  // loops: pending map loads of one never make the other wait
+  auto issue = [&](int s, auto mapped) {
     unsigned char* st = s_dyn + (s % Cfg::STAGES) * Cfg::STAGE_BYTES;
-    lp.issue(s, n_e, ldp, st, w);
-    lq.issue(s, n_e, ldq, st + Cfg::TILE_P, w);
+    if constexpr (decltype(mapped)::value) {
+      lp.issue_rows(pent, pdiv, ldp, st, w);
+      if ((s + 1) * Cfg::BK < n_e) lp.rows_of(s + 1, row0, n_e, pmap, pent);
+    } else {
+      lp.issue(s, row0, n_e, ldp, st, w);
+    }
+    lq.issue(s, row0, n_e, ldq, st + Cfg::TILE_P, w);
   };
 
   f32x16 acc[Cfg::MI][Cfg::NJ];
@@ -234,30 +265,35 @@ __global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwAr
   };
 
   const int steps = (n_e + Cfg::BK - 1) / Cfg::BK;
+  auto pipeline = [&](auto mapped) {
+    if constexpr (decltype(mapped)::value) lp.rows_of(0, row0, n_e, pmap, pent);
 #pragma unroll
-  for (int s = 0; s < Cfg::STAGES - 1; ++s)
-    if (s < steps) issue(s);
-  for (int s = 0; s < steps; ++s) {
-    // stage s has landed once at most (stages issued after it) x INS loads remain
-    const int ahead = min(Cfg::STAGES - 2, steps - 1 - s);
-    if (ahead >= 2) wait_vmcnt<2 * Cfg::INS>();
-    else if (ahead == 1) wait_vmcnt<Cfg::INS>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();
-    if (s + Cfg::STAGES - 1 < steps) issue(s + Cfg::STAGES - 1);
-    const int valid = n_e - s * Cfg::BK;
-    if (valid < Cfg::BK) {
-      // last stage: zero the rows past the expert's end in both operand tiles
-      unsigned char* st = s_dyn + (s % Cfg::STAGES) * Cfg::STAGE_BYTES;
-      for (int c = tid; c < Cfg::STAGE_BYTES / 16; c += 64 * Cfg::WAVES) {
-        const bool in_q = c >= Cfg::TILE_P / 16;
-        const int rr = in_q ? (c - Cfg::TILE_P / 16) / (Cfg::PITCH_Q / 16) : c / (Cfg::PITCH_P / 16);
-        if (rr >= valid) *(u32x4*)(st + 16 * c) = u32x4{0, 0, 0, 0};
+    for (int s = 0; s < Cfg::STAGES - 1; ++s)
+      if (s < steps) issue(s, mapped);
+    for (int s = 0; s < steps; ++s) {
+      // stage s has landed once at most (stages issued after it) x INS loads remain
+      const int ahead = min(Cfg::STAGES - 2, steps - 1 - s);
+      if (ahead >= 2) wait_vmcnt<2 * Cfg::INS>();
+      else if (ahead == 1) wait_vmcnt<Cfg::INS>();
+      else wait_vmcnt<0>();
+      barrier_no_fence();
+      if (s + Cfg::STAGES - 1 < steps) issue(s + Cfg::STAGES - 1, mapped);
+      const int valid = n_e - s * Cfg::BK;
+      if (valid < Cfg::BK) {
+        // last stage: zero the rows past the expert's end in both operand tiles
+        unsigned char* st = s_dyn + (s % Cfg::STAGES) * Cfg::STAGE_BYTES;
+        for (int c = tid; c < Cfg::STAGE_BYTES / 16; c += 64 * Cfg::WAVES) {
+          const bool in_q = c >= Cfg::TILE_P / 16;
+          const int rr = in_q ? (c - Cfg::TILE_P / 16) / (Cfg::PITCH_Q / 16) : c / (Cfg::PITCH_P / 16);
+          if (rr >= valid) *(u32x4*)(st + 16 * c) = u32x4{0, 0, 0, 0};
+        }
+        __syncthreads();
       }
-      __syncthreads();
+      compute(s);
     }
-    compute(s);
-  }
+  };
+  if (pmap != nullptr) pipeline(std::true_type{});
+  else pipeline(std::false_type{});
 
   // ---- epilogue, staged through LDS.  acc[i][j] register r -> tile row
   // TM wm + 32 i + l32, tile column TN wn + 32 j + 8 q + 4 hk + (0..3) with

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void row_gemm_f32_kernel(RowGemmArgs g) {
     }
     if (g.out1 != nullptr) ((float*)g.out1)[(size_t)row * F + col] = s0 / (1.0f + expf(-s0)) * s1;
   } else if (MODE == kGemmDA) {
-    const float* h = (const float*)g.h + (size_t)row * 2 * F;
+    const float* h = (const float*)g.h + h_row_of(g, row) * 2 * F;
     const float hg = h[col], hu = h[F + col];
     const float sg = 1.0f / (1.0f + expf(-hg));
     float* d = (float*)g.out0 + (size_t)row * 2 * F;
@@ -95,11 +95,15 @@ __global__ __launch_bounds__(256) void dw_f32_kernel(DwArgs g) {
   const int row0 = g.offsets[e], n_e = g.offsets[e + 1] - row0;
   const float *P, *Q;
   int ldp, ldq, m, n;
+  const int32_t* pmap;  // gathered rows of the left operand, or NULL
+  int pdiv;
   float* out;
   if (i < job1) {
     m = (int)(i / (2 * F));
     n = (int)(i - (int64_t)m * 2 * F);
     P = (const float*)g.x; ldp = H;
+    pmap = g.x_map;
+    pdiv = g.x_div;
     Q = (const float*)g.dh; ldq = 2 * F;
     out = (n < F) ? (float*)g.dwg + ((size_t)e * H + m) * F + n : (float*)g.dwu + ((size_t)e * H + m) * F + (n - F);
   } else {
@@ -107,11 +111,16 @@ __global__ __launch_bounds__(256) void dw_f32_kernel(DwArgs g) {
     m = (int)(j / H);
     n = (int)(j - (int64_t)m * H);
     P = (const float*)g.a; ldp = F;
+    pmap = g.a_map;
+    pdiv = 1;
     Q = (const float*)g.dO; ldq = H;
     out = (float*)g.dwd + ((size_t)e * F + m) * H + n;
   }
   float s = 0.0f;
-  for (int r = 0; r < n_e; ++r) s += P[(size_t)(row0 + r) * ldp + m] * Q[(size_t)(row0 + r) * ldq + n];
+  for (int r = 0; r < n_e; ++r) {
+    const int64_t pr = pmap != nullptr ? (int64_t)(pmap[row0 + r] / pdiv) : (int64_t)(row0 + r);
+    s += P[(size_t)pr * ldp + m] * Q[(size_t)(row0 + r) * ldq + n];
+  }
   *out = s;
 }
 

@@ -35,6 +35,7 @@ struct RowGemmArgs {
   uint16_t* out1;
   const int32_t* a_map;  // when set, row s of `a` is a[a_map[s] / a_div] (rows gathered on load)
   int a_div;
+  const int32_t* h_map;  // DA: when set, the saved pre-activations of row s are h[h_map[s]]
   int big_min_rows;   // set by launch_row_gemm_bf16: experts from this row count take the 256-row kernel
   int stream_ksplit;  // set by launch_row_gemm_bf16: reduction split of the skinny-expert kernel (1, 2 or 4)
   // fp8 weights (launch_row_gemm_fp8w): w0 / w1 point at E4M3 bytes, and every
@@ -46,8 +47,11 @@ struct RowGemmArgs {
 struct DwArgs {
   const int32_t* offsets;
   int E, H, F;
-  const uint16_t* x;   // [R,H]
-  const uint16_t* a;   // [R,F]
+  const uint16_t* x;   // [R,H], or gathered: row s is x[x_map[s] / x_div]
+  const uint16_t* a;   // [R,F], or gathered: row s is a[a_map[s]]
+  const int32_t* x_map;
+  int x_div;
+  const int32_t* a_map;
   const uint16_t* dO;  // [R,H]
   const uint16_t* dh;  // [R,2F]
   uint16_t* dwg;       // [E,H,F]
@@ -58,6 +62,11 @@ struct DwArgs {
 // Source row of operand row s of a row GEMM.
 __device__ __forceinline__ int64_t a_row_of(const RowGemmArgs& g, int s) {
   return g.a_map != nullptr ? (int64_t)(g.a_map[s] / g.a_div) : (int64_t)s;
+}
+
+// Row of the saved pre-activations that row s of a dA product reads.
+__device__ __forceinline__ int64_t h_row_of(const RowGemmArgs& g, int64_t s) {
+  return g.h_map != nullptr ? (int64_t)g.h_map[s] : s;
 }
 
 hipError_t launch_route_topk(int T, int E, int k, const float* logits, int32_t* idx, float* w, hipStream_t stream);

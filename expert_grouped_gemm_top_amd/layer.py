@@ -21,11 +21,15 @@ class MoeLayerBuffers:
         quota_cap: the per-expert quota directly (e.g. from
         moe.moe_quota_cap_for_budget), instead of rho.  keep_graph=False: the
         forward keeps no pre-activations [hg|hu]; the backward recomputes them
-        from the saved rows (the recompute path that pull request #44 keeps
-        behind keep_graph=False).  gather_rows: the forward reads x rows
-        through perm instead of a materialized x_sorted (moe_dispatch then
-        skips its row copy); None picks it whenever nothing later needs
-        x_sorted (no dW, no compaction, pre-activations kept)."""
+        from the token rows (the recompute path that pull request #44 keeps
+        behind keep_graph=False).  gather_rows: every GEMM reads the token
+        rows x and the saved activations through the pair / row indices
+        (perm, kept_perm, kept_src), so neither x_sorted nor the compacted
+        copies are materialized; False materializes them (moe_dispatch's row
+        copy, moe_compact_pairs' row gathers).  Results are the same bit for
+        bit.  None picks gathering unless dW runs over all pairs: there the
+        weight-gradient GEMM streams each expert's x rows many times, and
+        contiguous rows serve it better than one copy costs."""
         self.T, self.H, self.F, self.E, self.k = T, H, F, E, k
         self.keep_graph = keep_graph
         self.N = N = T * k
@@ -41,16 +45,15 @@ class MoeLayerBuffers:
         self.inv_perm = em(N, dt=i32)
         ws = moe.moe_dispatch_workspace_bytes(T, E, k)
         self.ws = em(max(ws, 16), dt=torch.uint8)
-        self.x_sorted = em(N, H)
+        compacted = rho is not None or quota_cap is not None
+        self.gather_rows = (compacted or not dw) if gather_rows is None else bool(gather_rows)
+        self.x_sorted = None if self.gather_rows else em(N, H)
         self.h_save = em(N, 2 * F)
         self.a_save = em(N, F)
         self.o_sorted = em(N, H)
         self.y = em(T, H)
         self.quota_cap = quota_cap
         self.compacted = rho is not None or quota_cap is not None
-        eligible = not dw and not self.compacted and keep_graph
-        self.gather_rows = eligible if gather_rows is None else bool(gather_rows)
-        assert eligible or not self.gather_rows, "dW, compaction and recompute read x_sorted"
         if self.compacted:
             cap = moe.moe_quota_cap(T, E, k, rho) if quota_cap is None else quota_cap
             self.R = min(N, E * cap)
@@ -59,9 +62,11 @@ class MoeLayerBuffers:
             self.kept_perm = em(self.R, dt=i32)
             self.kept_src = em(self.R, dt=i32)
             self.kept_inv = em(N, dt=i32)
-            self.x_kept = em(self.R, H)
-            self.a_kept = em(self.R, F)
-            self.h_kept = em(self.R, 2 * F)
+            g = self.gather_rows
+            self.x_kept = None if g else em(self.R, H)
+            self.a_kept = None if g or not dw else em(self.R, F)
+            # pre-activations of the kept rows: recomputed into it, or (materialized) gathered
+            self.h_kept = em(self.R, 2 * F) if (not keep_graph or not g) else None
             self.score = em(N, dt=f32)
         else:
             self.R = N
@@ -88,10 +93,10 @@ class MoeLayerBuffers:
         """With w_r (a layer built with router=True) the logits are x W_r and
         the `logits` argument is ignored.  With wq (moe.Fp8Weights of the same
         frozen weights) the expert GEMMs read the fp8 copy."""
+        self._x = x  # the backward reads token rows through the pair ids
         if w_r is not None:
             moe.moe_router_fwd(x, w_r, self.logits, self.router_ws, stream)
             logits = self.logits
-            self._x = x
         moe.moe_route_topk(logits, self.topk_idx, self.topk_w, self.k, stream)
         g = self.gather_rows  # index-only dispatch: the forward gathers x rows itself
         moe.moe_dispatch(self.topk_idx, None if g else x, self.counts, self.offsets, self.perm, self.inv_perm,
@@ -102,9 +107,9 @@ class MoeLayerBuffers:
                                             self.o_sorted, self.N, perm=self.perm if g else None, k=self.k,
                                             stream=stream)
         elif self.gather_rows:
-            moe.moe_grouped_swiglu_fwd_gather(self.offsets, x, self.perm, w_gate, w_up, w_down, self.h_save,
-                                              self.a_save, self.o_sorted, self.k, self.N, max_expert_rows=self.T,
-                                              stream=stream)
+            moe.moe_grouped_swiglu_fwd_gather(self.offsets, x, self.perm, w_gate, w_up, w_down,
+                                              self.h_save if self.keep_graph else None, self.a_save, self.o_sorted,
+                                              self.k, self.N, max_expert_rows=self.T, stream=stream)
         else:
             moe.moe_grouped_swiglu_fwd(self.offsets, self.x_sorted, w_gate, w_up, w_down,
                                        self.h_save if self.keep_graph else None, self.a_save, self.o_sorted, self.N,
@@ -114,11 +119,13 @@ class MoeLayerBuffers:
 
     # ----------------------------------------------------------------- backward
     def compact(self, score, stream=None):
-        kg = self.keep_graph
+        """Selection within the quotas; index-only when rows are gathered on load."""
+        kg, g = self.keep_graph, self.gather_rows
         moe.moe_compact_pairs(self.counts, self.offsets, self.perm, score, self.rho or 1.0, self.kept_counts,
                               self.kept_offsets, self.kept_perm, self.kept_src, self.kept_inv, self.T, self.k,
-                              self.x_sorted, self.a_save if self.dw else None, self.h_save if kg else None,
-                              self.x_kept, self.a_kept if self.dw else None, self.h_kept if kg else None, stream,
+                              None if g else self.x_sorted, None if g or not self.dw else self.a_save,
+                              None if g or not kg else self.h_save, None if g else self.x_kept,
+                              None if g or not self.dw else self.a_kept, None if g or not kg else self.h_kept, stream,
                               cap=self.quota_cap)
 
     def backward(self, dy, w_gate, w_up, w_down, score=None, stream=None, w_r=None, wq=None):
@@ -127,21 +134,33 @@ class MoeLayerBuffers:
         None (the routing weights) or "metric" (moe_pair_scores: the norm of
         each pair's rank-one dW_down term).  With w_r, the router's backward
         follows: dlogits, dw_r, and its share added to dx."""
+        g, k = self.gather_rows, self.k
         if self.compacted:
             if isinstance(score, str):
                 assert score == "metric", score
                 moe.moe_pair_scores(self.inv_perm, self.topk_w, self.a_save, dy, self.score, stream)
                 score = self.score
             self.compact(self.topk_w.view(-1) if score is None else score, stream)
-            offsets, inv, x_rows, a_rows, h_rows = (self.kept_offsets, self.kept_inv, self.x_kept, self.a_kept,
-                                                    self.h_kept)
+            offsets, inv, pairs, src = self.kept_offsets, self.kept_inv, self.kept_perm, self.kept_src
         else:
-            offsets, inv, x_rows, a_rows, h_rows = self.offsets, self.inv_perm, self.x_sorted, self.a_save, self.h_save
+            offsets, inv, pairs, src = self.offsets, self.inv_perm, self.perm, None
+        # rows of the backward: x, a and the pre-activations h, each either a
+        # contiguous buffer or a source buffer read through a row map
+        if g:
+            x_rows, x_src, a_rows, a_src = self._x, pairs, self.a_save, src
+        else:
+            x_rows, x_src = (self.x_kept if self.compacted else self.x_sorted), None
+            a_rows, a_src = (self.a_kept if self.compacted else self.a_save), None
         if not self.keep_graph:  # recompute [hg | hu] of the backward's rows
+            h_rows, h_src = (self.h_kept if self.compacted else self.h_save), None
             moe.moe_grouped_swiglu_recompute(offsets, x_rows, w_gate, w_up, h_rows, None, self.R,
-                                             max_expert_rows=self.T, stream=stream)
+                                             max_expert_rows=self.T, stream=stream, x_src=x_src, x_div=k)
+        elif self.compacted and not g:
+            h_rows, h_src = self.h_kept, None
+        else:
+            h_rows, h_src = self.h_save, src
         extra = dict(inv_all=self.inv_perm if self.want_dg else None, o_sorted=self.o_sorted if self.want_dg else None,
-                     dg=self.dg, stream=stream)
+                     dg=self.dg, stream=stream, h_src=h_src)
         if wq is not None:  # frozen fp8 weights: no weight gradient
             assert not self.dw, "fp8 weights are frozen: no dW"
             moe.moe_grouped_bwd_dx_fp8w(offsets, inv, dy, self.topk_w, h_rows, wq, self.dO, self.dh, self.dX,
@@ -151,7 +170,7 @@ class MoeLayerBuffers:
                                    self.dX, self.dx, self.R, **extra)
         if self.dw:
             moe.moe_grouped_bwd_dw(offsets, x_rows, a_rows, self.dO, self.dh, self.dw_gate, self.dw_up,
-                                   self.dw_down, self.R, stream)
+                                   self.dw_down, self.R, stream, x_src=x_src, x_div=k, a_src=a_src)
         if w_r is not None:
             moe.moe_router_bwd(self._x, w_r, self.topk_idx, self.topk_w, self.dg, self.dlogits, self.dw_r, self.dx,
                                True, self.router_ws, stream)

@@ -37,10 +37,10 @@ _SIGS = {
     "moe_dispatch": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_grouped_swiglu_fwd": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i),
     "moe_grouped_swiglu_fwd_gather": ([_i] * 7 + [_vp] * 10, _i),
-    "moe_grouped_swiglu_recompute": ([_i, _i, _i, _i, _i, _i] + [_vp] * 7, _i),
+    "moe_grouped_swiglu_recompute": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i] + [_vp] * 5, _i),
     "moe_combine": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
-    "moe_grouped_bwd_dx": ([_i, _i, _i, _i, _i, _i, _i] + [_vp] * 16, _i),
-    "moe_grouped_bwd_dw": ([_i, _i, _i, _i, _i] + [_vp] * 9, _i),
+    "moe_grouped_bwd_dx": ([_i, _i, _i, _i, _i, _i, _i] + [_vp] * 17, _i),
+    "moe_grouped_bwd_dw": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _i] + [_vp] * 8, _i),
     "moe_quota_cap": ([_i, _i, _i, _d], _i64),
     "moe_compact_pairs": ([_i, _i, _i, _i, _i, _i, _d] + [_vp] * 16, _i),
     "moe_compact_pairs_cap": ([_i, _i, _i, _i, _i, _i, _i] + [_vp] * 16, _i),
@@ -48,7 +48,7 @@ _SIGS = {
     "moe_pair_scores": ([_i, _i, _i, _i, _i] + [_vp] * 6, _i),
     "moe_quantize_weights_fp8": ([_i, _i64, _i64] + [_vp] * 6, _i),
     "moe_grouped_swiglu_fwd_fp8w": ([_i] * 5 + [_vp] * 12, _i),
-    "moe_grouped_bwd_dx_fp8w": ([_i] * 6 + [_vp] * 18, _i),
+    "moe_grouped_bwd_dx_fp8w": ([_i] * 6 + [_vp] * 19, _i),
 }
 
 
@@ -236,14 +236,16 @@ def moe_grouped_swiglu_fwd_fp8w(offsets, x_rows, wq: Fp8Weights, h_save, a_save,
 
 
 def moe_grouped_bwd_dx_fp8w(offsets, inv, dy, topk_w, h_rows, wq: Fp8Weights, dO_rows, dh_rows, dX_rows, dx,
-                            max_rows: int, inv_all=None, o_sorted=None, dg=None, stream=None):
+                            max_rows: int, inv_all=None, o_sorted=None, dg=None, stream=None, h_src=None):
     T, H = dy.shape
     E, F = wq.E, wq.F
     k = topk_w.shape[1]
     d, U8, R, N = torch.bfloat16, torch.uint8, max_rows, T * k
     _check(lib().moe_grouped_bwd_dx_fp8w(
         T, H, F, E, k, R, _ptr(offsets, "offsets", I32, E + 1), _ptr(inv, "inv", I32, N),
-        _ptr(dy, "dy", d, T * H), _ptr(topk_w, "topk_w", F32, N), _ptr(h_rows, "h_rows", d, R * 2 * F),
+        _ptr(dy, "dy", d, T * H), _ptr(topk_w, "topk_w", F32, N),
+        _ptr(h_rows, "h_rows", d, 2 * F if h_src is not None else R * 2 * F),
+        _ptr(h_src, "h_src", I32, R, allow_none=True),
         _ptr(wq.q_gate, "q_gate", U8, E * H * F), _ptr(wq.q_up, "q_up", U8, E * H * F),
         _ptr(wq.q_down, "q_down", U8, E * F * H), _ptr(wq.s_gu, "s_gu", F32, E), _ptr(wq.s_down, "s_down", F32, E),
         _ptr(inv_all, "inv_all", I32, N, allow_none=dg is None),
@@ -267,13 +269,15 @@ def moe_grouped_swiglu_fwd_gather(offsets, x, perm, w_gate, w_up, w_down, h_save
 
 
 def moe_grouped_swiglu_recompute(offsets, x_rows, w_gate, w_up, h_rows, a_rows, max_rows: int,
-                                 max_expert_rows: int | None = None, stream=None):
+                                 max_expert_rows: int | None = None, stream=None, x_src=None, x_div: int = 1):
+    """x_src: row s of x is x_rows[x_src[s] / x_div] (rows gathered on load)."""
     E, H, F = w_gate.shape
     dt, d = _dt(w_gate), w_gate.dtype
     R = max_rows
     _check(lib().moe_grouped_swiglu_recompute(
         H, F, E, R, R if max_expert_rows is None else max_expert_rows, dt, _ptr(offsets, "offsets", I32, E + 1),
-        _ptr(x_rows, "x_rows", d, R * H), _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F),
+        _ptr(x_rows, "x_rows", d, H if x_src is not None else R * H), _ptr(x_src, "x_src", I32, R, allow_none=True),
+        x_div, _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F),
         _ptr(h_rows, "h_rows", d, R * 2 * F), _ptr(a_rows, "a_rows", d, R * F, allow_none=True), _stream(stream)))
 
 
@@ -287,7 +291,8 @@ def moe_combine(rows, inv, topk_w, out, k: int, stream=None):
 
 
 def moe_grouped_bwd_dx(offsets, inv, dy, topk_w, h_rows, w_gate, w_up, w_down, dO_rows, dh_rows, dX_rows, dx,
-                       max_rows: int, inv_all=None, o_sorted=None, dg=None, stream=None):
+                       max_rows: int, inv_all=None, o_sorted=None, dg=None, stream=None, h_src=None):
+    """h_src: row r's pre-activations are h_rows[h_src[r]] (e.g. h_save with kept_src)."""
     T, H = dy.shape
     E, _, F = w_gate.shape
     k = topk_w.shape[1]
@@ -296,20 +301,28 @@ def moe_grouped_bwd_dx(offsets, inv, dy, topk_w, h_rows, w_gate, w_up, w_down, d
     N = T * k
     _check(lib().moe_grouped_bwd_dx(
         T, H, F, E, k, R, _dt(dy), _ptr(offsets, "offsets", I32, E + 1), _ptr(inv, "inv", I32, N), _ptr(dy, "dy", d, T * H), _ptr(topk_w, "topk_w", F32, N),
-        _ptr(h_rows, "h_rows", d, R * 2 * F), _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F),
+        _ptr(h_rows, "h_rows", d, 2 * F if h_src is not None else R * 2 * F),
+        _ptr(h_src, "h_src", I32, R, allow_none=True),
+        _ptr(w_gate, "w_gate", d, E * H * F), _ptr(w_up, "w_up", d, E * H * F),
         _ptr(w_down, "w_down", d, E * F * H), _ptr(inv_all, "inv_all", I32, N, allow_none=dg is None),
         _ptr(o_sorted, "o_sorted", d, N * H, allow_none=dg is None), _ptr(dg, "dg", F32, N, allow_none=True),
         _ptr(dO_rows, "dO_rows", d, R * H), _ptr(dh_rows, "dh_rows", d, R * 2 * F), _ptr(dX_rows, "dX_rows", d, R * H),
         _ptr(dx, "dx", d, T * H), _stream(stream)))
 
 
-def moe_grouped_bwd_dw(offsets, x_rows, a_rows, dO_rows, dh_rows, dw_gate, dw_up, dw_down, max_rows: int, stream=None):
+def moe_grouped_bwd_dw(offsets, x_rows, a_rows, dO_rows, dh_rows, dw_gate, dw_up, dw_down, max_rows: int, stream=None,
+                       x_src=None, x_div: int = 1, a_src=None):
+    """x_src / a_src: rows gathered on load (row r of x is x_rows[x_src[r] / x_div],
+    row r of a is a_rows[a_src[r]])."""
     E, H, F = dw_gate.shape
     d = dw_gate.dtype
     R = max_rows
     _check(lib().moe_grouped_bwd_dw(
-        H, F, E, R, _dt(dw_gate), _ptr(offsets, "offsets", I32, E + 1), _ptr(x_rows, "x_rows", d, R * H),
-        _ptr(a_rows, "a_rows", d, R * F), _ptr(dO_rows, "dO_rows", d, R * H), _ptr(dh_rows, "dh_rows", d, R * 2 * F),
+        H, F, E, R, _dt(dw_gate), _ptr(offsets, "offsets", I32, E + 1),
+        _ptr(x_rows, "x_rows", d, H if x_src is not None else R * H), _ptr(x_src, "x_src", I32, R, allow_none=True),
+        x_div, _ptr(a_rows, "a_rows", d, F if a_src is not None else R * F),
+        _ptr(a_src, "a_src", I32, R, allow_none=True),
+        _ptr(dO_rows, "dO_rows", d, R * H), _ptr(dh_rows, "dh_rows", d, R * 2 * F),
         _ptr(dw_gate, "dw_gate", d, E * H * F), _ptr(dw_up, "dw_up", d, E * H * F),
         _ptr(dw_down, "dw_down", d, E * F * H), _stream(stream)))
 

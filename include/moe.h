@@ -72,7 +72,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 const char* moe_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);
-/* ABI version, currently 3. */
+/* ABI version, currently 4. */
 int moe_abi_version(void);
 
 /* Kernels that moe_profile_kernel can bracket with events. */
@@ -183,11 +183,13 @@ int moe_grouped_swiglu_fwd_gather(int H, int F, int E, int k, int max_rows, int 
  * for the rows s of every expert e in offsets.  With the same offsets and row
  * capacities as a moe_grouped_swiglu_fwd call it gives that call's h_save and
  * a_save bit for bit.  Arguments as in moe_grouped_swiglu_fwd; x_rows [rows,
- * H] (device); h_rows [rows, 2F] (device, out); a_rows [rows, F] (device,
- * out) or NULL. */
+ * H] (device), or with x_src != NULL gathered on load: row s is
+ * x_rows[x_src[s] / x_div] (x_src [rows] int32, device; 1 <= x_div <= 16; e.g.
+ * the token matrix x with the pair ids perm or kept_perm and x_div = k);
+ * h_rows [rows, 2F] (device, out); a_rows [rows, F] (device, out) or NULL. */
 int moe_grouped_swiglu_recompute(int H, int F, int E, int max_rows, int max_expert_rows, int dtype,
-                                 const int32_t* offsets, const void* x_rows, const void* w_gate, const void* w_up,
-                                 void* h_rows, void* a_rows, void* stream);
+                                 const int32_t* offsets, const void* x_rows, const int32_t* x_src, int x_div,
+                                 const void* w_gate, const void* w_up, void* h_rows, void* a_rows, void* stream);
 
 /* Router-weighted combine (issue #14, Proposal: results scattered back):
  *   out[t] = sum_{j = 0..k-1, inv[t*k+j] >= 0} w[t,j] * rows[inv[t*k+j]]
@@ -202,7 +204,8 @@ int moe_combine(int T, int H, int k, int dtype, const void* rows, const int32_t*
  * backward dx, LoRA with frozen experts; LRMoE abstract: backward over the
  * retained, compacted pairs only).  Rows are either all pairs (offsets, inv
  * from moe_dispatch; h_rows = h_save) or the retained ones (kept_offsets,
- * kept_inv from moe_compact_pairs; h_rows = h_kept).  For each pair p with
+ * kept_inv from moe_compact_pairs; h_rows = h_kept, or h_rows = h_save read
+ * through h_src = kept_src without the compacted copy).  For each pair p with
  * r = inv[p] >= 0 (t = p / k):
  *   dO_rows[r]  = w[p] * dy[t]                                      [R, H]
  *   dA          = dO_rows[r] W_down[e]^T                             (length F)
@@ -214,13 +217,15 @@ int moe_combine(int T, int H, int k, int dtype, const void* rows, const int32_t*
  *   dg[p] = <dy[p / k], o_sorted[inv_all[p]]>  (fp32).
  * offsets [E+1], inv [T*k] int32 (device; every row r < offsets[E] is the
  * image of exactly one pair); dy [T, H];
- * topk_w [T, k] fp32; h_rows [max_rows, 2F]; weights as in the forward;
- * inv_all [T*k] and o_sorted [T*k, H] (device, only read when dg != NULL);
- * dO_rows, dh_rows, dX_rows [max_rows, *], dx [T, H] (device, out). */
+ * topk_w [T, k] fp32; h_rows [max_rows, 2F], or with h_src != NULL row r's
+ * pre-activations are h_rows[h_src[r]] (h_src [max_rows] int32, device);
+ * weights as in the forward; inv_all [T*k] and o_sorted [T*k, H] (device,
+ * only read when dg != NULL); dO_rows, dh_rows, dX_rows [max_rows, *],
+ * dx [T, H] (device, out). */
 int moe_grouped_bwd_dx(int T, int H, int F, int E, int k, int max_rows, int dtype,
                        const int32_t* offsets, const int32_t* inv,
-                       const void* dy, const float* topk_w, const void* h_rows, const void* w_gate,
-                       const void* w_up, const void* w_down, const int32_t* inv_all,
+                       const void* dy, const float* topk_w, const void* h_rows, const int32_t* h_src,
+                       const void* w_gate, const void* w_up, const void* w_down, const int32_t* inv_all,
                        const void* o_sorted, float* dg, void* dO_rows, void* dh_rows,
                        void* dX_rows, void* dx, void* stream);
 
@@ -264,7 +269,7 @@ int moe_grouped_swiglu_fwd_fp8w(int H, int F, int E, int k, int max_rows, const 
  * weights as in moe_grouped_swiglu_fwd_fp8w). */
 int moe_grouped_bwd_dx_fp8w(int T, int H, int F, int E, int k, int max_rows, const int32_t* offsets,
                             const int32_t* inv, const void* dy, const float* topk_w, const void* h_rows,
-                            const uint8_t* wq_gate, const uint8_t* wq_up, const uint8_t* wq_down,
+                            const int32_t* h_src, const uint8_t* wq_gate, const uint8_t* wq_up, const uint8_t* wq_down,
                             const float* s_gu, const float* s_down, const int32_t* inv_all,
                             const void* o_sorted, float* dg, void* dO_rows, void* dh_rows, void* dX_rows,
                             void* dx, void* stream);
@@ -276,11 +281,16 @@ int moe_grouped_bwd_dx_fp8w(int T, int H, int F, int E, int k, int max_rows, con
  * in fp32, rounded once to the weight dtype; overwritten, not accumulated; an
  * expert without rows gets exact zeros.  offsets [E+1] int32 (device);
  * x_rows [*, H], a_rows [*, F], dO_rows [*, H], dh_rows [*, 2F] (device);
- * dw_gate, dw_up [E, H, F], dw_down [E, F, H] (device, out). */
+ * dw_gate, dw_up [E, H, F], dw_down [E, F, H] (device, out).  Rows gathered on
+ * load: with x_src != NULL row r of x is x_rows[x_src[r] / x_div] (e.g. the
+ * token matrix x, x_src = perm or kept_perm, x_div = k; 1 <= x_div <= 16), and
+ * with a_src != NULL row r of a is a_rows[a_src[r]] (e.g. a_save with
+ * a_src = kept_src); x_src, a_src [max_rows] int32 (device) or NULL.  The
+ * results do not depend on whether rows are gathered. */
 int moe_grouped_bwd_dw(int H, int F, int E, int max_rows, int dtype, const int32_t* offsets,
-                       const void* x_rows, const void* a_rows, const void* dO_rows,
-                       const void* dh_rows, void* dw_gate, void* dw_up, void* dw_down,
-                       void* stream);
+                       const void* x_rows, const int32_t* x_src, int x_div, const void* a_rows,
+                       const int32_t* a_src, const void* dO_rows, const void* dh_rows, void* dw_gate,
+                       void* dw_up, void* dw_down, void* stream);
 
 /* Router backward with the selection held fixed (issue #14, Proposal and Done
  * when: the gradients of the device path match the host path's).  The weights

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(LIB)
     missing = [n for n in declared_functions() if not hasattr(raw, n)]
     assert not missing, missing
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def _err(lib):
@@ -83,14 +83,18 @@ def test_grouped_calls_validation(lib):
     assert f(128, 64, 8, 128, -1, 0, P, P, P, P, P, P, P, P, NULL) == 1 and "max_expert_rows" in _err(lib)
     assert f(128, 64, 8, 128, 128, 0, P, P, P, NULL, P, P, P, P, NULL) == 1 and "w_up" in _err(lib)
     dx = lib.moe_grouped_bwd_dx
-    base = [64, 128, 64, 8, 2, 128, 0] + [P] * 15 + [NULL]
+    base = [64, 128, 64, 8, 2, 128, 0] + [P] * 16 + [NULL]
     bad = list(base); bad[5] = 129
     assert dx(*bad) == 1 and "max_rows" in _err(lib)
-    bad = list(base); bad[16] = NULL  # dg given, o_sorted missing
+    bad = list(base); bad[17] = NULL  # dg given, o_sorted missing
     assert dx(*bad) == 1 and "o_sorted" in _err(lib)
     dw = lib.moe_grouped_bwd_dw
-    assert dw(128, 64, 8, 128, 0, P, P, P, P, P, P, P, NULL, NULL) == 1 and "dw_down" in _err(lib)
-    assert dw(128, 64, 8, 128, 3, P, P, P, P, P, P, P, P, NULL) == 1
+    assert dw(128, 64, 8, 128, 0, P, P, NULL, 1, P, NULL, P, P, P, P, NULL, NULL) == 1 and "dw_down" in _err(lib)
+    assert dw(128, 64, 8, 128, 3, P, P, NULL, 1, P, NULL, P, P, P, P, P, NULL) == 1
+    assert dw(128, 64, 8, 128, 0, P, P, P, 0, P, NULL, P, P, P, P, P, NULL) == 1 and "divisor" in _err(lib)
+    rc = lib.moe_grouped_swiglu_recompute
+    assert rc(128, 64, 8, 128, 128, 0, P, P, P, 17, P, P, P, NULL, NULL) == 1 and "divisor" in _err(lib)
+    assert rc(128, 64, 8, 128, 128, 0, P, NULL, NULL, 1, P, P, P, NULL, NULL) == 1 and "x_rows" in _err(lib)
     assert lib.moe_combine(0, 128, 2, 0, P, P, P, P, NULL) == 1
     assert lib.moe_combine(4, 128, 2, 0, P, NULL, P, P, NULL) == 1
 
@@ -172,8 +176,8 @@ def test_fp8_weight_calls_validation(lib):
     bad = list(ok); bad[7] = A; bad[3] = 0
     assert f(*bad) == 1 and "k=" in _err(lib)
     d = lib.moe_grouped_bwd_dx_fp8w
-    ok = [128, 2048, 768, 128, 8, 1024] + [A] * 17 + [NULL]
-    bad = list(ok); bad[15] = NULL
+    ok = [128, 2048, 768, 128, 8, 1024] + [A] * 18 + [NULL]
+    bad = list(ok); bad[16] = NULL
     assert d(*bad) == 1 and "s_down" in _err(lib)
     bad = list(ok); bad[5] = 2000
     assert d(*bad) == 1 and "max_rows" in _err(lib)

@@ -50,13 +50,14 @@ def _full_compare(wl, d, L, rho=None, score=None):
             assert np.array_equal(getattr(L, "kept_" + name).cpu().numpy(), c[name]), "kept_" + name
         assert np.array_equal(L.kept_perm.cpu().numpy()[:R], c["perm"]), "kept_perm"
         assert np.array_equal(L.kept_src.cpu().numpy()[:R], c["src"]), "kept_src"
-        assert np.array_equal(np32(L.x_kept)[:R], xs[c["src"]]), "x_kept"
-        if L.keep_graph:
-            assert np.array_equal(np32(L.h_kept)[:R], np32(L.h_save)[c["src"]]), "h_kept"
-        else:  # recomputed over the kept rows
+        if not L.gather_rows:  # materialized compacted copies
+            assert np.array_equal(np32(L.x_kept)[:R], xs[c["src"]]), "x_kept"
+            if L.keep_graph:
+                assert np.array_equal(np32(L.h_kept)[:R], np32(L.h_save)[c["src"]]), "h_kept"
+            if wl.dw:
+                assert np.array_equal(np32(L.a_kept)[:R], np32(L.a_save)[c["src"]]), "a_kept"
+        if not L.keep_graph:  # recomputed over the kept rows
             assert_close("h_kept", np32(L.h_kept)[:R], h_ref[c["perm"]], tol)
-        if wl.dw:
-            assert np.array_equal(np32(L.a_kept)[:R], np32(L.a_save)[c["src"]]), "a_kept"
         retained = c["retained"]
         rows_pairs = c["perm"]
     dx, dg, bt = oracle.backward(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"], d["dy"], retained=retained,
@@ -197,24 +198,36 @@ def test_recompute_path_compacted_matches_oracle():
 
 @pytest.mark.parametrize("wl", [
     W.custom("bf16_gather", T=300, H=256, F=256, E=16, k=4, dtype="bf16", skew=True, dw=False),
-    W.custom("bf16_gather_big", T=700, H=256, F=256, E=4, k=2, dtype="bf16", skew=True, dw=False),
-    W.custom("fp32_gather", T=90, H=64, F=40, E=6, k=3, dtype="f32", skew=True, dw=False),
+    W.custom("bf16_gather_big", T=700, H=256, F=256, E=4, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("fp32_gather", T=90, H=64, F=40, E=6, k=3, dtype="f32", skew=True, dw=True),
+    W.custom("bf16_gather_compact", T=300, H=256, F=256, E=8, k=4, dtype="bf16", skew=True, dw=True, rho=0.6),
 ], ids=lambda w: w.name)
-def test_gather_on_load_is_bitwise_the_materialized_path(wl):
+@pytest.mark.parametrize("keep_graph", [True, False])
+def test_gather_on_load_is_bitwise_the_materialized_path(wl, keep_graph):
+    """Every GEMM reading token rows and saved activations through pair / row
+    indices (no x_sorted, no compacted copies) against the materialized path:
+    the same values read from other addresses, so every output is equal."""
     from expert_grouped_gemm_top_amd.layer import MoeLayerBuffers
     d = W.generate(wl, seed=9)
     logits = torch.from_numpy(logits_of(wl, d)).cuda()
     t = to_dev(wl, d)
     out = []
     for gather in (False, True):
-        L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, t["x"].dtype, "cuda", dw=False, gather_rows=gather)
+        L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, t["x"].dtype, "cuda", rho=wl.rho, dw=wl.dw,
+                            gather_rows=gather, keep_graph=keep_graph)
         L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"])
         L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"])
         out.append(L)
     torch.cuda.synchronize()
     assert out[1].gather_rows and not out[0].gather_rows
-    for n in ("h_save", "a_save", "o_sorted", "y", "dx", "dg"):
+    names = ["a_save", "o_sorted", "y", "dx", "dg"] + (["dw_gate", "dw_up", "dw_down"] if wl.dw else [])
+    names += ["h_save"] if keep_graph else []
+    names += ["kept_inv"] if wl.rho else []
+    for n in names:
         assert torch.equal(getattr(out[0], n), getattr(out[1], n)), n
+    R = int(out[0].kept_offsets[-1]) if wl.rho else wl.N  # rows the backward wrote
+    for n in ["dO", "dh", "dX"] + (["kept_perm", "kept_src"] if wl.rho else []):
+        assert torch.equal(getattr(out[0], n)[:R], getattr(out[1], n)[:R]), n
 
 
 def test_deterministic_bitwise():
@@ -223,7 +236,7 @@ def test_deterministic_bitwise():
     logits = logits_of(wl, d)
     a = run_gpu(wl, d, logits)
     b = run_gpu(wl, d, logits)
-    for n in ("topk_idx", "topk_w", "perm", "x_sorted", "h_save", "a_save", "o_sorted", "y", "dO", "dh", "dX", "dx",
+    for n in ("topk_idx", "topk_w", "perm", "h_save", "a_save", "o_sorted", "y", "dO", "dh", "dX", "dx",
               "dg", "dw_gate", "dw_up", "dw_down"):
         assert torch.equal(getattr(a, n), getattr(b, n)), n
 
