@@ -58,12 +58,13 @@ def to_dev(wl, d, dev="cuda"):
     return {n: torch.from_numpy(np.ascontiguousarray(d[n])).to(dev).to(dt) for n in ("x", "W_gate", "W_up", "W_down", "dy")}
 
 
-def run_gpu(wl, d, logits, rho=None, score=None, dw=None, dg=True, keep_graph=True):
-    note(f"gpu run {wl.name} T={wl.T} H={wl.H} F={wl.F} E={wl.E} k={wl.k} {wl.dtype} rho={rho} keep_graph={keep_graph}")
+def run_gpu(wl, d, logits, rho=None, score=None, dw=None, dg=True, keep_graph=True, gather_rows=None):
+    note(f"gpu run {wl.name} T={wl.T} H={wl.H} F={wl.F} E={wl.E} k={wl.k} {wl.dtype} rho={rho} keep_graph={keep_graph}"
+         f" gather_rows={gather_rows}")
     t = to_dev(wl, d)
     dt = t["x"].dtype
     L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, dt, "cuda", rho=rho, dw=wl.dw if dw is None else dw, dg=dg,
-                        keep_graph=keep_graph)
+                        keep_graph=keep_graph, gather_rows=gather_rows)
     L.forward(torch.from_numpy(np.ascontiguousarray(logits)).cuda(), t["x"], t["W_gate"], t["W_up"], t["W_down"])
     sc = None if score is None else torch.from_numpy(np.ascontiguousarray(score, dtype=np.float32)).cuda()
     L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], score=sc)

@@ -230,6 +230,40 @@ def test_gather_on_load_is_bitwise_the_materialized_path(wl, keep_graph):
         assert torch.equal(getattr(out[0], n)[:R], getattr(out[1], n)[:R]), n
 
 
+# Seeded random layer shapes, each option drawn at random (skew, dW, quota,
+# recompute, gathered or materialized rows), every output against the oracle.
+# At least 8 tokens: the tolerance is relative to a tensor's largest entry,
+# which presumes many entries (dg of a single pair is one dot product, which
+# can cancel to a few per cent of its terms; single-token layers have their
+# own cases above).
+def _random_case(i):
+    rng = np.random.default_rng(1000 + i)
+    E = int(rng.choice([1, 3, 8, 16, 37, 64]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.choice([8, 13, 33, 120, 257, 600]))
+    H = int(rng.choice([128, 256, 384]))
+    F = int(rng.choice([128, 256, 384]))
+    opts = dict(skew=bool(rng.integers(2)), dw=bool(rng.integers(2)))
+    rho = float(rng.choice([0.3, 0.7, 1.5])) if rng.integers(3) == 0 else None
+    keep_graph = bool(rng.integers(4))  # mostly kept
+    gather = bool(rng.integers(2))
+    wl = W.custom(f"rand{i}", T=T, H=H, F=F, E=E, k=k, dtype="bf16", rho=rho, **opts)
+    return wl, keep_graph, gather
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_layer_shapes(i):
+    wl, keep_graph, gather = _random_case(i)
+    d = W.generate(wl, seed=i)
+    logits = logits_of(wl, d)
+    score = None
+    if wl.rho is not None:
+        _, w = oracle.route_topk(logits, wl.k)
+        score = w.reshape(-1).astype(np.float32)
+    L = run_gpu(wl, d, logits, rho=wl.rho, score=score, keep_graph=keep_graph, gather_rows=gather)
+    _full_compare(wl, d, L, rho=wl.rho, score=score)
+
+
 def test_deterministic_bitwise():
     wl = W.custom("bf16_det", T=300, H=256, F=256, E=16, k=4, dtype="bf16", skew=True, dw=True)
     d = W.generate(wl, seed=4)
