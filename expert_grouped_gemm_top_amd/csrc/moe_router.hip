@@ -8,16 +8,21 @@
 //     dlogits[t, idx_j] = w_j (g_j - s_t),  dlogits[t, e] = 0 otherwise,
 //     dW_r = x^T dlogits,   dx += dlogits W_r^T.
 //
-// The three products are small next to the experts' (E columns against k * 3F),
-// so they run on one tiled fp32 kernel: 128 x 128 output tiles, reduction depth
-// 16 per LDS stage, 8 x 8 outputs per thread, every operand converted to fp32
-// on its way into LDS.  Two of them have few outputs and a long reduction
+// The three products are small next to the experts' (E columns against k * 3F).
+// In bf16 layers they run on the 16x16x32 bf16 matrix core: 64 x 64 output
+// tiles, four waves of 16 rows, operands staged through LDS as [row][k] bf16
+// whatever their layout in memory; the fp32 operand (dlogits) enters as two
+// bf16 parts, hi = bf16(v) and lo = bf16(v - hi), multiplied separately, so
+// its precision is kept to ~2^-16.  fp32 layers use a tiled fp32 kernel:
+// 128 x 128 output tiles, reduction depth 16 per LDS stage, 8 x 8 outputs per
+// thread.  Two of the products have few outputs and a long reduction
 // (logits: T x E over H; dW_r: H x E over T), so the reduction is cut into S
 // slices run by separate workgroups that write fp32 partial tiles to the
 // caller's workspace; a second kernel adds the S partials of each output in
 // slice order and rounds once.  Every output is thus reduced in one fixed
 // order (deterministic, no atomics).
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_common.h"
 #include "moe_launch.h"
@@ -120,6 +125,84 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(int M, int N, int K, c
   }
 }
 
+// The same product on the 16x16x32 bf16 matrix core (at least one operand bf16;
+// an fp32 operand is split into bf16 hi and lo parts).  Workgroup = 64 x 64
+// outputs, wave w owns rows 16 w .. 16 w + 15 and four 16-column blocks; the
+// reduction advances kMK at a time through LDS tiles [row][k].  Same slicing
+// and epilogue contract as router_gemm_kernel.
+constexpr int kMT = 64, kMK = 32, kMPitch = kMK + 8;  // tile, k-step, LDS row pitch (elements)
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 first, u32x4 second, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, first), __builtin_bit_cast(bf16x8, second),
+                                                  acc, 0, 0, 0);
+}
+
+template <typename TA, typename TB, typename TC, bool A_KC, bool B_KC, bool ACC>
+__global__ __launch_bounds__(256) void router_mfma_kernel(int M, int N, int K, const TA* __restrict__ a, int lda,
+                                                          const TB* __restrict__ b, int ldb, TC* __restrict__ c,
+                                                          int kslice, float* __restrict__ part) {
+  constexpr bool SA = std::is_same<TA, float>::value, SB = std::is_same<TB, float>::value;  // split operands
+  static_assert(!(SA && SB), "one operand is bf16");
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[SA ? 2 : 1][kMT][kMPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[SB ? 2 : 1][kMT][kMPitch];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int m0 = blockIdx.x * kMT, n0 = blockIdx.y * kMT;
+  const int kb0 = blockIdx.z * kslice, kb1 = min(K, kb0 + kslice);
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = kb0; k0 < kb1; k0 += kMK) {
+#pragma unroll
+    for (int i = 0; i < kMT * kMK / 256; ++i) {
+      const int q = tid + 256 * i;  // element of the 64 x 32 tile, contiguous index fastest
+      const int mm = A_KC ? q / kMK : q % kMT, kk = A_KC ? q % kMK : q / kMT;
+      const int m = m0 + mm, k = k0 + kk;
+      float v = 0.0f;
+      if (m < M && k < kb1) v = to_f32<TA>(A_KC ? a[(size_t)m * lda + k] : a[(size_t)k * lda + m]);
+      const uint32_t hv = f2bf(v);
+      s_a[0][mm][kk] = (uint16_t)hv;
+      if constexpr (SA) s_a[SA ? 1 : 0][mm][kk] = (uint16_t)f2bf(v - bf2f((uint16_t)hv));
+      const int nn = B_KC ? q / kMK : q % kMT, kq = B_KC ? q % kMK : q / kMT;
+      const int n = n0 + nn, kn = k0 + kq;
+      float u = 0.0f;
+      if (n < N && kn < kb1) u = to_f32<TB>(B_KC ? b[(size_t)n * ldb + kn] : b[(size_t)kn * ldb + n]);
+      const uint32_t hu = f2bf(u);
+      s_b[0][nn][kq] = (uint16_t)hu;
+      if constexpr (SB) s_b[SB ? 1 : 0][nn][kq] = (uint16_t)f2bf(u - bf2f((uint16_t)hu));
+    }
+    __syncthreads();
+    // fragments: lane l takes row / column l % 16 and k 8 (l / 16) .. + 7
+    const int fr = l & 15, fk = 8 * (l >> 4);
+    const u32x4 af = *(const u32x4*)&s_a[0][16 * w + fr][fk];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 bf = *(const u32x4*)&s_b[0][16 * j + fr][fk];
+      acc[j] = mfma16(af, bf, acc[j]);
+      if constexpr (SA) acc[j] = mfma16(*(const u32x4*)&s_a[SA ? 1 : 0][16 * w + fr][fk], bf, acc[j]);
+      if constexpr (SB) acc[j] = mfma16(af, *(const u32x4*)&s_b[SB ? 1 : 0][16 * j + fr][fk], acc[j]);
+    }
+    __syncthreads();
+  }
+  // register rr of lane l in block j: row 16 w + 4 (l / 16) + rr, column 16 j + l % 16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 16 * j + (l & 15);
+    if (n >= N) continue;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int m = m0 + 16 * w + 4 * (l >> 4) + rr;
+      if (m >= M) continue;
+      if (part != nullptr) {
+        part[((size_t)blockIdx.z * M + m) * N + n] = acc[j][rr];
+      } else {
+        TC* p = c + (size_t)m * N + n;
+        const float v = ACC ? to_f32<TC>(*p) + acc[j][rr] : acc[j][rr];
+        *p = from_f32<TC>(v);
+      }
+    }
+  }
+}
+
 // c[i] = sum_{z < slices} part[z*MN + i], z ascending, rounded once.
 template <typename TC>
 __global__ __launch_bounds__(256) void router_sum_slices_kernel(int64_t MN, int slices, const float* __restrict__ part,
@@ -181,8 +264,9 @@ int64_t slice_count(int M, int N, int K, bool may_split = true) {
 }
 
 int slice_length(int K, int64_t slices) {
+  // a multiple of both kernels' reduction step (16 and 32)
   const int64_t per = (K + slices - 1) / slices;
-  return (int)((per + kRBK - 1) / kRBK * kRBK);
+  return (int)((per + kMK - 1) / kMK * kMK);
 }
 
 size_t split_bytes(int M, int N, int K) {
@@ -200,7 +284,12 @@ hipError_t gemm(int M, int N, int K, const void* a, int lda, const void* b, int 
   const int tile = tile_of(M, N, K, may_split);
   const dim3 grid((M + tile - 1) / tile, (N + tile - 1) / tile, (unsigned)(slices > 1 ? used : 1));
   float* part = slices > 1 ? ws : nullptr;
-  if (tile == 128)
+  if constexpr (!std::is_same<TA, float>::value || !std::is_same<TB, float>::value) {
+    // bf16 layer: the matrix core, 64 x 64 tiles
+    const dim3 mgrid((M + kMT - 1) / kMT, (N + kMT - 1) / kMT, grid.z);
+    hipLaunchKernelGGL((router_mfma_kernel<TA, TB, TC, A_KC, B_KC, ACC>), mgrid, dim3(256), 0, stream, M, N, K,
+                       (const TA*)a, lda, (const TB*)b, ldb, (TC*)c, kslice, part);
+  } else if (tile == 128)
     hipLaunchKernelGGL((router_gemm_kernel<128, TA, TB, TC, A_KC, B_KC, ACC>), grid, dim3(256), 0, stream, M, N, K,
                        (const TA*)a, lda, (const TB*)b, ldb, (TC*)c, kslice, part);
   else
