@@ -137,12 +137,74 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 first, u32x4 second, f32x4 acc) {
                                                   acc, 0, 0, 0);
 }
 
+// Eight consecutive elements p[o * ld + c + j], j < 8, of an operand as fp32
+// (zero where o >= olim or c + j >= clim): one 16-byte load (two for fp32)
+// when the run is whole and aligned, else element by element.
+template <typename T>
+__device__ __forceinline__ void load_run(const T* __restrict__ p, int ld, int o, int olim, int c, int clim,
+                                         float (&v)[8]) {
+  const T* src = p + (size_t)(o < olim ? o : 0) * ld + c;
+  if (o < olim && c + 8 <= clim && ((uintptr_t)src & 15) == 0) {
+    if constexpr (std::is_same<T, float>::value) {
+      const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = lo[j];
+        v[4 + j] = hi[j];
+      }
+    } else {
+      const u32x4 r = *(const u32x4*)src;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf2f(r[j] & 0xffffu);
+        v[2 * j + 1] = bf2f(r[j] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (o < olim && c + j < clim) ? to_f32<T>(src[j]) : 0.0f;
+  }
+}
+
+// One thread's run of a 64 x kMK operand tile, stored [row][k] as bf16 (and,
+// for SPLIT, the residual v - hi in s[1]).  KC (k contiguous in memory): row
+// tid / 4, k 8 (tid % 4) .. + 7, one 16-byte LDS write; otherwise k tid / 8,
+// rows 8 (tid % 8) .. + 7, eight 2-byte writes (the transpose).
+template <bool KC>
+__device__ __forceinline__ int run_row(int tid) { return KC ? tid >> 2 : 8 * (tid & 7); }
+template <bool KC>
+__device__ __forceinline__ int run_k(int tid) { return KC ? 8 * (tid & 3) : tid >> 3; }
+
+template <bool KC, bool SPLIT>
+__device__ __forceinline__ void store_run(uint16_t (*s)[kMT][kMPitch], int tid, const float (&v)[8]) {
+  const int r = run_row<KC>(tid), kk = run_k<KC>(tid);
+  if constexpr (KC) {
+    u32x4 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t h0 = f2bf(v[2 * j]), h1 = f2bf(v[2 * j + 1]);
+      hi[j] = h0 | (h1 << 16);
+      if constexpr (SPLIT) lo[j] = f2bf(v[2 * j] - bf2f(h0)) | (f2bf(v[2 * j + 1] - bf2f(h1)) << 16);
+    }
+    *(u32x4*)&s[0][r][kk] = hi;
+    if constexpr (SPLIT) *(u32x4*)&s[1][r][kk] = lo;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t h = f2bf(v[j]);
+      s[0][r + j][kk] = (uint16_t)h;
+      if constexpr (SPLIT) s[1][r + j][kk] = (uint16_t)f2bf(v[j] - bf2f(h));
+    }
+  }
+}
+
 template <typename TA, typename TB, typename TC, bool A_KC, bool B_KC, bool ACC>
 __global__ __launch_bounds__(256) void router_mfma_kernel(int M, int N, int K, const TA* __restrict__ a, int lda,
                                                           const TB* __restrict__ b, int ldb, TC* __restrict__ c,
                                                           int kslice, float* __restrict__ part) {
   constexpr bool SA = std::is_same<TA, float>::value, SB = std::is_same<TB, float>::value;  // split operands
   static_assert(!(SA && SB), "one operand is bf16");
+  static_assert(kMT * kMK == 256 * 8, "one run of eight elements per thread and operand");
   __shared__ __attribute__((aligned(16))) uint16_t s_a[SA ? 2 : 1][kMT][kMPitch];
   __shared__ __attribute__((aligned(16))) uint16_t s_b[SB ? 2 : 1][kMT][kMPitch];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -151,26 +213,21 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(int M, int N, int K, c
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ra[8], rb[8];  // the next k-step's runs, loaded while this one computes
+  auto gload = [&](int k0) {
+    const int ar = m0 + run_row<A_KC>(tid), ak = k0 + run_k<A_KC>(tid);
+    if constexpr (A_KC) load_run(a, lda, ar, M, ak, kb1, ra);
+    else load_run(a, lda, ak, kb1, ar, M, ra);
+    const int br = n0 + run_row<B_KC>(tid), bk = k0 + run_k<B_KC>(tid);
+    if constexpr (B_KC) load_run(b, ldb, br, N, bk, kb1, rb);
+    else load_run(b, ldb, bk, kb1, br, N, rb);
+  };
+  if (kb0 < kb1) gload(kb0);
   for (int k0 = kb0; k0 < kb1; k0 += kMK) {
-#pragma unroll
-    for (int i = 0; i < kMT * kMK / 256; ++i) {
-      const int q = tid + 256 * i;  // element of the 64 x 32 tile, contiguous index fastest
-      const int mm = A_KC ? q / kMK : q % kMT, kk = A_KC ? q % kMK : q / kMT;
-      const int m = m0 + mm, k = k0 + kk;
-      float v = 0.0f;
-      if (m < M && k < kb1) v = to_f32<TA>(A_KC ? a[(size_t)m * lda + k] : a[(size_t)k * lda + m]);
-      const uint32_t hv = f2bf(v);
-      s_a[0][mm][kk] = (uint16_t)hv;
-      if constexpr (SA) s_a[SA ? 1 : 0][mm][kk] = (uint16_t)f2bf(v - bf2f((uint16_t)hv));
-      const int nn = B_KC ? q / kMK : q % kMT, kq = B_KC ? q % kMK : q / kMT;
-      const int n = n0 + nn, kn = k0 + kq;
-      float u = 0.0f;
-      if (n < N && kn < kb1) u = to_f32<TB>(B_KC ? b[(size_t)n * ldb + kn] : b[(size_t)kn * ldb + n]);
-      const uint32_t hu = f2bf(u);
-      s_b[0][nn][kq] = (uint16_t)hu;
-      if constexpr (SB) s_b[SB ? 1 : 0][nn][kq] = (uint16_t)f2bf(u - bf2f((uint16_t)hu));
-    }
+    store_run<A_KC, SA>(s_a, tid, ra);
+    store_run<B_KC, SB>(s_b, tid, rb);
     __syncthreads();
+    if (k0 + kMK < kb1) gload(k0 + kMK);
     // fragments: lane l takes row / column l % 16 and k 8 (l / 16) .. + 7
     const int fr = l & 15, fk = 8 * (l >> 4);
     const u32x4 af = *(const u32x4*)&s_a[0][16 * w + fr][fk];

@@ -51,6 +51,7 @@ SHAPES = [
     (300, 384, 128, 8, "bf16"),
     (70, 136, 256, 16, "f32"),
     (1, 128, 1, 1, "bf16"),
+    (33, 104, 20, 3, "bf16"),  # rows of W_r at alternating 16-byte alignment, a ragged reduction tail
     (4096, 2048, 128, 8, "bf16"),  # the Qwen3-30B-A3B router at 4096 tokens
 ]
 
