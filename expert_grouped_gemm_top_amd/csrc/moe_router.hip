@@ -26,6 +26,7 @@
 
 #include "moe_common.h"
 #include "moe_launch.h"
+#include "moe_lds32.h"
 
 namespace moe {
 
@@ -128,9 +129,20 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(int M, int N, int K, c
 // The same product on the 16x16x32 bf16 matrix core (at least one operand bf16;
 // an fp32 operand is split into bf16 hi and lo parts).  Workgroup = 64 x 64
 // outputs, wave w owns rows 16 w .. 16 w + 15 and four 16-column blocks; the
-// reduction advances kMK at a time through LDS tiles [row][k].  Same slicing
-// and epilogue contract as router_gemm_kernel.
-constexpr int kMT = 64, kMK = 32, kMPitch = kMK + 8;  // tile, k-step, LDS row pitch (elements)
+// reduction advances kMK at a time.  Each thread moves kRuns runs of eight
+// consecutive elements of each operand per k-step (a 16-byte load each, two
+// for fp32), loaded one k-step ahead, and writes each to LDS as one 16-byte
+// chunk in the operand's own memory order: [row][k] when k is contiguous in
+// memory, else [k][row], whose fragments are read with the gfx950 transpose
+// read ds_read_b64_tr_b16.  The output tile is staged through LDS so that
+// every row leaves as 16-byte stores.  Same slicing and epilogue contract as router_gemm_kernel.
+constexpr int kMT = 64, kMK = 32;  // (k-steps of 64 measured slower: fewer workgroups fit a CU)
+constexpr int kRuns = kMT * kMK / (256 * 8);  // runs of eight elements per thread and operand tile
+constexpr int kKcPitch = kMK + 8;  // [row][k] tiles: 80-byte rows
+constexpr int kRcPitch = kMT + 8;  // [k][row] tiles: 144-byte rows (the 4 k rows of a transpose read hit distinct banks)
+constexpr int kPart = kMT * kKcPitch;  // elements of one bf16 tile part (either layout)
+constexpr int kCPitch = kMT + 4;       // fp32 output staging, floats per row
+static_assert(kMK * kRcPitch <= kPart, "tile part size");
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 first, u32x4 second, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, first), __builtin_bit_cast(bf16x8, second),
@@ -166,34 +178,88 @@ __device__ __forceinline__ void load_run(const T* __restrict__ p, int ld, int o,
   }
 }
 
-// One thread's run of a 64 x kMK operand tile, stored [row][k] as bf16 (and,
-// for SPLIT, the residual v - hi in s[1]).  KC (k contiguous in memory): row
-// tid / 4, k 8 (tid % 4) .. + 7, one 16-byte LDS write; otherwise k tid / 8,
-// rows 8 (tid % 8) .. + 7, eight 2-byte writes (the transpose).
+// Run q (= thread + 256 i) of a 64 x kMK operand tile: KC (k contiguous) row
+// q / (kMK / 8), k 8 (q % (kMK / 8)) .. + 7; otherwise k q / 8, rows
+// 8 (q % 8) .. + 7.
+static_assert(kMT == 64 && kMK % 32 == 0 && kRuns >= 1, "run mapping");
+constexpr int kKcRuns = kMK / 8;  // runs per row of a KC tile
 template <bool KC>
-__device__ __forceinline__ int run_row(int tid) { return KC ? tid >> 2 : 8 * (tid & 7); }
+__device__ __forceinline__ int run_row(int q) { return KC ? q / kKcRuns : 8 * (q & 7); }
 template <bool KC>
-__device__ __forceinline__ int run_k(int tid) { return KC ? 8 * (tid & 3) : tid >> 3; }
+__device__ __forceinline__ int run_k(int q) { return KC ? 8 * (q % kKcRuns) : q >> 3; }
 
+// The run as bf16 into part 0 of the tile (and, SPLIT, the residuals v - hi
+// into part 1), one 16-byte chunk each.
 template <bool KC, bool SPLIT>
-__device__ __forceinline__ void store_run(uint16_t (*s)[kMT][kMPitch], int tid, const float (&v)[8]) {
-  const int r = run_row<KC>(tid), kk = run_k<KC>(tid);
+__device__ __forceinline__ void store_run(uint16_t* s, int q, const float (&v)[8]) {
+  const int off = KC ? run_row<KC>(q) * kKcPitch + run_k<KC>(q) : run_k<KC>(q) * kRcPitch + run_row<KC>(q);
+  u32x4 hi, lo;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t h0 = f2bf(v[2 * j]), h1 = f2bf(v[2 * j + 1]);
+    hi[j] = h0 | (h1 << 16);
+    if constexpr (SPLIT) lo[j] = f2bf(v[2 * j] - bf2f(h0)) | (f2bf(v[2 * j + 1] - bf2f(h1)) << 16);
+  }
+  *(u32x4*)&s[off] = hi;
+  if constexpr (SPLIT) *(u32x4*)&s[kPart + off] = lo;
+}
+
+// 16x16x32 fragment of tile rows row0 .. row0 + 15 and k k0 .. k0 + 31: lane
+// l gets row row0 + l % 16, k k0 + 8 (l / 16) .. + 7.  From a [k][row] tile by
+// two transpose reads: in 16-lane group G, lane r points at k row
+// k0 + 8 G + 4 h + r / 4 and rows row0 + 4 (r % 4) .. + 3, and receives the 4 k
+// of row row0 + r.
+template <bool KC>
+__device__ __forceinline__ u32x4 frag(const uint16_t* s, int row0, int k0) {
+  const int l = __lane_id();
   if constexpr (KC) {
-    u32x4 hi, lo;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t h0 = f2bf(v[2 * j]), h1 = f2bf(v[2 * j + 1]);
-      hi[j] = h0 | (h1 << 16);
-      if constexpr (SPLIT) lo[j] = f2bf(v[2 * j] - bf2f(h0)) | (f2bf(v[2 * j + 1] - bf2f(h1)) << 16);
-    }
-    *(u32x4*)&s[0][r][kk] = hi;
-    if constexpr (SPLIT) *(u32x4*)&s[1][r][kk] = lo;
+    return *(const u32x4*)&s[(row0 + (l & 15)) * kKcPitch + k0 + 8 * (l >> 4)];
   } else {
+    const int G = l >> 4, r = l & 15;
+    v4i16 q[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t h = f2bf(v[j]);
-      s[0][r + j][kk] = (uint16_t)h;
-      if constexpr (SPLIT) s[1][r + j][kk] = (uint16_t)f2bf(v[j] - bf2f(h));
+    for (int h = 0; h < 2; ++h)
+      q[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(lds_void*)&s[(k0 + 8 * G + 4 * h + (r >> 2)) * kRcPitch + row0 + 4 * (r & 3)]);
+    return u32x4{(uint32_t)(uint16_t)q[0][0] | ((uint32_t)(uint16_t)q[0][1] << 16),
+                 (uint32_t)(uint16_t)q[0][2] | ((uint32_t)(uint16_t)q[0][3] << 16),
+                 (uint32_t)(uint16_t)q[1][0] | ((uint32_t)(uint16_t)q[1][1] << 16),
+                 (uint32_t)(uint16_t)q[1][2] | ((uint32_t)(uint16_t)q[1][3] << 16)};
+  }
+}
+
+// Sixteen consecutive outputs of row m from the staging row, written (and for
+// ACC added to the current contents) as 16-byte runs when whole and aligned.
+template <typename TC, bool ACC>
+__device__ __forceinline__ void store_out(TC* __restrict__ dst, const float* src, int cols) {
+  constexpr int V = 16 / sizeof(TC);  // outputs per 16-byte chunk
+  if (cols >= 16 && ((uintptr_t)dst & 15) == 0) {
+#pragma unroll
+    for (int q = 0; q < 16 / V; ++q) {
+      if constexpr (std::is_same<TC, float>::value) {
+        f32x4 o = *(const f32x4*)&src[4 * q];
+        if constexpr (ACC) o += *(const f32x4*)&dst[4 * q];
+        *(f32x4*)&dst[4 * q] = o;
+      } else {
+        u32x4 o;
+        u32x4 cur;
+        if constexpr (ACC) cur = *(const u32x4*)&dst[8 * q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v0 = src[8 * q + 2 * j], v1 = src[8 * q + 2 * j + 1];
+          if constexpr (ACC) {
+            v0 += bf2f(cur[j] & 0xffffu);
+            v1 += bf2f(cur[j] >> 16);
+          }
+          o[j] = f2bf(v0) | (f2bf(v1) << 16);
+        }
+        *(u32x4*)&dst[8 * q] = o;
+      }
+    }
+  } else {
+    for (int j = 0; j < 16 && j < cols; ++j) {
+      const float v = ACC ? to_f32<TC>(dst[j]) + src[j] : src[j];
+      dst[j] = from_f32<TC>(v);
     }
   }
 }
@@ -204,60 +270,69 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(int M, int N, int K, c
                                                           int kslice, float* __restrict__ part) {
   constexpr bool SA = std::is_same<TA, float>::value, SB = std::is_same<TB, float>::value;  // split operands
   static_assert(!(SA && SB), "one operand is bf16");
-  static_assert(kMT * kMK == 256 * 8, "one run of eight elements per thread and operand");
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[SA ? 2 : 1][kMT][kMPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[SB ? 2 : 1][kMT][kMPitch];
+  constexpr int PA = SA ? 2 : 1, PB = SB ? 2 : 1;
+  constexpr int kOpBytes = (PA + PB) * kPart * 2, kOutBytes = kMT * kCPitch * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kOpBytes > kOutBytes ? kOpBytes : kOutBytes];
+  uint16_t* s_a = (uint16_t*)smem;
+  uint16_t* s_b = s_a + PA * kPart;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int m0 = blockIdx.x * kMT, n0 = blockIdx.y * kMT;
   const int kb0 = blockIdx.z * kslice, kb1 = min(K, kb0 + kslice);
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ra[8], rb[8];  // the next k-step's runs, loaded while this one computes
+  float ra[kRuns][8], rb[kRuns][8];  // the next k-step's runs, loaded while this one computes
   auto gload = [&](int k0) {
-    const int ar = m0 + run_row<A_KC>(tid), ak = k0 + run_k<A_KC>(tid);
-    if constexpr (A_KC) load_run(a, lda, ar, M, ak, kb1, ra);
-    else load_run(a, lda, ak, kb1, ar, M, ra);
-    const int br = n0 + run_row<B_KC>(tid), bk = k0 + run_k<B_KC>(tid);
-    if constexpr (B_KC) load_run(b, ldb, br, N, bk, kb1, rb);
-    else load_run(b, ldb, bk, kb1, br, N, rb);
+#pragma unroll
+    for (int i = 0; i < kRuns; ++i) {
+      const int q = tid + 256 * i;
+      const int ar = m0 + run_row<A_KC>(q), ak = k0 + run_k<A_KC>(q);
+      if constexpr (A_KC) load_run(a, lda, ar, M, ak, kb1, ra[i]);
+      else load_run(a, lda, ak, kb1, ar, M, ra[i]);
+      const int br = n0 + run_row<B_KC>(q), bk = k0 + run_k<B_KC>(q);
+      if constexpr (B_KC) load_run(b, ldb, br, N, bk, kb1, rb[i]);
+      else load_run(b, ldb, bk, kb1, br, N, rb[i]);
+    }
   };
   if (kb0 < kb1) gload(kb0);
   for (int k0 = kb0; k0 < kb1; k0 += kMK) {
-    store_run<A_KC, SA>(s_a, tid, ra);
-    store_run<B_KC, SB>(s_b, tid, rb);
+#pragma unroll
+    for (int i = 0; i < kRuns; ++i) {
+      store_run<A_KC, SA>(s_a, tid + 256 * i, ra[i]);
+      store_run<B_KC, SB>(s_b, tid + 256 * i, rb[i]);
+    }
     __syncthreads();
     if (k0 + kMK < kb1) gload(k0 + kMK);
-    // fragments: lane l takes row / column l % 16 and k 8 (l / 16) .. + 7
-    const int fr = l & 15, fk = 8 * (l >> 4);
-    const u32x4 af = *(const u32x4*)&s_a[0][16 * w + fr][fk];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 bf = *(const u32x4*)&s_b[0][16 * j + fr][fk];
-      acc[j] = mfma16(af, bf, acc[j]);
-      if constexpr (SA) acc[j] = mfma16(*(const u32x4*)&s_a[SA ? 1 : 0][16 * w + fr][fk], bf, acc[j]);
-      if constexpr (SB) acc[j] = mfma16(af, *(const u32x4*)&s_b[SB ? 1 : 0][16 * j + fr][fk], acc[j]);
+    for (int ks = 0; ks < kMK; ks += 32) {
+      const u32x4 af = frag<A_KC>(s_a, 16 * w, ks);
+      u32x4 al;
+      if constexpr (SA) al = frag<A_KC>(s_a + kPart, 16 * w, ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 bf = frag<B_KC>(s_b, 16 * j, ks);
+        acc[j] = mfma16(af, bf, acc[j]);
+        if constexpr (SA) acc[j] = mfma16(al, bf, acc[j]);
+        if constexpr (SB) acc[j] = mfma16(af, frag<B_KC>(s_b + kPart, 16 * j, ks), acc[j]);
+      }
     }
     __syncthreads();
   }
-  // register rr of lane l in block j: row 16 w + 4 (l / 16) + rr, column 16 j + l % 16
+  // register rr of lane l in block j: tile row 16 w + 4 (l / 16) + rr, column
+  // 16 j + l % 16 -> staging; then thread t writes row t / 4, columns
+  // 16 (t % 4) .. + 15
+  float* s_c = (float*)smem;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 16 * j + (l & 15);
-    if (n >= N) continue;
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int m = m0 + 16 * w + 4 * (l >> 4) + rr;
-      if (m >= M) continue;
-      if (part != nullptr) {
-        part[((size_t)blockIdx.z * M + m) * N + n] = acc[j][rr];
-      } else {
-        TC* p = c + (size_t)m * N + n;
-        const float v = ACC ? to_f32<TC>(*p) + acc[j][rr] : acc[j][rr];
-        *p = from_f32<TC>(v);
-      }
-    }
-  }
+    for (int rr = 0; rr < 4; ++rr) s_c[(16 * w + 4 * (l >> 4) + rr) * kCPitch + 16 * j + (l & 15)] = acc[j][rr];
+  __syncthreads();
+  const int r = tid >> 2, c0 = 16 * (tid & 3);
+  const int m = m0 + r, n = n0 + c0;
+  if (m >= M || n >= N) return;
+  const float* src = &s_c[r * kCPitch + c0];
+  if (part != nullptr) store_out<float, false>(part + ((size_t)blockIdx.z * M + m) * N + n, src, N - n);
+  else store_out<TC, ACC>(c + (size_t)m * N + n, src, N - n);
 }
 
 // c[i] = sum_{z < slices} part[z*MN + i], z ascending, rounded once.
@@ -314,6 +389,8 @@ int tile_of(int M, int N, int K, bool may_split) {
   return t128 * slices_for(t128, K, may_split) >= 256 ? 128 : 64;
 }
 
+// (the matrix-core kernel takes the same slices over its 64 x 64 tiles; a
+// chip-sized grid of workgroups that walk the tiles measured slower)
 int64_t slice_count(int M, int N, int K, bool may_split = true) {
   const int tile = tile_of(M, N, K, may_split);
   const int64_t tiles = (int64_t)((M + tile - 1) / tile) * ((N + tile - 1) / tile);
