@@ -39,7 +39,7 @@ K_ROUTER_FWD, K_ROUTER_DW = 10, 11
 KERNEL_NAMES = {K_GATEUP: "row_gemm_bf16_kernel<GATEUP>", K_DOWN: "row_gemm_bf16_kernel<DOWN>",
                 K_DA: "row_gemm_bf16_kernel<DA>", K_DX: "row_gemm_bf16_kernel<DX>", K_DW: "dw_bf16_kernel",
                 K_DISPATCH_ROWS: "dispatch_rows_kernel", K_GRAD_ROWS: "grad_rows_kernel",
-                K_COMBINE: "combine_kernel", K_ROUTER_FWD: "router_gemm_kernel<logits>",
+                K_COMBINE: "combine_kernel", K_ROUTER_FWD: "router logits (x W_r)",
                 K_ROUTER_DW: "router_bwd (dlogits, dW_r, dx)"}
 
 
@@ -215,7 +215,11 @@ def main():
 
     gemm_kernels = [K_GATEUP, K_DOWN] + ([] if args.forward_only else [K_DA, K_DX] + ([K_DW] if wl.dw else []))
     router_kernels = ([K_ROUTER_FWD] + ([] if args.forward_only else [K_ROUTER_DW])) if args.router else []
-    profiled = gemm_kernels + router_kernels
+    # HBM-bound row kernels launched once per step (the first combine of a step
+    # is the forward's); the row copy of dispatch only when rows are materialized
+    hbm_kernels = ([] if L.gather_rows else [K_DISPATCH_ROWS]) + [K_COMBINE] + \
+                  ([] if args.forward_only else [K_GRAD_ROWS])
+    profiled = gemm_kernels + router_kernels + hbm_kernels
     lib = moe.lib()
     lib.moe_profile_kernel.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
 
@@ -288,14 +292,19 @@ def main():
                    "experts_with_rows": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max())},
         "tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
         "mfma_frac_of_step": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "kernel_us": {KERNEL_NAMES[kk]: kernel_ms[kk] * 1e3 for kk in profiled},
+        "kernel_us": {KERNEL_NAMES[kk]: kernel_ms[kk] * 1e3 for kk in gemm_kernels + router_kernels},
         "roofline": roof,
+        # dispatch / combine / dO rows against the HBM peak (algorithmic bytes)
+        "hbm_kernels": {KERNEL_NAMES[kk]: {"us": kernel_ms[kk] * 1e3,
+                                           "GB/s": alg[kk][0] / (kernel_ms[kk] * 1e-3) / 1e9,
+                                           "frac": alg[kk][0] / (kernel_ms[kk] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                        for kk in hbm_kernels},
     }
     if args.router:
-        # router kernels run on the fp32 vector ALUs (roofline: fp32 vector peak)
+        # bf16 router products run on the bf16 matrix cores (roofline: bf16 MFMA peak)
         out["router"] = {KERNEL_NAMES[kk]: {"us": kernel_ms[kk] * 1e3,
                                             "TFLOP/s": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12,
-                                            "frac_fp32_alu": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
+                                            "frac_bf16_mfma": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                             "GB/s": alg[kk][0] / (kernel_ms[kk] * 1e-3) / 1e9}
                          for kk in router_kernels}
     if args.copy_probe_mib > 0:

@@ -304,18 +304,21 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   }
 
   if (split) {
-    // parts 1.. -> each into its own wave's LDS area (which only it has used);
-    // part 0 adds them in part order
+    // parts 1.. -> each into its own wave's LDS area (for K-contiguous weights
+    // the one only it has used for its stages); part 0 adds them in part order
     constexpr int NACC = NN ? 8 : 4;
+    // a wave's partials go to its own area: 8 KiB (N-contiguous weights use no
+    // other LDS here) or the 16 KiB of its K-contiguous stages
+    constexpr int kRedBytes = NN ? NACC * kWave * 16 : 16384;
     if (kpart > 0) {
-      f32x4* red = reinterpret_cast<f32x4*>(lds + w * 16384);
+      f32x4* red = reinterpret_cast<f32x4*>(lds + w * kRedBytes);
 #pragma unroll
       for (int j = 0; j < NACC; ++j) red[j * kWave + l] = acc[j];
     }
     __syncthreads();
     if (kpart > 0) return;
     for (int p = 1; p < ks; ++p) {
-      const f32x4* red = reinterpret_cast<const f32x4*>(lds + (w + p * cpw) * 16384);
+      const f32x4* red = reinterpret_cast<const f32x4*>(lds + (w + p * cpw) * kRedBytes);
 #pragma unroll
       for (int j = 0; j < NACC; ++j) acc[j] = acc[j] + red[j * kWave + l];
     }
@@ -660,7 +663,8 @@ template <int MODE>
 __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, int n_stream, int n_tile) {
   __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
   // 64 KiB: the tiled kernel's double-buffered A and B tiles, or the streaming
-  // kernel's four per-wave 16 KiB areas
+  // kernel's four per-wave areas (16 KiB of stages, or 8 KiB of split partial
+  // sums for N-contiguous weights)
   __shared__ __attribute__((aligned(16))) uint16_t s_ab[2 * kTBM * kTPitch + 2 * kTBN * kTPitch];
   static_assert(sizeof(s_ab) == 4 * 16384, "streaming kernel: 16 KiB of LDS per wave");
   if ((int)blockIdx.x < n_stream)
@@ -670,11 +674,14 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, in
 }
 
 // fp8 weights: every expert on the streaming kernel (one wave per 16-row tile
-// and column block), so weight bytes are read once per 16 rows.
+// and column block), so weight bytes are read once per 16 rows.  Gate/up and
+// down need only 8 KiB of LDS per wave (split partial sums), which lets more
+// workgroups share a CU (gate/up: four waves per SIMD instead of two).
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void row_gemm_fp8w_kernel(RowGemmArgs g) {
   __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
-  __shared__ __attribute__((aligned(16))) unsigned char s_lds[4 * 16384];  // 16 KiB per wave
+  // per wave: 8 KiB of split partial sums (N-contiguous) or 16 KiB of stages
+  __shared__ __attribute__((aligned(16))) unsigned char s_lds[RowGemmShape<MODE>::kNN ? 4 * 8192 : 4 * 16384];
   stream_gemm<MODE, true>(g, blockIdx.x, s_start, s_off, s_tmp, s_lds);
 }
 
