@@ -12,7 +12,11 @@ dominant kernel (its duration from HIP events on its own stream, inside the
 timed steps), and the CPU oracle timed on the host cores.  Between the warmup
 and the timed steps, a few untimed steps with every GEMM bracketed by events
 give the per-kernel durations and pick the dominant kernel; inside the timed
-steps only that kernel is bracketed (each event costs stream time).
+steps only that kernel is bracketed (each event costs stream time).  After the
+timed steps (untimed, --no-probes skips them): the per-step time distribution
+(median, p10, p90; back to back and with the last-level cache flushed before
+every step) and probes of plain read / write / copy bandwidth and of a bf16
+library matmul on the same GPU, as context for the roofline fractions.
 """
 from __future__ import annotations
 
@@ -65,6 +69,8 @@ def parse():
     p.add_argument("--fp8-weights", action="store_true",
                    help="frozen expert weights stored once in fp8 (E4M3, one power-of-two scale per expert) and read "
                         "by the GEMMs (LoRA and forward-only workloads; not the headline configuration)")
+    p.add_argument("--no-probes", action="store_true",
+                   help="skip the per-step distribution pass and the bandwidth / matrix-core probes")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after the timed steps, run one plain elementwise copy of this many MiB (read and write "
                         "each) so that HBM byte counters can be calibrated against a kernel of known traffic")
@@ -139,6 +145,66 @@ def algorithmic(wl, counts, kept_counts=None, gathered=False, weight_bytes=None)
         K_ROUTER_DW: (2 * T * H * b + H * wl.E * b + 8 * T * wl.E + H * wl.E * b + T * H * b + 12 * T * k,
                       4.0 * T * H * wl.E),
     }
+
+
+def step_distribution(step, stream, dev, n):
+    """Untimed pass after the timed steps: every step bracketed by HIP events on
+    the layer's stream; median / p10 / p90 in ms, once back to back and once
+    with a 512 MiB buffer overwritten before every step, so that nothing the
+    previous step left in the 256 MB last-level cache is reused."""
+    import numpy as np
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def run(flushed):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in ev:  # no host sync between steps: the stream stays fed
+            if flushed:
+                flush.fill_(1)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        q = np.percentile([a.elapsed_time(b) for a, b in ev], [10, 50, 90])
+        return {"p10": float(q[0]), "median": float(q[1]), "p90": float(q[2])}
+
+    out = {"steps": n, "back_to_back": run(False), "cache_flushed": run(True)}
+    del flush
+    return out
+
+
+def probes(dev):
+    """What this GPU reaches on plain work, as context for the roofline
+    fractions (torch's own kernels): a write (fill) and a copy (read + write,
+    both counted) over 1 GiB, and a bf16 8192^3 matmul (hipBLASLt).  No read
+    probe: torch's reductions do not stream at HBM speed."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+
+    def best_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    res = {"write_GBs": n / best_ms(lambda: dst.fill_(2.0)) / 1e6,
+           "copy_GBs": 2 * n / best_ms(lambda: dst.copy_(src)) / 1e6,
+           "bf16_matmul_8192_TFLOPs": 2 * 8192 ** 3 / best_ms(lambda: torch.mm(a, b)) / 1e9}
+    del src, dst, a, b
+    return res
 
 
 def cpu_baseline(wl, d, logits, sample_tokens):
@@ -307,6 +373,9 @@ def main():
                                             "frac_bf16_mfma": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                             "GB/s": alg[kk][0] / (kernel_ms[kk] * 1e-3) / 1e9}
                          for kk in router_kernels}
+    if not args.no_probes:
+        out["step_ms"] = step_distribution(step, stream, dev, n=max(10, min(args.steps, 20)))
+        out["probes"] = probes(dev)
     if args.copy_probe_mib > 0:
         # one read + one write of copy_probe_mib MiB each, outside the timed steps
         src = torch.ones(args.copy_probe_mib << 19, dtype=torch.bfloat16, device=dev)
