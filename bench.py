@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens of the CPU-oracle sample (0: auto)")
     p.add_argument("--router", action="store_true",
                    help="run the router in front of the path (logits = x W_r, drawn W_r) and its backward after dx")
+    p.add_argument("--overlap-dw", action="store_true",
+                   help="full fine-tuning: weight gradients on a second stream alongside the dX GEMM and the dx sum")
     p.add_argument("--no-keep-graph", action="store_true",
                    help="recompute path: the forward keeps no pre-activations, the backward recomputes them")
     p.add_argument("--forward-only", action="store_true",
@@ -260,7 +262,8 @@ def main():
                                                  not args.no_keep_graph, args.budget_mib << 20)
         assert quota_cap >= 1, "the budget does not hold one row per expert"
     L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho if quota_cap is None else None,
-                        dw=wl.dw, dg=True, router=args.router, keep_graph=not args.no_keep_graph, quota_cap=quota_cap)
+                        dw=wl.dw, dg=True, router=args.router, keep_graph=not args.no_keep_graph, quota_cap=quota_cap,
+                        overlap_dw=args.overlap_dw)
     score = "metric" if args.metric_score else None
     wq = None
     if args.fp8_weights:
@@ -350,6 +353,7 @@ def main():
                            + (f"+compact(rho={wl.rho})" if wl.rho and not quota_cap else "")
                            + ("+router_bwd" if args.router else "")
                            + ("+recompute_h" if args.no_keep_graph else "")
+                           + ("+dW_overlapped" if args.overlap_dw and wl.dw and not args.forward_only else "")
                            + ("+metric_score" if args.metric_score else "")
                            + (f"+budget({args.budget_mib} MiB: cap {quota_cap})" if quota_cap else "")
                            + ("+fp8_weights" if wq is not None else ""),

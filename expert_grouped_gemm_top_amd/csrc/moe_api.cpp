@@ -23,6 +23,10 @@ struct Armed {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 thread_local Armed g_armed[MOE_K_COUNT];
+// one-shot event armed by moe_signal_dh_ready; the next dx call takes it
+thread_local hipEvent_t g_dh_ready = nullptr;
+
+hipError_t record_if(hipEvent_t ev, hipStream_t s) { return ev == nullptr ? hipSuccess : hipEventRecord(ev, s); }
 
 // Runs one kernel launch `f` (returning hipError_t) between the armed events of `kind`.
 template <typename Fn>
@@ -191,6 +195,8 @@ int bwd_dx(const char* fn, int T, int H, int F, int E, int k, int max_rows, int 
            void* dO_rows, void* dh_rows, void* dX_rows, void* dx, void* stream, const float* s_gu,
            const float* s_down) {
   const bool w8 = s_gu != nullptr;
+  const hipEvent_t dh_ready = g_dh_ready;  // taken by this call whatever its outcome
+  g_dh_ready = nullptr;
   int rc = check_routing_dims(fn, T, E, k);
   if (rc || (rc = check_expert_dims(fn, H, F, E, dtype)) || (rc = check_rows(fn, max_rows))) return rc;
   REQUIRE(max_rows <= T * k, MOE_ERR_INVALID_ARGUMENT, "%s: max_rows=%d exceeds T*k=%d", fn, max_rows, T * k);
@@ -241,6 +247,7 @@ int bwd_dx(const char* fn, int T, int H, int F, int E, int k, int max_rows, int 
     g.out0 = (uint16_t*)dh_rows;
     g.wscale = s_down;
     if ((rc = hip_status(run(moe::kGemmDA), fn))) return rc;
+    if ((rc = hip_status(record_if(dh_ready, s), fn))) return rc;
     g.a = (const uint16_t*)dh_rows;
     g.w0 = (const uint16_t*)w_gate;
     g.w1 = (const uint16_t*)w_up;
@@ -249,6 +256,8 @@ int bwd_dx(const char* fn, int T, int H, int F, int E, int k, int max_rows, int 
     g.out0 = (uint16_t*)dX_rows;
     g.wscale = s_gu;
     if ((rc = hip_status(run(moe::kGemmDX), fn))) return rc;
+  } else if ((rc = hip_status(record_if(dh_ready, s), fn))) {  // no rows: dO (and dg) are all there is
+    return rc;
   }
   return hip_status(timed(MOE_K_COMBINE, s, [&] { return moe::launch_combine(T, H, k, es, dX_rows, inv, nullptr, dx, s); }),
                     fn);
@@ -280,6 +289,11 @@ int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
           "%s: give both events or neither", fn);
   g_armed[kernel].start = reinterpret_cast<hipEvent_t>(start_event);
   g_armed[kernel].stop = reinterpret_cast<hipEvent_t>(stop_event);
+  return MOE_OK;
+}
+
+int moe_signal_dh_ready(void* event) {
+  g_dh_ready = reinterpret_cast<hipEvent_t>(event);
   return MOE_OK;
 }
 

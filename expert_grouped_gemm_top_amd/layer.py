@@ -16,7 +16,7 @@ from . import moe
 
 class MoeLayerBuffers:
     def __init__(self, T, H, F, E, k, dtype=torch.bfloat16, device="cuda", rho=None, dw=True, dg=True,
-                 router=False, keep_graph=True, quota_cap=None, gather_rows=None):
+                 router=False, keep_graph=True, quota_cap=None, gather_rows=None, overlap_dw=False):
         """rho: quota ratio of the compacted backward (None: no compaction);
         quota_cap: the per-expert quota directly (e.g. from
         moe.moe_quota_cap_for_budget), instead of rho.  keep_graph=False: the
@@ -29,12 +29,22 @@ class MoeLayerBuffers:
         copy, moe_compact_pairs' row gathers).  Results are the same bit for
         bit.  None picks gathering unless dW runs over all pairs: there the
         weight-gradient GEMM streams each expert's x rows many times, and
-        contiguous rows serve it better than one copy costs."""
+        contiguous rows serve it better than one copy costs.  overlap_dw: the
+        weight gradients run on a second stream (default priority) alongside
+        the dX GEMM and the dx sum, from the point where the dx call signals dO
+        and dh complete (moe_signal_dh_ready); the caller's stream then waits
+        for them.  Results are the same bit for bit."""
         self.T, self.H, self.F, self.E, self.k = T, H, F, E, k
         self.keep_graph = keep_graph
         self.N = N = T * k
         self.dtype, self.rho, self.dw, self.want_dg = dtype, rho, dw, dg
         dev = torch.device(device)
+        self.device = dev
+        self.overlap_dw = bool(overlap_dw) and dw
+        if self.overlap_dw:
+            self._dw_stream = torch.cuda.Stream(device=dev)  # default priority
+            self._dh_ready = torch.cuda.Event()
+            self._dh_ready.record(torch.cuda.current_stream(dev))  # creates the underlying hipEvent
         i32, f32 = torch.int32, torch.float32
         em = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
         self.topk_idx = em(T, k, dt=i32)
@@ -161,6 +171,8 @@ class MoeLayerBuffers:
             h_rows, h_src = self.h_save, src
         extra = dict(inv_all=self.inv_perm if self.want_dg else None, o_sorted=self.o_sorted if self.want_dg else None,
                      dg=self.dg, stream=stream, h_src=h_src)
+        if self.dw and self.overlap_dw:
+            moe.moe_signal_dh_ready(self._dh_ready)
         if wq is not None:  # frozen fp8 weights: no weight gradient
             assert not self.dw, "fp8 weights are frozen: no dW"
             moe.moe_grouped_bwd_dx_fp8w(offsets, inv, dy, self.topk_w, h_rows, wq, self.dO, self.dh, self.dX,
@@ -169,8 +181,16 @@ class MoeLayerBuffers:
             moe.moe_grouped_bwd_dx(offsets, inv, dy, self.topk_w, h_rows, w_gate, w_up, w_down, self.dO, self.dh,
                                    self.dX, self.dx, self.R, **extra)
         if self.dw:
+            # dW reads dO and dh only: on the side stream it runs alongside dX
+            # and the dx sum, from the moment the dx call signals them complete
+            s_main = stream if stream is not None else torch.cuda.current_stream(self.device)
+            s_dw = self._dw_stream if self.overlap_dw else s_main
+            if self.overlap_dw:
+                s_dw.wait_event(self._dh_ready)
             moe.moe_grouped_bwd_dw(offsets, x_rows, a_rows, self.dO, self.dh, self.dw_gate, self.dw_up,
-                                   self.dw_down, self.R, stream, x_src=x_src, x_div=k, a_src=a_src)
+                                   self.dw_down, self.R, s_dw, x_src=x_src, x_div=k, a_src=a_src)
+            if self.overlap_dw:
+                s_main.wait_stream(s_dw)
         if w_r is not None:
             moe.moe_router_bwd(self._x, w_r, self.topk_idx, self.topk_w, self.dg, self.dlogits, self.dw_r, self.dx,
                                True, self.router_ws, stream)

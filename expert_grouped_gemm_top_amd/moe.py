@@ -29,6 +29,7 @@ _SIGS = {
     "moe_status_string": ([_i], ctypes.c_char_p),
     "moe_last_error": ([], ctypes.c_char_p),
     "moe_abi_version": ([], _i),
+    "moe_signal_dh_ready": ([_vp], _i),
     "moe_router_workspace_bytes": ([_i, _i, _i], _sz),
     "moe_router_fwd": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp], _i),
     "moe_route_topk": ([_i, _i, _i, _vp, _vp, _vp, _vp], _i),
@@ -308,6 +309,12 @@ def moe_grouped_bwd_dx(offsets, inv, dy, topk_w, h_rows, w_gate, w_up, w_down, d
         _ptr(o_sorted, "o_sorted", d, N * H, allow_none=dg is None), _ptr(dg, "dg", F32, N, allow_none=True),
         _ptr(dO_rows, "dO_rows", d, R * H), _ptr(dh_rows, "dh_rows", d, R * 2 * F), _ptr(dX_rows, "dX_rows", d, R * H),
         _ptr(dx, "dx", d, T * H), _stream(stream)))
+
+
+def moe_signal_dh_ready(event):
+    """Arm the next moe_grouped_bwd_dx* call of this thread to record `event`
+    (a torch.cuda.Event, already created) once dO and dh are written."""
+    _check(lib().moe_signal_dh_ready(ctypes.c_void_p(event.cuda_event if event is not None else None)))
 
 
 def moe_grouped_bwd_dw(offsets, x_rows, a_rows, dO_rows, dh_rows, dw_gate, dw_up, dw_down, max_rows: int, stream=None,

@@ -100,6 +100,18 @@ typedef enum moe_kernel {
  * armed at once.  Results of the calls are unaffected. */
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event);
 
+/* Fork point between the input gradient and the weight gradients (issue #14,
+ * Scope: dW for full fine-tuning reads the same dO and dh rows as dx).  Arms a
+ * one-shot request on the calling thread: the next moe_grouped_bwd_dx or
+ * moe_grouped_bwd_dx_fp8w call made from this thread records `event` (a
+ * hipEvent_t created by the caller) on its stream as soon as dO_rows and
+ * dh_rows are complete, that is after the dA GEMM and before the dX GEMM.  A
+ * moe_grouped_bwd_dw launched on another stream that waits for the event then
+ * runs alongside dX and the dx sum; the caller joins the streams afterwards.
+ * The next call takes the request whatever its outcome (one that fails
+ * records nothing).  NULL disarms.  Results are unaffected.  Returns MOE_OK. */
+int moe_signal_dh_ready(void* event);
+
 /* Workspace (device bytes) that moe_router_fwd and moe_router_bwd need for T
  * tokens, hidden size H and E experts: fp32 partial sums of the long
  * reductions (at most ~8.5 MB; 0 when no reduction is split).  Host-only. */

@@ -230,6 +230,40 @@ def test_gather_on_load_is_bitwise_the_materialized_path(wl, keep_graph):
         assert torch.equal(getattr(out[0], n)[:R], getattr(out[1], n)[:R]), n
 
 
+@pytest.mark.parametrize("wl", [
+    W.custom("bf16_overlap", T=700, H=256, F=256, E=4, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_overlap_many", T=300, H=256, F=128, E=16, k=4, dtype="bf16", skew=True, dw=True),
+    W.custom("fp32_overlap", T=90, H=64, F=40, E=6, k=3, dtype="f32", skew=True, dw=True),
+    W.custom("bf16_overlap_compact", T=300, H=256, F=256, E=8, k=4, dtype="bf16", skew=True, dw=True, rho=0.6),
+], ids=lambda w: w.name)
+@pytest.mark.parametrize("keep_graph", [True, False])
+def test_overlapped_dw_is_bitwise_the_serial_path(wl, keep_graph):
+    """dW on a second stream from the dx call's dh-ready signal, alongside dX
+    and the dx sum: the same kernels on the same rows, so every output equals
+    the single-stream backward's, on two steps in a row (the event is
+    re-armed and re-recorded each step)."""
+    d = W.generate(wl, seed=5)
+    logits = torch.from_numpy(logits_of(wl, d)).cuda()
+    t = to_dev(wl, d)
+    out = []
+    for overlap in (False, True):
+        L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, t["x"].dtype, "cuda", rho=wl.rho, dw=True,
+                            keep_graph=keep_graph, overlap_dw=overlap)
+        snaps = []
+        for _ in range(2):
+            for n in ("dw_gate", "dw_up", "dw_down", "dx"):
+                getattr(L, n).fill_(7.0)  # stale values would show
+            L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"])
+            L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"])
+            torch.cuda.synchronize()
+            snaps.append({n: getattr(L, n).clone() for n in ("dw_gate", "dw_up", "dw_down", "dx", "dg")})
+        assert L.overlap_dw == overlap
+        out.append(snaps)
+    for step in range(2):
+        for n in out[0][step]:
+            assert torch.equal(out[0][step][n], out[1][step][n]), f"step {step}: {n}"
+
+
 # Seeded random layer shapes, each option drawn at random (skew, dW, quota,
 # recompute, gathered or materialized rows), every output against the oracle.
 # At least 8 tokens: the tolerance is relative to a tensor's largest entry,
