@@ -280,7 +280,7 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int moe_abi_version(void) { return 4; }
+int moe_abi_version(void) { return 5; }
 
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
   const char* fn = "moe_profile_kernel";

@@ -72,7 +72,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 const char* moe_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);
-/* ABI version, currently 4. */
+/* ABI version, currently 5. */
 int moe_abi_version(void);
 
 /* Kernels that moe_profile_kernel can bracket with events. */
