@@ -152,18 +152,20 @@ def algorithmic(wl, counts, kept_counts=None, gathered=False, weight_bytes=None)
 def step_distribution(step, stream, dev, n):
     """Untimed pass after the timed steps: every step bracketed by HIP events on
     the layer's stream; median / p10 / p90 in ms, once back to back and once
-    with a 512 MiB buffer overwritten before every step, so that nothing the
-    previous step left in the 256 MB last-level cache is reused."""
+    with a 512 MiB buffer read before every step, so that nothing the previous
+    step left in the 256 MB last-level cache is reused (a read evicts with
+    clean lines: a fill would leave dirty lines whose write-back then competes
+    with the step)."""
     import numpy as np
     import torch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = torch.ones(256 << 20, dtype=torch.float16, device=dev)  # 512 MiB
 
     def run(flushed):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         torch.cuda.synchronize()
         for a, b in ev:  # no host sync between steps: the stream stays fed
             if flushed:
-                flush.fill_(1)
+                flush.sum(dtype=torch.float32)
             a.record(stream)
             step()
             b.record(stream)
