@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens of the CPU-oracle sample (0: auto)")
     p.add_argument("--router", action="store_true",
                    help="run the router in front of the path (logits = x W_r, drawn W_r) and its backward after dx")
+    p.add_argument("--gather-rows", choices=("auto", "on", "off"), default="auto",
+                   help="GEMMs read token rows through the pair indices (on) or from the materialized x_sorted "
+                        "(off); auto: the layer's choice (gathered unless dW runs over all pairs)")
     p.add_argument("--overlap-dw", action="store_true",
                    help="full fine-tuning: weight gradients on a second stream alongside the dX GEMM and the dx sum")
     p.add_argument("--no-keep-graph", action="store_true",
@@ -265,7 +268,8 @@ def main():
         assert quota_cap >= 1, "the budget does not hold one row per expert"
     L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho if quota_cap is None else None,
                         dw=wl.dw, dg=True, router=args.router, keep_graph=not args.no_keep_graph, quota_cap=quota_cap,
-                        overlap_dw=args.overlap_dw)
+                        overlap_dw=args.overlap_dw,
+                        gather_rows=None if args.gather_rows == "auto" else args.gather_rows == "on")
     score = "metric" if args.metric_score else None
     wq = None
     if args.fp8_weights:
@@ -356,6 +360,7 @@ def main():
                            + ("+router_bwd" if args.router else "")
                            + ("+recompute_h" if args.no_keep_graph else "")
                            + ("+dW_overlapped" if args.overlap_dw and wl.dw and not args.forward_only else "")
+                           + ("" if args.gather_rows == "auto" else f"+gather_rows={args.gather_rows}")
                            + ("+metric_score" if args.metric_score else "")
                            + (f"+budget({args.budget_mib} MiB: cap {quota_cap})" if quota_cap else "")
                            + ("+fp8_weights" if wq is not None else ""),
