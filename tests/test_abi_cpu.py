@@ -181,3 +181,15 @@ def test_fp8_weight_calls_validation(lib):
     assert d(*bad) == 1 and "s_down" in _err(lib)
     bad = list(ok); bad[5] = 2000
     assert d(*bad) == 1 and "max_rows" in _err(lib)
+
+
+def test_dh_ready_signal_is_taken_by_the_next_dx_call(lib):
+    """Arming the fork point enqueues nothing by itself; the next dx call takes
+    the request whatever its outcome, and one that fails validation records
+    nothing (the event here is a fake handle that a record would fault on)."""
+    assert lib.moe_signal_dh_ready(NULL) == 0
+    assert lib.moe_signal_dh_ready(ctypes.c_void_p(0x1000)) == 0
+    dx = lib.moe_grouped_bwd_dx
+    bad = [64, 128, 64, 8, 2, 129, 0] + [P] * 16 + [NULL]  # max_rows > T k: rejected before any launch
+    assert dx(*bad) == 1 and "max_rows" in _err(lib)
+    assert lib.moe_signal_dh_ready(NULL) == 0
