@@ -152,6 +152,20 @@ def algorithmic(wl, counts, kept_counts=None, gathered=False, weight_bytes=None)
     }
 
 
+def environment(dev):
+    """GPU, software versions and the host CPU the oracle baseline runs on."""
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"gpu": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__, "host_cpu": cpu, "host_threads": os.cpu_count()}
+
+
 def step_distribution(step, stream, dev, n):
     """Untimed pass after the timed steps: every step bracketed by HIP events on
     the layer's stream; median / p10 / p90 in ms, once back to back and once
@@ -384,6 +398,7 @@ def main():
                                             "frac_bf16_mfma": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                             "GB/s": alg[kk][0] / (kernel_ms[kk] * 1e-3) / 1e9}
                          for kk in router_kernels}
+    out["env"] = environment(dev)
     if not args.no_probes:
         out["step_ms"] = step_distribution(step, stream, dev, n=max(10, min(args.steps, 20)))
         out["probes"] = probes(dev)
