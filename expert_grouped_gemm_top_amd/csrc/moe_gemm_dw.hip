@@ -12,6 +12,11 @@
 // use.  Every output is reduced in row order by one workgroup (deterministic,
 // no atomics); an expert without rows stores exact zeros.
 //
+// Experts with at most one stage of rows (BK, empty ones included) are left to
+// dw_small_bf16_kernel: their tiles are bound by their stores and by the
+// workgroup's own latency, so they run on 128 x 128 tiles with 32 KiB of LDS,
+// several workgroups per CU, instead of one 256 x 256 workgroup per CU.
+//
 // Work order: workgroups take experts in order of decreasing row count, so the
 // longest reductions start first; the tiles of one expert are dealt to the 8
 // XCDs in contiguous runs (tiles next to each other share an operand block,
@@ -55,6 +60,7 @@ struct DwCfg {
   static_assert(64 * WAVES >= kMaxExperts, "every expert has a thread in the ranking");
 };
 using Cfg = DwCfg<MOE_DW_CFG>;
+constexpr int kSmallMaxRows = Cfg::BK;  // experts with at most this many rows go to the small-expert kernel
 
 struct DwShape {
   int nt1, tiles1;  // gate/up: column tiles, all tiles
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwAr
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_rank[kMaxExperts];
-  __shared__ int s_expert;
+  __shared__ int s_expert, s_nbig;
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l32 = l & 31, hk = l >> 5;
   const int wm = w % Cfg::WM, wn = w / Cfg::WM;
@@ -141,12 +147,16 @@ __global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwAr
   // ---- which expert has that rank in decreasing row count (ties: lower id
   // first).  Each expert's rank is summed from `parts` threads' partial counts.
   for (int i = tid; i <= E; i += 64 * Cfg::WAVES) s_off[i] = g.offsets[i];
+  if (tid == 0) s_nbig = 0;
   __syncthreads();
   if (tid < E) {
     s_cnt[tid] = s_off[tid + 1] - s_off[tid];
     s_rank[tid] = 0;
+    if (s_cnt[tid] > kSmallMaxRows) atomicAdd(&s_nbig, 1);
   }
   __syncthreads();
+  // the experts ranked past the large ones are the small-expert kernel's
+  if (rank >= s_nbig) return;
   {
     const int parts = (64 * Cfg::WAVES) / E;
     if (tid < parts * E) {
@@ -329,9 +339,173 @@ __global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwAr
   }
 }
 
+// ---- experts with at most one stage of rows ---------------------------------
+// Workgroup = one 128 x 128 output tile of one such expert, four waves of
+// 64 x 64 on the 32x32x16 matrix core; both operand blocks ([rows][128
+// columns], 16 KiB each) come in with direct global->LDS loads and are read
+// with the transposing LDS read, as in the large-expert kernel; only the
+// 16-row sub-steps that hold rows of the expert are multiplied (the rows past
+// its end within them are zeroed); an expert without rows stores zeros.  The
+// output tile is staged through the operand buffers for full 16-byte row
+// stores.  32 KiB of LDS lets several workgroups share a CU, so one tile's
+// loads and stores overlap another's.  Work order: the j-th small expert (in
+// id order) takes the j-th run of workgroups, its tiles dealt to the 8 XCDs in
+// contiguous runs like the large-expert kernel's.
+constexpr int kSmallBM = 128, kSmallBN = 128;
+constexpr int kSmallPitch = 2 * kSmallBN;            // bytes per reduced row of either operand block
+constexpr int kSmallTile = Cfg::BK * kSmallPitch;    // 16 KiB
+constexpr int kSmallIns = kSmallTile / 1024 / 4;     // direct loads per wave per operand
+
+struct DwSmallShape {
+  int nt1, tiles1;  // gate/up: column tiles, all tiles
+  int nt2;          // down: column tiles
+  int tiles;        // tiles per expert
+};
+
+// bf16 layers have H and F multiples of 128, so the tiles divide exactly.
+__host__ __device__ inline DwSmallShape dw_small_shape(int H, int F) {
+  DwSmallShape s;
+  s.nt1 = 2 * F / kSmallBN;
+  s.tiles1 = (H / kSmallBM) * s.nt1;
+  s.nt2 = H / kSmallBN;
+  s.tiles = s.tiles1 + (F / kSmallBM) * s.nt2;
+  return s;
+}
+
+__global__ __launch_bounds__(256) void dw_small_bf16_kernel(DwArgs g) {
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_list[kMaxExperts];
+  __shared__ int s_tmp[4];
+  __shared__ __attribute__((aligned(16))) unsigned char s_t[2 * kSmallTile];  // P | Q, then the output tile
+  static_assert(kSmallBM * kSmallBN * 2 == 2 * kSmallTile, "the output tile fills the operand buffers");
+  static_assert(kSmallIns * 1024 * 4 == kSmallTile && 64 / (kSmallPitch / 16) * kSmallIns * 4 == Cfg::BK,
+                "four waves load the BK rows of a block");
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l32 = l & 31, hk = l >> 5;
+  const int wm = w & 1, wn = w >> 1;
+  const int H = g.H, F = g.F, E = g.E;
+  const DwSmallShape sh = dw_small_shape(H, F);
+  const int slots = (sh.tiles + 7) & ~7;
+  const int unit = blockIdx.x / slots, traw = blockIdx.x - unit * slots;
+  const int t = (traw & 7) * (slots >> 3) + (traw >> 3);
+  if (t >= sh.tiles) return;  // uniform across the workgroup
+
+  // the small experts in id order
+  for (int i = tid; i <= E; i += 256) s_off[i] = g.offsets[i];
+  __syncthreads();
+  const int small = (tid < E && s_off[tid + 1] - s_off[tid] <= kSmallMaxRows) ? 1 : 0;
+  int n_small;
+  const int pos = block256_exclusive_scan(small, s_tmp, n_small);
+  if (small) s_list[pos] = tid;
+  __syncthreads();
+  if (unit >= n_small) return;
+  const int e = s_list[unit];
+  const int row0 = s_off[e], n_e = s_off[e + 1] - row0;
+
+  // the product this tile belongs to
+  const uint16_t *P, *Q;
+  const int32_t* pmap;
+  int ldp, ldq, M, N, mt, nt, pdiv;
+  if (t < sh.tiles1) {  // [dW_gate | dW_up] = x^T [dHg | dHu]
+    mt = t / sh.nt1;
+    nt = t - mt * sh.nt1;
+    P = g.x; ldp = H; M = H;
+    pmap = g.x_map; pdiv = g.x_div;
+    Q = g.dh; ldq = 2 * F; N = 2 * F;
+  } else {              // dW_down = a^T dO
+    const int tt = t - sh.tiles1;
+    mt = tt / sh.nt2;
+    nt = tt - mt * sh.nt2;
+    P = g.a; ldp = F; M = F;
+    pmap = g.a_map; pdiv = 1;
+    Q = g.dO; ldq = H; N = H;
+  }
+  const int m0 = mt * kSmallBM, n0 = nt * kSmallBN;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  if (n_e > 0) {
+    DwLoader<kSmallIns> lp, lq;
+    lp.init(P, m0, M, kSmallPitch / 16, w, l);
+    lq.init(Q, n0, N, kSmallPitch / 16, w, l);
+    if (pmap != nullptr) {
+      int pent[kSmallIns];
+      lp.rows_of(0, row0, n_e, pmap, pent);
+      lp.issue_rows(pent, pdiv, ldp, s_t, w);
+    } else {
+      lp.issue(0, row0, n_e, ldp, s_t, w);
+    }
+    lq.issue(0, row0, n_e, ldq, s_t + kSmallTile, w);
+    wait_vmcnt<0>();
+    barrier_no_fence();
+    const int used = (n_e + 15) & ~15;  // rows of the sub-steps that hold rows of the expert
+    if (n_e < used) {
+      for (int c = tid; c < 2 * kSmallTile / 16; c += 256) {
+        const int rr = (c & (kSmallTile / 16 - 1)) / (kSmallPitch / 16);
+        if (rr >= n_e && rr < used) *(u32x4*)(s_t + 16 * c) = u32x4{0, 0, 0, 0};
+      }
+      __syncthreads();
+    }
+    for (int sub = 0; sub < used / 16; ++sub) {
+      u32x4 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = tr_frag32(s_t, kSmallPitch, sub, 64 * wm + 32 * i);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = tr_frag32(s_t + kSmallTile, kSmallPitch, sub, 64 * wn + 32 * j);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][j] = mfma32(fb[j], fa[i], acc[i][j]);
+    }
+  }
+
+  // epilogue, staged through the operand buffers.  acc[i][j] register r ->
+  // tile row 64 wm + 32 i + l32, tile column 64 wn + 32 j + 8 q + 4 hk +
+  // (0..3), q = r / 4; LDS row m holds the tile row, its 16-byte chunk c at
+  // position c ^ (m % 16).
+  __syncthreads();  // every wave is done with the operand blocks
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = 64 * wm + 32 * i + l32;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = (64 * wn + 32 * j + 8 * q) >> 3;
+        *(u32x2*)(s_t + m * kSmallPitch + 16 * (c ^ (m & 15)) + 8 * hk) =
+            u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]), pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {  // a wave stores 32 rows, 4 per instruction
+    const int m = 32 * w + 4 * it + (l >> 4), c = l & 15;
+    const int gm = m0 + m, gn = n0 + 8 * c;
+    if (gm < M && gn < N) {
+      const u32x4 v = *(const u32x4*)(s_t + m * kSmallPitch + 16 * (c ^ (m & 15)));
+      uint16_t* dst;
+      if (t < sh.tiles1) dst = (gn < F) ? g.dwg + ((size_t)e * H + gm) * F + gn : g.dwu + ((size_t)e * H + gm) * F + (gn - F);
+      else dst = g.dwd + ((size_t)e * F + gm) * H + gn;
+      *(u32x4*)dst = v;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream) {
+  // experts with at most one stage of rows (empty ones included)
+  const DwSmallShape ss = dw_small_shape(g.H, g.F);
+  const int64_t sblocks = (int64_t)g.E * ((ss.tiles + 7) & ~7);
+  hipLaunchKernelGGL(dw_small_bf16_kernel, dim3((unsigned)sblocks), dim3(256), 0, stream, g);
+  hipError_t serr = hipGetLastError();
+  if (serr != hipSuccess) return serr;
+  // the others
   const DwShape sh = dw_shape(g.H, g.F);
   const int64_t blocks = (int64_t)g.E * dw_slots(sh);
   const size_t lds = (size_t)Cfg::LDS_BYTES;

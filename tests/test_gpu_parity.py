@@ -199,6 +199,7 @@ def test_recompute_path_compacted_matches_oracle():
 @pytest.mark.parametrize("wl", [
     W.custom("bf16_gather", T=300, H=256, F=256, E=16, k=4, dtype="bf16", skew=True, dw=False),
     W.custom("bf16_gather_big", T=700, H=256, F=256, E=4, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_gather_small_dw", T=40, H=256, F=128, E=8, k=2, dtype="bf16", skew=True, dw=True),
     W.custom("fp32_gather", T=90, H=64, F=40, E=6, k=3, dtype="f32", skew=True, dw=True),
     W.custom("bf16_gather_compact", T=300, H=256, F=256, E=8, k=4, dtype="bf16", skew=True, dw=True, rho=0.6),
 ], ids=lambda w: w.name)
@@ -484,10 +485,11 @@ def test_budget_quota_with_metric_scores():
 # ----------------------------------------------------------------------------- row-count regime boundaries
 def test_row_count_regime_boundaries():
     """Experts with row counts on both sides of every kernel-regime boundary
-    (16-row tiles, 48: LDS tiles, 256: 256-row tiles), empty and one-row
-    experts, through the whole layer with dW: routing is steered by one-hot
-    logits so every expert gets exactly its count."""
-    counts = np.array([47, 48, 255, 256, 257, 0, 1, 16, 17, 300])
+    (16-row tiles, 48: LDS tiles, 256: 256-row tiles; dW: 64, one stage, on
+    the small-expert kernel), empty and one-row experts, through the whole
+    layer with dW: routing is steered by one-hot logits so every expert gets
+    exactly its count."""
+    counts = np.array([47, 48, 255, 256, 257, 0, 1, 16, 17, 300, 63, 64, 65])
     E = len(counts)
     T = int(counts.sum())
     wl = W.custom("bf16_regimes", T=T, H=256, F=256, E=E, k=1, dtype="bf16", skew=False, dw=True)
