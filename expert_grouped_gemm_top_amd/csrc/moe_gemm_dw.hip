@@ -349,12 +349,17 @@ __global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwAr
 // output tile is staged through the operand buffers for full 16-byte row
 // stores.  32 KiB of LDS lets several workgroups share a CU, so one tile's
 // loads and stores overlap another's.  Work order: the j-th small expert (in
-// id order) takes the j-th run of workgroups, its tiles dealt to the 8 XCDs in
-// contiguous runs like the large-expert kernel's.
+// id order) takes the j-th run of workgroups, each workgroup kSmallTpw
+// consecutive tiles (one schedule for several tiles), the runs dealt to the 8
+// XCDs in contiguous blocks like the large-expert kernel's tiles.
 constexpr int kSmallBM = 128, kSmallBN = 128;
 constexpr int kSmallPitch = 2 * kSmallBN;            // bytes per reduced row of either operand block
 constexpr int kSmallTile = Cfg::BK * kSmallPitch;    // 16 KiB
 constexpr int kSmallIns = kSmallTile / 1024 / 4;     // direct loads per wave per operand
+#ifndef MOE_DW_SMALL_TPW
+#define MOE_DW_SMALL_TPW 4
+#endif
+constexpr int kSmallTpw = MOE_DW_SMALL_TPW;          // consecutive tiles of one expert per workgroup
 
 struct DwSmallShape {
   int nt1, tiles1;  // gate/up: column tiles, all tiles
@@ -372,7 +377,12 @@ __host__ __device__ inline DwSmallShape dw_small_shape(int H, int F) {
   return s;
 }
 
-__global__ __launch_bounds__(256) void dw_small_bf16_kernel(DwArgs g) {
+// Workgroups per expert: its tiles in runs of kSmallTpw, rounded up to a multiple of the 8 XCDs.
+__host__ __device__ inline int dw_small_slots(const DwSmallShape& s) {
+  return ((s.tiles + kSmallTpw - 1) / kSmallTpw + 7) & ~7;
+}
+
+__global__ __launch_bounds__(256, 3) void dw_small_bf16_kernel(DwArgs g) {
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_list[kMaxExperts];
   __shared__ int s_tmp[4];
@@ -384,10 +394,11 @@ __global__ __launch_bounds__(256) void dw_small_bf16_kernel(DwArgs g) {
   const int wm = w & 1, wn = w >> 1;
   const int H = g.H, F = g.F, E = g.E;
   const DwSmallShape sh = dw_small_shape(H, F);
-  const int slots = (sh.tiles + 7) & ~7;
+  const int slots = dw_small_slots(sh);
   const int unit = blockIdx.x / slots, traw = blockIdx.x - unit * slots;
-  const int t = (traw & 7) * (slots >> 3) + (traw >> 3);
-  if (t >= sh.tiles) return;  // uniform across the workgroup
+  const int t_first = ((traw & 7) * (slots >> 3) + (traw >> 3)) * kSmallTpw;
+  if (t_first >= sh.tiles) return;  // uniform across the workgroup
+  const int t_end = min(t_first + kSmallTpw, sh.tiles);
 
   // the small experts in id order
   for (int i = tid; i <= E; i += 256) s_off[i] = g.offsets[i];
@@ -401,98 +412,101 @@ __global__ __launch_bounds__(256) void dw_small_bf16_kernel(DwArgs g) {
   const int e = s_list[unit];
   const int row0 = s_off[e], n_e = s_off[e + 1] - row0;
 
-  // the product this tile belongs to
-  const uint16_t *P, *Q;
-  const int32_t* pmap;
-  int ldp, ldq, M, N, mt, nt, pdiv;
-  if (t < sh.tiles1) {  // [dW_gate | dW_up] = x^T [dHg | dHu]
-    mt = t / sh.nt1;
-    nt = t - mt * sh.nt1;
-    P = g.x; ldp = H; M = H;
-    pmap = g.x_map; pdiv = g.x_div;
-    Q = g.dh; ldq = 2 * F; N = 2 * F;
-  } else {              // dW_down = a^T dO
-    const int tt = t - sh.tiles1;
-    mt = tt / sh.nt2;
-    nt = tt - mt * sh.nt2;
-    P = g.a; ldp = F; M = F;
-    pmap = g.a_map; pdiv = 1;
-    Q = g.dO; ldq = H; N = H;
-  }
-  const int m0 = mt * kSmallBM, n0 = nt * kSmallBN;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  if (n_e > 0) {
-    DwLoader<kSmallIns> lp, lq;
-    lp.init(P, m0, M, kSmallPitch / 16, w, l);
-    lq.init(Q, n0, N, kSmallPitch / 16, w, l);
-    if (pmap != nullptr) {
-      int pent[kSmallIns];
-      lp.rows_of(0, row0, n_e, pmap, pent);
-      lp.issue_rows(pent, pdiv, ldp, s_t, w);
-    } else {
-      lp.issue(0, row0, n_e, ldp, s_t, w);
+  for (int t = t_first; t < t_end; ++t) {
+    // the product this tile belongs to
+    const uint16_t *P, *Q;
+    const int32_t* pmap;
+    int ldp, ldq, M, N, mt, nt, pdiv;
+    if (t < sh.tiles1) {  // [dW_gate | dW_up] = x^T [dHg | dHu]
+      mt = t / sh.nt1;
+      nt = t - mt * sh.nt1;
+      P = g.x; ldp = H; M = H;
+      pmap = g.x_map; pdiv = g.x_div;
+      Q = g.dh; ldq = 2 * F; N = 2 * F;
+    } else {              // dW_down = a^T dO
+      const int tt = t - sh.tiles1;
+      mt = tt / sh.nt2;
+      nt = tt - mt * sh.nt2;
+      P = g.a; ldp = F; M = F;
+      pmap = g.a_map; pdiv = 1;
+      Q = g.dO; ldq = H; N = H;
     }
-    lq.issue(0, row0, n_e, ldq, s_t + kSmallTile, w);
-    wait_vmcnt<0>();
-    barrier_no_fence();
-    const int used = (n_e + 15) & ~15;  // rows of the sub-steps that hold rows of the expert
-    if (n_e < used) {
-      for (int c = tid; c < 2 * kSmallTile / 16; c += 256) {
-        const int rr = (c & (kSmallTile / 16 - 1)) / (kSmallPitch / 16);
-        if (rr >= n_e && rr < used) *(u32x4*)(s_t + 16 * c) = u32x4{0, 0, 0, 0};
-      }
-      __syncthreads();
-    }
-    for (int sub = 0; sub < used / 16; ++sub) {
-      u32x4 fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = tr_frag32(s_t, kSmallPitch, sub, 64 * wm + 32 * i);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = tr_frag32(s_t + kSmallTile, kSmallPitch, sub, 64 * wn + 32 * j);
-#pragma unroll
+    const int m0 = mt * kSmallBM, n0 = nt * kSmallBN;
+
+    f32x16 acc[2][2];
+  #pragma unroll
+    for (int i = 0; i < 2; ++i)
+  #pragma unroll
       for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) acc[i][j] = mfma32(fb[j], fa[i], acc[i][j]);
-    }
-  }
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // epilogue, staged through the operand buffers.  acc[i][j] register r ->
-  // tile row 64 wm + 32 i + l32, tile column 64 wn + 32 j + 8 q + 4 hk +
-  // (0..3), q = r / 4; LDS row m holds the tile row, its 16-byte chunk c at
-  // position c ^ (m % 16).
-  __syncthreads();  // every wave is done with the operand blocks
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = 64 * wm + 32 * i + l32;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = (64 * wn + 32 * j + 8 * q) >> 3;
-        *(u32x2*)(s_t + m * kSmallPitch + 16 * (c ^ (m & 15)) + 8 * hk) =
-            u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]), pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+    if (n_e > 0) {
+      DwLoader<kSmallIns> lp, lq;
+      lp.init(P, m0, M, kSmallPitch / 16, w, l);
+      lq.init(Q, n0, N, kSmallPitch / 16, w, l);
+      if (pmap != nullptr) {
+        int pent[kSmallIns];
+        lp.rows_of(0, row0, n_e, pmap, pent);
+        lp.issue_rows(pent, pdiv, ldp, s_t, w);
+      } else {
+        lp.issue(0, row0, n_e, ldp, s_t, w);
       }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {  // a wave stores 32 rows, 4 per instruction
-    const int m = 32 * w + 4 * it + (l >> 4), c = l & 15;
-    const int gm = m0 + m, gn = n0 + 8 * c;
-    if (gm < M && gn < N) {
-      const u32x4 v = *(const u32x4*)(s_t + m * kSmallPitch + 16 * (c ^ (m & 15)));
-      uint16_t* dst;
-      if (t < sh.tiles1) dst = (gn < F) ? g.dwg + ((size_t)e * H + gm) * F + gn : g.dwu + ((size_t)e * H + gm) * F + (gn - F);
-      else dst = g.dwd + ((size_t)e * F + gm) * H + gn;
-      *(u32x4*)dst = v;
+      lq.issue(0, row0, n_e, ldq, s_t + kSmallTile, w);
+      wait_vmcnt<0>();
+      barrier_no_fence();
+      const int used = (n_e + 15) & ~15;  // rows of the sub-steps that hold rows of the expert
+      if (n_e < used) {
+        for (int c = tid; c < 2 * kSmallTile / 16; c += 256) {
+          const int rr = (c & (kSmallTile / 16 - 1)) / (kSmallPitch / 16);
+          if (rr >= n_e && rr < used) *(u32x4*)(s_t + 16 * c) = u32x4{0, 0, 0, 0};
+        }
+        __syncthreads();
+      }
+      for (int sub = 0; sub < used / 16; ++sub) {
+        u32x4 fa[2], fb[2];
+  #pragma unroll
+        for (int i = 0; i < 2; ++i) fa[i] = tr_frag32(s_t, kSmallPitch, sub, 64 * wm + 32 * i);
+  #pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = tr_frag32(s_t + kSmallTile, kSmallPitch, sub, 64 * wn + 32 * j);
+  #pragma unroll
+        for (int j = 0; j < 2; ++j)
+  #pragma unroll
+          for (int i = 0; i < 2; ++i) acc[i][j] = mfma32(fb[j], fa[i], acc[i][j]);
+      }
     }
+
+    // epilogue, staged through the operand buffers.  acc[i][j] register r ->
+    // tile row 64 wm + 32 i + l32, tile column 64 wn + 32 j + 8 q + 4 hk +
+    // (0..3), q = r / 4; LDS row m holds the tile row, its 16-byte chunk c at
+    // position c ^ (m % 16).
+    __syncthreads();  // every wave is done with the operand blocks
+  #pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = 64 * wm + 32 * i + l32;
+  #pragma unroll
+      for (int j = 0; j < 2; ++j)
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (64 * wn + 32 * j + 8 * q) >> 3;
+          *(u32x2*)(s_t + m * kSmallPitch + 16 * (c ^ (m & 15)) + 8 * hk) =
+              u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]), pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+        }
+    }
+    __syncthreads();
+  #pragma unroll
+    for (int it = 0; it < 8; ++it) {  // a wave stores 32 rows, 4 per instruction
+      const int m = 32 * w + 4 * it + (l >> 4), c = l & 15;
+      const int gm = m0 + m, gn = n0 + 8 * c;
+      if (gm < M && gn < N) {
+        const u32x4 v = *(const u32x4*)(s_t + m * kSmallPitch + 16 * (c ^ (m & 15)));
+        uint16_t* dst;
+        if (t < sh.tiles1) dst = (gn < F) ? g.dwg + ((size_t)e * H + gm) * F + gn : g.dwu + ((size_t)e * H + gm) * F + (gn - F);
+        else dst = g.dwd + ((size_t)e * F + gm) * H + gn;
+        *(u32x4*)dst = v;
+      }
+    }
+    __syncthreads();  // the next tile's loads overwrite the staged tile
   }
 }
 
@@ -501,7 +515,7 @@ __global__ __launch_bounds__(256) void dw_small_bf16_kernel(DwArgs g) {
 hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream) {
   // experts with at most one stage of rows (empty ones included)
   const DwSmallShape ss = dw_small_shape(g.H, g.F);
-  const int64_t sblocks = (int64_t)g.E * ((ss.tiles + 7) & ~7);
+  const int64_t sblocks = (int64_t)g.E * dw_small_slots(ss);
   hipLaunchKernelGGL(dw_small_bf16_kernel, dim3((unsigned)sblocks), dim3(256), 0, stream, g);
   hipError_t serr = hipGetLastError();
   if (serr != hipSuccess) return serr;
