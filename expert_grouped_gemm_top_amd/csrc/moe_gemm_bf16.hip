@@ -13,10 +13,10 @@
 //   DX      [n_e,2F] x [W_gate|W_up][e]^T (K-contiguous)        -> dX
 // One launch covers two regimes, both scheduled on the device from the
 // offsets (build_tile_starts / lookup_tile):
-//   * experts with fewer than 48 rows: every wave streams one 16-row tile x one
+//   * experts with fewer than 32 rows: every wave streams one 16-row tile x one
 //     column block straight from memory (the weights are the traffic), with
 //     an optional split of K between waves of a workgroup;
-//   * experts with 48 .. big_min_rows rows: 128 x 128 workgroup tiles staged
+//   * experts with 32 .. big_min_rows rows: 128 x 128 workgroup tiles staged
 //     through double-buffered, swizzled LDS.
 // Experts with more rows run in the 256-row kernel of moe_gemm_big.hip.
 // In every case the MFMA takes the weights as its first operand, so a lane

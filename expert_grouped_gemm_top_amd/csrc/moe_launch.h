@@ -14,7 +14,7 @@ enum RowGemmMode { kGemmGateUp = 0, kGemmDown = 1, kGemmDA = 2, kGemmDX = 3 };
 // Row GEMM regimes by an expert's row count n_e: n_e < kMidTileMinRows -> streaming
 // kernel (16-row wave tiles); up to big_gemm_min_rows(...) -> 128 x 128 LDS
 // tiles; above -> 256 x 256 LDS tiles fed by direct global->LDS loads.
-constexpr int kMidTileMinRows = 48;
+constexpr int kMidTileMinRows = 32;
 constexpr int kBigTileMinRows = 256;
 constexpr int kNoBigTiles = 0x40000000;  // above every row count
 

@@ -485,11 +485,11 @@ def test_budget_quota_with_metric_scores():
 # ----------------------------------------------------------------------------- row-count regime boundaries
 def test_row_count_regime_boundaries():
     """Experts with row counts on both sides of every kernel-regime boundary
-    (16-row tiles, 48: LDS tiles, 256: 256-row tiles; dW: 64, one stage, on
+    (16-row tiles, 32: LDS tiles, 256: 256-row tiles; dW: 64, one stage, on
     the small-expert kernel), empty and one-row experts, through the whole
     layer with dW: routing is steered by one-hot logits so every expert gets
     exactly its count."""
-    counts = np.array([47, 48, 255, 256, 257, 0, 1, 16, 17, 300, 63, 64, 65])
+    counts = np.array([31, 32, 255, 256, 257, 0, 1, 16, 17, 300, 63, 64, 65, 47, 48])
     E = len(counts)
     T = int(counts.sum())
     wl = W.custom("bf16_regimes", T=T, H=256, F=256, E=E, k=1, dtype="bf16", skew=False, dw=True)
