@@ -425,6 +425,32 @@ def test_full_size_layer(name):
             assert not L.dw_gate[e].any() and not L.dw_up[e].any() and not L.dw_down[e].any(), f"expert {e} not zero"
 
 
+def test_full_size_paths_are_bitwise_equal():
+    """qwen3_ft_t4096 at full size: materialized rows on one stream against
+    rows gathered on load with dW on a second stream (both dW kernels reading
+    x and a through the pair indices, the fork at the dx call's dh-ready
+    signal): the same arithmetic on the same values, so y, dx, dg and every dW
+    are equal bit for bit (the oracle checks of the materialized path are in
+    test_full_size_layer)."""
+    wl = W.WORKLOADS["qwen3_ft_t4096"]
+    note("generating qwen3_ft_t4096")
+    d = W.generate(wl, seed=0)
+    logits = torch.from_numpy(d["logits"]).cuda()
+    t = to_dev(wl, d)
+    out = []
+    for gather, overlap in ((False, False), (True, True)):
+        note(f"gpu run gather_rows={gather} overlap_dw={overlap}")
+        L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, "cuda", dw=True, gather_rows=gather,
+                            overlap_dw=overlap)
+        L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"])
+        L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"])
+        torch.cuda.synchronize()
+        out.append({n: getattr(L, n).clone() for n in ("y", "dx", "dg", "dw_gate", "dw_up", "dw_down")})
+        del L
+    for n in out[0]:
+        assert torch.equal(out[0][n], out[1][n]), n
+
+
 # ----------------------------------------------------------------------------- quota metric and budget
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_pair_scores_match_oracle(dtype):
