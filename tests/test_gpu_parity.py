@@ -98,6 +98,8 @@ SMALL_BF16 = [
     W.custom("bf16_big_tiles", T=700, H=256, F=256, E=4, k=2, dtype="bf16", skew=True, dw=True),
     W.custom("bf16_big_tiles_f384", T=600, H=384, F=384, E=6, k=1, dtype="bf16", skew=True, dw=True),
     W.custom("bf16_e256_k16", T=64, H=128, F=128, E=256, k=16, dtype="bf16", skew=True, dw=True),
+    # E = 256 with a few experts past 64 and 256 rows among many small ones: both dW kernels and every row regime
+    W.custom("bf16_e256_mixed", T=800, H=128, F=128, E=256, k=2, dtype="bf16", skew=True, dw=True),
     W.custom("bf16_e1", T=300, H=128, F=128, E=1, k=1, dtype="bf16", skew=False, dw=True),
 ]
 
