@@ -162,8 +162,18 @@ def environment(dev):
             cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
+    clocks = None
+    try:  # current shader / memory clocks as the driver reports them (best effort)
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        found = {key: m.group(1) for key in ("sclk", "mclk")
+                 for m in [re.search(rf"{key} clock level: \d+: \((\d+\s*Mhz)\)", r.stdout)] if m}
+        clocks = found or None
+    except (OSError, subprocess.SubprocessError):
+        pass
     return {"gpu": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
-            "hip": torch.version.hip, "torch": torch.__version__, "host_cpu": cpu, "host_threads": os.cpu_count()}
+            "clocks": clocks, "hip": torch.version.hip, "torch": torch.__version__, "host_cpu": cpu,
+            "host_threads": os.cpu_count()}
 
 
 def step_distribution(step, stream, dev, n):
