@@ -167,7 +167,7 @@ def environment(dev):
         import subprocess
         r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
         found = {key: m.group(1) for key in ("sclk", "mclk")
-                 for m in [re.search(rf"{key} clock level: \d+: \((\d+\s*Mhz)\)", r.stdout)] if m}
+                 for m in [re.search(rf"{key} clock level: [^:]+: \((\d+\s*Mhz)\)", r.stdout)] if m}
         clocks = found or None
     except (OSError, subprocess.SubprocessError):
         pass
