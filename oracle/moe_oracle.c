@@ -100,7 +100,17 @@ void oracle_router_backward(int T, int H, int E, int k, const double* x, const d
  * written as an insertion sort -- and the first k are kept.  Weights are the
  * softmax over the k selected logits:
  *     w[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)
- * which equals a softmax over all E renormalised to the selected k.           */
+ * which equals a softmax over all E renormalised to the selected k.
+ * The pages say nothing of NaN logits.  Reading taken: a NaN ranks above every
+ * number (the order of torch's sort and top-k), NaNs among themselves by the
+ * lower expert index; a token with a NaN logit then selects it first and all
+ * its weights are NaN.  +0.0 and -0.0 are equal.                             */
+static int ranks_above(double a, double b) {
+  if (isnan(a)) return !isnan(b);
+  if (isnan(b)) return 0;
+  return a > b;
+}
+
 void oracle_route_topk(int T, int E, int k, const double* logits, int32_t* idx, double* w) {
 #pragma omp parallel
   {
@@ -109,9 +119,9 @@ void oracle_route_topk(int T, int E, int k, const double* logits, int32_t* idx, 
     for (int t = 0; t < T; ++t) {
       const double* l = logits + (size_t)t * E;
       for (int e = 0; e < E; ++e) {
-        /* insert e after every earlier expert whose logit is >= l[e] */
+        /* insert e after every earlier expert whose logit l[e] does not rank above */
         int pos = e;
-        while (pos > 0 && l[order[pos - 1]] < l[e]) {
+        while (pos > 0 && ranks_above(l[e], l[order[pos - 1]])) {
           order[pos] = order[pos - 1];
           --pos;
         }

@@ -113,6 +113,32 @@ def test_route_closed_forms():
     np.testing.assert_allclose(w, np.take_along_axis(sm, idx.astype(np.int64), 1), rtol=1e-14)
 
 
+def test_route_order_matches_a_stable_library_sort_with_nan_and_signed_zero():
+    """The selection order (logit descending, lower expert first on ties, +0
+    and -0 equal, NaN above every number) is the order of torch's stable
+    descending sort; a token with a NaN logit gets NaN weights, others sum to 1."""
+    rng = np.random.default_rng(11)
+    E, T = 24, 64
+    vals = np.array([np.nan, -np.inf, -2.0, -0.0, 0.0, 0.5, 1.0, 3.0, np.inf], np.float64)
+    l = rng.choice(vals, size=(T, E))
+    l[:16] = rng.standard_normal((16, E))       # finite rows
+    l[16:20] = np.nan                           # all-NaN rows
+    l[20:24] = rng.standard_normal((4, E))
+    l[20:24, [3, 7]] = np.nan                   # two NaNs among finite values
+    ref = torch.sort(torch.tensor(l), dim=1, descending=True, stable=True).indices.numpy()
+    for k in (1, 3, 8, E):
+        idx, w = oracle.route_topk(l, k)
+        assert np.array_equal(idx, ref[:, :k]), k
+        has_nan = np.isnan(l).any(axis=1)
+        assert np.isnan(w[has_nan]).all()
+        fin = np.isfinite(l).all(axis=1)
+        assert np.abs(w[fin].sum(1) - 1).max() <= 1e-12
+    idx, _ = oracle.route_topk(l[16:17], 4)
+    assert idx.tolist() == [[0, 1, 2, 3]]
+    idx, _ = oracle.route_topk(l[20:21], 3)
+    assert idx[0, :2].tolist() == [3, 7]
+
+
 def test_route_weights_sum_to_one(tiny):
     rng = np.random.default_rng(5)
     for k in (1, 2, 4, 8):
