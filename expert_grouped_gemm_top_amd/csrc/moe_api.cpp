@@ -263,6 +263,35 @@ int bwd_dx(const char* fn, int T, int H, int F, int E, int k, int max_rows, int 
                     fn);
 }
 
+int check_dispatch(const char* fn, int T, int H, int E, int k, int dtype, const int32_t* topk_idx, const void* x,
+                   const int32_t* counts, const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm,
+                   const void* x_sorted) {
+  int rc = check_routing_dims(fn, T, E, k);
+  if (rc) return rc;
+  if ((rc = check_dtype(fn, dtype)) || (rc = check_row_width(fn, "H", H))) return rc;
+  NONNULL(topk_idx);
+  NONNULL(counts);
+  NONNULL(offsets);
+  NONNULL(perm);
+  NONNULL(inv_perm);
+  REQUIRE((x == nullptr) == (x_sorted == nullptr), MOE_ERR_INVALID_ARGUMENT,
+          "%s: x and x_sorted must both be given or both be NULL", fn);
+  return MOE_OK;
+}
+
+// The dispatch kernels with workspace `ws` (at least dispatch_workspace_bytes).
+int dispatch_launch(const char* fn, int T, int H, int E, int k, int dtype, const int32_t* topk_idx, const void* x,
+                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_sorted, void* ws,
+                    hipStream_t s) {
+  int rc;
+  if ((rc = hip_status(moe::launch_dispatch_index(T, E, k, topk_idx, counts, offsets, perm, inv_perm, ws, s), fn)))
+    return rc;
+  if (x_sorted == nullptr) return MOE_OK;
+  return hip_status(timed(MOE_K_DISPATCH_ROWS, s,
+                          [&] { return moe::launch_dispatch_rows(T, H, k, esize_of(dtype), x, inv_perm, x_sorted, s); }),
+                    fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,28 +367,14 @@ int moe_dispatch(int T, int H, int E, int k, int dtype, const int32_t* topk_idx,
                  int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_sorted, void* workspace,
                  size_t workspace_bytes, void* stream) {
   const char* fn = "moe_dispatch";
-  int rc = check_routing_dims(fn, T, E, k);
+  int rc = check_dispatch(fn, T, H, E, k, dtype, topk_idx, x, counts, offsets, perm, inv_perm, x_sorted);
   if (rc) return rc;
-  if ((rc = check_dtype(fn, dtype)) || (rc = check_row_width(fn, "H", H))) return rc;
-  NONNULL(topk_idx);
-  NONNULL(counts);
-  NONNULL(offsets);
-  NONNULL(perm);
-  NONNULL(inv_perm);
-  REQUIRE((x == nullptr) == (x_sorted == nullptr), MOE_ERR_INVALID_ARGUMENT,
-          "%s: x and x_sorted must both be given or both be NULL", fn);
   const size_t need = moe::dispatch_workspace_bytes((int64_t)T * k, E);
   REQUIRE(workspace_bytes >= need, MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn,
           workspace_bytes, need);
   REQUIRE(need == 0 || workspace != nullptr, MOE_ERR_INVALID_ARGUMENT, "%s: workspace must not be NULL", fn);
-  hipStream_t s = as_stream(stream);
-  if ((rc = hip_status(
-           moe::launch_dispatch_index(T, E, k, topk_idx, counts, offsets, perm, inv_perm, workspace, s), fn)))
-    return rc;
-  if (x_sorted == nullptr) return MOE_OK;
-  return hip_status(timed(MOE_K_DISPATCH_ROWS, s,
-                          [&] { return moe::launch_dispatch_rows(T, H, k, esize_of(dtype), x, inv_perm, x_sorted, s); }),
-                    fn);
+  return dispatch_launch(fn, T, H, E, k, dtype, topk_idx, x, counts, offsets, perm, inv_perm, x_sorted, workspace,
+                         as_stream(stream));
 }
 
 int moe_grouped_swiglu_fwd(int H, int F, int E, int max_rows, int max_expert_rows, int dtype, const int32_t* offsets,

@@ -226,15 +226,9 @@ hipError_t launch_compact(int64_t N, int E, int cap, const int32_t* counts, cons
   (void)N;
   const size_t lds = 2 * kLdsPairs * sizeof(uint32_t);
   // dynamic LDS above 64 KiB must be allowed explicitly, once per device
-  static bool attr_set[64] = {};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  static PerDeviceOnce lds_once;
+  hipError_t err = allow_dynamic_lds(lds_once, (const void*)compact_select_kernel, lds);
   if (err != hipSuccess) return err;
-  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    err = hipFuncSetAttribute((const void*)compact_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) attr_set[dev] = true;
-  }
   hipLaunchKernelGGL(compact_select_kernel, dim3(E), dim3(256), lds, stream, E, cap, counts, offsets, perm, score,
                      kept_counts, kept_offsets, kept_perm, kept_src, kept_inv);
   return hipGetLastError();

@@ -244,7 +244,11 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
     // stage goes through this wave's 16 KiB of LDS (16-byte chunks XOR-swizzled
     // by row & 15) and comes back as MFMA fragments: lane (c, gq) takes weight
     // rows c + 16 jj, k chunks 4 gq + q, matching its activation chunks.
-    // LDS operations of one wave complete in order, so no barrier is needed.
+    // Lanes read chunks other lanes wrote: the LDS operations of one wave
+    // complete in order, so a wave barrier with a wavefront-scope fence (which
+    // emits no instruction) after the stage's writes, and again before the
+    // next stage overwrites it, is all the ordering needed; it keeps the
+    // compiler from moving a read above the writes or a write above the reads.
     const int lrow = l >> 4, lchunk = l & 15;
     const WE* w_lo;  // rows for k in [0, Kw)
     const WE* w_hi;  // DX only: rows for k in [F, 2F)
@@ -272,12 +276,18 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
 #pragma unroll
       for (int q = 0; q < 4; ++q) aq[q] = *(const u32x4*)(a_ptr + (size_t)s * 128 + 8 * q);
     };
+    auto wave_sync = [] {
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    };
     auto compute = [&](const WV* bq, const u32x4* aq) {
+      wave_sync();  // the previous stage's reads before these writes
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 4 * i + lrow;
         *(u32x4*)(xs + row * 256 + 16 * (lchunk ^ (row & 15))) = WF::widen(bq[i]);
       }
+      wave_sync();  // every lane's writes before any lane's reads
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const u32x4 av = a_ok ? aq[q] : zero4;

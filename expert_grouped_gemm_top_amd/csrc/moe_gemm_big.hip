@@ -347,15 +347,9 @@ struct BigCfg {
     const size_t lds = (size_t)STAGES * (BM + BN) * BK * 2;
     auto kern = big_gemm_bf16_kernel<MODE, BM, BN, BK, NW, WM, STAGES, WPC>;
     // dynamic LDS above 64 KiB must be allowed explicitly, once per device
-    static bool attr_set[64] = {};
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
+    static PerDeviceOnce lds_once;
+    hipError_t err = allow_dynamic_lds(lds_once, (const void*)kern, lds);
     if (err != hipSuccess) return err;
-    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-      err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (err != hipSuccess) return err;
-      if (dev >= 0 && dev < 64) attr_set[dev] = true;
-    }
     hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(64 * NW), lds, stream, g);
     return hipGetLastError();
   }

@@ -524,15 +524,9 @@ hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream) {
   const int64_t blocks = (int64_t)g.E * dw_slots(sh);
   const size_t lds = (size_t)Cfg::LDS_BYTES;
   // dynamic LDS above 64 KiB must be allowed explicitly, once per device
-  static bool attr_set[64] = {};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  static PerDeviceOnce lds_once;
+  hipError_t err = allow_dynamic_lds(lds_once, (const void*)dw_bf16_kernel, lds);
   if (err != hipSuccess) return err;
-  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    err = hipFuncSetAttribute((const void*)dw_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) attr_set[dev] = true;
-  }
   hipLaunchKernelGGL(dw_bf16_kernel, dim3((unsigned)blocks), dim3(64 * Cfg::WAVES), lds, stream, g);
   return hipGetLastError();
 }

@@ -6,7 +6,41 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace moe {
+
+// Per-device set-up run once per GPU, safe when several host threads make
+// their first call at the same time.  A failed attempt is not recorded, so the
+// next call tries again.  Devices past kDevices run the set-up on every call.
+class PerDeviceOnce {
+ public:
+  static constexpr int kDevices = 64;
+  template <typename Fn>
+  hipError_t run(Fn&& fn) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kDevices) return fn(dev);
+    if (done_[dev].load(std::memory_order_acquire)) return hipSuccess;
+    std::lock_guard<std::mutex> lock(mu_);
+    if (done_[dev].load(std::memory_order_relaxed)) return hipSuccess;
+    err = fn(dev);
+    if (err == hipSuccess) done_[dev].store(true, std::memory_order_release);
+    return err;
+  }
+
+ private:
+  std::atomic<bool> done_[kDevices] = {};
+  std::mutex mu_;
+};
+
+// Allows `kern` dynamic LDS of `bytes` (needed above 64 KiB) on the current
+// device, once per device per `once`.
+inline hipError_t allow_dynamic_lds(PerDeviceOnce& once, const void* kern, size_t bytes) {
+  return once.run([&](int) { return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes); });
+}
 
 constexpr int kMaxExpertsHost = 256;  // expert ids fit in 8 bits
 enum RowGemmMode { kGemmGateUp = 0, kGemmDown = 1, kGemmDA = 2, kGemmDX = 3 };

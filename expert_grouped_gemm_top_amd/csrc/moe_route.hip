@@ -2,8 +2,9 @@
 //
 // Routing of each token to k of E experts (npu-train issue #14, sections
 // Evidence and Proposal).  Ranking: logit descending, equal logits to the lower
-// expert index (+0.0 and -0.0 compare equal).  Weights: softmax over the k
-// selected logits with the largest one subtracted.
+// expert index (+0.0 and -0.0 compare equal), a NaN above every number (NaNs
+// among themselves by index).  Weights: softmax over the k selected logits
+// with the largest one subtracted (NaN for a token with a NaN logit).
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -11,9 +12,18 @@ namespace moe {
 
 namespace {
 
-// (va, ia) ranks before (vb, ib)?
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+// Total-order key of a logit: larger key = ranks first.  -0.0 maps to the key
+// of +0.0 and every NaN to the largest key, so the ranks of one token's logits
+// are always a permutation of 0..E-1.
+__device__ __forceinline__ uint32_t rank_key(float v) {
+  if (v != v) return 0xffffffffu;
+  const uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// (key a, index ia) ranks before (key b, index ib)?
+__device__ __forceinline__ bool ranks_before(uint32_t ka, int ia, uint32_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -31,7 +41,7 @@ __device__ __forceinline__ float wave_max(float v) {
 template <int SLOTS>
 __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k, const float* __restrict__ logits,
                                                          int32_t* __restrict__ idx, float* __restrict__ w) {
-  __shared__ __attribute__((aligned(16))) float s_l[4][kMaxExperts];
+  __shared__ __attribute__((aligned(16))) uint32_t s_l[4][kMaxExperts];  // rank keys
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave exits; only this wave's LDS row is used below
@@ -40,22 +50,26 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k, co
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) v[i] = lt[min(lane + 64 * i, E - 1)];  // in bounds, no branch
   const int E4 = (E + 3) & ~3;
+  uint32_t key[SLOTS];
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) {
     const int e = lane + 64 * i;
-    // entries E..E4-1 are -inf: they never rank before a finite logit
-    if (e < E4) s_l[wv][e] = (e < E) ? v[i] : -__builtin_inff();
+    key[i] = rank_key(v[i]);
+    // entries E..E4-1 hold key 0 and an index past every expert: they never
+    // rank before a real logit
+    if (e < E4) s_l[wv][e] = (e < E) ? key[i] : 0u;
   }
+  __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the wave's LDS writes before its reads
   int rank[SLOTS];
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) rank[i] = 0;
   for (int j = 0; j < E4; j += 4) {
-    const f32x4 q = *(const f32x4*)&s_l[wv][j];
+    const u32x4 q = *(const u32x4*)&s_l[wv][j];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < SLOTS; ++i) rank[i] += ranks_before(q[u], j + u, v[i], lane + 64 * i) ? 1 : 0;
+      for (int i = 0; i < SLOTS; ++i) rank[i] += ranks_before(q[u], j + u, key[i], lane + 64 * i) ? 1 : 0;
   }
   float top = -__builtin_inff();
 #pragma unroll

@@ -128,10 +128,14 @@ int moe_router_fwd(int T, int H, int E, int dtype, const void* x, const void* w_
 
 /* Top-k routing (issue #14, Evidence and Proposal: each token is routed to k
  * of E experts).  For token t the experts are ranked by logit descending, equal
- * logits by lower expert index; topk_idx[t, 0..k) lists the first k in that
- * order.  The weights are the softmax over the k selected logits,
+ * logits by lower expert index (+0.0 equals -0.0); topk_idx[t, 0..k) lists the
+ * first k in that order.  The weights are the softmax over the k selected
+ * logits,
  *   topk_w[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0).
- * logits [T, E] fp32 (device, finite); topk_idx [T, k] int32 (device, out);
+ * NaN logits (the pages say nothing of them) rank above every number, NaNs
+ * among themselves by lower index, so topk_idx always holds k distinct experts;
+ * a token with a NaN logit gets NaN weights.
+ * logits [T, E] fp32 (device); topk_idx [T, k] int32 (device, out);
  * topk_w [T, k] fp32 (device, out). */
 int moe_route_topk(int T, int E, int k, const float* logits, int32_t* topk_idx, float* topk_w,
                    void* stream);

@@ -339,6 +339,27 @@ def test_route_edge_cases(T, E, k):
         assert np.abs(w.sum(1) - 1).max() <= 1e-6
 
 
+@pytest.mark.parametrize("T,E,k", [(40, 256, 16), (40, 128, 8), (24, 7, 3), (24, 65, 1)])
+def test_route_nan_and_infinite_logits(T, E, k):
+    """NaN rows, rows with a few NaNs, infinities and signed zeros: the
+    selection is bit-exact (every slot written with a distinct expert) and the
+    weights are NaN exactly where the oracle's are, else within tolerance."""
+    rng = np.random.default_rng(T * 7 + E)
+    vals = np.array([np.nan, -np.inf, -2.0, -0.0, 0.0, 0.5, 3.0, np.inf], np.float32)
+    logits = rng.choice(vals, size=(T, E)).astype(np.float32)
+    logits[:8] = rng.standard_normal((8, E))
+    logits[8:12] = np.nan
+    logits[12:16] = rng.standard_normal((4, E))
+    logits[12:16, :: max(1, E // 3)] = np.nan
+    idx, w = _gpu_route(logits, k)
+    ridx, rw = oracle.route_topk(logits, k)
+    assert np.array_equal(idx, ridx)
+    assert all(len(set(r)) == k for r in idx.tolist())
+    assert np.array_equal(np.isnan(w), np.isnan(rw))
+    ok = ~np.isnan(rw)
+    assert np.abs(w[ok] - rw[ok]).max() <= 1e-6
+
+
 @pytest.mark.parametrize("T,E,k,skew", [(1000, 128, 8, True), (129, 8, 8, False), (16384, 128, 8, True),
                                         (4097, 256, 1, True), (3, 4, 2, False)])
 def test_dispatch_edge_cases(T, E, k, skew):
