@@ -309,7 +309,7 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int moe_abi_version(void) { return 5; }
+int moe_abi_version(void) { return 6; }
 
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
   const char* fn = "moe_profile_kernel";
@@ -374,6 +374,25 @@ int moe_dispatch(int T, int H, int E, int k, int dtype, const int32_t* topk_idx,
           workspace_bytes, need);
   REQUIRE(need == 0 || workspace != nullptr, MOE_ERR_INVALID_ARGUMENT, "%s: workspace must not be NULL", fn);
   return dispatch_launch(fn, T, H, E, k, dtype, topk_idx, x, counts, offsets, perm, inv_perm, x_sorted, workspace,
+                         as_stream(stream));
+}
+
+size_t moe_dispatch_noalloc_max_workspace(void) { return moe::kDispatchScratchBytes; }
+
+int moe_dispatch_noalloc(int T, int H, int E, int k, int dtype, const int32_t* topk_idx, const void* x,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_sorted,
+                         void* stream) {
+  const char* fn = "moe_dispatch_noalloc";
+  int rc = check_dispatch(fn, T, H, E, k, dtype, topk_idx, x, counts, offsets, perm, inv_perm, x_sorted);
+  if (rc) return rc;
+  const size_t need = moe::dispatch_workspace_bytes((int64_t)T * k, E);
+  REQUIRE(need <= moe::kDispatchScratchBytes, MOE_ERR_UNSUPPORTED,
+          "%s: T=%d, E=%d, k=%d need %zu bytes of workspace, above the library's %zu (use moe_dispatch with a "
+          "caller workspace)",
+          fn, T, E, k, need, moe::kDispatchScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && (rc = hip_status(moe::dispatch_scratch(&ws), fn))) return rc;
+  return dispatch_launch(fn, T, H, E, k, dtype, topk_idx, x, counts, offsets, perm, inv_perm, x_sorted, ws,
                          as_stream(stream));
 }
 

@@ -202,6 +202,36 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(int T, int k, int ro
 
 }  // namespace
 
+// Library-owned dispatch workspace for callers that cannot allocate device
+// memory (moe_dispatch_noalloc).  Every GPU the library runs on holds its own
+// copy until the process ends.  Host code must use the device address that
+// hipGetSymbolAddress returns for it (dispatch_scratch below), never the
+// array's name, which on the host is only a stand-in for the symbol.
+// Nothing in it needs to start at zero: the histogram kernel writes every
+// entry it uses before the scan reads it, and the scan writes every base the
+// rank kernel reads.
+static __device__ __align__(256) unsigned char scratch[kDispatchScratchBytes];
+
+hipError_t dispatch_scratch(void** out) {
+  static PerDeviceOnce once;
+  static void* addr[PerDeviceOnce::kDevices];
+  void* fresh = nullptr;
+  hipError_t err = once.run([&](int dev) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess) {
+      fresh = p;
+      if (dev >= 0 && dev < PerDeviceOnce::kDevices) addr[dev] = p;
+    }
+    return e;
+  });
+  if (err != hipSuccess) return err;
+  int dev = 0;
+  if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
+  *out = (dev >= 0 && dev < PerDeviceOnce::kDevices) ? addr[dev] : fresh;
+  return *out != nullptr ? hipSuccess : hipErrorInvalidSymbol;
+}
+
 size_t dispatch_workspace_bytes(int64_t N, int E) {
   const int64_t nblocks = (N + kPairsPerBlock - 1) / kPairsPerBlock;
   if (nblocks <= 1) return 0;

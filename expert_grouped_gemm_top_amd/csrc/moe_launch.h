@@ -106,6 +106,11 @@ __device__ __forceinline__ int64_t h_row_of(const RowGemmArgs& g, int64_t s) {
 hipError_t launch_route_topk(int T, int E, int k, const float* logits, int32_t* idx, float* w, hipStream_t stream);
 
 size_t dispatch_workspace_bytes(int64_t N, int E);
+// Size of the library-owned dispatch workspace of moe_dispatch_noalloc (per GPU).
+constexpr size_t kDispatchScratchBytes = (size_t)4 << 20;
+// Device address of that workspace on the current device (looked up once per
+// device).
+hipError_t dispatch_scratch(void** out);
 hipError_t launch_dispatch_index(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
                                  int32_t* perm, int32_t* inv_perm, void* ws, hipStream_t stream);
 hipError_t launch_dispatch_rows(int T, int H, int k, int esize, const void* x, const int32_t* inv_perm, void* x_sorted,

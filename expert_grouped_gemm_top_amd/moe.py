@@ -36,6 +36,8 @@ _SIGS = {
     "moe_router_bwd": ([_i, _i, _i, _i, _i] + [_vp] * 8 + [_i, _vp, _sz, _vp], _i),
     "moe_dispatch_workspace_bytes": ([_i, _i, _i], _sz),
     "moe_dispatch": ([_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i),
+    "moe_dispatch_noalloc": ([_i, _i, _i, _i, _i] + [_vp] * 8, _i),
+    "moe_dispatch_noalloc_max_workspace": ([], _sz),
     "moe_grouped_swiglu_fwd": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i),
     "moe_grouped_swiglu_fwd_gather": ([_i] * 7 + [_vp] * 10, _i),
     "moe_grouped_swiglu_recompute": ([_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i] + [_vp] * 5, _i),
@@ -176,6 +178,25 @@ def moe_dispatch(topk_idx, x, counts, offsets, perm, inv_perm, x_sorted, workspa
                               _ptr(x_sorted, "x_sorted", x.dtype if x is not None else None, N * H, allow_none=True),
                               _ptr(workspace, "workspace", None, None, allow_none=ws_need == 0), ws_bytes,
                               _stream(stream)))
+
+
+def moe_dispatch_noalloc(topk_idx, x, counts, offsets, perm, inv_perm, x_sorted, E: int, stream=None):
+    """moe_dispatch with the library-held workspace (no allocation anywhere)."""
+    T, k = topk_idx.shape
+    H = x.shape[1] if x is not None else 8
+    dt = _dt(x) if x is not None else MOE_BF16
+    N = T * k
+    _check(lib().moe_dispatch_noalloc(T, H, E, k, dt, _ptr(topk_idx, "topk_idx", I32, N),
+                                      _ptr(x, "x", None, T * H, allow_none=True), _ptr(counts, "counts", I32, E),
+                                      _ptr(offsets, "offsets", I32, E + 1), _ptr(perm, "perm", I32, N),
+                                      _ptr(inv_perm, "inv_perm", I32, N),
+                                      _ptr(x_sorted, "x_sorted", x.dtype if x is not None else None, N * H,
+                                           allow_none=True),
+                                      _stream(stream)))
+
+
+def moe_dispatch_noalloc_max_workspace() -> int:
+    return int(lib().moe_dispatch_noalloc_max_workspace())
 
 
 def moe_grouped_swiglu_fwd(offsets, x_sorted, w_gate, w_up, w_down, h_save, a_save, o_sorted, max_rows: int,

@@ -30,7 +30,8 @@
  *
  * Conventions for every call:
  *  - Pointers marked (device) are device pointers owned by the caller; the
- *    library allocates no memory and keeps no pointer after a call returns.
+ *    library allocates no memory and keeps no pointer after a call returns
+ *    (its one device array, moe_dispatch_noalloc's workspace, is static).
  *  - `stream` is a hipStream_t (NULL = the default stream).  A call only
  *    enqueues work on it: no device synchronisation, no device-to-host copy.
  *    Data-dependent sizes (row counts, offsets, the retained total) stay on the
@@ -72,7 +73,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 const char* moe_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);
-/* ABI version, currently 5. */
+/* ABI version, currently 6. */
 int moe_abi_version(void);
 
 /* Kernels that moe_profile_kernel can bracket with events. */
@@ -156,6 +157,26 @@ size_t moe_dispatch_workspace_bytes(int T, int E, int k);
 int moe_dispatch(int T, int H, int E, int k, int dtype, const int32_t* topk_idx, const void* x,
                  int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_sorted,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_dispatch for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, kernels and results as moe_dispatch, without the workspace: the
+ * dispatch workspace is an array the library holds on every GPU it runs on,
+ * until the process ends, of moe_dispatch_noalloc_max_workspace() bytes
+ * (4 MiB).  A call whose moe_dispatch_workspace_bytes(T, E, k) exceeds that is
+ * rejected with MOE_ERR_UNSUPPORTED before anything is enqueued (4 MiB holds
+ * T*k up to 4194304 pairs at E = 128, 2097152 at E = 256).  The call allocates
+ * nothing; its first call on a device looks up the array's device address
+ * once.  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (on different streams, or from host threads without an
+ * order between them) race and give wrong results; calls on one stream are
+ * ordered and safe.  Nothing in the array needs clearing between calls. */
+int moe_dispatch_noalloc(int T, int H, int E, int k, int dtype, const int32_t* topk_idx, const void* x,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_sorted,
+                         void* stream);
+/* Bytes of the library-held dispatch workspace of moe_dispatch_noalloc.
+ * Host-only. */
+size_t moe_dispatch_noalloc_max_workspace(void);
 
 /* SwiGLU expert forward as a ragged grouped GEMM (issue #14, Proposal: expert
  * forward graphs; pull request #44, Changes: forward keeps the activations that

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(LIB)
     missing = [n for n in declared_functions() if not hasattr(raw, n)]
     assert not missing, missing
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def _err(lib):
@@ -73,6 +73,23 @@ def test_dispatch_validation(lib):
     assert lib.moe_dispatch(*bad) == 2
     bad = list(args); bad[12] = NULL
     assert lib.moe_dispatch(*bad) == 1
+
+
+def test_dispatch_noalloc_validation(lib):
+    """The library-held workspace has a stated maximum; a call that needs more
+    is rejected (before any HIP call) with a message naming the limit."""
+    cap = lib.moe_dispatch_noalloc_max_workspace()
+    assert cap == 4 << 20
+    f = lib.moe_dispatch_noalloc
+    # largest T at E = 128, k = 8 whose workspace fits, and the next block of pairs past it
+    assert lib.moe_dispatch_workspace_bytes(524288, 128, 8) == cap
+    assert lib.moe_dispatch_workspace_bytes(524288 + 128, 128, 8) > cap
+    assert f(524288 + 128, 2048, 128, 8, 1, P, P, P, P, P, P, P, NULL) == 2
+    assert "4194304" in _err(lib) and "moe_dispatch" in _err(lib)
+    assert f(1 << 20, 2048, 256, 8, 1, P, P, P, P, P, P, P, NULL) == 2
+    assert f(4096, 2048, 128, 8, 1, P, NULL, P, P, P, P, P, NULL) == 1 and "x_sorted" in _err(lib)
+    assert f(4096, 2048, 128, 8, 1, NULL, P, P, P, P, P, P, NULL) == 1 and "topk_idx" in _err(lib)
+    assert f(4096, 100, 128, 8, 1, P, P, P, P, P, P, P, NULL) == 2
 
 
 def test_grouped_calls_validation(lib):
