@@ -9,7 +9,12 @@ experts frozen: forward + dx).
 
 Prints ONE JSON line: tokens/s over K timed steps, the roofline of the
 dominant kernel (its duration from HIP events on its own stream, inside the
-timed steps), and the CPU oracle timed on the host cores.  Between the warmup
+timed steps), and the CPU oracle timed on the host cores.  By default the line
+also carries one record per other workload under "configs" (the tiny fp32
+layer, full fine-tuning at the Qwen3 and GLM-Air shapes, the compacted
+backward): step time, tokens/s, TFLOPS against the matrix-core peak, the
+dominant kernel's roofline, the row kernels against HBM and a per-phase oracle
+baseline on a token prefix.  Between the warmup
 and the timed steps, a few untimed steps with every GEMM bracketed by events
 give the per-kernel durations and pick the dominant kernel; inside the timed
 steps only that kernel is bracketed (each event costs stream time).  After the
@@ -40,14 +45,18 @@ PEAK_F32_TFLOPS = 157.3
 # kernel ids of include/moe.h (moe_kernel)
 K_GATEUP, K_DOWN, K_COMBINE, K_GRAD_ROWS, K_DA, K_DX, K_DW, K_DISPATCH_ROWS = 2, 3, 4, 5, 6, 7, 8, 1
 K_ROUTER_FWD, K_ROUTER_DW = 10, 11
-KERNEL_NAMES = {K_GATEUP: "row_gemm_bf16_kernel<GATEUP>", K_DOWN: "row_gemm_bf16_kernel<DOWN>",
-                K_DA: "row_gemm_bf16_kernel<DA>", K_DX: "row_gemm_bf16_kernel<DX>", K_DW: "dw_bf16_kernel",
+# Phases bracketed by moe_profile_kernel; a GEMM phase is every kernel one
+# call launches (bf16: experts below 256 rows on row_gemm_bf16_kernel, larger
+# ones on big_gemm_bf16_kernel; dW: dw_small_bf16_kernel then dw_bf16_kernel;
+# fp32: row_gemm_f32_kernel, dw_f32_kernel), timed as one.
+KERNEL_NAMES = {K_GATEUP: "gate/up GEMM + SwiGLU", K_DOWN: "down GEMM", K_DA: "dA GEMM + SwiGLU backward",
+                K_DX: "dX GEMM", K_DW: "dW GEMMs",
                 K_DISPATCH_ROWS: "dispatch_rows_kernel", K_GRAD_ROWS: "grad_rows_kernel",
                 K_COMBINE: "combine_kernel", K_ROUTER_FWD: "router logits (x W_r)",
                 K_ROUTER_DW: "router_bwd (dlogits, dW_r, dx)"}
 
 
-def parse():
+def _parser():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
@@ -79,7 +88,20 @@ def parse():
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after the timed steps, run one plain elementwise copy of this many MiB (read and write "
                         "each) so that HBM byte counters can be calibrated against a kernel of known traffic")
-    return p.parse_args()
+    p.add_argument("--no-configs", action="store_true",
+                   help="measure only the chosen workload (by default the tiny fp32 layer, full fine-tuning at the "
+                        "Qwen3 and GLM-Air shapes and the compacted backward follow, one record each under "
+                        "\"configs\")")
+    return p
+
+
+def parse():
+    return _parser().parse_args()
+
+
+def parse_defaults():
+    """The default path options (no flags)."""
+    return _parser().parse_args([])
 
 
 # Sources whose code decides the HBM traffic of each kernel; a stored counter
@@ -238,9 +260,11 @@ def probes(dev):
     return res
 
 
-def cpu_baseline(wl, d, logits, sample_tokens):
-    """The oracle (as it stands) on a token prefix of the same workload:
-    route -> dispatch -> forward/combine -> backward dx, dg (-> dW)."""
+def cpu_baseline(wl, d, logits, sample_tokens, min_seconds=10.0):
+    """The oracle (as it stands, IEEE double) on a token prefix of the same
+    workload, phase by phase: route -> dispatch -> forward (with the combine)
+    -> [compaction] -> backward dx, dg -> [dW].  The whole sample is repeated
+    until about ``min_seconds`` of host work has been timed."""
     import numpy as np
 
     import oracle
@@ -249,29 +273,43 @@ def cpu_baseline(wl, d, logits, sample_tokens):
     sub = {n: np.ascontiguousarray(d[n][:T], dtype=np.float64) for n in ("x", "dy")}
     W64 = {n: np.ascontiguousarray(d[n], dtype=np.float64) for n in ("W_gate", "W_up", "W_down")}
     lg = np.ascontiguousarray(logits[:T], dtype=np.float64)
-    # repeat the whole sample until about 10 s of host work has been timed
+    Wg, Wu, Wd = W64["W_gate"], W64["W_up"], W64["W_down"]
+    phases = {"route": 0.0, "dispatch": 0.0, "forward+combine": 0.0}
+    if wl.rho is not None:
+        phases["compact"] = 0.0
+    phases["backward dx+dg"] = 0.0
+    if wl.dw:
+        phases["dW"] = 0.0
     reps, dt = 0, 0.0
-    while dt < 10.0 and reps < 20:
-        t0 = time.perf_counter()
-        idx, w = oracle.route_topk(lg, wl.k)
-        oracle.dispatch(idx, wl.E)
-        oracle.forward(sub["x"], idx, w, W64["W_gate"], W64["W_up"], W64["W_down"])
-        oracle.backward(sub["x"], idx, w, W64["W_gate"], W64["W_up"], W64["W_down"], sub["dy"])
+    while dt < min_seconds and reps < 20:
+        def timed(name, fn, *a, **kw):
+            t0 = time.perf_counter()
+            r = fn(*a, **kw)
+            phases[name] += time.perf_counter() - t0
+            return r
+        idx, w = timed("route", oracle.route_topk, lg, wl.k)
+        counts, offsets, perm, _ = timed("dispatch", oracle.dispatch, idx, wl.E)
+        timed("forward+combine", oracle.forward, sub["x"], idx, w, Wg, Wu, Wd)
+        retained = None
+        if wl.rho is not None:
+            retained = timed("compact", oracle.compact, T, wl.E, wl.k, counts, offsets, perm, w, wl.rho)["retained"]
+        timed("backward dx+dg", oracle.backward, sub["x"], idx, w, Wg, Wu, Wd, sub["dy"], retained=retained)
         if wl.dw:
-            oracle.backward_dw(sub["x"], idx, w, W64["W_gate"], W64["W_up"], W64["W_down"], sub["dy"])
-        dt += time.perf_counter() - t0
+            timed("dW", oracle.backward_dw, sub["x"], idx, w, Wg, Wu, Wd, sub["dy"], retained=retained)
+        dt = sum(phases.values())
         reps += 1
+    steps = "route+dispatch+forward+combine" + ("+compact" if wl.rho is not None else "") + "+dx+dg" + \
+            ("+dW" if wl.dw else "")
     return {"value": T * reps / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{T} of {wl.T} tokens of {wl.name}, {reps} repetitions (fp64 oracle, route+dispatch+forward"
-                      f"+combine+dx+dg{'+dW' if wl.dw else ''}), {dt:.2f} s wall"}
+            "precision": "fp64",
+            "sample": f"{T} of {wl.T} tokens of {wl.name}, {reps} repetitions (fp64 oracle, {steps}), {dt:.2f} s wall",
+            "phase_s_per_rep": {n: v / reps for n, v in phases.items()}}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=False):
+    """One workload on the GPU: warmup, an untimed pass with every kernel
+    bracketed (per-kernel durations, the dominant kernel), then ``steps`` timed
+    steps with only the dominant kernel bracketed.  Returns the record."""
     import numpy as np
     import torch
 
@@ -279,28 +317,39 @@ def main():
     from expert_grouped_gemm_top_amd import workloads as W
     from expert_grouped_gemm_top_amd.layer import MoeLayerBuffers
 
-    wl = W.WORKLOADS[args.workload]
-    assert wl.dtype == "bf16", "the benchmark runs the bf16 workloads"
+    f32 = wl.dtype == "f32"
+    tdt = torch.float32 if f32 else torch.bfloat16
     d = W.generate(wl, seed=0)
     dev = torch.device("cuda:0")
-    t = {n: torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in ("x", "W_gate", "W_up", "W_down", "dy")}
-    logits = torch.from_numpy(d["logits"]).to(dev)
+    t = {n: torch.from_numpy(d[n]).to(dev).to(tdt) for n in ("x", "W_gate", "W_up", "W_down", "dy")}
+    if wl.router == "wr":
+        # router-weight workloads: the logits x W_r are an input of the step,
+        # computed once here with the library's router kernel
+        w_r_in = torch.from_numpy(d["W_r"]).to(dev).to(tdt)
+        logits = torch.empty(wl.T, wl.E, dtype=torch.float32, device=dev)
+        rws = torch.empty(max(moe.moe_router_workspace_bytes(wl.T, wl.H, wl.E), 16), dtype=torch.uint8, device=dev)
+        moe.moe_router_fwd(t["x"], w_r_in, logits, rws)
+        torch.cuda.synchronize()
+        logits_host = None
+    else:
+        logits = torch.from_numpy(d["logits"]).to(dev)
+        logits_host = d["logits"]
     quota_cap = None
     if args.budget_mib > 0 and wl.rho is not None:
-        quota_cap = moe.moe_quota_cap_for_budget(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, wl.dw,
+        quota_cap = moe.moe_quota_cap_for_budget(wl.T, wl.H, wl.F, wl.E, wl.k, tdt, wl.dw,
                                                  not args.no_keep_graph, args.budget_mib << 20)
         assert quota_cap >= 1, "the budget does not hold one row per expert"
-    L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, torch.bfloat16, dev, rho=wl.rho if quota_cap is None else None,
+    L = MoeLayerBuffers(wl.T, wl.H, wl.F, wl.E, wl.k, tdt, dev, rho=wl.rho if quota_cap is None else None,
                         dw=wl.dw, dg=True, router=args.router, keep_graph=not args.no_keep_graph, quota_cap=quota_cap,
                         overlap_dw=args.overlap_dw,
                         gather_rows=None if args.gather_rows == "auto" else args.gather_rows == "on")
     score = "metric" if args.metric_score else None
     wq = None
     if args.fp8_weights:
-        assert not wl.dw and wl.rho is None and not args.no_keep_graph, \
-            "fp8 weights are frozen: LoRA or forward-only workloads, pre-activations kept"
+        assert not wl.dw and wl.rho is None and not args.no_keep_graph and not f32, \
+            "fp8 weights are frozen: bf16 LoRA or forward-only workloads, pre-activations kept"
         wq = moe.Fp8Weights(t["W_gate"], t["W_up"], t["W_down"])  # once, before any timing
-    w_r = torch.from_numpy(W.router_weights(wl, seed=0)).to(dev).to(torch.bfloat16) if args.router else None
+    w_r = torch.from_numpy(W.router_weights(wl, seed=0)).to(dev).to(tdt) if args.router else None
     stream = torch.cuda.current_stream()
 
     def step():
@@ -308,7 +357,7 @@ def main():
         if not args.forward_only:
             L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream, w_r=w_r, score=score, wq=wq)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
@@ -346,23 +395,25 @@ def main():
         return dt, {kk: float(np.mean([a.elapsed_time(b) for a, b in ev[kk]])) for kk in kinds}
 
     # untimed pass: every GEMM's duration, to find the dominant kernel
-    _, kernel_ms = run_steps(max(3, min(args.steps, 10)), profiled)
+    _, kernel_ms = run_steps(max(3, min(steps, 10)), profiled)
     dom = max(gemm_kernels, key=lambda kk: kernel_ms[kk])
     # timed steps: only the dominant kernel is bracketed by events
-    elapsed, dom_ms = run_steps(args.steps, [dom])
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = wl.T * args.steps / elapsed
+    elapsed, dom_ms = run_steps(steps, [dom])
+    ms_per_step = elapsed * 1e3 / steps
+    tokens_per_s = wl.T * steps / elapsed
 
     counts = L.counts.cpu().numpy()
     kept = L.kept_counts.cpu().numpy() if L.compacted else None
     alg = algorithmic(wl, counts, kept, gathered=L.gather_rows, weight_bytes=1 if wq is not None else None)
     step_flops = sum(alg[kk][1] for kk in gemm_kernels)
+    peak_flops = PEAK_F32_TFLOPS if f32 else PEAK_BF16_TFLOPS
     byts, flops = alg[dom]
-    ai = flops / byts
-    mfma_bound = ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    compute_bound = flops / byts > peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
     sec = dom_ms[dom] * 1e-3
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    if compute_bound:
+        # fp32 layers run on plain fp32 FMAs (vector ALU), bf16 on the matrix cores
+        roof = {"bound": "alu" if f32 else "mfma", "achieved": flops / sec / 1e12, "peak": peak_flops,
+                "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": byts / sec / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -372,28 +423,31 @@ def main():
     roof["kernel_us"] = dom_ms[dom] * 1e3
     roof["algorithmic_bytes"] = byts
     roof["algorithmic_flops"] = flops
+    roof["mfma_frac"] = flops / sec / 1e12 / peak_flops  # the phase's flops against the matrix-core peak
+    roof["hbm_frac"] = byts / sec / 1e9 / PEAK_HBM_GBS
 
-    out = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "F": wl.F, "E": wl.E, "k": wl.k,
-                   "pass": ("router+" if args.router else "") + ("fwd" if args.forward_only else "fwd+dx+dg")
-                           + ("+dW" if wl.dw and not args.forward_only else "")
-                           + (f"+compact(rho={wl.rho})" if wl.rho and not quota_cap else "")
-                           + ("+router_bwd" if args.router else "")
-                           + ("+recompute_h" if args.no_keep_graph else "")
-                           + ("+dW_overlapped" if args.overlap_dw and wl.dw and not args.forward_only else "")
-                           + ("" if args.gather_rows == "auto" else f"+gather_rows={args.gather_rows}")
-                           + ("+metric_score" if args.metric_score else "")
-                           + (f"+budget({args.budget_mib} MiB: cap {quota_cap})" if quota_cap else "")
-                           + ("+fp8_weights" if wq is not None else ""),
-                   "weights": "fp8 E4M3 (per-expert power-of-two scale), widened to bf16" if wq is not None
-                              else "bf16",
-                   "experts_with_rows": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max())},
+    rec = {
+        "workload": wl.name, "T": wl.T, "H": wl.H, "F": wl.F, "E": wl.E, "k": wl.k, "dtype": "f32" if f32 else "bf16",
+        "pass": ("router+" if args.router else "") + ("fwd" if args.forward_only else "fwd+dx+dg")
+                + ("+dW" if wl.dw and not args.forward_only else "")
+                + (f"+compact(rho={wl.rho})" if wl.rho and not quota_cap else "")
+                + ("+router_bwd" if args.router else "")
+                + ("+recompute_h" if args.no_keep_graph else "")
+                + ("+dW_overlapped" if args.overlap_dw and wl.dw and not args.forward_only else "")
+                + ("" if args.gather_rows == "auto" else f"+gather_rows={args.gather_rows}")
+                + ("+metric_score" if args.metric_score else "")
+                + (f"+budget({args.budget_mib} MiB: cap {quota_cap})" if quota_cap else "")
+                + ("+fp8_weights" if wq is not None else ""),
+        "weights": "fp8 E4M3 (per-expert power-of-two scale), widened to bf16" if wq is not None
+                   else ("fp32" if f32 else "bf16"),
+        "experts_with_rows": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max()),
+        "retained_pairs": int(kept.sum()) if kept is not None else wl.N,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s,
         "tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
-        "mfma_frac_of_step": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "mfma_frac_of_step": step_flops / (ms_per_step * 1e-3) / 1e12 / peak_flops,
+        "peak_tflops": peak_flops,
         "kernel_us": {KERNEL_NAMES[kk]: kernel_ms[kk] * 1e3 for kk in gemm_kernels + router_kernels},
+        "gemm_tflops": {KERNEL_NAMES[kk]: alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12 for kk in gemm_kernels},
         "roofline": roof,
         # dispatch / combine / dO rows against the HBM peak (algorithmic bytes)
         "hbm_kernels": {KERNEL_NAMES[kk]: {"us": kernel_ms[kk] * 1e3,
@@ -403,15 +457,13 @@ def main():
     }
     if args.router:
         # bf16 router products run on the bf16 matrix cores (roofline: bf16 MFMA peak)
-        out["router"] = {KERNEL_NAMES[kk]: {"us": kernel_ms[kk] * 1e3,
+        rec["router"] = {KERNEL_NAMES[kk]: {"us": kernel_ms[kk] * 1e3,
                                             "TFLOP/s": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12,
                                             "frac_bf16_mfma": alg[kk][1] / (kernel_ms[kk] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                             "GB/s": alg[kk][0] / (kernel_ms[kk] * 1e-3) / 1e9}
                          for kk in router_kernels}
-    out["env"] = environment(dev)
-    if not args.no_probes:
-        out["step_ms"] = step_distribution(step, stream, dev, n=max(10, min(args.steps, 20)))
-        out["probes"] = probes(dev)
+    if dist_and_probes:
+        rec["step_ms"] = step_distribution(step, stream, dev, n=max(10, min(steps, 20)))
     if args.copy_probe_mib > 0:
         # one read + one write of copy_probe_mib MiB each, outside the timed steps
         src = torch.ones(args.copy_probe_mib << 19, dtype=torch.bfloat16, device=dev)
@@ -420,9 +472,65 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu_baseline:
-        n = args.cpu_tokens or min(wl.T, 128)
-        out["cpu_baseline"] = cpu_baseline(wl, d, d["logits"], n)
+    del L, t, logits, wq
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu_tokens > 0:
+        if logits_host is None:  # logits of a router-weight workload: x W_r by the oracle, in fp32
+            import oracle
+            logits_host = oracle.router_logits(d["x"], d["W_r"]).astype(np.float32)
+        rec["cpu_baseline"] = cpu_baseline(wl, d, logits_host, min(cpu_tokens, wl.T), cpu_seconds)
+    return rec
+
+
+# Every default run also measures these workloads (one record each under
+# "configs"): the tiny fp32 layer, full fine-tuning at the Qwen3 and GLM-Air
+# shapes and the compacted backward, each with a shorter run and an oracle
+# sample of a token prefix (tokens, seconds of host work).
+SUB_CONFIGS = {"tiny_fp32": (64, 3.0), "qwen3_ft_t4096": (64, 5.0), "glm45air_t8192": (32, 5.0),
+               "qwen3_compact_t16384": (64, 5.0)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from expert_grouped_gemm_top_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    assert wl.dtype == "bf16", "the headline runs a bf16 workload"
+    cpu_tokens = 0 if args.no_cpu_baseline else (args.cpu_tokens or min(wl.T, 128))
+    rec = measure(wl, args, args.steps, args.warmup, cpu_tokens, 10.0, dist_and_probes=not args.no_probes)
+    out = {
+        "metric": METRIC, "value": rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {k: rec[k] for k in ("workload", "T", "H", "F", "E", "k", "pass", "weights", "experts_with_rows",
+                                       "max_rows_per_expert")},
+    }
+    for key in ("tflops", "mfma_frac_of_step", "kernel_us", "gemm_tflops", "roofline", "hbm_kernels", "router",
+                "step_ms"):
+        if key in rec:
+            out[key] = rec[key]
+    dev = torch.device("cuda:0")
+    out["env"] = environment(dev)
+    if not args.no_probes:
+        out["probes"] = probes(dev)
+    if "cpu_baseline" in rec:
+        out["cpu_baseline"] = rec["cpu_baseline"]
+    if not args.no_configs:
+        # the other workloads, each on the default path options
+        base = parse_defaults()
+        out["configs"] = {}
+        for name, (toks, secs) in SUB_CONFIGS.items():
+            if name == wl.name:
+                continue
+            print(f"bench: measuring {name}", file=sys.stderr, flush=True)
+            out["configs"][name] = measure(W.WORKLOADS[name], base, 10, 3, 0 if args.no_cpu_baseline else toks, secs)
     print(json.dumps(out), flush=True)
 
 
