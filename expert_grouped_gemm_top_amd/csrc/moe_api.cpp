@@ -14,6 +14,13 @@
 #include "moe.h"
 #include "moe_launch.h"
 
+namespace moe {
+namespace {
+thread_local int64_t g_launches = 0;  // kernel launches made from this thread
+}  // namespace
+void note_launch() { ++g_launches; }
+}  // namespace moe
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -309,7 +316,9 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int moe_abi_version(void) { return 6; }
+int moe_abi_version(void) { return 7; }
+
+int64_t moe_launch_count(void) { return moe::g_launches; }
 
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
   const char* fn = "moe_profile_kernel";

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void compact_select_kernel(int E, int cap, con
 hipError_t launch_fill_i32(int32_t* a, int64_t n, int32_t v, hipStream_t stream) {
   const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n, v);
+  MOE_LAUNCH(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n, v);
   return hipGetLastError();
 }
 
@@ -229,7 +229,7 @@ hipError_t launch_compact(int64_t N, int E, int cap, const int32_t* counts, cons
   static PerDeviceOnce lds_once;
   hipError_t err = allow_dynamic_lds(lds_once, (const void*)compact_select_kernel, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(compact_select_kernel, dim3(E), dim3(256), lds, stream, E, cap, counts, offsets, perm, score,
+  MOE_LAUNCH(compact_select_kernel, dim3(E), dim3(256), lds, stream, E, cap, counts, offsets, perm, score,
                      kept_counts, kept_offsets, kept_perm, kept_src, kept_inv);
   return hipGetLastError();
 }

@@ -243,15 +243,15 @@ hipError_t launch_dispatch_index(int T, int E, int k, const int32_t* idx, int32_
   const int64_t N = (int64_t)T * k;
   const int64_t nblocks = (N + kPairsPerBlock - 1) / kPairsPerBlock;
   if (nblocks <= 1) {
-    hipLaunchKernelGGL(dispatch_rank_kernel<true>, dim3(1), dim3(256), 0, stream, N, E, idx, nullptr, counts, offsets,
+    MOE_LAUNCH(dispatch_rank_kernel<true>, dim3(1), dim3(256), 0, stream, N, E, idx, nullptr, counts, offsets,
                        perm, inv_perm);
   } else {
     int32_t* hist = (int32_t*)ws;
     int32_t* base = hist + nblocks * E;
-    hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, N, E, idx, hist);
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, stream, (int)nblocks, E, hist, base, counts,
+    MOE_LAUNCH(dispatch_hist_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, N, E, idx, hist);
+    MOE_LAUNCH(dispatch_scan_kernel, dim3(1), dim3(256), 0, stream, (int)nblocks, E, hist, base, counts,
                        offsets);
-    hipLaunchKernelGGL(dispatch_rank_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream, N, E, idx, base,
+    MOE_LAUNCH(dispatch_rank_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream, N, E, idx, base,
                        counts, offsets, perm, inv_perm);
   }
   return hipGetLastError();
@@ -261,7 +261,7 @@ hipError_t launch_dispatch_rows(int T, int H, int k, int esize, const void* x, c
                                 hipStream_t stream) {
   const int row_chunks = (int)((int64_t)H * esize / 16);
   const int grid = T < 16384 ? T : 16384;
-  hipLaunchKernelGGL(dispatch_rows_kernel, dim3(grid), dim3(256), 0, stream, T, k, row_chunks, (const u32x4*)x,
+  MOE_LAUNCH(dispatch_rows_kernel, dim3(grid), dim3(256), 0, stream, T, k, row_chunks, (const u32x4*)x,
                      inv_perm, (u32x4*)x_sorted);
   return hipGetLastError();
 }

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(int64_t n0, int64_t n
 
 hipError_t launch_quantize_fp8(int E, int64_t n0, int64_t n1, const uint16_t* w0, const uint16_t* w1, uint8_t* q0,
                                uint8_t* q1, float* scale, hipStream_t stream) {
-  hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)E), dim3(256), 0, stream, n0, n1, w0, w1, q0, q1, scale);
+  MOE_LAUNCH(quantize_fp8_kernel, dim3((unsigned)E), dim3(256), 0, stream, n0, n1, w0, w1, q0, q1, scale);
   return hipGetLastError();
 }
 

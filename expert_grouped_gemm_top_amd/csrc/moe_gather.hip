@@ -222,10 +222,10 @@ void launch_combine_kp(int T_, int H, int k, const void* rows, const int32_t* in
   const int64_t items = (int64_t)T_ * (H / 8);
   const int64_t blocks = std::min<int64_t>((items + 127) / 128, 65536);
   if (w != nullptr)
-    hipLaunchKernelGGL((combine_kernel<T, KP, true>), dim3((unsigned)blocks), dim3(128), 0, stream, T_, H, k,
+    MOE_LAUNCH((combine_kernel<T, KP, true>), dim3((unsigned)blocks), dim3(128), 0, stream, T_, H, k,
                        (const T*)rows, inv, w, (T*)out);
   else
-    hipLaunchKernelGGL((combine_kernel<T, KP, false>), dim3((unsigned)blocks), dim3(128), 0, stream, T_, H, k,
+    MOE_LAUNCH((combine_kernel<T, KP, false>), dim3((unsigned)blocks), dim3(128), 0, stream, T_, H, k,
                        (const T*)rows, inv, w, (T*)out);
 }
 
@@ -233,10 +233,10 @@ template <typename T, int KP>
 void launch_grad_rows_kp(int T_, int H, int k, const void* dy, const float* w, const int32_t* inv, void* dO_rows,
                          const int32_t* inv_all, const void* o_sorted, float* dg, hipStream_t stream) {
   if (dg != nullptr)
-    hipLaunchKernelGGL((grad_rows_kernel<T, KP, true>), dim3(token_grid(T_)), dim3(256), 0, stream, T_, H, k,
+    MOE_LAUNCH((grad_rows_kernel<T, KP, true>), dim3(token_grid(T_)), dim3(256), 0, stream, T_, H, k,
                        (const T*)dy, w, inv, (T*)dO_rows, inv_all, (const T*)o_sorted, dg);
   else
-    hipLaunchKernelGGL((grad_rows_kernel<T, KP, false>), dim3(token_grid(T_)), dim3(256), 0, stream, T_, H, k,
+    MOE_LAUNCH((grad_rows_kernel<T, KP, false>), dim3(token_grid(T_)), dim3(256), 0, stream, T_, H, k,
                        (const T*)dy, w, inv, (T*)dO_rows, inv_all, (const T*)o_sorted, dg);
 }
 
@@ -289,10 +289,10 @@ hipError_t launch_grad_rows(int T, int H, int k, int esize, const void* dy, cons
 hipError_t launch_pair_scores(int T, int H, int F, int k, int esize, const int32_t* inv, const float* w,
                               const void* a_rows, const void* dy, float* score, hipStream_t stream) {
   if (esize == 4)
-    hipLaunchKernelGGL(pair_scores_kernel<float>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, F, k, inv, w,
+    MOE_LAUNCH(pair_scores_kernel<float>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, F, k, inv, w,
                        (const float*)a_rows, (const float*)dy, score);
   else
-    hipLaunchKernelGGL(pair_scores_kernel<uint16_t>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, F, k, inv, w,
+    MOE_LAUNCH(pair_scores_kernel<uint16_t>, dim3(token_grid(T)), dim3(256), 0, stream, T, H, F, k, inv, w,
                        (const uint16_t*)a_rows, (const uint16_t*)dy, score);
   return hipGetLastError();
 }
@@ -302,7 +302,7 @@ hipError_t launch_gather_rows(const int32_t* R_ptr, const int32_t* src, int max_
                               void* c_dst, int c_bytes, hipStream_t stream) {
   if (max_rows <= 0) return hipSuccess;
   const int grid = max_rows < 65536 ? max_rows : 65536;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), 0, stream, R_ptr, src, max_rows,
+  MOE_LAUNCH(gather_rows_kernel, dim3(grid), dim3(256), 0, stream, R_ptr, src, max_rows,
                      (const u32x4*)a_src, (u32x4*)a_dst, a_bytes / 16, (const u32x4*)b_src, (u32x4*)b_dst,
                      b_bytes / 16, (const u32x4*)c_src, (u32x4*)c_dst, c_bytes / 16);
   return hipGetLastError();

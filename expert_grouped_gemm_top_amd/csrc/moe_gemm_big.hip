@@ -220,10 +220,8 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
   };
   // Sub-steps are software-pipelined: the fragments of sub-step t+1 are read
   // from LDS while the MFMAs of sub-step t run.
-#ifndef MOE_BIG_SCHED
-#define MOE_BIG_SCHED 3  // bit 0: raise wave priority over the MFMA runs; bit 1: weave fragment reads between MFMAs
-#endif
-  constexpr int kSched = MOE_BIG_SCHED;
+  // bit 0: raise wave priority over the MFMA runs; bit 1: weave fragment reads between MFMAs
+  constexpr int kSched = 3;
   // one sub-step's MFMAs with the next sub-step's fragment reads woven in
   auto mfmas_interleaved = [&](const Frags& cur, const unsigned char* st, int next_sub, Frags& nxt) {
     if (kSched & 1) __builtin_amdgcn_s_setprio(1);
@@ -326,9 +324,6 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
   }
 }
 
-#ifndef MOE_BIG_CFG
-#define MOE_BIG_CFG 256, 256, 64, 8, 2, 2, 1   // BM, BN, BK, waves, waves along M, stages, workgroups per CU
-#endif
 
 template <int MODE, int BM, int BN, int BK, int NW, int WM, int STAGES, int WPC>
 struct BigCfg {
@@ -350,13 +345,13 @@ struct BigCfg {
     static PerDeviceOnce lds_once;
     hipError_t err = allow_dynamic_lds(lds_once, (const void*)kern, lds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(64 * NW), lds, stream, g);
+    MOE_LAUNCH(kern, dim3((unsigned)wgs), dim3(64 * NW), lds, stream, g);
     return hipGetLastError();
   }
 };
 
 template <int MODE>
-using Big = BigCfg<MODE, MOE_BIG_CFG>;
+using Big = BigCfg<MODE, 256, 256, 64, 8, 2, 2, 1>;  // BM, BN, BK, waves, waves along M, stages, workgroups per CU
 
 }  // namespace
 

@@ -33,12 +33,6 @@ namespace moe {
 
 namespace {
 
-#ifndef MOE_DW_CFG
-#define MOE_DW_CFG 256, 8, 64, 2, 1
-#endif
-#ifndef MOE_DW_SCHED
-#define MOE_DW_SCHED 1
-#endif
 
 template <int BN_, int WAVES_, int BK_, int STAGES_, int OCC_>
 struct DwCfg {
@@ -59,7 +53,7 @@ struct DwCfg {
   static_assert(BM * BN * 2 <= LDS_BYTES, "the output tile fits the stage buffers");
   static_assert(64 * WAVES >= kMaxExperts, "every expert has a thread in the ranking");
 };
-using Cfg = DwCfg<MOE_DW_CFG>;
+using Cfg = DwCfg<256, 8, 64, 2, 1>;  // 256 x 256 tiles, 8 waves, 64-deep stages, 2 stages, 1 workgroup per CU
 constexpr int kSmallMaxRows = Cfg::BK;  // experts with at most this many rows go to the small-expert kernel
 
 struct DwShape {
@@ -256,7 +250,6 @@ __global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwAr
   auto compute = [&](int s) {
     const unsigned char* st = s_dyn + (s % Cfg::STAGES) * Cfg::STAGE_BYTES;
     constexpr int SUBS = Cfg::BK / 16;
-#if MOE_DW_SCHED
     Frags f0, f1;
     read_frags(st, 0, f0);
 #pragma unroll
@@ -264,14 +257,6 @@ __global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwAr
       mfmas_interleaved(f0, st, u + 1 < SUBS ? u + 1 : -1, f1);
       if (u + 1 < SUBS) mfmas_interleaved(f1, st, u + 2 < SUBS ? u + 2 : -1, f0);
     }
-#else
-#pragma unroll
-    for (int sub = 0; sub < SUBS; ++sub) {
-      Frags f;
-      read_frags(st, sub, f);
-      mfmas(f);
-    }
-#endif
   };
 
   const int steps = (n_e + Cfg::BK - 1) / Cfg::BK;
@@ -356,10 +341,7 @@ constexpr int kSmallBM = 128, kSmallBN = 128;
 constexpr int kSmallPitch = 2 * kSmallBN;            // bytes per reduced row of either operand block
 constexpr int kSmallTile = Cfg::BK * kSmallPitch;    // 16 KiB
 constexpr int kSmallIns = kSmallTile / 1024 / 4;     // direct loads per wave per operand
-#ifndef MOE_DW_SMALL_TPW
-#define MOE_DW_SMALL_TPW 4
-#endif
-constexpr int kSmallTpw = MOE_DW_SMALL_TPW;          // consecutive tiles of one expert per workgroup
+constexpr int kSmallTpw = 4;          // consecutive tiles of one expert per workgroup
 
 struct DwSmallShape {
   int nt1, tiles1;  // gate/up: column tiles, all tiles
@@ -516,7 +498,7 @@ hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream) {
   // experts with at most one stage of rows (empty ones included)
   const DwSmallShape ss = dw_small_shape(g.H, g.F);
   const int64_t sblocks = (int64_t)g.E * dw_small_slots(ss);
-  hipLaunchKernelGGL(dw_small_bf16_kernel, dim3((unsigned)sblocks), dim3(256), 0, stream, g);
+  MOE_LAUNCH(dw_small_bf16_kernel, dim3((unsigned)sblocks), dim3(256), 0, stream, g);
   hipError_t serr = hipGetLastError();
   if (serr != hipSuccess) return serr;
   // the others
@@ -527,7 +509,7 @@ hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream) {
   static PerDeviceOnce lds_once;
   hipError_t err = allow_dynamic_lds(lds_once, (const void*)dw_bf16_kernel, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dw_bf16_kernel, dim3((unsigned)blocks), dim3(64 * Cfg::WAVES), lds, stream, g);
+  MOE_LAUNCH(dw_bf16_kernel, dim3((unsigned)blocks), dim3(64 * Cfg::WAVES), lds, stream, g);
   return hipGetLastError();
 }
 

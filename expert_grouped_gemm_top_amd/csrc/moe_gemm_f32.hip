@@ -131,10 +131,10 @@ hipError_t launch_row_gemm_f32(int mode, const RowGemmArgs& g, int max_rows, hip
   const int ncols = (mode == kGemmGateUp || mode == kGemmDA) ? g.F : g.H;
   const dim3 grid((unsigned)max_rows, (unsigned)((ncols + 255) / 256));
   switch (mode) {
-    case kGemmGateUp: hipLaunchKernelGGL(row_gemm_f32_kernel<kGemmGateUp>, grid, dim3(256), 0, stream, g); break;
-    case kGemmDown: hipLaunchKernelGGL(row_gemm_f32_kernel<kGemmDown>, grid, dim3(256), 0, stream, g); break;
-    case kGemmDA: hipLaunchKernelGGL(row_gemm_f32_kernel<kGemmDA>, grid, dim3(256), 0, stream, g); break;
-    default: hipLaunchKernelGGL(row_gemm_f32_kernel<kGemmDX>, grid, dim3(256), 0, stream, g); break;
+    case kGemmGateUp: MOE_LAUNCH(row_gemm_f32_kernel<kGemmGateUp>, grid, dim3(256), 0, stream, g); break;
+    case kGemmDown: MOE_LAUNCH(row_gemm_f32_kernel<kGemmDown>, grid, dim3(256), 0, stream, g); break;
+    case kGemmDA: MOE_LAUNCH(row_gemm_f32_kernel<kGemmDA>, grid, dim3(256), 0, stream, g); break;
+    default: MOE_LAUNCH(row_gemm_f32_kernel<kGemmDX>, grid, dim3(256), 0, stream, g); break;
   }
   return hipGetLastError();
 }
@@ -142,7 +142,7 @@ hipError_t launch_row_gemm_f32(int mode, const RowGemmArgs& g, int max_rows, hip
 hipError_t launch_dw_f32(DwArgs g, hipStream_t stream) {
   const int64_t outputs = (int64_t)3 * g.H * g.F;
   const dim3 grid((unsigned)((outputs + 255) / 256), (unsigned)g.E);
-  hipLaunchKernelGGL(dw_f32_kernel, grid, dim3(256), 0, stream, g);
+  MOE_LAUNCH(dw_f32_kernel, grid, dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 

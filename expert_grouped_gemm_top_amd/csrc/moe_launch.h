@@ -42,6 +42,15 @@ inline hipError_t allow_dynamic_lds(PerDeviceOnce& once, const void* kern, size_
   return once.run([&](int) { return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes); });
 }
 
+// Every kernel launch of the library goes through MOE_LAUNCH, which counts it
+// on the calling thread (moe_launch_count) and then launches it.
+void note_launch();
+#define MOE_LAUNCH(...)          \
+  do {                           \
+    ::moe::note_launch();        \
+    hipLaunchKernelGGL(__VA_ARGS__); \
+  } while (0)
+
 constexpr int kMaxExpertsHost = 256;  // expert ids fit in 8 bits
 enum RowGemmMode { kGemmGateUp = 0, kGemmDown = 1, kGemmDA = 2, kGemmDX = 3 };
 

@@ -99,10 +99,10 @@ hipError_t launch_route_topk(int T, int E, int k, const float* logits, int32_t* 
                              hipStream_t stream) {
   const dim3 grid((T + 3) / 4), block(256);
   switch ((E + 63) / 64) {
-    case 1: hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
-    case 2: hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
-    case 3: hipLaunchKernelGGL(route_topk_kernel<3>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
-    default: hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
+    case 1: MOE_LAUNCH(route_topk_kernel<1>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
+    case 2: MOE_LAUNCH(route_topk_kernel<2>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
+    case 3: MOE_LAUNCH(route_topk_kernel<3>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
+    default: MOE_LAUNCH(route_topk_kernel<4>, grid, block, 0, stream, T, E, k, logits, idx, w); break;
   }
   return hipGetLastError();
 }

@@ -421,19 +421,19 @@ hipError_t gemm(int M, int N, int K, const void* a, int lda, const void* b, int 
   if constexpr (!std::is_same<TA, float>::value || !std::is_same<TB, float>::value) {
     // bf16 layer: the matrix core, 64 x 64 tiles
     const dim3 mgrid((M + kMT - 1) / kMT, (N + kMT - 1) / kMT, grid.z);
-    hipLaunchKernelGGL((router_mfma_kernel<TA, TB, TC, A_KC, B_KC, ACC>), mgrid, dim3(256), 0, stream, M, N, K,
+    MOE_LAUNCH((router_mfma_kernel<TA, TB, TC, A_KC, B_KC, ACC>), mgrid, dim3(256), 0, stream, M, N, K,
                        (const TA*)a, lda, (const TB*)b, ldb, (TC*)c, kslice, part);
   } else if (tile == 128)
-    hipLaunchKernelGGL((router_gemm_kernel<128, TA, TB, TC, A_KC, B_KC, ACC>), grid, dim3(256), 0, stream, M, N, K,
+    MOE_LAUNCH((router_gemm_kernel<128, TA, TB, TC, A_KC, B_KC, ACC>), grid, dim3(256), 0, stream, M, N, K,
                        (const TA*)a, lda, (const TB*)b, ldb, (TC*)c, kslice, part);
   else
-    hipLaunchKernelGGL((router_gemm_kernel<64, TA, TB, TC, A_KC, B_KC, ACC>), grid, dim3(256), 0, stream, M, N, K,
+    MOE_LAUNCH((router_gemm_kernel<64, TA, TB, TC, A_KC, B_KC, ACC>), grid, dim3(256), 0, stream, M, N, K,
                        (const TA*)a, lda, (const TB*)b, ldb, (TC*)c, kslice, part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || slices == 1) return err;
   const int64_t MN = (int64_t)M * N;
   const int64_t blocks = std::min<int64_t>((MN + 255) / 256, 4096);
-  hipLaunchKernelGGL((router_sum_slices_kernel<TC>), dim3((unsigned)blocks), dim3(256), 0, stream, MN, (int)used,
+  MOE_LAUNCH((router_sum_slices_kernel<TC>), dim3((unsigned)blocks), dim3(256), 0, stream, MN, (int)used,
                      (const float*)ws, (TC*)c);
   return hipGetLastError();
 }
@@ -442,7 +442,7 @@ template <typename T>
 hipError_t router_bwd_typed(int T_, int H, int E, int k, const void* x, const void* w_r, const int32_t* idx,
                             const float* w, const float* dg, float* dl, void* dw_r, void* dx, bool dx_acc,
                             float* ws, hipStream_t stream) {
-  hipLaunchKernelGGL(router_dlogits_kernel, dim3((T_ + 3) / 4), dim3(256), 0, stream, T_, E, k, idx, w, dg, dl);
+  MOE_LAUNCH(router_dlogits_kernel, dim3((T_ + 3) / 4), dim3(256), 0, stream, T_, E, k, idx, w, dg, dl);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // dW_r [H,E] = x^T dl: A(h,t) = x[t*H + h], B(t,e) = dl[t*E + e]; reduction over T

@@ -29,6 +29,7 @@ _SIGS = {
     "moe_status_string": ([_i], ctypes.c_char_p),
     "moe_last_error": ([], ctypes.c_char_p),
     "moe_abi_version": ([], _i),
+    "moe_launch_count": ([], _i64),
     "moe_signal_dh_ready": ([_vp], _i),
     "moe_router_workspace_bytes": ([_i, _i, _i], _sz),
     "moe_router_fwd": ([_i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp], _i),
@@ -115,6 +116,11 @@ I32, F32 = torch.int32, torch.float32
 
 def moe_abi_version() -> int:
     return lib().moe_abi_version()
+
+
+def moe_launch_count() -> int:
+    """Kernel launches made so far by library calls from this thread."""
+    return int(lib().moe_launch_count())
 
 
 def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:

@@ -73,8 +73,32 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 const char* moe_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);
-/* ABI version, currently 6. */
+/* ABI version, currently 7. */
 int moe_abi_version(void);
+
+/* Kernel launches made so far by library calls from the calling thread (a
+ * debug counter; it never resets).  Every call launches a fixed number of
+ * kernels given by its arguments alone (a call rejected by validation
+ * launches none); with Nk = T*k pairs, R = max_rows and B(c) = 1 when experts
+ * of 256 rows and more get the 256-row kernel for a product with c output
+ * columns (bf16, c a multiple of 256, the expert-row bound of the call and R
+ * both >= 256), else 0:
+ *   moe_route_topk                          1
+ *   moe_dispatch, moe_dispatch_noalloc      (Nk <= 1024 ? 1 : 3) + (x_sorted ? 1 : 0)
+ *   moe_grouped_swiglu_fwd[_gather]         R = 0: 0; bf16: 2 + B(2F) + B(H) with the
+ *                                           bound max_expert_rows; fp32: 2
+ *   moe_grouped_swiglu_fwd_fp8w             R = 0: 0; else 2
+ *   moe_grouped_swiglu_recompute            R = 0: 0; bf16: 1 + B(2F); fp32: 1
+ *   moe_combine                             1
+ *   moe_grouped_bwd_dx                      2 + (R > 0 ? 2 + B(H) : 0), bound min(R, T)
+ *                                           (fp32 and fp8 weights: B = 0)
+ *   moe_grouped_bwd_dw                      bf16: 2; fp32: 1
+ *   moe_compact_pairs[_cap]                 2 + (any row source given ? 1 : 0)
+ *   moe_pair_scores, moe_quantize_weights_fp8   1
+ *   moe_router_fwd                          1, plus 1 when its workspace is used
+ *   moe_router_bwd                          3, plus 1 when its dW_r reduction is split
+ * These counts are what a HIP graph of a layer step captures. */
+int64_t moe_launch_count(void);
 
 /* Kernels that moe_profile_kernel can bracket with events. */
 typedef enum moe_kernel {

@@ -1,0 +1,137 @@
+"""Fixed, documented kernel-launch count per call (the device-call count the
+hot-expert test of npu-train pull request #44, Changes, checks per layer):
+every library call of a layer step launches the number of kernels that
+include/moe.h documents for its arguments, read from the library's own launch
+counter (moe_launch_count)."""
+import numpy as np
+import pytest
+import torch
+
+from expert_grouped_gemm_top_amd import moe
+from expert_grouped_gemm_top_amd import workloads as W
+from expert_grouped_gemm_top_amd.layer import MoeLayerBuffers
+
+pytestmark = pytest.mark.gpu
+
+
+class Recorder:
+    """Wraps the binding's entry points; records (name, launches) per call."""
+
+    def __init__(self, monkeypatch):
+        self.calls = []
+        for name in dir(moe):
+            f = getattr(moe, name)
+            if name.startswith("moe_") and callable(f) and name not in ("moe_launch_count", "moe_abi_version") \
+                    and not name.endswith(("_bytes", "_cap", "_workspace", "_budget")):
+                monkeypatch.setattr(moe, name, self._wrap(name, f))
+
+    def _wrap(self, name, f):
+        def g(*a, **kw):
+            before = moe.moe_launch_count()
+            r = f(*a, **kw)
+            self.calls.append((name, moe.moe_launch_count() - before))
+            return r
+        return g
+
+
+def big(c, bound, R, bf16):
+    """B(c) of include/moe.h: the 256-row kernel serves a product with c output columns."""
+    return int(bf16 and c % 256 == 0 and bound >= 256 and R >= 256)
+
+
+def expected(name, L, bf16, gather, x_rows_given=True, any_rows=False):
+    T, H, F, k, N, R = L.T, L.H, L.F, L.k, L.N, L.R
+    if name == "moe_route_topk":
+        return 1
+    if name in ("moe_dispatch", "moe_dispatch_noalloc"):
+        return (1 if N <= 1024 else 3) + (0 if gather else 1)
+    if name in ("moe_grouped_swiglu_fwd", "moe_grouped_swiglu_fwd_gather"):
+        return 2 + big(2 * F, T, N, bf16) + big(H, T, N, bf16) if bf16 else 2
+    if name == "moe_grouped_swiglu_fwd_fp8w":
+        return 2
+    if name == "moe_grouped_swiglu_recompute":
+        return 1 + big(2 * F, T, R, bf16)
+    if name in ("moe_combine", "moe_pair_scores"):
+        return 1
+    if name == "moe_grouped_bwd_dx":
+        return 2 + (2 + big(H, min(R, T), R, bf16) if R > 0 else 0)
+    if name == "moe_grouped_bwd_dx_fp8w":
+        return 4
+    if name == "moe_grouped_bwd_dw":
+        return 2 if bf16 else 1
+    if name in ("moe_compact_pairs", "moe_compact_pairs_cap"):
+        return 2 + (1 if any_rows else 0)
+    raise AssertionError(name)
+
+
+CASES = [
+    # name, T, H, F, E, k, dtype, rho, keep_graph, gather_rows, fp8
+    ("bf16_big", 512, 512, 256, 8, 2, "bf16", None, True, None, False),
+    ("bf16_gathered", 700, 512, 256, 8, 4, "bf16", None, True, True, False),
+    ("bf16_compact_recompute", 600, 256, 128, 8, 2, "bf16", 0.5, False, False, False),
+    ("bf16_compact_gathered", 600, 512, 384, 16, 4, "bf16", 0.5, True, None, False),
+    ("bf16_decode", 4, 256, 128, 8, 2, "bf16", None, True, None, False),
+    ("fp32_tiny", 64, 128, 64, 8, 2, "f32", None, True, None, False),
+    ("fp8_lora", 96, 256, 128, 8, 2, "bf16", None, True, True, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_launches_per_call_match_the_documented_counts(case, monkeypatch):
+    name, T, H, F, E, k, dt, rho, keep_graph, gather, fp8 = case
+    print(f"launch count: {name}", flush=True)
+    wl = W.custom(name, T=T, H=H, F=F, E=E, k=k, dtype=dt, skew=True, dw=not fp8, rho=rho)
+    d = W.generate(wl, seed=1)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    t = {n: torch.from_numpy(d[n]).cuda().to(tdt) for n in ("x", "W_gate", "W_up", "W_down", "dy")}
+    logits = torch.from_numpy(d["logits"]).cuda()
+    L = MoeLayerBuffers(T, H, F, E, k, tdt, "cuda", rho=rho, dw=not fp8, dg=True, keep_graph=keep_graph,
+                        gather_rows=gather)
+    wq = moe.Fp8Weights(t["W_gate"], t["W_up"], t["W_down"]) if fp8 else None
+    rec = Recorder(monkeypatch)
+    L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], wq=wq)
+    L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], wq=wq)
+    torch.cuda.synchronize()
+    assert rec.calls, "no library call was recorded"
+    any_rows = not L.gather_rows
+    for call, n in rec.calls:
+        assert n == expected(call, L, dt == "bf16", L.gather_rows, any_rows=any_rows), (call, n)
+    # the whole step: a fixed number of launches for the shape
+    total = sum(n for _, n in rec.calls)
+    print(f"  {len(rec.calls)} calls, {total} launches: {rec.calls}", flush=True)
+
+
+def test_router_launches_within_documented_bounds():
+    T, H, E, k = 512, 1024, 64, 4
+    wl = W.custom("router_count", T=T, H=H, F=64, E=E, k=k, dtype="bf16")
+    d = W.generate(wl, seed=2, weights=False)
+    x = torch.from_numpy(d["x"]).cuda().to(torch.bfloat16)
+    w_r = torch.from_numpy(W.router_weights(wl, seed=2)).cuda().to(torch.bfloat16)
+    ws_bytes = moe.moe_router_workspace_bytes(T, H, E)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    logits = torch.empty(T, E, device="cuda")
+    before = moe.moe_launch_count()
+    moe.moe_router_fwd(x, w_r, logits, ws)
+    n_fwd = moe.moe_launch_count() - before
+    assert n_fwd in ((1, 2) if ws_bytes > 0 else (1,))
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, device="cuda")
+    moe.moe_route_topk(logits, idx, w, k)
+    dg = torch.randn(T, k, device="cuda")
+    dl = torch.empty(T, E, device="cuda")
+    dw_r = torch.empty(H, E, dtype=torch.bfloat16, device="cuda")
+    dx = torch.zeros(T, H, dtype=torch.bfloat16, device="cuda")
+    before = moe.moe_launch_count()
+    moe.moe_router_bwd(x, w_r, idx, w, dg, dl, dw_r, dx, True, ws)
+    assert moe.moe_launch_count() - before in (3, 4)
+    torch.cuda.synchronize()
+
+
+def test_a_rejected_call_launches_nothing():
+    idx = torch.zeros(4, 2, dtype=torch.int32, device="cuda")
+    w = torch.zeros(4, 2, device="cuda")
+    bad_logits = torch.zeros(4, 300, device="cuda")  # E above 256
+    before = moe.moe_launch_count()
+    with pytest.raises(moe.MoeError):
+        moe.moe_route_topk(bad_logits, idx, w, 2)
+    assert moe.moe_launch_count() == before
