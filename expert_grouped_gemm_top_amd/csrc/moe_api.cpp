@@ -107,9 +107,6 @@ int check_expert_dims(const char* fn, int H, int F, int E, int dtype) {
   if ((rc = check_row_width(fn, "H", H)) || (rc = check_row_width(fn, "F", F))) return rc;
   REQUIRE(E >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: E=%d must be >= 1", fn, E);
   REQUIRE(E <= moe::kMaxExpertsHost, MOE_ERR_UNSUPPORTED, "%s: E=%d exceeds 256", fn, E);
-  if (dtype == MOE_BF16)
-    REQUIRE(H % 128 == 0 && F % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: bf16 needs H=%d and F=%d to be multiples of 128", fn,
-            H, F);
   REQUIRE((int64_t)E * H * F < ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "%s: weights too large", fn);
   return MOE_OK;
 }

@@ -34,6 +34,13 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(l
 
 __device__ __forceinline__ float sigmoidf_fast(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// 64 bytes of zeros in device memory, never written: the load source of every
+// 16-byte operand chunk that lies past the end of a reduction (K not a multiple
+// of the stage depth), so that such chunks contribute nothing and the loads
+// stay unpredicated (direct global->LDS loads cannot be zeroed in flight).
+static __device__ __attribute__((aligned(64))) uint32_t kZeroChunk[16];
+__device__ __forceinline__ const uint16_t* zero_chunk() { return reinterpret_cast<const uint16_t*>(kZeroChunk); }
+
 // ---- wave-level primitives -------------------------------------------------
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

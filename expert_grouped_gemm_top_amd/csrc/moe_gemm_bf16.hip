@@ -132,10 +132,18 @@ struct RowGemmShape<kGemmDX> { static constexpr bool kNN = false; };
 template <int MODE>
 __host__ __device__ constexpr int row_gemm_cols() { return RowGemmShape<MODE>::kNN ? 128 : 64; }
 
-// column blocks of one expert tile
+// column blocks of one expert tile (the last one partial when the output width
+// is not a multiple of the block; its columns past the edge are never stored)
 template <int MODE>
 __host__ __device__ inline int row_gemm_blocks(int H, int F) {
-  return MODE == kGemmGateUp ? (2 * F) / 128 : (MODE == kGemmDown ? H / 128 : (MODE == kGemmDA ? F / 64 : H / 64));
+  return MODE == kGemmGateUp ? (F + 63) / 64
+                             : (MODE == kGemmDown ? (H + 127) / 128 : (MODE == kGemmDA ? (F + 63) / 64 : (H + 63) / 64));
+}
+
+// Output columns of a row GEMM (gate/up: features, each a gate and an up column).
+template <int MODE>
+__host__ __device__ inline int row_gemm_cols(int H, int F) {
+  return (MODE == kGemmGateUp || MODE == kGemmDA) ? F : H;
 }
 
 //
@@ -191,25 +199,33 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
 
   if constexpr (NN) {
     // B operand: lane c reads columns [col, col+8) of rows k0 + 8gq + (0..7)
+    // (columns past the output edge read column 0: never stored)
     const WE* b_ptr;
     size_t ldb;
     if (MODE == kGemmGateUp) {
       // even lanes read W_gate, odd lanes W_up, at the same 8 features f
       const WE* W = (const WE*)((c & 1) ? g.w1 : g.w0);
-      b_ptr = W + (size_t)e * H * F + nb * 64 + 8 * (c >> 1);
+      const int f = nb * 64 + 8 * (c >> 1);
+      b_ptr = W + (size_t)e * H * F + (f < F ? f : 0);
       ldb = F;
     } else {
-      b_ptr = (const WE*)g.w0 + (size_t)e * F * H + nb * 128 + 8 * c;
+      const int col = nb * 128 + 8 * c;
+      b_ptr = (const WE*)g.w0 + (size_t)e * F * H + (col < H ? col : 0);
       ldb = H;
     }
-    b_ptr += (size_t)(k_begin + 8 * gq) * ldb;
+    const WE* b_first = b_ptr + (size_t)k_begin * ldb;  // rows k_begin .. k_begin + 7 (Kp >= 8)
+    b_ptr = b_first + (size_t)(8 * gq) * ldb;
     const uint16_t* a_ptr = a_row + 8 * gq;
-    const int steps = Kp / 32, last = steps - 1;
+    // the last step may run past Kp (Kp a multiple of 8, not of 32): a lane
+    // whose 8 k of that step lie past it reads the first 8 weight rows and a
+    // zero activation chunk, so they add nothing
+    const int steps = (Kp + 31) / 32, last = steps - 1;
     auto load = [&](int s, WV* bq, u32x4& aq) {
-      const WE* bp = b_ptr + (size_t)s * 32 * ldb;
+      const bool kin = s * 32 + 8 * gq < Kp;
+      const WE* bp = kin ? b_ptr + (size_t)s * 32 * ldb : b_first;
 #pragma unroll
       for (int r = 0; r < 8; ++r) bq[r] = *(const WV*)(bp + (size_t)r * ldb);
-      aq = *(const u32x4*)(a_ptr + (size_t)s * 32);
+      aq = *(const u32x4*)(kin ? a_ptr + (size_t)s * 32 : zero_chunk());
     };
     auto compute = [&](const WV* bq, const u32x4& aq) {
       const u32x4 av = a_ok ? aq : zero4;
@@ -253,27 +269,39 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
     const WE* w_hi;  // DX only: rows for k in [F, 2F)
     size_t ldw;
     int Kw;
+    const int Nw = MODE == kGemmDA ? F : H;  // weight rows (output columns)
     if (MODE == kGemmDA) {
-      w_lo = (const WE*)g.w0 + (size_t)e * F * H + (size_t)(nb * 64 + lrow) * H + 8 * lchunk;
+      w_lo = (const WE*)g.w0 + (size_t)e * F * H;
       w_hi = w_lo;
       ldw = H;
       Kw = K;
     } else {
-      w_lo = (const WE*)g.w0 + (size_t)e * H * F + (size_t)(nb * 64 + lrow) * F + 8 * lchunk;
-      w_hi = (const WE*)g.w1 + (size_t)e * H * F + (size_t)(nb * 64 + lrow) * F + 8 * lchunk;
+      w_lo = (const WE*)g.w0 + (size_t)e * H * F;
+      w_hi = (const WE*)g.w1 + (size_t)e * H * F;
       ldw = F;
       Kw = F;
     }
     unsigned char* xs = lds + w * 16384;
     const uint16_t* a_ptr = a_row + 32 * gq;
-    const int stages = Kp / 128, last = stages - 1;
+    // The last stage may run past Kp (a multiple of 8, not of 128): this lane's
+    // chunk (8 k) past the end reads columns 0..7 of the weights and the
+    // activation chunks past it read zeros.  Weight rows past the output edge read row 0
+    // (never stored).  A chunk never straddles Kw (F is a multiple of 8).
+    const int stages = (Kp + 127) / 128, last = stages - 1;
+    const int row0 = nb * 64 + lrow;
     auto load = [&](int s, WV* bq, u32x4* aq) {
-      const int k0 = k_begin + s * 128;  // stages never straddle Kw (Kw % 128 == 0)
-      const WE* wp = (k0 < Kw) ? w_lo + k0 : w_hi + (k0 - Kw);
+      const int k = k_begin + s * 128 + 8 * lchunk;  // this lane's weight chunk
+      const WE* wp = (k < Kw) ? w_lo + k : (k < K ? w_hi + (k - Kw) : w_lo);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) bq[i] = *(const WV*)(wp + (size_t)(4 * i) * ldw);
+      for (int i = 0; i < 16; ++i) {
+        const int n = row0 + 4 * i;
+        bq[i] = *(const WV*)(wp + (size_t)(n < Nw ? n : 0) * ldw);
+      }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) aq[q] = *(const u32x4*)(a_ptr + (size_t)s * 128 + 8 * q);
+      for (int q = 0; q < 4; ++q) {
+        const int ka = s * 128 + 32 * gq + 8 * q;
+        aq[q] = *(const u32x4*)(ka < Kp ? a_ptr + (size_t)s * 128 + 8 * q : zero_chunk());
+      }
     };
     auto wave_sync = [] {
       __builtin_amdgcn_wave_barrier();
@@ -361,6 +389,7 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
     uint16_t* arow = g.out1 + grow * F;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      if (f + 8 * h >= F) break;  // features past the edge
       const float* G = hg + 8 * h;
       const float* U = hu + 8 * h;
       const float* V = av + 8 * h;
@@ -376,16 +405,19 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
     }
   } else if (MODE == kGemmDown) {
     // MFMA jj, register r: column 128 nb + 32 gq + 8 r + jj
-    uint16_t* orow = g.out0 + grow * H + nb * 128 + 32 * gq;
+    const int col0 = nb * 128 + 32 * gq;
+    uint16_t* orow = g.out0 + grow * H + col0;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      *(u32x4*)(orow + 8 * r) = u32x4{pack_bf2(acc[0][r], acc[1][r]), pack_bf2(acc[2][r], acc[3][r]),
-                                      pack_bf2(acc[4][r], acc[5][r]), pack_bf2(acc[6][r], acc[7][r])};
+      if (col0 + 8 * r < H)
+        *(u32x4*)(orow + 8 * r) = u32x4{pack_bf2(acc[0][r], acc[1][r]), pack_bf2(acc[2][r], acc[3][r]),
+                                        pack_bf2(acc[4][r], acc[5][r]), pack_bf2(acc[6][r], acc[7][r])};
   } else {
     // MFMA jj, register r: column 64 nb + 16 jj + 4 gq + r
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int col = nb * 64 + 16 * jj + 4 * gq;
+      if (col >= row_gemm_cols<MODE>(H, F)) continue;  // past the edge (4 columns, all or none)
       if (MODE == kGemmDA) {
         // SwiGLU backward with the saved pre-activations hg, hu
         const uint16_t* hrow = g.h + h_row_of(g, grow) * 2 * F;
@@ -423,7 +455,7 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
 // W_gate / W_up features so each lane owns hg and hu of the same 8 features.
 template <int MODE>
 __host__ __device__ inline int tile_gemm_blocks(int H, int F) {
-  return MODE == kGemmGateUp ? (2 * F) / kTBN : (MODE == kGemmDA ? F / kTBN : H / kTBN);
+  return MODE == kGemmGateUp ? (2 * F + kTBN - 1) / kTBN : (MODE == kGemmDA ? (F + kTBN - 1) / kTBN : (H + kTBN - 1) / kTBN);
 }
 
 template <int MODE>
@@ -471,46 +503,58 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
   }
   // B, N-contiguous: thread -> 8 k-rows (8 kb .. 8 kb + 7) x 4 columns of one matrix
   // B, K-contiguous: thread -> 4 chunks (16 B) of weight rows
+  // Columns (weight rows) past the output edge read column (row) 0 and are
+  // never stored; k chunks past K read the first 8 k (N-contiguous) or column
+  // 0 (K-contiguous) of the weights against zero activation chunks.
   const uint16_t* b_src[4];
   int b_dst[4];
   size_t ldb = 0;
-  const uint16_t* b_hi = nullptr;  // DX: same rows in W_up for k >= F
+  const uint16_t* b_lo = nullptr;  // K-contiguous: expert base for k < Kw (W_down for DA, W_gate for DX)
+  const uint16_t* b_hi = nullptr;  // DX: W_up for F <= k < 2F
+  int kb = 0;
   if (NN) {
-    const int kb = tid >> 5, cb = tid & 31;
+    kb = tid >> 5;
+    const int cb = tid & 31;
     const int bw = cb >> 4, cq = cb & 15;  // wave column block, quad within it
     const uint16_t* W;
     int gcol;
     if (MODE == kGemmGateUp) {
       W = (cq & 1) ? g.w1 : g.w0;
       gcol = nb * 64 + 32 * bw + 4 * (cq >> 1);
+      if (gcol >= F) gcol = 0;
       ldb = F;
       W += (size_t)e * H * F;
     } else {
       W = g.w0 + (size_t)e * F * H;
       gcol = nb * 128 + 64 * bw + 4 * cq;
+      if (gcol >= H) gcol = 0;
       ldb = H;
     }
-    b_src[0] = W + (size_t)(8 * kb) * ldb + gcol;
+    b_src[0] = W + gcol;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 64 * bw + 16 * i + cq;
       b_dst[i] = row * kTPitch + 8 * (kb ^ (row & 7));
     }
   } else {
+    const int Nw = MODE == kGemmDA ? F : H;
+    if (MODE == kGemmDA) {
+      b_lo = g.w0 + (size_t)e * F * H;
+      ldb = H;
+    } else {
+      b_lo = g.w0 + (size_t)e * H * F;
+      b_hi = g.w1 + (size_t)e * H * F;
+      ldb = F;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i, nl = ch >> 3, kc = ch & 7;
+      const int ch = tid + 256 * i, nl = ch >> 3;
       const int n = nb * kTBN + nl;
       const int bw = nl >> 6, nw = nl & 63;
       const int brow = 64 * bw + 16 * (nw & 3) + (nw >> 2);
-      b_dst[i] = brow * kTPitch + 8 * (kc ^ (brow & 7));
-      if (MODE == kGemmDA) {
-        b_src[i] = g.w0 + (size_t)e * F * H + (size_t)n * H + 8 * kc;
-      } else {
-        b_src[i] = g.w0 + (size_t)e * H * F + (size_t)n * F + 8 * kc;
-      }
+      b_dst[i] = brow * kTPitch + 8 * ((ch & 7) ^ (brow & 7));
+      b_src[i] = b_lo + (size_t)(n < Nw ? n : 0) * ldb;  // row start; the k offset is added per step
     }
-    if (MODE == kGemmDX) b_hi = g.w1 + (size_t)e * H * F;
   }
 
   // global -> register staging of one K-step
@@ -520,19 +564,27 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
     u32x4 bt[4];
   };
   const u32x4 z4 = {0u, 0u, 0u, 0u};
-  const int steps = K / kTBK;
+  const int steps = (K + kTBK - 1) / kTBK;
   auto gload = [&](int s, Stage& st) {
     const int k0 = s * kTBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.a[i] = *(const u32x4*)(a_src[i] + k0);
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + 8 * ((tid + 256 * i) & 7);
+      st.a[i] = *(const u32x4*)(k < K ? a_src[i] + k0 : zero_chunk());
+    }
     if (NN) {
+      const int kr = k0 + 8 * kb < K ? k0 + 8 * kb : 0;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) st.bn[r] = *(const u32x2*)(b_src[0] + (size_t)(k0 + r) * ldb);
+      for (int r = 0; r < 8; ++r) st.bn[r] = *(const u32x2*)(b_src[0] + (size_t)(kr + r) * ldb);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint16_t* src = b_src[i] + k0;
-        if (MODE == kGemmDX && k0 >= F) src = b_src[i] - (g.w0 + (size_t)e * H * F) + b_hi + (k0 - F);
+        const int k = k0 + 8 * ((tid + 256 * i) & 7);
+        const uint16_t* src;
+        if (MODE == kGemmDX)
+          src = k < F ? b_src[i] + k : (k < K ? b_src[i] - b_lo + b_hi + (k - F) : b_src[i]);
+        else
+          src = k < K ? b_src[i] + k : b_src[i];
         st.bt[i] = *(const u32x4*)src;
       }
     }
@@ -609,6 +661,7 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
 #pragma unroll
       for (int i = 0; i < 8; ++i) av[i] = hg[i] * sigmoidf_fast(hg[i]) * hu[i];
       const int f = nb * 64 + 32 * wn + 8 * gq;
+      if (f >= F) continue;  // features past the edge (8 of them, all or none)
       if (g.out0 != nullptr) {
         uint16_t* hrow = g.out0 + grow * 2 * F;
         *(u32x4*)(hrow + f) =
@@ -627,10 +680,14 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) v[4 * r + jb] = acc[ia][jb][r];
       const int col = nb * kTBN + 64 * wn + 16 * gq;
+      const int ncols = row_gemm_cols<MODE>(H, F);
+      if (col >= ncols) continue;  // past the edge; col + 8 .. + 15 are checked below
+      const bool hi_ok = col + 8 < ncols;
       if (MODE == kGemmDA) {
         const uint16_t* hrow = g.h + h_row_of(g, grow) * 2 * F;
-        const u32x4 g0 = *(const u32x4*)(hrow + col), g1 = *(const u32x4*)(hrow + col + 8);
-        const u32x4 u0 = *(const u32x4*)(hrow + F + col), u1 = *(const u32x4*)(hrow + F + col + 8);
+        const int col1 = hi_ok ? col + 8 : col;  // the second 8 columns, when inside
+        const u32x4 g0 = *(const u32x4*)(hrow + col), g1 = *(const u32x4*)(hrow + col1);
+        const u32x4 u0 = *(const u32x4*)(hrow + F + col), u1 = *(const u32x4*)(hrow + F + col1);
         float dgv[16], duv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -645,6 +702,7 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
         uint16_t* drow = g.out0 + grow * 2 * F;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+          if (h == 1 && !hi_ok) break;
           const float* G = dgv + 8 * h;
           const float* U = duv + 8 * h;
           *(u32x4*)(drow + col + 8 * h) =
@@ -656,6 +714,7 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
         uint16_t* orow = g.out0 + grow * H + col;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+          if (h == 1 && !hi_ok) break;
           const float* V = v + 8 * h;
           *(u32x4*)(orow + 8 * h) =
               u32x4{pack_bf2(V[0], V[1]), pack_bf2(V[2], V[3]), pack_bf2(V[4], V[5]), pack_bf2(V[6], V[7])};

@@ -52,7 +52,11 @@ __device__ __forceinline__ int kc_swz(int row, int chunk) {
 
 // Tile of BM rows x BN columns, reduction depth BK per stage, NW waves laid out
 // WM x (NW / WM); STAGES stages resident in LDS; WPC workgroups per CU.
-template <int MODE, int BM, int BN, int BK, int NW, int WM, int STAGES, int WPC>
+// TAIL: the reduction length is not a multiple of BK, or the output width not
+// one of BN (or, for dX, F not one of BK): every direct load then picks its
+// source per stage, and 16-byte chunks past the reduction or the output edge
+// come from a chunk of zeros; output columns past the edge are not stored.
+template <int MODE, int BM, int BN, int BK, int NW, int WM, int STAGES, int WPC, bool TAIL>
 __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs g) {
   constexpr bool NN = BigShape<MODE>::kNN;
   const int kMinRows = g.big_min_rows;  // experts with at least this many rows use this kernel
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
     __syncthreads();
   }
   const int H = g.H, F = g.F;
-  const int nblk = big_out_cols<MODE>(H, F) / BN;
+  const int nblk = (big_out_cols<MODE>(H, F) + BN - 1) / BN;
   const int item = xcd_item(blockIdx.x, s_start[g.E] * nblk);
   if (item >= s_start[g.E] * nblk) return;
   int lo = 0, hi = g.E;  // expert of this item
@@ -123,15 +127,19 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
   // ---- loader: 1 KiB per direct-load instruction
   // A (K-contiguous rows of 2 BK bytes): instruction covers 64 / CPR rows
   const uint16_t* a_src[A_INS];
+  int a_k[A_INS];  // k offset of this lane's chunk within a stage
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
     const int row = (64 / CPR) * (A_INS * w + i) + l / CPR;
     const int chunk = kc_swz<CPR>(row, l % CPR);  // LDS position l % CPR holds this chunk
     const int r = row < ts.rows ? row : ts.rows - 1;
+    a_k[i] = 8 * chunk;
     a_src[i] = g.a + a_row_of(g, ts.row_begin + r) * K + 8 * chunk;
   }
   const uint16_t* b_src[B_INS];
   const uint16_t* b_hi[B_INS];  // DX: the same rows in W_up for k >= F
+  int b_k[B_INS];               // NN: k row of this lane within a stage; NT: k offset of its chunk
+  bool b_ok[B_INS];             // the chunk's columns (NN) or weight row (NT) lie inside the output
   size_t b_kstride;             // elements per k for NN (row stride), 1 for NT
   if (NN) {
     // [BK k][BN]: a k row is BN/8 chunks; instruction covers 512 / BN k rows
@@ -148,11 +156,14 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
         // virtual chunks alternate W_gate / W_up over the same 8 features
         W = ((vchunk & 1) ? g.w1 : g.w0) + (size_t)e * H * F;
         col = nb * (BN / 2) + 8 * (vchunk >> 1);
+        b_ok[i] = col < F;
       } else {
         W = g.w0 + (size_t)e * F * H;
         col = nb * BN + 8 * vchunk;
+        b_ok[i] = col < H;
       }
-      b_src[i] = W + (size_t)k * b_kstride + col;
+      b_k[i] = k;
+      b_src[i] = W + (size_t)k * b_kstride + (b_ok[i] ? col : 0);
       b_hi[i] = b_src[i];
     }
   } else {
@@ -162,9 +173,12 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
       const int row = (64 / CPR) * (B_INS * w + i) + l / CPR;  // output column within the tile
       const int chunk = kc_swz<CPR>(row, l % CPR);
       const int n = nb * BN + row;
+      b_ok[i] = n < H;
+      const size_t nrow = (size_t)(b_ok[i] ? n : 0) * F;
+      b_k[i] = 8 * chunk;
       // DX: k < F from W_gate, k >= F from W_up
-      b_src[i] = g.w0 + (size_t)e * H * F + (size_t)n * F + 8 * chunk;
-      b_hi[i] = g.w1 + (size_t)e * H * F + (size_t)n * F + 8 * chunk;
+      b_src[i] = g.w0 + (size_t)e * H * F + nrow + 8 * chunk;
+      b_hi[i] = g.w1 + (size_t)e * H * F + nrow + 8 * chunk;
     }
   }
 
@@ -172,12 +186,24 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
     unsigned char* st = s_dyn + (s % STAGES) * STAGE_BYTES;
     const int k0 = s * BK;
 #pragma unroll
-    for (int i = 0; i < A_INS; ++i) g2lds(a_src[i] + k0, st + 1024 * (A_INS * w + i));
+    for (int i = 0; i < A_INS; ++i) {
+      const uint16_t* src = a_src[i] + k0;
+      if (TAIL && k0 + a_k[i] >= K) src = zero_chunk();
+      g2lds(src, st + 1024 * (A_INS * w + i));
+    }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
       const uint16_t* src;
-      if (NN) src = b_src[i] + (size_t)k0 * b_kstride;
-      else src = (MODE == kGemmDX && k0 >= F) ? b_hi[i] + (k0 - F) : b_src[i] + k0;
+      if (NN) {
+        src = b_src[i] + (size_t)k0 * b_kstride;
+        if (TAIL && (!b_ok[i] || k0 + b_k[i] >= K)) src = zero_chunk();
+      } else if (!TAIL) {
+        src = (MODE == kGemmDX && k0 >= F) ? b_hi[i] + (k0 - F) : b_src[i] + k0;
+      } else {
+        const int k = k0 + b_k[i];  // chunks never straddle F (a multiple of 8)
+        src = (MODE == kGemmDX && k >= F) ? b_hi[i] + (k0 - F) : b_src[i] + k0;
+        if (!b_ok[i] || k >= K) src = zero_chunk();
+      }
       g2lds(src, st + A_BYTES + 1024 * (B_INS * w + i));
     }
   };
@@ -265,7 +291,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
     }
   };
 
-  const int steps = K / BK;
+  const int steps = (K + BK - 1) / BK;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < steps) issue(s);
@@ -305,6 +331,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
             hu[e2] = acc[i][j][8 * p + 4 + e2];
             av[e2] = hg[e2] * sigmoidf_fast(hg[e2]) * hu[e2];
           }
+          if (TAIL && f >= F) continue;  // features past the edge (4 of them, all or none)
           if (g.out0 != nullptr) {
             *(u32x2*)(hrow + f) = u32x2{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3])};
             *(u32x2*)(hrow + F + f) = u32x2{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3])};
@@ -316,6 +343,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = nb * BN + TN * wn + 32 * j + 8 * q + 4 * hk;
+          if (TAIL && col >= H) continue;  // columns past the edge (4 of them, all or none)
           *(u32x2*)(orow + col) = u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                                         pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
         }
@@ -327,10 +355,18 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
 
 template <int MODE, int BM, int BN, int BK, int NW, int WM, int STAGES, int WPC>
 struct BigCfg {
-  static int min_rows(int H, int F) {
-    // whole column blocks only
-    if (big_out_cols<MODE>(H, F) % BN != 0) return kNoBigTiles;
-    return kBigTileMinRows;
+  static int min_rows(int, int) { return kBigTileMinRows; }
+
+  template <bool TAIL>
+  static hipError_t launch_as(const RowGemmArgs& g, int64_t wgs, hipStream_t stream) {
+    const size_t lds = (size_t)STAGES * (BM + BN) * BK * 2;
+    auto kern = big_gemm_bf16_kernel<MODE, BM, BN, BK, NW, WM, STAGES, WPC, TAIL>;
+    // dynamic LDS above 64 KiB must be allowed explicitly, once per device
+    static PerDeviceOnce lds_once;
+    hipError_t err = allow_dynamic_lds(lds_once, (const void*)kern, lds);
+    if (err != hipSuccess) return err;
+    MOE_LAUNCH(kern, dim3((unsigned)wgs), dim3(64 * NW), lds, stream, g);
+    return hipGetLastError();
   }
 
   static hipError_t launch(const RowGemmArgs& g, int max_rows, hipStream_t stream) {
@@ -338,15 +374,11 @@ struct BigCfg {
     const int64_t big_experts = std::min<int64_t>(E, N / g.big_min_rows);
     if (big_experts == 0) return hipSuccess;
     const int64_t tiles = (N + big_experts * (BM - 1)) / BM;
-    const int64_t wgs = ((tiles * (big_out_cols<MODE>(g.H, g.F) / BN) + 7) / 8) * 8;
-    const size_t lds = (size_t)STAGES * (BM + BN) * BK * 2;
-    auto kern = big_gemm_bf16_kernel<MODE, BM, BN, BK, NW, WM, STAGES, WPC>;
-    // dynamic LDS above 64 KiB must be allowed explicitly, once per device
-    static PerDeviceOnce lds_once;
-    hipError_t err = allow_dynamic_lds(lds_once, (const void*)kern, lds);
-    if (err != hipSuccess) return err;
-    MOE_LAUNCH(kern, dim3((unsigned)wgs), dim3(64 * NW), lds, stream, g);
-    return hipGetLastError();
+    const int cols = big_out_cols<MODE>(g.H, g.F);
+    const int64_t wgs = ((tiles * ((cols + BN - 1) / BN) + 7) / 8) * 8;
+    const int K = MODE == kGemmGateUp ? g.H : (MODE == kGemmDown ? g.F : 2 * g.F);
+    const bool tail = K % BK != 0 || cols % BN != 0 || (MODE == kGemmDX && g.F % BK != 0);
+    return tail ? launch_as<true>(g, wgs, stream) : launch_as<false>(g, wgs, stream);
   }
 };
 

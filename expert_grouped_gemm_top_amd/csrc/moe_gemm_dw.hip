@@ -349,13 +349,15 @@ struct DwSmallShape {
   int tiles;        // tiles per expert
 };
 
-// bf16 layers have H and F multiples of 128, so the tiles divide exactly.
+// Tiles cover the outputs; the last row or column tile of a product is partial
+// when H or F is not a multiple of 128 (its loads past the edge read column 0,
+// its stores past the edge are skipped).
 __host__ __device__ inline DwSmallShape dw_small_shape(int H, int F) {
   DwSmallShape s;
-  s.nt1 = 2 * F / kSmallBN;
-  s.tiles1 = (H / kSmallBM) * s.nt1;
-  s.nt2 = H / kSmallBN;
-  s.tiles = s.tiles1 + (F / kSmallBM) * s.nt2;
+  s.nt1 = (2 * F + kSmallBN - 1) / kSmallBN;
+  s.tiles1 = ((H + kSmallBM - 1) / kSmallBM) * s.nt1;
+  s.nt2 = (H + kSmallBN - 1) / kSmallBN;
+  s.tiles = s.tiles1 + ((F + kSmallBM - 1) / kSmallBM) * s.nt2;
   return s;
 }
 

@@ -44,8 +44,9 @@
  *    nearest even once, at the store.
  *  - Layouts are row-major.  Pair id p = t*k + j (token t, slot j of its top-k).
  *    Expert weights: W_gate and W_up [E, H, F], W_down [E, F, H].
- *  - Limits: 1 <= k <= E <= 256, k <= 16, T*k < 2^31.  bf16: H and F multiples
- *    of 128.  fp32: H and F multiples of 8.
+ *  - Limits: 1 <= k <= E <= 256, k <= 16, T*k < 2^31, H and F multiples of 8
+ *    (any dtype; widths that are not multiples of the kernels' tiles run on
+ *    the same kernels with the reduction and column tails masked).
  *  - Results are deterministic: the same inputs on the same GPU give bitwise
  *    identical outputs (no order-dependent atomics).
  */

@@ -94,7 +94,8 @@ def test_dispatch_noalloc_validation(lib):
 
 def test_grouped_calls_validation(lib):
     f = lib.moe_grouped_swiglu_fwd
-    assert f(2048, 700, 128, 1024, 128, 1, P, P, P, P, P, P, P, P, NULL) == 2   # F not a multiple of 128 (bf16)
+    assert f(2048, 700, 128, 1024, 128, 1, P, P, P, P, P, P, P, P, NULL) == 2   # F not a multiple of 8 (bf16)
+    assert f(2048, 704, 128, 1024, 128, 1, P, P, P, NULL, P, P, P, P, NULL) == 1  # F = 704 passes the width check (bf16)
     assert f(100, 64, 8, 128, 128, 0, P, P, P, P, P, P, P, P, NULL) == 2       # H not a multiple of 8
     assert f(128, 64, 8, -1, 0, 0, P, P, P, P, P, P, P, P, NULL) == 1
     assert f(128, 64, 8, 128, -1, 0, P, P, P, P, P, P, P, P, NULL) == 1 and "max_expert_rows" in _err(lib)

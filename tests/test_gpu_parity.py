@@ -111,6 +111,41 @@ def test_small_layers(wl):
     _full_compare(wl, d, L)
 
 
+# Widths that are multiples of 8 but not of the kernels' tiles (16-row streaming
+# tiles over 64 / 128 columns and 32 / 128 k, 128 x 128 tiles over 64 k,
+# 256 x 256 tiles over 64 k): reduction tails, column tails and, for dX, the
+# gate / up boundary inside a stage.  T = 700, E = 8, k = 2 with the skewed
+# routing gives experts of 547 and 347 rows (256-row kernel), 190 / 127 / 73 /
+# 50 / 41 (128-row tiles; 50, 41 and 25 on the small-expert dW kernel) and 25
+# (streaming kernel).
+UNALIGNED = [
+    W.custom("bf16_h200_f136", T=700, H=200, F=136, E=8, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_h136_f200", T=700, H=136, F=200, E=8, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_h2880_f360", T=700, H=2880, F=360, E=8, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_h8_f8", T=300, H=8, F=8, E=4, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_decode_h200_f136", T=3, H=200, F=136, E=8, k=2, dtype="bf16", skew=False, dw=True),
+]
+
+
+@pytest.mark.parametrize("wl", UNALIGNED, ids=lambda w: w.name)
+def test_unaligned_widths_full_layer(wl):
+    d = W.generate(wl, seed=3)
+    L = run_gpu(wl, d, logits_of(wl, d))
+    _full_compare(wl, d, L)
+
+
+def test_unaligned_widths_gathered_compacted_recompute():
+    """The same widths through gathered rows, compaction and the recompute path."""
+    wl = W.custom("bf16_h200_f136_c", T=700, H=200, F=136, E=8, k=2, dtype="bf16", skew=True, dw=True, rho=0.6)
+    d = W.generate(wl, seed=4)
+    logits = logits_of(wl, d)
+    _, w = oracle.route_topk(logits, wl.k)
+    score = w.reshape(-1).astype(np.float32)
+    for keep_graph, gather in ((True, True), (False, False)):
+        L = run_gpu(wl, d, logits, rho=0.6, score=score, keep_graph=keep_graph, gather_rows=gather)
+        _full_compare(wl, d, L, rho=0.6, score=score)
+
+
 @pytest.mark.parametrize("rho", [0.5, 0.26, 1.0])
 def test_small_compacted_backward(rho):
     wl = W.custom("bf16_compact", T=256, H=256, F=128, E=8, k=2, dtype="bf16", skew=True, dw=True, rho=rho)
