@@ -623,8 +623,11 @@ int64_t moe_quota_cap_for_budget(int T, int H, int F, int E, int k, int dtype, i
 int moe_pair_scores(int T, int H, int F, int k, int dtype, const int32_t* inv_perm, const float* topk_w,
                     const void* a_save, const void* dy, float* score, void* stream) {
   const char* fn = "moe_pair_scores";
-  int rc = check_routing_dims(fn, T, k, k);
-  if (rc || (rc = check_dtype(fn, dtype)) || (rc = check_row_width(fn, "H", H)) || (rc = check_row_width(fn, "F", F)))
+  REQUIRE(T >= 1 && k >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: T=%d, k=%d must be >= 1", fn, T, k);
+  REQUIRE(k <= 16, MOE_ERR_UNSUPPORTED, "%s: k=%d exceeds 16", fn, k);
+  REQUIRE((int64_t)T * k < (int64_t)1 << 31, MOE_ERR_UNSUPPORTED, "%s: T*k=%lld reaches 2^31", fn, (long long)T * k);
+  int rc;
+  if ((rc = check_dtype(fn, dtype)) || (rc = check_row_width(fn, "H", H)) || (rc = check_row_width(fn, "F", F)))
     return rc;
   NONNULL(inv_perm);
   NONNULL(topk_w);

@@ -385,8 +385,11 @@ int64_t moe_quota_cap(int T, int E, int k, double rho);
  *   x_kept[r] = x_sorted[kept_src[r]], a_kept[r] = a_save[..], h_kept[r] = h_save[..]
  * The row gathers are skipped for NULL sources.  counts [E], offsets [E+1],
  * perm [T*k] int32 and score [T*k] fp32 (device, pair-indexed, finite);
- * kept_* int32 (device, out; kept_perm and kept_src hold T*k entries of which
- * the first R are written). */
+ * kept_counts [E], kept_offsets [E+1], kept_inv [T*k] int32 (device, out);
+ * kept_perm and kept_src int32 (device, out) and x_kept, a_kept, h_kept
+ * (device, out) hold at least min(T*k, E*cap) entries or rows, cap =
+ * moe_quota_cap(T, E, k, rho) (the given cap for moe_compact_pairs_cap), of
+ * which the first R (<= that bound) are written. */
 int moe_compact_pairs(int T, int H, int F, int E, int k, int dtype, double rho,
                       const int32_t* counts, const int32_t* offsets, const int32_t* perm,
                       const float* score, int32_t* kept_counts, int32_t* kept_offsets,

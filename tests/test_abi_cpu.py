@@ -172,6 +172,9 @@ def test_quota_metric_calls(lib):
     s = lib.moe_pair_scores
     assert s(64, 128, 64, 2, 1, P, P, P, P, NULL, NULL) == 1 and "score" in _err(lib)
     assert s(64, 100, 64, 2, 1, P, P, P, P, P, NULL) == 2
+    assert s(64, 128, 64, 17, 1, P, P, P, P, P, NULL) == 2 and "k=17" in _err(lib)
+    assert s(0, 128, 64, 2, 1, P, P, P, P, P, NULL) == 1 and "T=0" in _err(lib)
+    assert s(1 << 28, 128, 64, 16, 1, P, P, P, P, P, NULL) == 2 and "2^31" in _err(lib)
 
 
 def test_fp8_weight_calls_validation(lib):
