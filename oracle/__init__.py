@@ -285,3 +285,41 @@ def dequantize_fp8(q, scale):
     q = np.asarray(q, dtype=np.uint8)
     s = np.asarray(scale, dtype=np.float64).reshape((-1,) + (1,) * (q.ndim - 1))
     return table[q] * s
+
+
+def quantize_rows_fp8(x):
+    """Per-row fp8 storage of activations x [rows, n]: codes [rows, n] and one
+    power-of-two scale per row (the rule of quantize_fp8, rows as experts)."""
+    q, _, scale = quantize_fp8(x)
+    return q, scale
+
+
+def forward_fp8(x, idx, w, Wg, Wu, Wd):
+    """The expert forward on E4M3 operands (oracle_forward_fp8): x quantized
+    per token row, the weights per expert (W_gate and W_up sharing a scale),
+    the SwiGLU output rounded to bf16 and quantized per pair row before the
+    down product.  Returns y [T,H] and a dict of the pair-indexed hg, hu, a
+    (bf16-rounded), aq codes, ascale, o, and the x codes / scales."""
+    x = _f64(x)
+    T, H = x.shape
+    Wg, Wu, Wd = _f64(Wg), _f64(Wu), _f64(Wd)
+    E, _, F = Wg.shape
+    idx = _i32(idx)
+    k = idx.shape[1]
+    N = T * k
+    w = _f64(w)
+    qx, sx = quantize_rows_fp8(x)
+    qg, qu, sgu = quantize_fp8(Wg, Wu)
+    qd, _, sd = quantize_fp8(Wd)
+    xd = np.ascontiguousarray(dequantize_fp8(qx, sx))
+    Wgd = np.ascontiguousarray(dequantize_fp8(qg, sgu))
+    Wud = np.ascontiguousarray(dequantize_fp8(qu, sgu))
+    Wdd = np.ascontiguousarray(dequantize_fp8(qd, sd))
+    y = np.zeros((T, H))
+    hg = np.zeros((N, F)); hu = np.zeros((N, F)); a = np.zeros((N, F)); o = np.zeros((N, H))
+    aq = np.zeros((N, F), np.uint8)
+    ascale = np.zeros(N)
+    _load().oracle_forward_fp8(T, H, F, E, k, _p(xd), _p(idx), _p(w), _p(Wgd), _p(Wud), _p(Wdd), _p(y), _p(hg), _p(hu),
+                               _p(a), _p(aq), _p(ascale), _p(o))
+    return y, dict(hg=hg, hu=hu, a=a, aq=aq, ascale=ascale, o=o, qx=qx, sx=sx)
+

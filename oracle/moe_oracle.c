@@ -596,3 +596,91 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------- */
+/* Round to the nearest bf16 value (8 significant bits, ties to even; bf16 has
+ * fp32's exponent range, so below 2^-126 the quantum is fixed at 2^-133).    */
+static double round_bf16(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  if (fabs(v) < ldexp(1.0, -126)) return ldexp(nearbyint(ldexp(v, 133)), -133);
+  int ex;
+  const double m = frexp(v, &ex); /* v = m 2^ex, 0.5 <= |m| < 1 */
+  return ldexp(nearbyint(ldexp(m, 8)), ex - 8);
+}
+
+/* Expert forward on fp8 (E4M3) operands: the grouped GEMMs run on the fp8
+ * matrix cores (LRMoE abstract: variable-size grouped GEMMs; the pages fix no
+ * precision).  Reading taken: every operand of both products is E4M3 with one
+ * power-of-two scale per row of activations (per token for x, per pair for a)
+ * and per expert for the weights (the rule of oracle_quantize_fp8), products
+ * accumulated exactly; the SwiGLU output is stored in bf16 as in the bf16 path
+ * and that stored value is what gets quantized for the down product.  Per token
+ * t and slot j (e = idx[t,j]), on the decoded inputs xd [T,H] and weights Wgd,
+ * Wud [E,H,F], Wdd [E,F,H]:
+ *     hg[f] = sum_h xd[t,h] Wgd[e,h,f],  hu[f] = sum_h xd[t,h] Wud[e,h,f]
+ *     a16[f] = bf16(silu(hg[f]) hu[f])
+ *     s = 2^oracle_fp8_scale_exp(max_f |a16[f]|),  aq[f] = E4M3(a16[f] / s)
+ *     o[h] = sum_f decode(aq[f]) s Wdd[e,f,h],   y[t,h] += w[t,j] o[h]  (j ascending)
+ * Outputs (pair-indexed p = t k + j, each optional): hg, hu, a16 [N,F]; aq
+ * [N,F] codes and ascale [N]; o [N,H].                                       */
+void oracle_forward_fp8(int T, int H, int F, int E, int k, const double* xd, const int32_t* idx, const double* w,
+                        const double* Wgd, const double* Wud, const double* Wdd, double* y, double* hg_out,
+                        double* hu_out, double* a_out, uint8_t* aq_out, double* ascale_out, double* o_out) {
+  (void)E;
+#pragma omp parallel
+  {
+    double* hg = (double*)malloc(sizeof(double) * (size_t)F);
+    double* hu = (double*)malloc(sizeof(double) * (size_t)F);
+    double* a = (double*)malloc(sizeof(double) * (size_t)F);
+    uint8_t* q = (uint8_t*)malloc((size_t)F);
+    double* o = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(static)
+    for (int t = 0; t < T; ++t) {
+      for (int h = 0; h < H; ++h) y[(size_t)t * H + h] = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const size_t p = (size_t)t * k + j;
+        const int e = idx[p];
+        const double* wg = Wgd + (size_t)e * H * F;
+        const double* wu = Wud + (size_t)e * H * F;
+        const double* wd = Wdd + (size_t)e * F * H;
+        for (int f = 0; f < F; ++f) {
+          double sg = 0.0, su = 0.0;
+          for (int h = 0; h < H; ++h) {
+            sg += xd[(size_t)t * H + h] * wg[(size_t)h * F + f];
+            su += xd[(size_t)t * H + h] * wu[(size_t)h * F + f];
+          }
+          hg[f] = sg;
+          hu[f] = su;
+          a[f] = round_bf16(sg / (1.0 + exp(-sg)) * su);
+        }
+        double amax = 0.0;
+        for (int f = 0; f < F; ++f) amax = fmax(amax, fabs(a[f]));
+        const int ks = oracle_fp8_scale_exp(amax);
+        for (int f = 0; f < F; ++f) q[f] = oracle_e4m3_encode(ldexp(a[f], -ks));
+        for (int h = 0; h < H; ++h) {
+          double sum = 0.0;
+          for (int f = 0; f < F; ++f) sum += ldexp(oracle_e4m3_decode(q[f]), ks) * wd[(size_t)f * H + h];
+          o[h] = sum;
+          y[(size_t)t * H + h] += w[p] * sum;
+        }
+        if (hg_out)
+          for (int f = 0; f < F; ++f) hg_out[p * F + f] = hg[f];
+        if (hu_out)
+          for (int f = 0; f < F; ++f) hu_out[p * F + f] = hu[f];
+        if (a_out)
+          for (int f = 0; f < F; ++f) a_out[p * F + f] = a[f];
+        if (aq_out)
+          for (int f = 0; f < F; ++f) aq_out[p * F + f] = q[f];
+        if (ascale_out) ascale_out[p] = ldexp(1.0, ks);
+        if (o_out)
+          for (int h = 0; h < H; ++h) o_out[p * H + h] = o[h];
+      }
+    }
+    free(hg);
+    free(hu);
+    free(a);
+    free(q);
+    free(o);
+  }
+}
+

@@ -607,3 +607,79 @@ def test_quantize_fp8_shared_scale_and_error_bound():
     grid = oracle.e4m3_decode(np.arange(0, 0x7F, 5, dtype=np.uint8))[None, :, None] * np.ones((1, 1, 2))
     qg, _, sg = oracle.quantize_fp8(grid * 2.0 ** -4)
     assert sg[0] == 2.0 ** -4 and np.array_equal(oracle.dequantize_fp8(qg, sg), grid * 2.0 ** -4)
+
+
+# ---- the expert forward on fp8 (E4M3) operands --------------------------------
+FP8_LAYER = W.custom("fp8_pin", T=24, H=64, F=48, E=4, k=2, dtype="bf16", skew=True, dw=False)
+
+
+def _fp8_inputs(seed=5):
+    d = W.generate(FP8_LAYER, seed=seed)
+    idx, w = oracle.route_topk(d["logits"], FP8_LAYER.k)
+    return d, idx, w
+
+
+def test_forward_fp8_stores_the_nearest_bf16_of_the_swiglu_output():
+    d, idx, w = _fp8_inputs()
+    _, it = oracle.forward_fp8(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"])
+    exact = it["hg"] / (1 + np.exp(-it["hg"])) * it["hu"]
+    a = it["a"]
+    # on the bf16 grid: the fp32 value has its 16 low bits clear
+    assert (np.float32(a).view(np.uint32) & 0xFFFF == 0).all()
+    assert np.array_equal(np.float32(a).astype(np.float64), a)
+    # and nearest: within half a bf16 step (2^-8 relative to the binade) of the exact value
+    _, ex = np.frexp(exact)
+    assert (np.abs(a - exact) <= np.ldexp(0.5, ex - 8) * (1 + 1e-12)).all()
+
+
+def test_forward_fp8_quantizes_the_stored_activations_with_the_pinned_quantizer():
+    d, idx, w = _fp8_inputs()
+    _, it = oracle.forward_fp8(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"])
+    q, s = oracle.quantize_rows_fp8(it["a"])
+    assert np.array_equal(q, it["aq"]) and np.array_equal(s, it["ascale"])
+    qx, sx = oracle.quantize_rows_fp8(d["x"])
+    assert np.array_equal(qx, it["qx"]) and np.array_equal(sx, it["sx"])
+
+
+def test_forward_fp8_is_exact_on_inputs_the_format_holds():
+    """x and weights drawn from values E4M3 holds exactly at their scales: the
+    pre-activations are the plain oracle's, bit for bit."""
+    rng = np.random.default_rng(6)
+    T, H, F, E, k = 16, 32, 24, 3, 2
+    vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 1.5, -2.0, 3.0], np.float64)
+    x = rng.choice(vals, size=(T, H))
+    x[:, 0] = 3.0  # every row's amax (scale 2^-7: 3.0 / 2^-7 = 384 is an E4M3 value)
+    Wg = rng.choice(vals, size=(E, H, F)) / 64
+    Wu = rng.choice(vals, size=(E, H, F)) / 64
+    Wd = rng.choice(vals, size=(E, F, H)) / 64
+    Wg[:, 0, 0] = Wu[:, 0, 0] = Wd[:, 0, 0] = 3.0 / 64
+    idx, w = oracle.route_topk(rng.standard_normal((T, E)), k)
+    _, it = oracle.forward_fp8(x, idx, w, Wg, Wu, Wd)
+    _, ref = oracle.forward(x, idx, w, Wg, Wu, Wd, intermediates=True)
+    assert np.array_equal(it["hg"], ref["hg"]) and np.array_equal(it["hu"], ref["hu"])
+
+
+def test_forward_fp8_power_of_two_scalings_are_exact():
+    """Scaling W_down by 2^j scales o and y by 2^j exactly (codes unchanged,
+    scale times 2^j) and leaves a alone; scaling W_gate and W_up together by
+    2^j scales hg and hu by 2^j exactly."""
+    d, idx, w = _fp8_inputs()
+    y0, it0 = oracle.forward_fp8(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"])
+    y1, it1 = oracle.forward_fp8(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"] * 8)
+    assert np.array_equal(y1, 8 * y0) and np.array_equal(it1["o"], 8 * it0["o"])
+    assert np.array_equal(it1["a"], it0["a"])
+    # W_gate and W_up share one scale: scaling both keeps their codes, so the
+    # pre-activations scale exactly
+    _, it3 = oracle.forward_fp8(d["x"], idx, w, d["W_gate"] * 0.25, d["W_up"] * 0.25, d["W_down"])
+    assert np.array_equal(it3["hg"], 0.25 * it0["hg"]) and np.array_equal(it3["hu"], 0.25 * it0["hu"])
+
+
+def test_forward_fp8_within_the_format_error_of_the_exact_forward():
+    """Quantizing x, the weights and a to E4M3 (relative error <= 2^-4 each)
+    moves y by a few per cent of its scale, never by a missing scale factor, a
+    dropped term or a transposed operand (each of which is an O(1) error)."""
+    d, idx, w = _fp8_inputs()
+    y8, _ = oracle.forward_fp8(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"])
+    y = oracle.forward(d["x"], idx, w, d["W_gate"], d["W_up"], d["W_down"])
+    err = np.abs(y8 - y).max() / np.abs(y).max()
+    assert 1e-4 < err < 0.15, err
