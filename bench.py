@@ -41,6 +41,7 @@ METRIC = "MoE-layer fwd+bwd tokens/sec and TFLOPS (% bf16 MFMA peak), Qwen3-30B-
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 
 # kernel ids of include/moe.h (moe_kernel)
 K_GATEUP, K_DOWN, K_COMBINE, K_GRAD_ROWS, K_DA, K_DX, K_DW, K_DISPATCH_ROWS = 2, 3, 4, 5, 6, 7, 8, 1
@@ -83,6 +84,9 @@ def _parser():
     p.add_argument("--fp8-weights", action="store_true",
                    help="frozen expert weights stored once in fp8 (E4M3, one power-of-two scale per expert) and read "
                         "by the GEMMs (LoRA and forward-only workloads; not the headline configuration)")
+    p.add_argument("--fp8-mma", action="store_true",
+                   help="forward only, both expert GEMMs on the fp8 matrix cores (E4M3 operands: token rows and the "
+                        "SwiGLU output quantized per row, weights per expert); peak: the fp8 one")
     p.add_argument("--no-probes", action="store_true",
                    help="skip the per-step distribution pass and the bandwidth / matrix-core probes")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -144,23 +148,27 @@ def measured_traffic(kernel, workload):
     return int(m_b.group(1))
 
 
-def algorithmic(wl, counts, kept_counts=None, gathered=False, weight_bytes=None):
+def algorithmic(wl, counts, kept_counts=None, gathered=False, weight_bytes=None, fp8_inputs=False):
     """Per-kernel algorithmic bytes and flops (real rows only, no padding).
     gathered: the gate/up product reads token rows [T,H] through perm instead of
     the materialized x_sorted [N,H].  weight_bytes: bytes per expert-weight
-    element when it differs from the activations' (1 for fp8 weights)."""
+    element when it differs from the activations' (1 for fp8 weights).
+    fp8_inputs: the forward products read their activation rows as fp8 codes
+    (1 byte) with one fp32 scale per row."""
     b = 2 if wl.dtype == "bf16" else 4
     wb = b if weight_bytes is None else weight_bytes
+    ab = 1 if fp8_inputs else b  # bytes per activation element read by the forward products
     H, F, T, k = wl.H, wl.F, wl.T, wl.k
     N = wl.N
     Ea = int((counts > 0).sum())
     R = int(kept_counts.sum()) if kept_counts is not None else N
     Ea_b = int((kept_counts > 0).sum()) if kept_counts is not None else Ea
+    sx = 4 * T if fp8_inputs else 0  # row scales
     return {
         K_DISPATCH_ROWS: (T * H * b + N * H * b + 4 * N, 0.0),
-        K_GATEUP: (2 * H * F * wb * Ea + (T * H * b + 4 * N if gathered else N * H * b) + N * 2 * F * b + N * F * b,
-                   4.0 * H * F * N),
-        K_DOWN: (H * F * wb * Ea + N * F * b + N * H * b, 2.0 * H * F * N),
+        K_GATEUP: (2 * H * F * wb * Ea + (T * H * ab + 4 * N if gathered else N * H * ab) + sx + N * 2 * F * b
+                   + N * F * b, 4.0 * H * F * N),
+        K_DOWN: (H * F * wb * Ea + N * F * ab + (4 * N if fp8_inputs else 0) + N * H * b, 2.0 * H * F * N),
         K_COMBINE: (N * H * b + 8 * N + T * H * b, 0.0),
         K_GRAD_ROWS: (T * H * b + R * H * b + 8 * N + N * H * b, 0.0),
         K_DA: (H * F * wb * Ea_b + R * H * b + 2 * R * 2 * F * b, 2.0 * H * F * R),
@@ -344,7 +352,11 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
                         overlap_dw=args.overlap_dw,
                         gather_rows=None if args.gather_rows == "auto" else args.gather_rows == "on")
     score = "metric" if args.metric_score else None
-    wq = None
+    wq = wt = None
+    if args.fp8_mma:
+        assert not f32, "the fp8 matrix-core forward takes bf16 inputs"
+        wt = moe.Fp8KMajorWeights(moe.Fp8Weights(t["W_gate"], t["W_up"], t["W_down"]))  # once, before any timing
+        args = argparse.Namespace(**{**vars(args), "forward_only": True})
     if args.fp8_weights:
         assert not wl.dw and wl.rho is None and not args.no_keep_graph and not f32, \
             "fp8 weights are frozen: bf16 LoRA or forward-only workloads, pre-activations kept"
@@ -353,7 +365,7 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
     stream = torch.cuda.current_stream()
 
     def step():
-        L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], stream, w_r=w_r, wq=wq)
+        L.forward(logits, t["x"], t["W_gate"], t["W_up"], t["W_down"], stream, w_r=w_r, wq=wq, wt=wt)
         if not args.forward_only:
             L.backward(t["dy"], t["W_gate"], t["W_up"], t["W_down"], stream=stream, w_r=w_r, score=score, wq=wq)
 
@@ -365,7 +377,7 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
     router_kernels = ([K_ROUTER_FWD] + ([] if args.forward_only else [K_ROUTER_DW])) if args.router else []
     # HBM-bound row kernels launched once per step (the first combine of a step
     # is the forward's); the row copy of dispatch only when rows are materialized
-    hbm_kernels = ([] if L.gather_rows else [K_DISPATCH_ROWS]) + [K_COMBINE] + \
+    hbm_kernels = ([] if L.gather_rows or wt is not None else [K_DISPATCH_ROWS]) + [K_COMBINE] + \
                   ([] if args.forward_only else [K_GRAD_ROWS])
     profiled = gemm_kernels + router_kernels + hbm_kernels
     lib = moe.lib()
@@ -404,9 +416,10 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
 
     counts = L.counts.cpu().numpy()
     kept = L.kept_counts.cpu().numpy() if L.compacted else None
-    alg = algorithmic(wl, counts, kept, gathered=L.gather_rows, weight_bytes=1 if wq is not None else None)
+    alg = algorithmic(wl, counts, kept, gathered=L.gather_rows or wt is not None,
+                      weight_bytes=1 if (wq is not None or wt is not None) else None, fp8_inputs=wt is not None)
     step_flops = sum(alg[kk][1] for kk in gemm_kernels)
-    peak_flops = PEAK_F32_TFLOPS if f32 else PEAK_BF16_TFLOPS
+    peak_flops = PEAK_F32_TFLOPS if f32 else (PEAK_FP8_TFLOPS if wt is not None else PEAK_BF16_TFLOPS)
     byts, flops = alg[dom]
     compute_bound = flops / byts > peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
     sec = dom_ms[dom] * 1e-3
@@ -418,7 +431,7 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
         roof = {"bound": "hbm", "achieved": byts / sec / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # the stored counter readings are of the bf16-weight kernels
-    roof["traffic"] = None if wq is not None else measured_traffic(dom, wl.name)
+    roof["traffic"] = None if (wq is not None or wt is not None) else measured_traffic(dom, wl.name)
     roof["kernel"] = KERNEL_NAMES[dom]
     roof["kernel_us"] = dom_ms[dom] * 1e3
     roof["algorithmic_bytes"] = byts
@@ -437,9 +450,13 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
                 + ("" if args.gather_rows == "auto" else f"+gather_rows={args.gather_rows}")
                 + ("+metric_score" if args.metric_score else "")
                 + (f"+budget({args.budget_mib} MiB: cap {quota_cap})" if quota_cap else "")
-                + ("+fp8_weights" if wq is not None else ""),
+                + ("+fp8_weights" if wq is not None else "")
+                + ("+fp8_matrix_cores" if wt is not None else ""),
         "weights": "fp8 E4M3 (per-expert power-of-two scale), widened to bf16" if wq is not None
-                   else ("fp32" if f32 else "bf16"),
+                   else ("fp8 E4M3 codes, K-major (per-expert power-of-two scale)" if wt is not None
+                         else ("fp32" if f32 else "bf16")),
+        "gemm_operands": "fp8 E4M3 x E4M3 (rows and experts scaled by powers of two), fp32 accumulate"
+                         if wt is not None else ("fp32" if f32 else "bf16, fp32 accumulate"),
         "experts_with_rows": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max()),
         "retained_pairs": int(kept.sum()) if kept is not None else wl.N,
         "steps": steps, "warmup": warmup, "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s,
@@ -472,7 +489,7 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    del L, t, logits, wq
+    del L, t, logits, wq, wt
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if cpu_tokens > 0:
@@ -489,6 +506,11 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
 # sample of a token prefix (tokens, seconds of host work).
 SUB_CONFIGS = {"tiny_fp32": (64, 3.0), "qwen3_ft_t4096": (64, 5.0), "glm45air_t8192": (32, 5.0),
                "qwen3_compact_t16384": (64, 5.0)}
+
+
+# Their forward on the fp8 matrix cores as well (no oracle sample: the fp8
+# oracle is the bf16 one's loops on decoded operands).
+FP8_CONFIGS = ("glm45air_t8192", "qwen3_compact_t16384")
 
 
 def main():
@@ -531,6 +553,11 @@ def main():
                 continue
             print(f"bench: measuring {name}", file=sys.stderr, flush=True)
             out["configs"][name] = measure(W.WORKLOADS[name], base, 10, 3, 0 if args.no_cpu_baseline else toks, secs)
+        # the forward of the matrix-core-bound layers on the fp8 matrix cores
+        fp8 = argparse.Namespace(**{**vars(base), "fp8_mma": True})
+        for name in FP8_CONFIGS:
+            print(f"bench: measuring {name} forward on fp8", file=sys.stderr, flush=True)
+            out["configs"][name + "_fp8_fwd"] = measure(W.WORKLOADS[name], fp8, 10, 3, 0, 0.0)
     print(json.dumps(out), flush=True)
 
 

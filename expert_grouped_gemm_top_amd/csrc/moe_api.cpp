@@ -313,7 +313,7 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int moe_abi_version(void) { return 7; }
+int moe_abi_version(void) { return 8; }
 
 int64_t moe_launch_count(void) { return moe::g_launches; }
 
@@ -443,6 +443,96 @@ int moe_quantize_weights_fp8(int E, int64_t n0, int64_t n1, const void* w0, cons
   hipStream_t s = as_stream(stream);
   return hip_status(moe::launch_quantize_fp8(E, n0, n1, (const uint16_t*)w0, (const uint16_t*)w1, q0, q1, scale, s),
                     fn);
+}
+
+int moe_quantize_rows_fp8(int rows, int cols, const void* x, uint8_t* q, float* scale, void* stream) {
+  const char* fn = "moe_quantize_rows_fp8";
+  REQUIRE(rows >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: rows=%d must be >= 1", fn, rows);
+  REQUIRE(cols >= 8 && cols % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: cols=%d must be a positive multiple of 8", fn, cols);
+  NONNULL(x);
+  NONNULL(q);
+  NONNULL(scale);
+  REQUIRE((uintptr_t)x % 16 == 0 && (uintptr_t)q % 8 == 0, MOE_ERR_INVALID_ARGUMENT,
+          "%s: x must be 16-byte and q 8-byte aligned", fn);
+  REQUIRE((int64_t)rows * cols < ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "%s: matrix too large", fn);
+  return hip_status(moe::launch_quantize_fp8(rows, cols, 0, (const uint16_t*)x, nullptr, q, nullptr, scale,
+                                             as_stream(stream)),
+                    fn);
+}
+
+int moe_transpose_fp8(int E, int rows, int cols, const uint8_t* in, uint8_t* out, void* stream) {
+  const char* fn = "moe_transpose_fp8";
+  REQUIRE(E >= 1 && rows >= 1 && cols >= 1, MOE_ERR_INVALID_ARGUMENT, "%s: E=%d, rows=%d, cols=%d must be >= 1", fn, E,
+          rows, cols);
+  REQUIRE(rows % 16 == 0 && cols % 16 == 0, MOE_ERR_UNSUPPORTED, "%s: rows=%d and cols=%d must be multiples of 16", fn,
+          rows, cols);
+  REQUIRE(rows <= (1 << 24) && cols <= (1 << 24) && E <= 65535, MOE_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  NONNULL(in);
+  NONNULL(out);
+  REQUIRE(in != out, MOE_ERR_INVALID_ARGUMENT, "%s: in and out must not be the same buffer", fn);
+  REQUIRE(((uintptr_t)in | (uintptr_t)out) % 16 == 0, MOE_ERR_INVALID_ARGUMENT, "%s: in and out must be 16-byte aligned",
+          fn);
+  return hip_status(moe::launch_transpose_u8(E, rows, cols, in, out, as_stream(stream)), fn);
+}
+
+int moe_grouped_swiglu_fwd_fp8(int H, int F, int E, int k, int max_rows, const int32_t* offsets, const uint8_t* xq,
+                               const float* x_scale, const int32_t* perm, const uint8_t* wt_gate,
+                               const uint8_t* wt_up, const uint8_t* wt_down, const float* s_gu, const float* s_down,
+                               void* h_save, void* a_save, uint8_t* aq, float* a_scale, void* o_sorted,
+                               void* stream) {
+  const char* fn = "moe_grouped_swiglu_fwd_fp8";
+  int rc = check_expert_dims(fn, H, F, E, MOE_BF16);
+  if (rc || (rc = check_rows(fn, max_rows))) return rc;
+  REQUIRE(H % 16 == 0 && F % 16 == 0, MOE_ERR_UNSUPPORTED, "%s: H=%d and F=%d must be multiples of 16", fn, H, F);
+  REQUIRE(perm == nullptr || (k >= 1 && k <= 16), MOE_ERR_INVALID_ARGUMENT, "%s: k=%d must be in 1..16", fn, k);
+  NONNULL(offsets);
+  NONNULL(xq);
+  NONNULL(x_scale);
+  NONNULL(wt_gate);
+  NONNULL(wt_up);
+  NONNULL(wt_down);
+  NONNULL(s_gu);
+  NONNULL(s_down);
+  NONNULL(a_save);
+  NONNULL(aq);
+  NONNULL(a_scale);
+  NONNULL(o_sorted);
+  REQUIRE(((uintptr_t)xq | (uintptr_t)wt_gate | (uintptr_t)wt_up | (uintptr_t)wt_down | (uintptr_t)aq |
+           (uintptr_t)a_save) % 16 == 0,
+          MOE_ERR_INVALID_ARGUMENT, "%s: codes and a_save must be 16-byte aligned", fn);
+  if (max_rows == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  moe::Fp8GemmArgs g{};
+  g.offsets = offsets;
+  g.E = E;
+  g.H = H;
+  g.F = F;
+  g.a = xq;
+  g.a_map = perm;
+  g.a_div = perm ? k : 1;
+  g.ascale = x_scale;
+  g.w0 = wt_gate;
+  g.w1 = wt_up;
+  g.wscale = s_gu;
+  g.out0 = (uint16_t*)h_save;
+  g.out1 = (uint16_t*)a_save;
+  if ((rc = hip_status(timed(MOE_K_GEMM_GATEUP, s, [&] { return moe::launch_gemm_fp8(moe::kGemmGateUp, g, max_rows, s); }),
+                       fn)))
+    return rc;
+  // the stored SwiGLU output, one power-of-two scale per row, for the down product
+  if ((rc = hip_status(moe::launch_quantize_fp8(max_rows, F, 0, (const uint16_t*)a_save, nullptr, aq, nullptr, a_scale, s),
+                       fn)))
+    return rc;
+  g.a = aq;
+  g.a_map = nullptr;
+  g.a_div = 1;
+  g.ascale = a_scale;
+  g.w0 = wt_down;
+  g.w1 = nullptr;
+  g.wscale = s_down;
+  g.out0 = (uint16_t*)o_sorted;
+  g.out1 = nullptr;
+  return hip_status(timed(MOE_K_GEMM_DOWN, s, [&] { return moe::launch_gemm_fp8(moe::kGemmDown, g, max_rows, s); }), fn);
 }
 
 int moe_grouped_swiglu_fwd_gather(int H, int F, int E, int k, int max_rows, int max_expert_rows, int dtype,

@@ -102,6 +102,27 @@ struct DwArgs {
   uint16_t* dwd;       // [E,F,H]
 };
 
+// Pointers of one grouped GEMM of the forward on fp8 (E4M3) codes; every
+// operand row is K-contiguous codes, every product scaled by the activation
+// row's scale times the expert's.
+//   GATEUP: a = x codes [*, H] (row s is a[a_map[s] / a_div] when a_map is
+//           set), w0 / w1 = W_gate^T / W_up^T codes [E][F][H], out0 = h [R,2F]
+//           (or NULL), out1 = a [R,F] (bf16)
+//   DOWN:   a = SwiGLU-output codes [R,F], w0 = W_down^T codes [E][H][F], out0 = o [R,H] (bf16)
+struct Fp8GemmArgs {
+  const int32_t* offsets;
+  int E, H, F;
+  const uint8_t* a;
+  const int32_t* a_map;
+  int a_div;
+  const float* ascale;  // per source row of a
+  const uint8_t* w0;
+  const uint8_t* w1;
+  const float* wscale;  // per expert
+  uint16_t* out0;
+  uint16_t* out1;
+};
+
 // Source row of operand row s of a row GEMM.
 __device__ __forceinline__ int64_t a_row_of(const RowGemmArgs& g, int s) {
   return g.a_map != nullptr ? (int64_t)(g.a_map[s] / g.a_div) : (int64_t)s;
@@ -149,6 +170,10 @@ hipError_t launch_row_gemm_fp8w(int mode, const RowGemmArgs& g, int max_rows, hi
 hipError_t launch_quantize_fp8(int E, int64_t n0, int64_t n1, const uint16_t* w0, const uint16_t* w1, uint8_t* q0,
                                uint8_t* q1, float* scale, hipStream_t stream);
 hipError_t launch_big_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
+// fp8 forward products (kGemmGateUp, kGemmDown), every expert on 256 x 256 tiles.
+hipError_t launch_gemm_fp8(int mode, const Fp8GemmArgs& g, int max_rows, hipStream_t stream);
+// out[e][c][r] = in[e][r][c] (bytes; rows and cols multiples of 16).
+hipError_t launch_transpose_u8(int E, int rows, int cols, const uint8_t* in, uint8_t* out, hipStream_t stream);
 // Row count from which an expert takes the 256-row kernel for this product and
 // shape; kNoBigTiles where that kernel does not apply.
 int big_gemm_min_rows(int mode, int H, int F);

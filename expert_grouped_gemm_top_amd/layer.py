@@ -99,19 +99,33 @@ class MoeLayerBuffers:
             self.router_ws = em(max(moe.moe_router_workspace_bytes(T, H, E), 16), dt=torch.uint8)
 
     # ------------------------------------------------------------------ forward
-    def forward(self, logits, x, w_gate, w_up, w_down, stream=None, w_r=None, wq=None):
+    def forward(self, logits, x, w_gate, w_up, w_down, stream=None, w_r=None, wq=None, wt=None):
         """With w_r (a layer built with router=True) the logits are x W_r and
         the `logits` argument is ignored.  With wq (moe.Fp8Weights of the same
-        frozen weights) the expert GEMMs read the fp8 copy."""
+        frozen weights) the expert GEMMs read the fp8 copy.  With wt
+        (moe.Fp8KMajorWeights) both expert GEMMs run on the fp8 matrix cores:
+        the token rows are quantized per row, then gathered on load."""
         self._x = x  # the backward reads token rows through the pair ids
         if w_r is not None:
             moe.moe_router_fwd(x, w_r, self.logits, self.router_ws, stream)
             logits = self.logits
         moe.moe_route_topk(logits, self.topk_idx, self.topk_w, self.k, stream)
-        g = self.gather_rows  # index-only dispatch: the forward gathers x rows itself
+        g = self.gather_rows or wt is not None  # index-only dispatch: the forward gathers x rows itself
         moe.moe_dispatch(self.topk_idx, None if g else x, self.counts, self.offsets, self.perm, self.inv_perm,
                          None if g else self.x_sorted, self.ws, self.E, stream)
-        if wq is not None:
+        if wt is not None:
+            if not hasattr(self, "xq"):
+                dev, u8, f32 = self.device, torch.uint8, torch.float32
+                self.xq = torch.empty(self.T, self.H, dtype=u8, device=dev)
+                self.x_scale = torch.empty(self.T, dtype=f32, device=dev)
+                self.aq = torch.empty(self.N, self.F, dtype=u8, device=dev)
+                self.a_scale = torch.empty(self.N, dtype=f32, device=dev)
+            moe.moe_quantize_rows_fp8(x, self.xq, self.x_scale, stream)
+            moe.moe_grouped_swiglu_fwd_fp8(self.offsets, self.xq, self.x_scale, wt,
+                                           self.h_save if self.keep_graph else None, self.a_save, self.aq,
+                                           self.a_scale, self.o_sorted, self.N, perm=self.perm, k=self.k,
+                                           stream=stream)
+        elif wq is not None:
             assert self.keep_graph, "the fp8 path keeps the pre-activations"
             moe.moe_grouped_swiglu_fwd_fp8w(self.offsets, x if g else self.x_sorted, wq, self.h_save, self.a_save,
                                             self.o_sorted, self.N, perm=self.perm if g else None, k=self.k,

@@ -53,6 +53,9 @@ _SIGS = {
     "moe_quantize_weights_fp8": ([_i, _i64, _i64] + [_vp] * 6, _i),
     "moe_grouped_swiglu_fwd_fp8w": ([_i] * 5 + [_vp] * 12, _i),
     "moe_grouped_bwd_dx_fp8w": ([_i] * 6 + [_vp] * 19, _i),
+    "moe_quantize_rows_fp8": ([_i, _i, _vp, _vp, _vp, _vp], _i),
+    "moe_transpose_fp8": ([_i, _i, _i, _vp, _vp, _vp], _i),
+    "moe_grouped_swiglu_fwd_fp8": ([_i] * 5 + [_vp] * 15, _i),
 }
 
 
@@ -235,6 +238,56 @@ class Fp8Weights:
         self.s_down = torch.empty(E, dtype=F32, device=dev)
         moe_quantize_weights_fp8(w_gate, w_up, self.q_gate, self.q_up, self.s_gu, stream)
         moe_quantize_weights_fp8(w_down, None, self.q_down, None, self.s_down, stream)
+
+
+class Fp8KMajorWeights:
+    """fp8 (E4M3) weight codes in the K-major layout of the fp8 matrix-core
+    forward (moe_grouped_swiglu_fwd_fp8): W_gate^T, W_up^T [E,F,H] and
+    W_down^T [E,H,F] codes, transposed once from Fp8Weights' codes, with the
+    same per-expert scales."""
+
+    def __init__(self, wq: "Fp8Weights", stream=None):
+        E, H, F = wq.E, wq.H, wq.F
+        dev = wq.q_gate.device
+        self.E, self.H, self.F = E, H, F
+        self.t_gate = torch.empty(E, F, H, dtype=torch.uint8, device=dev)
+        self.t_up = torch.empty(E, F, H, dtype=torch.uint8, device=dev)
+        self.t_down = torch.empty(E, H, F, dtype=torch.uint8, device=dev)
+        self.s_gu, self.s_down = wq.s_gu, wq.s_down
+        moe_transpose_fp8(wq.q_gate, self.t_gate, stream)
+        moe_transpose_fp8(wq.q_up, self.t_up, stream)
+        moe_transpose_fp8(wq.q_down, self.t_down, stream)
+
+
+def moe_transpose_fp8(q_in, q_out, stream=None):
+    E, rows, cols = q_in.shape
+    U8 = torch.uint8
+    _check(lib().moe_transpose_fp8(E, rows, cols, _ptr(q_in, "in", U8, E * rows * cols),
+                                   _ptr(q_out, "out", U8, E * rows * cols), _stream(stream)))
+
+
+def moe_quantize_rows_fp8(x, q, scale, stream=None):
+    rows, cols = x.shape
+    _check(lib().moe_quantize_rows_fp8(rows, cols, _ptr(x, "x", torch.bfloat16, rows * cols),
+                                       _ptr(q, "q", torch.uint8, rows * cols), _ptr(scale, "scale", F32, rows),
+                                       _stream(stream)))
+
+
+def moe_grouped_swiglu_fwd_fp8(offsets, xq, x_scale, wt: Fp8KMajorWeights, h_save, a_save, aq, a_scale, o_sorted,
+                               max_rows: int, perm=None, k: int = 1, stream=None):
+    """xq / x_scale: quantized rows of x_sorted, or with perm the quantized token
+    rows (gathered on load)."""
+    E, H, F = wt.E, wt.H, wt.F
+    d, U8, R = torch.bfloat16, torch.uint8, max_rows
+    nx = (R // k) if perm is not None else R
+    _check(lib().moe_grouped_swiglu_fwd_fp8(
+        H, F, E, k, R, _ptr(offsets, "offsets", I32, E + 1), _ptr(xq, "xq", U8, nx * H),
+        _ptr(x_scale, "x_scale", F32, nx), _ptr(perm, "perm", I32, R, allow_none=True),
+        _ptr(wt.t_gate, "t_gate", U8, E * F * H), _ptr(wt.t_up, "t_up", U8, E * F * H),
+        _ptr(wt.t_down, "t_down", U8, E * H * F), _ptr(wt.s_gu, "s_gu", F32, E), _ptr(wt.s_down, "s_down", F32, E),
+        _ptr(h_save, "h_save", d, R * 2 * F, allow_none=True), _ptr(a_save, "a_save", d, R * F),
+        _ptr(aq, "aq", U8, R * F), _ptr(a_scale, "a_scale", F32, R), _ptr(o_sorted, "o_sorted", d, R * H),
+        _stream(stream)))
 
 
 def moe_quantize_weights_fp8(w0, w1, q0, q1, scale, stream=None):

@@ -74,7 +74,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 const char* moe_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);
-/* ABI version, currently 7. */
+/* ABI version, currently 8. */
 int moe_abi_version(void);
 
 /* Kernel launches made so far by library calls from the calling thread (a
@@ -95,7 +95,9 @@ int moe_abi_version(void);
  *                                           (fp32 and fp8 weights: B = 0)
  *   moe_grouped_bwd_dw                      bf16: 2; fp32: 1
  *   moe_compact_pairs[_cap]                 2 + (any row source given ? 1 : 0)
- *   moe_pair_scores, moe_quantize_weights_fp8   1
+ *   moe_pair_scores, moe_quantize_weights_fp8, moe_quantize_rows_fp8,
+ *   moe_transpose_fp8                       1
+ *   moe_grouped_swiglu_fwd_fp8              R = 0: 0; else 3
  *   moe_router_fwd                          1, plus 1 when its workspace is used
  *   moe_router_bwd                          3, plus 1 when its dW_r reduction is split
  * These counts are what a HIP graph of a layer step captures. */
@@ -335,6 +337,51 @@ int moe_grouped_bwd_dx_fp8w(int T, int H, int F, int E, int k, int max_rows, con
                             const float* s_gu, const float* s_down, const int32_t* inv_all,
                             const void* o_sorted, float* dg, void* dO_rows, void* dh_rows, void* dX_rows,
                             void* dx, void* stream);
+
+/* ---- the forward on the fp8 matrix cores ----------------------------------
+ * The expert forward's two grouped GEMMs on E4M3 x E4M3 operands
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, twice the bf16 rate; LRMoE abstract:
+ * variable-size grouped GEMMs; the pages fix no precision).  Every operand row
+ * carries one power-of-two scale (the rule of moe_quantize_weights_fp8): per
+ * token for x, per expert for the weights (W_gate and W_up sharing one), per
+ * row for the SwiGLU output; products are accumulated in fp32 and multiplied
+ * by the two scales (exact).  The SwiGLU output is stored in bf16 (a_save) and
+ * that stored value is quantized for the down product.  H and F multiples of
+ * 16.  Forward only. */
+
+/* Per-row fp8 storage of bf16 activations x [rows, cols] (device, 16-byte
+ * aligned; cols a multiple of 8): q [rows, cols] E4M3 codes (device, 8-byte
+ * aligned, out) and scale [rows] fp32 (device, out), the smallest power of two
+ * s with max_j |x[r,j]| <= 448 s, codes E4M3(x / s) rounded to nearest even,
+ * saturating.  One workgroup per row. */
+int moe_quantize_rows_fp8(int rows, int cols, const void* x, uint8_t* q, float* scale, void* stream);
+
+/* out[e][c][r] = in[e][r][c] for E matrices of rows x cols bytes (device,
+ * 16-byte aligned, distinct buffers; rows and cols multiples of 16): the
+ * K-major copy of fp8 weight codes that moe_grouped_swiglu_fwd_fp8 reads
+ * (W_gate, W_up [E,H,F] -> [E,F,H]; W_down [E,F,H] -> [E,H,F]). */
+int moe_transpose_fp8(int E, int rows, int cols, const uint8_t* in, uint8_t* out, void* stream);
+
+/* The expert forward on fp8 operands, over every expert's rows s in
+ * [offsets[e], offsets[e+1]) (all on 256-row tiles):
+ *   hg, hu = xd[s] W_gate_d[e], xd[s] W_up_d[e]       (d: decoded codes x scale)
+ *   a_save[s] = bf16(silu(hg) hu),  h_save[s] = [hg | hu] (bf16; h_save may be NULL)
+ *   aq[s], a_scale[s] = moe_quantize_rows_fp8 of a_save[s]
+ *   o_sorted[s] = ad[s] W_down_d[e]                     (bf16)
+ * xq [*, H] codes with x_scale [*] (device): with perm == NULL row s is xq[s]
+ * (rows of x_sorted, quantized); otherwise xq holds the token rows and row s
+ * is xq[perm[s] / k] (perm [T*k] from moe_dispatch, 1 <= k <= 16).  wt_gate,
+ * wt_up [E, F, H] and wt_down [E, H, F]: K-major codes (moe_transpose_fp8 of
+ * moe_quantize_weights_fp8's), with s_gu, s_down [E] (device).  h_save
+ * [max_rows, 2F], a_save [max_rows, F] bf16; aq [max_rows, F] uint8 and
+ * a_scale [max_rows] fp32 (device, out: the down product's input);
+ * o_sorted [max_rows, H] bf16 (device, out).  max_rows = offsets[E] (every
+ * row is quantized).  Codes, a_save and xq 16-byte aligned. */
+int moe_grouped_swiglu_fwd_fp8(int H, int F, int E, int k, int max_rows, const int32_t* offsets, const uint8_t* xq,
+                               const float* x_scale, const int32_t* perm, const uint8_t* wt_gate,
+                               const uint8_t* wt_up, const uint8_t* wt_down, const float* s_gu, const float* s_down,
+                               void* h_save, void* a_save, uint8_t* aq, float* a_scale, void* o_sorted,
+                               void* stream);
 
 /* Expert weight gradients (issue #14, Scope: dW for full fine-tuning), over the
  * rows r of each expert e (all pairs or the retained ones):

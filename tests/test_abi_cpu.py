@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(LIB)
     missing = [n for n in declared_functions() if not hasattr(raw, n)]
     assert not missing, missing
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
 
 
 def _err(lib):

@@ -70,3 +70,14 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_fp8_matrix_core_forward_counts_one_byte_per_operand_element():
+    wl = W.WORKLOADS["glm45air_t8192"]
+    H, F, T, N, E = wl.H, wl.F, wl.T, wl.N, wl.E
+    counts = np.full(E, N // E)
+    a = bench.algorithmic(wl, counts, gathered=True, weight_bytes=1, fp8_inputs=True)
+    # gate/up: fp8 weights of every expert, fp8 token rows + pair ids + row scales, bf16 h and a out
+    assert a[bench.K_GATEUP] == (2 * H * F * E + T * H + 4 * N + 4 * T + N * 2 * F * 2 + N * F * 2, 4.0 * H * F * N)
+    # down: fp8 weights, fp8 a rows + their scales, bf16 o out
+    assert a[bench.K_DOWN] == (H * F * E + N * F + 4 * N + N * H * 2, 2.0 * H * F * N)
