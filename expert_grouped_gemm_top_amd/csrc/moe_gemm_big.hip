@@ -43,11 +43,14 @@ __host__ __device__ inline int big_out_cols(int H, int F) {
 }
 
 // K-contiguous tile rows of BK elements (CPR 16-byte chunks): swizzled chunk
-// position; measured conflict-free for 16-byte fragment reads of 16
-// consecutive rows (64 B rows: key (row >> 1) & 3; 128 B rows: key row & 7).
+// position, so that the 16-byte fragment reads of 16 consecutive rows hit
+// distinct bank groups (the LDS serves 256 bytes of banks at once: 64-byte
+// rows, key (row >> 1) & 3; 128-byte rows, key (row >> 1) & 7 -- the key
+// row & 7 had rows r and r + 8 collide, measured as 10 % of the kernel's
+// cycles in bank conflicts, now none).
 template <int CPR>
 __device__ __forceinline__ int kc_swz(int row, int chunk) {
-  return CPR == 4 ? (chunk ^ ((row >> 1) & 3)) : (chunk ^ (row & 7));
+  return CPR == 4 ? (chunk ^ ((row >> 1) & 3)) : (chunk ^ ((row >> 1) & 7));
 }
 
 // Tile of BM rows x BN columns, reduction depth BK per stage, NW waves laid out
@@ -292,19 +295,41 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
   };
 
   const int steps = (K + BK - 1) / BK;
+  static_assert(STAGES == 2 && (BK / 16) % 2 == 0, "two stage buffers, an even number of sub-steps per stage");
+  // Stage handoff before the last sub-step: stage s + 1 is waited for and the
+  // workgroup synchronized while stage s's last fragments are in registers,
+  // so the next stage's first fragments are read under the last MFMAs of this
+  // one (no fragment-read bubble at stage starts).  After that barrier every
+  // wave is done reading stage s's buffer, which then takes stage s + 2.
+  issue(0);
+  wait_vmcnt<0>();
+  barrier_no_fence();
+  if (steps > 1) issue(1);
+  {
+    constexpr int SUBS = BK / 16;
+    Frags f0, f1;
+    // sub-steps 0 .. SUBS-2 of the stage in `st`, starting with f0 holding
+    // sub-step 0; leaves f1 holding sub-step SUBS-1 (read, not yet used)
+    auto stage_body = [&](const unsigned char* st) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < steps) issue(s);
-  for (int s = 0; s < steps; ++s) {
-    // stage s is complete once at most (stages issued after it) x INS loads remain
-    const int ahead = min(STAGES - 2, steps - 1 - s);
-    if (ahead >= 3) wait_vmcnt<3 * INS>();
-    else if (ahead == 2) wait_vmcnt<2 * INS>();
-    else if (ahead == 1) wait_vmcnt<INS>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();
-    if (s + STAGES - 1 < steps) issue(s + STAGES - 1);
-    compute(s);
+      for (int t = 0; t + 2 < SUBS; t += 2) {
+        mfmas_interleaved(f0, st, t + 1, f1);
+        mfmas_interleaved(f1, st, t + 2, f0);
+      }
+      mfmas_interleaved(f0, st, SUBS - 1, f1);
+    };
+    read_frags(s_dyn, 0, f0);
+    stage_body(s_dyn);
+    for (int s = 1; s < steps; ++s) {
+      const unsigned char* st = s_dyn + (s & 1) * STAGE_BYTES;
+      wait_vmcnt<0>();                      // stage s has landed (the only loads in flight)
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s - 1 are done
+      barrier_no_fence();                   // ... and every wave's: its buffer can take stage s + 1
+      if (s + 1 < steps) issue(s + 1);
+      mfmas_interleaved(f1, st, 0, f0);     // stage s - 1's last sub-step, stage s's first fragments
+      stage_body(st);
+    }
+    mfmas_interleaved(f1, s_dyn, -1, f0);
   }
 
   // ---- epilogue.  acc[i][j] register r -> row TM wm + 32 i + l32, tile
