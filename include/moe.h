@@ -80,18 +80,17 @@ int moe_abi_version(void);
 /* Kernel launches made so far by library calls from the calling thread (a
  * debug counter; it never resets).  Every call launches a fixed number of
  * kernels given by its arguments alone (a call rejected by validation
- * launches none); with Nk = T*k pairs, R = max_rows and B(c) = 1 when experts
- * of 256 rows and more get the 256-row kernel for a product with c output
- * columns (bf16, c a multiple of 256, the expert-row bound of the call and R
- * both >= 256), else 0:
+ * launches none); with Nk = T*k pairs, R = max_rows and B = 1 when experts
+ * of 256 rows and more get the 256-row kernel for a product (bf16, the
+ * expert-row bound of the call and R both >= 256), else 0:
  *   moe_route_topk                          1
  *   moe_dispatch, moe_dispatch_noalloc      (Nk <= 1024 ? 1 : 3) + (x_sorted ? 1 : 0)
- *   moe_grouped_swiglu_fwd[_gather]         R = 0: 0; bf16: 2 + B(2F) + B(H) with the
+ *   moe_grouped_swiglu_fwd[_gather]         R = 0: 0; bf16: 2 + 2 B with the
  *                                           bound max_expert_rows; fp32: 2
  *   moe_grouped_swiglu_fwd_fp8w             R = 0: 0; else 2
- *   moe_grouped_swiglu_recompute            R = 0: 0; bf16: 1 + B(2F); fp32: 1
+ *   moe_grouped_swiglu_recompute            R = 0: 0; bf16: 1 + B; fp32: 1
  *   moe_combine                             1
- *   moe_grouped_bwd_dx                      2 + (R > 0 ? 2 + B(H) : 0), bound min(R, T)
+ *   moe_grouped_bwd_dx                      2 + (R > 0 ? 2 + B : 0), bound min(R, T)
  *                                           (fp32 and fp8 weights: B = 0)
  *   moe_grouped_bwd_dw                      bf16: 2; fp32: 1
  *   moe_compact_pairs[_cap]                 2 + (any row source given ? 1 : 0)
