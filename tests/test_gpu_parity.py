@@ -426,6 +426,48 @@ FULL = ["qwen3_lora_t128", "qwen3_ft_t4096", "glm45air_t8192", "qwen3_compact_t1
         "qwen3_decode_t8"]
 
 
+def _parity_tokens(wl, idx, counts, rng):
+    """Every token of layers up to 256 tokens (every row of every saved
+    tensor is then compared); above, at least 64 tokens that together route
+    to every expert with rows (a first token of each, picked greedily), plus
+    two tokens of the hottest expert, the first and the last token."""
+    if wl.T <= 256:
+        return np.arange(wl.T, dtype=np.int32)
+    chosen = set()
+    covered = np.zeros(wl.E, bool)
+    for e in np.argsort(-counts, kind="stable"):
+        if counts[e] == 0 or covered[e]:
+            continue
+        t = int(np.nonzero((idx == e).any(axis=1))[0][0])
+        chosen.add(t)
+        covered[idx[t]] = True
+    hot = np.nonzero((idx == int(np.argmax(counts))).any(axis=1))[0]
+    chosen |= {int(hot[0]), int(hot[-1]), 0, wl.T - 1}
+    rest = np.setdiff1d(np.arange(wl.T), np.array(sorted(chosen)))
+    if len(chosen) < 64:
+        chosen |= set(int(t) for t in rng.choice(rest, 64 - len(chosen), replace=False))
+    assert covered[counts > 0].all()
+    return np.array(sorted(chosen), dtype=np.int32)
+
+
+def _dw_tile_queries(wl, counts, rng):
+    """One weight-gradient entry in every 256 x 256 output tile of dW_gate,
+    dW_up and dW_down for the hottest, a median and the smallest non-empty
+    expert (the last, partial tiles included: e.g. F = 1408 = 5.5 x 256)."""
+    nz = np.nonzero(counts > 0)[0]
+    order = nz[np.argsort(-counts[nz], kind="stable")]
+    experts = dict.fromkeys([int(order[0]), int(order[len(order) // 2]), int(order[-1])])
+    q = []
+    for e in experts:
+        for m in (0, 1, 2):
+            rows, cols = (wl.H, wl.F) if m < 2 else (wl.F, wl.H)
+            for r0 in range(0, rows, 256):
+                for c0 in range(0, cols, 256):
+                    q.append((e, m, int(rng.integers(r0, min(r0 + 256, rows))),
+                              int(rng.integers(c0, min(c0 + 256, cols)))))
+    return q
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_layer(name):
     wl = W.WORKLOADS[name]
@@ -452,10 +494,8 @@ def test_full_size_layer(name):
         retained = c["retained"]
         rows_of_pair = c["inv"]
     rng = np.random.default_rng(123)
-    hot = np.nonzero(idx.reshape(-1) == int(np.argmax(counts)))[0] // wl.k
-    tokens = np.unique(np.concatenate([rng.choice(wl.T, min(6, wl.T), replace=False), hot[:2],
-                                       [0, wl.T - 1]])).astype(np.int32)
-    note(f"oracle on {len(tokens)} sampled tokens")
+    tokens = _parity_tokens(wl, idx, counts, rng)
+    note(f"oracle on {len(tokens)} tokens")
     y, dx, dg, it, bt = oracle_tokens(wl, d, idx, w, tokens, retained=retained)
     tt = torch.from_numpy(tokens).long().cuda()
     assert_close("y", np32(L.y[tt]), y[tokens], tol)
@@ -472,7 +512,7 @@ def test_full_size_layer(name):
     assert_close("dX", np32(L.dX[krows]), bt["dX"][kept], tol)
     if wl.dw:
         kc = (c["counts"] if wl.rho else counts)
-        q = dw_queries(wl, kc, rng)
+        q = dw_queries(wl, kc, rng) + _dw_tile_queries(wl, kc, rng)
         note(f"oracle on {len(q)} sampled dW entries")
         ref = oracle_dw_sample(wl, d, idx, w, q, retained=retained)
         got = gpu_dw_entries(L, q)
