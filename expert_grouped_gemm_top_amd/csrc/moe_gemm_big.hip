@@ -45,12 +45,13 @@ __host__ __device__ inline int big_out_cols(int H, int F) {
 // K-contiguous tile rows of BK elements (CPR 16-byte chunks): swizzled chunk
 // position, so that the 16-byte fragment reads of 16 consecutive rows hit
 // distinct bank groups (the LDS serves 256 bytes of banks at once: 64-byte
-// rows, key (row >> 1) & 3; 128-byte rows, key (row >> 1) & 7 -- the key
-// row & 7 had rows r and r + 8 collide, measured as 10 % of the kernel's
-// cycles in bank conflicts, now none).
+// rows, key (row >> 2) & 3, so rows r, r + 4, r + 8, r + 12 -- same offset
+// within 256 bytes -- take distinct chunks; 128-byte rows, key (row >> 1) & 7
+// -- the key row & 7 had rows r and r + 8 collide, measured as 10 % of the
+// kernel's cycles in bank conflicts, now none).
 template <int CPR>
 __device__ __forceinline__ int kc_swz(int row, int chunk) {
-  return CPR == 4 ? (chunk ^ ((row >> 1) & 3)) : (chunk ^ ((row >> 1) & 7));
+  return CPR == 4 ? (chunk ^ ((row >> 2) & 3)) : (chunk ^ ((row >> 1) & 7));
 }
 
 // Tile of BM rows x BN columns, reduction depth BK per stage, NW waves laid out
