@@ -182,8 +182,10 @@ def algorithmic(wl, counts, kept_counts=None, gathered=False, weight_bytes=None,
     }
 
 
-def environment(dev):
-    """GPU, software versions and the host CPU the oracle baseline runs on."""
+def environment(dev, read_clocks=True):
+    """GPU, software versions and the host CPU the oracle baseline runs on.
+    read_clocks: ask rocm-smi for the current clocks (a child process; skipped
+    for profiled runs, which pass --no-probes)."""
     import torch
     p = torch.cuda.get_device_properties(dev)
     cpu = ""
@@ -195,6 +197,8 @@ def environment(dev):
     clocks = None
     try:  # current shader / memory clocks as the driver reports them (best effort)
         import subprocess
+        if not read_clocks:
+            raise OSError("not asked for")
         r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
         found = {key: m.group(1) for key in ("sclk", "mclk")
                  for m in [re.search(rf"{key} clock level: [^:]+: \((\d+\s*Mhz)\)", r.stdout)] if m}
@@ -265,6 +269,14 @@ def probes(dev):
            "copy_GBs": 2 * n / best_ms(lambda: dst.copy_(src)) / 1e6,
            "bf16_matmul_8192_TFLOPs": 2 * 8192 ** 3 / best_ms(lambda: torch.mm(a, b)) / 1e9}
     del src, dst, a, b
+    # the library GEMM on one expert's gate/up product (M rows x K = H, N = 2F)
+    # at the GLM-Air and Qwen3 shapes, beside the grouped kernels' per-phase rates
+    res["bf16_matmul_expert_TFLOPs"] = {}
+    for M, K, N in ((4096, 4096, 2816), (2048, 4096, 2816), (4096, 2048, 1536), (2048, 2048, 1536)):
+        a = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
+        b = torch.randn(K, N, dtype=torch.bfloat16, device=dev)
+        res["bf16_matmul_expert_TFLOPs"][f"{M}x{K}x{N}"] = 2 * M * K * N / best_ms(lambda: torch.mm(a, b), reps=10) / 1e9
+        del a, b
     return res
 
 
@@ -539,7 +551,7 @@ def main():
         if key in rec:
             out[key] = rec[key]
     dev = torch.device("cuda:0")
-    out["env"] = environment(dev)
+    out["env"] = environment(dev, read_clocks=not args.no_probes)
     if not args.no_probes:
         out["probes"] = probes(dev)
     if "cpu_baseline" in rec:
@@ -558,7 +570,29 @@ def main():
         for name in FP8_CONFIGS:
             print(f"bench: measuring {name} forward on fp8", file=sys.stderr, flush=True)
             out["configs"][name + "_fp8_fwd"] = measure(W.WORKLOADS[name], fp8, 10, 3, 0, 0.0)
+    sclk = (out["env"].get("clocks") or {}).get("sclk")
+    if sclk:
+        for r in [out] + list(out.get("configs", {}).values()):
+            clock_scaled(r, float(sclk.split()[0]))
     print(json.dumps(out), flush=True)
+
+
+# The published matrix-core peaks assume this shader clock.
+PEAK_CLOCK_MHZ = 2400.0
+
+
+def clock_scaled(rec, sclk_mhz):
+    """Matrix-core fractions against the peak scaled to the shader clock the
+    driver reported (the published peak assumes 2.4 GHz): how far the kernels
+    are from what the chip can do at the clock it ran, beside the fractions
+    against the published peak, which stay the reported ones."""
+    scale = PEAK_CLOCK_MHZ / sclk_mhz
+    if "mfma_frac_of_step" in rec:
+        rec["mfma_frac_of_step_at_read_sclk"] = rec["mfma_frac_of_step"] * scale
+    roof = rec.get("roofline") or {}
+    if "mfma_frac" in roof:
+        roof["mfma_frac_at_read_sclk"] = roof["mfma_frac"] * scale
+        roof["read_sclk_mhz"] = sclk_mhz
 
 
 if __name__ == "__main__":
