@@ -570,15 +570,21 @@ def main():
         for name in FP8_CONFIGS:
             print(f"bench: measuring {name} forward on fp8", file=sys.stderr, flush=True)
             out["configs"][name + "_fp8_fwd"] = measure(W.WORKLOADS[name], fp8, 10, 3, 0, 0.0)
-    sclk = (out["env"].get("clocks") or {}).get("sclk")
+    sclk = read_mhz((out["env"].get("clocks") or {}).get("sclk"))
     if sclk:
         for r in [out] + list(out.get("configs", {}).values()):
-            clock_scaled(r, float(sclk.split()[0]))
+            clock_scaled(r, sclk)
     print(json.dumps(out), flush=True)
 
 
 # The published matrix-core peaks assume this shader clock.
 PEAK_CLOCK_MHZ = 2400.0
+
+
+def read_mhz(text):
+    """MHz from a clock reading as rocm-smi prints it ('2229Mhz', '1908 Mhz'), or None."""
+    m = re.match(r"\s*(\d+(?:\.\d+)?)", text or "")
+    return float(m.group(1)) if m and float(m.group(1)) > 0 else None
 
 
 def clock_scaled(rec, sclk_mhz):

@@ -95,3 +95,10 @@ def test_clock_scaled_fractions_divide_by_the_read_clock():
     bare = {"roofline": {"bound": "hbm", "frac": 0.5}}
     bench.clock_scaled(bare, 1920.0)
     assert "mfma_frac_at_read_sclk" not in bare["roofline"]
+
+
+def test_clock_readings_parse_as_rocm_smi_prints_them():
+    import bench
+    assert bench.read_mhz("2229Mhz") == 2229.0
+    assert bench.read_mhz("1908 Mhz") == 1908.0
+    assert bench.read_mhz(None) is None and bench.read_mhz("") is None and bench.read_mhz("0Mhz") is None
