@@ -27,6 +27,11 @@ struct Vec8<float> {
     const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
+  // the same, for data this step reads once (non-temporal hint)
+  static __device__ __forceinline__ void load_once(const float* p, float* v) {
+    const f32x4 a = __builtin_nontemporal_load((const f32x4*)p), b = __builtin_nontemporal_load((const f32x4*)(p + 4));
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
   static __device__ __forceinline__ void store(float* p, const float* v) {
     *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
     *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
@@ -34,8 +39,11 @@ struct Vec8<float> {
 };
 template <>
 struct Vec8<uint16_t> {
-  static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
-    const u32x4 a = *(const u32x4*)p;
+  static __device__ __forceinline__ void load(const uint16_t* p, float* v) { unpack(*(const u32x4*)p, v); }
+  static __device__ __forceinline__ void load_once(const uint16_t* p, float* v) {
+    unpack(__builtin_nontemporal_load((const u32x4*)p), v);
+  }
+  static __device__ __forceinline__ void unpack(const u32x4 a, float* v) {
     v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
     v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
   }
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(128) void combine_kernel(int Tn, int H, int k, cons
     float v[KP][8];
 #pragma unroll
     for (int j = 0; j < KP; ++j)
-      Vec8<T>::load(src[j] >= 0 ? rows + (size_t)src[j] * H + c * 8 : (const T*)orow, v[j]);
+      Vec8<T>::load_once(src[j] >= 0 ? rows + (size_t)src[j] * H + c * 8 : (const T*)orow, v[j]);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < KP; ++j)
@@ -113,12 +121,12 @@ __global__ __launch_bounds__(256) void grad_rows_kernel(int Tn, int H, int k, co
     const T* dyrow = dy + (size_t)t * H;
     for (int c = tid; c < chunks; c += 256) {
       float g[8];
-      Vec8<T>::load(dyrow + c * 8, g);
+      Vec8<T>::load_once(dyrow + c * 8, g);
       float o[KP][8];
       if constexpr (DG) {
 #pragma unroll
         for (int j = 0; j < KP; ++j)
-          Vec8<T>::load(o_sorted + (size_t)(osrc[j] >= 0 ? osrc[j] : 0) * H + c * 8, o[j]);
+          Vec8<T>::load_once(o_sorted + (size_t)(osrc[j] >= 0 ? osrc[j] : 0) * H + c * 8, o[j]);
       }
 #pragma unroll
       for (int j = 0; j < KP; ++j) {

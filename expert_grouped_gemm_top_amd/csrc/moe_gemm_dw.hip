@@ -21,7 +21,10 @@
 // longest reductions start first; the tiles of one expert are dealt to the 8
 // XCDs in contiguous runs (tiles next to each other share an operand block,
 // which then stays in that XCD's L2).  The output tile is staged through LDS
-// so that every store is a full 16-byte lane of a contiguous row segment.
+// so that every store is a full 16-byte lane of a contiguous row segment; the
+// stores carry the non-temporal hint, since nothing in the step reads dW
+// (measured: dW 615 -> 595 us at qwen3_ft_t4096, 684 -> 660 us at
+// qwen3_compact_t16384).
 #include <algorithm>
 #include <type_traits>
 
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(64 * Cfg::WAVES, Cfg::OCC) void dw_bf16_kernel(DwAr
       uint16_t* dst;
       if (t < sh.tiles1) dst = (gn < F) ? g.dwg + ((size_t)e * H + gm) * F + gn : g.dwu + ((size_t)e * H + gm) * F + (gn - F);
       else dst = g.dwd + ((size_t)e * F + gm) * H + gn;
-      *(u32x4*)dst = v;
+      __builtin_nontemporal_store(v, (u32x4*)dst);  // nothing in the step reads dW again
     }
   }
 }
@@ -487,7 +490,7 @@ __global__ __launch_bounds__(256, 3) void dw_small_bf16_kernel(DwArgs g) {
         uint16_t* dst;
         if (t < sh.tiles1) dst = (gn < F) ? g.dwg + ((size_t)e * H + gm) * F + gn : g.dwu + ((size_t)e * H + gm) * F + (gn - F);
         else dst = g.dwd + ((size_t)e * F + gm) * H + gn;
-        *(u32x4*)dst = v;
+        __builtin_nontemporal_store(v, (u32x4*)dst);  // nothing in the step reads dW again
       }
     }
     __syncthreads();  // the next tile's loads overwrite the staged tile
