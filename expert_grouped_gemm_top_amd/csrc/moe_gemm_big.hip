@@ -1,9 +1,9 @@
 // moe_gemm_big.hip -- row GEMMs of the SwiGLU experts for experts with many
 // rows (>= 256), where the grouped GEMM is bound by the matrix cores.
 //
-// Gate/up, down and dX, the products of the other row GEMMs but dA (expert
-// forward and backward dx: npu-train issue #14, sections Proposal and Scope;
-// variable-size grouped GEMMs: LRMoE abstract), tiled for gfx950:
+// The four products of the row GEMMs (expert forward and backward dx:
+// npu-train issue #14, sections Proposal and Scope; variable-size grouped
+// GEMMs: LRMoE abstract), tiled for gfx950:
 //   * workgroup tile BM rows x BN columns, waves laid out WM x (NW / WM), each
 //     wave a grid of 32 x 32 blocks on v_mfma_f32_32x32x16_bf16
 //     (on gfx950 it sustains ~2.4 PFLOP/s where the 16x16x32 form stops near
@@ -19,7 +19,10 @@
 //     one column -- half of a 32x32x16 B fragment; 64-byte chunk groups are
 //     XOR-swizzled by 4 (k & 3) so the rows of one read fall in distinct banks;
 //   * rows past the tile's real rows re-read the tile's last row: they only
-//     produce output rows that are never stored.
+//     produce output rows that are never stored;
+//   * dA's SwiGLU backward needs the saved pre-activations of every output:
+//     its tile is staged through the idle stage buffers so that h is read and
+//     dh written as 16-byte runs of one row.
 #include <algorithm>
 
 #include "moe_common.h"
@@ -32,14 +35,17 @@ namespace {
 
 template <int MODE>
 struct BigShape {
-  // the product with the transposed down projection (dA) stays on 128-row tiles
-  static_assert(MODE != kGemmDA, "no 256-row dA kernel");
   static constexpr bool kNN = (MODE == kGemmGateUp || MODE == kGemmDown);
 };
 
 template <int MODE>
 __host__ __device__ inline int big_out_cols(int H, int F) {
-  return MODE == kGemmGateUp ? 2 * F : H;
+  return MODE == kGemmGateUp ? 2 * F : (MODE == kGemmDA ? F : H);
+}
+
+template <int MODE>
+__host__ __device__ inline int big_reduction(int H, int F) {
+  return (MODE == kGemmGateUp || MODE == kGemmDA) ? H : (MODE == kGemmDown ? F : 2 * F);
 }
 
 // K-contiguous tile rows of BK elements (CPR 16-byte chunks): swizzled chunk
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
   const int nb = within / gm;
   const TileSlot ts = lookup_tile(s_start, s_off, g.E, BM, s_start[lo] + mt);
   const int e = ts.expert;
-  const int K = MODE == kGemmGateUp ? H : (MODE == kGemmDown ? F : 2 * F);
+  const int K = big_reduction<MODE>(H, F);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wm = w % WM, wn = w / WM;
   const int l32 = l & 31, hk = l >> 5;  // MFMA row/column and k-group of this lane
@@ -177,12 +183,19 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
       const int row = (64 / CPR) * (B_INS * w + i) + l / CPR;  // output column within the tile
       const int chunk = kc_swz<CPR>(row, l % CPR);
       const int n = nb * BN + row;
-      b_ok[i] = n < H;
-      const size_t nrow = (size_t)(b_ok[i] ? n : 0) * F;
       b_k[i] = 8 * chunk;
-      // DX: k < F from W_gate, k >= F from W_up
-      b_src[i] = g.w0 + (size_t)e * H * F + nrow + 8 * chunk;
-      b_hi[i] = g.w1 + (size_t)e * H * F + nrow + 8 * chunk;
+      if (MODE == kGemmDA) {
+        // W_down [F,H]: output column n is weight row n
+        b_ok[i] = n < F;
+        b_src[i] = g.w0 + (size_t)e * F * H + (size_t)(b_ok[i] ? n : 0) * H + 8 * chunk;
+        b_hi[i] = b_src[i];
+      } else {
+        b_ok[i] = n < H;
+        const size_t nrow = (size_t)(b_ok[i] ? n : 0) * F;
+        // DX: k < F from W_gate, k >= F from W_up
+        b_src[i] = g.w0 + (size_t)e * H * F + nrow + 8 * chunk;
+        b_hi[i] = g.w1 + (size_t)e * H * F + nrow + 8 * chunk;
+      }
     }
   }
 
@@ -335,6 +348,70 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
 
   // ---- epilogue.  acc[i][j] register r -> row TM wm + 32 i + l32, tile
   // column TN wn + 32 j + 8 q + 4 hk + e with q = r / 4, e = r % 4.
+  if constexpr (MODE == kGemmDA) {
+    // dA -> dh = [dHg | dHu] through the SwiGLU backward.  The fp32 tile goes
+    // to LDS in two halves of HC = BN / 2 columns (the stage buffers hold
+    // one), each read back as 8 consecutive columns of one row per thread, so
+    // h is read and dh written as contiguous row segments.  16-byte chunk c
+    // of staged row r sits at chunk c ^ (r & 15): the MFMA-layout writes (16
+    // rows, one chunk) touch 16 distinct bank groups, and so do the row reads
+    // (HC = 64: two rows of opposite parity per 16 lanes; HC = 128: one row,
+    // odd chunk first in the upper 8 lanes).
+    constexpr int HC = BN / 2;
+    static_assert(BM * HC * 4 <= STAGES * STAGE_BYTES && WNW % 2 == 0 && (HC == 64 || HC == 128), "dA staging");
+    float* s_f = reinterpret_cast<float*>(s_dyn);
+    auto staged = [&](int row, int chunk) { return s_f + row * HC + 4 * (chunk ^ (row & 15)); };
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's last fragment reads are done
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      barrier_no_fence();  // every wave is done with the stage buffers / the previous half
+      if (wn / (WNW / 2) == half) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int row = TM * wm + 32 * i + l32;
+              const int col = TN * (wn % (WNW / 2)) + 32 * j + 8 * q + 4 * hk;
+              *(f32x4*)staged(row, col >> 2) =
+                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the staged values are written
+      barrier_no_fence();
+      constexpr int C8 = HC / 8;  // 8-column groups per staged row
+#pragma unroll 2
+      for (int it = tid; it < BM * C8; it += 64 * NW) {
+        const int row = it / C8, c8 = it % C8;
+        const int f = nb * BN + half * HC + 8 * c8;  // feature of the group's first column
+        if (row >= ts.rows || (TAIL && f >= F)) continue;  // F is a multiple of 8: a group is all in or all out
+        const int first = 2 * c8 + (HC == 128 ? ((c8 >> 3) & 1) : 0);
+        const f32x4 d_first = *(const f32x4*)staged(row, first);
+        const f32x4 d_second = *(const f32x4*)staged(row, first ^ 1);
+        const f32x4 d_lo = (first & 1) ? d_second : d_first, d_hi = (first & 1) ? d_first : d_second;
+        const int64_t grow = (int64_t)ts.row_begin + row;
+        const uint16_t* hrow = g.h + h_row_of(g, grow) * 2 * F;
+        const u32x4 hg = *(const u32x4*)(hrow + f), hu = *(const u32x4*)(hrow + F + f);
+        float dg[8], du[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float da = c < 4 ? d_lo[c] : d_hi[c - 4];
+          const float hgv = (c & 1) ? bf_hi(hg[c >> 1]) : bf_lo(hg[c >> 1]);
+          const float huv = (c & 1) ? bf_hi(hu[c >> 1]) : bf_lo(hu[c >> 1]);
+          const float sg = sigmoidf_fast(hgv);
+          dg[c] = da * huv * sg * (1.0f + hgv * (1.0f - sg));
+          du[c] = da * hgv * sg;
+        }
+        uint16_t* drow = g.out0 + grow * 2 * F;
+        *(u32x4*)(drow + f) = u32x4{pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]), pack_bf2(dg[4], dg[5]),
+                                    pack_bf2(dg[6], dg[7])};
+        *(u32x4*)(drow + F + f) = u32x4{pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]), pack_bf2(du[4], du[5]),
+                                        pack_bf2(du[6], du[7])};
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int row = TM * wm + 32 * i + l32;
@@ -379,9 +456,15 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
 }
 
 
+// dA takes the 256-row kernel only for F of at least this many features: with
+// fewer than four 256-column blocks per row tile its tiles are too few to
+// fill the chip, and the 128-row tiles measured faster (F = 768: dA 251 ->
+// 268 us at qwen3_ft_t4096; F = 1408: 1289 -> 1214 us at glm45air_t8192).
+constexpr int kBigDaMinF = 1024;
+
 template <int MODE, int BM, int BN, int BK, int NW, int WM, int STAGES, int WPC>
 struct BigCfg {
-  static int min_rows(int, int) { return kBigTileMinRows; }
+  static int min_rows(int, int F) { return (MODE == kGemmDA && F < kBigDaMinF) ? kNoBigTiles : kBigTileMinRows; }
 
   template <bool TAIL>
   static hipError_t launch_as(const RowGemmArgs& g, int64_t wgs, hipStream_t stream) {
@@ -402,7 +485,7 @@ struct BigCfg {
     const int64_t tiles = (N + big_experts * (BM - 1)) / BM;
     const int cols = big_out_cols<MODE>(g.H, g.F);
     const int64_t wgs = ((tiles * ((cols + BN - 1) / BN) + 7) / 8) * 8;
-    const int K = MODE == kGemmGateUp ? g.H : (MODE == kGemmDown ? g.F : 2 * g.F);
+    const int K = big_reduction<MODE>(g.H, g.F);
     const bool tail = K % BK != 0 || cols % BN != 0 || (MODE == kGemmDX && g.F % BK != 0);
     return tail ? launch_as<true>(g, wgs, stream) : launch_as<false>(g, wgs, stream);
   }
@@ -417,8 +500,8 @@ int big_gemm_min_rows(int mode, int H, int F) {
   switch (mode) {
     case kGemmGateUp: return Big<kGemmGateUp>::min_rows(H, F);
     case kGemmDown: return Big<kGemmDown>::min_rows(H, F);
-    case kGemmDX: return Big<kGemmDX>::min_rows(H, F);
-    default: return kNoBigTiles;
+    case kGemmDA: return Big<kGemmDA>::min_rows(H, F);
+    default: return Big<kGemmDX>::min_rows(H, F);
   }
 }
 
@@ -426,8 +509,8 @@ hipError_t launch_big_gemm_bf16(int mode, const RowGemmArgs& g, int max_rows, hi
   switch (mode) {
     case kGemmGateUp: return Big<kGemmGateUp>::launch(g, max_rows, stream);
     case kGemmDown: return Big<kGemmDown>::launch(g, max_rows, stream);
-    case kGemmDX: return Big<kGemmDX>::launch(g, max_rows, stream);
-    default: return hipSuccess;  // DA always runs on 128-row tiles
+    case kGemmDA: return Big<kGemmDA>::launch(g, max_rows, stream);
+    default: return Big<kGemmDX>::launch(g, max_rows, stream);
   }
 }
 

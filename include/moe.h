@@ -90,8 +90,9 @@ int moe_abi_version(void);
  *   moe_grouped_swiglu_fwd_fp8w             R = 0: 0; else 2
  *   moe_grouped_swiglu_recompute            R = 0: 0; bf16: 1 + B; fp32: 1
  *   moe_combine                             1
- *   moe_grouped_bwd_dx                      2 + (R > 0 ? 2 + B : 0), bound min(R, T)
- *                                           (fp32 and fp8 weights: B = 0)
+ *   moe_grouped_bwd_dx                      2 + (R > 0 ? 2 + B + B_dA : 0), bound min(R, T),
+ *                                           B_dA = B when F >= 1024, else 0
+ *                                           (fp32 and fp8 weights: B = B_dA = 0)
  *   moe_grouped_bwd_dw                      bf16: 2; fp32: 1
  *   moe_compact_pairs[_cap]                 2 + (any row source given ? 1 : 0)
  *   moe_pair_scores, moe_quantize_weights_fp8, moe_quantize_rows_fp8,

@@ -54,7 +54,9 @@ def expected(name, L, bf16, gather, x_rows_given=True, any_rows=False):
     if name in ("moe_combine", "moe_pair_scores"):
         return 1
     if name == "moe_grouped_bwd_dx":
-        return 2 + (2 + big(H, min(R, T), R, bf16) if R > 0 else 0)
+        # dA takes the 256-row kernel only from F = 1024 on
+        big_da = big(F, min(R, T), R, bf16) if F >= 1024 else 0
+        return 2 + (2 + big_da + big(H, min(R, T), R, bf16) if R > 0 else 0)
     if name == "moe_grouped_bwd_dx_fp8w":
         return 4
     if name == "moe_grouped_bwd_dw":
@@ -67,6 +69,7 @@ def expected(name, L, bf16, gather, x_rows_given=True, any_rows=False):
 CASES = [
     # name, T, H, F, E, k, dtype, rho, keep_graph, gather_rows, fp8
     ("bf16_big", 512, 512, 256, 8, 2, "bf16", None, True, None, False),
+    ("bf16_big_wide_f", 512, 256, 1032, 4, 2, "bf16", None, True, None, False),
     ("bf16_gathered", 700, 512, 256, 8, 4, "bf16", None, True, True, False),
     ("bf16_compact_recompute", 600, 256, 128, 8, 2, "bf16", 0.5, False, False, False),
     ("bf16_compact_gathered", 600, 512, 384, 16, 4, "bf16", 0.5, True, None, False),

@@ -124,6 +124,10 @@ UNALIGNED = [
     W.custom("bf16_h2880_f360", T=700, H=2880, F=360, E=8, k=2, dtype="bf16", skew=True, dw=True),
     W.custom("bf16_h8_f8", T=300, H=8, F=8, E=4, k=2, dtype="bf16", skew=True, dw=True),
     W.custom("bf16_decode_h200_f136", T=3, H=200, F=136, E=8, k=2, dtype="bf16", skew=False, dw=True),
+    # F >= 1024: dA of experts with 256 rows and more on the 256-row kernel,
+    # whole 256-column blocks (1024) and a partial last block (1032)
+    W.custom("bf16_h256_f1024", T=640, H=256, F=1024, E=4, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_h264_f1032", T=640, H=264, F=1032, E=4, k=2, dtype="bf16", skew=True, dw=True),
 ]
 
 
