@@ -570,35 +570,7 @@ def main():
         for name in FP8_CONFIGS:
             print(f"bench: measuring {name} forward on fp8", file=sys.stderr, flush=True)
             out["configs"][name + "_fp8_fwd"] = measure(W.WORKLOADS[name], fp8, 10, 3, 0, 0.0)
-    sclk = read_mhz((out["env"].get("clocks") or {}).get("sclk"))
-    if sclk:
-        for r in [out] + list(out.get("configs", {}).values()):
-            clock_scaled(r, sclk)
     print(json.dumps(out), flush=True)
-
-
-# The published matrix-core peaks assume this shader clock.
-PEAK_CLOCK_MHZ = 2400.0
-
-
-def read_mhz(text):
-    """MHz from a clock reading as rocm-smi prints it ('2229Mhz', '1908 Mhz'), or None."""
-    m = re.match(r"\s*(\d+(?:\.\d+)?)", text or "")
-    return float(m.group(1)) if m and float(m.group(1)) > 0 else None
-
-
-def clock_scaled(rec, sclk_mhz):
-    """Matrix-core fractions against the peak scaled to the shader clock the
-    driver reported (the published peak assumes 2.4 GHz): how far the kernels
-    are from what the chip can do at the clock it ran, beside the fractions
-    against the published peak, which stay the reported ones."""
-    scale = PEAK_CLOCK_MHZ / sclk_mhz
-    if "mfma_frac_of_step" in rec:
-        rec["mfma_frac_of_step_at_read_sclk"] = rec["mfma_frac_of_step"] * scale
-    roof = rec.get("roofline") or {}
-    if "mfma_frac" in roof:
-        roof["mfma_frac_at_read_sclk"] = roof["mfma_frac"] * scale
-        roof["read_sclk_mhz"] = sclk_mhz
 
 
 if __name__ == "__main__":

@@ -82,23 +82,3 @@ def test_fp8_matrix_core_forward_counts_one_byte_per_operand_element():
     # down: fp8 weights, fp8 a rows + their scales, bf16 o out
     assert a[bench.K_DOWN] == (H * F * E + N * F + 4 * N + N * H * 2, 2.0 * H * F * N)
 
-
-def test_clock_scaled_fractions_divide_by_the_read_clock():
-    """At the read shader clock the matrix cores give peak x sclk / 2400 MHz, so
-    the same achieved rate is a larger share of it."""
-    import bench
-    rec = {"mfma_frac_of_step": 0.2, "roofline": {"bound": "mfma", "mfma_frac": 0.3, "frac": 0.3}}
-    bench.clock_scaled(rec, 1920.0)
-    assert abs(rec["mfma_frac_of_step_at_read_sclk"] - 0.25) < 1e-12
-    assert abs(rec["roofline"]["mfma_frac_at_read_sclk"] - 0.375) < 1e-12
-    assert rec["roofline"]["frac"] == 0.3  # the reported fraction stays against the published peak
-    bare = {"roofline": {"bound": "hbm", "frac": 0.5}}
-    bench.clock_scaled(bare, 1920.0)
-    assert "mfma_frac_at_read_sclk" not in bare["roofline"]
-
-
-def test_clock_readings_parse_as_rocm_smi_prints_them():
-    import bench
-    assert bench.read_mhz("2229Mhz") == 2229.0
-    assert bench.read_mhz("1908 Mhz") == 1908.0
-    assert bench.read_mhz(None) is None and bench.read_mhz("") is None and bench.read_mhz("0Mhz") is None
