@@ -192,7 +192,8 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(int T, int k, int ro
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) dst[j] = (j < k) ? inv_perm[(size_t)t * k + j] : -1;
     for (int c = threadIdx.x; c < row_chunks; c += 256) {
-      const u32x4 v = x[(size_t)t * row_chunks + c];
+      // x is read once here (the GEMMs read x_sorted): non-temporal
+      const u32x4 v = __builtin_nontemporal_load(x + (size_t)t * row_chunks + c);
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j)
         if (j < k && dst[j] >= 0) x_sorted[(size_t)dst[j] * row_chunks + c] = v;
