@@ -412,45 +412,102 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
     }
     return;
   }
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int row = TM * wm + 32 * i + l32;
-    if (row >= ts.rows) continue;
-    const size_t grow = (size_t)ts.row_begin + row;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (MODE == kGemmGateUp) {
-        // 8-column chunk (TN wn + 32 j) / 8 + q: even q -> W_gate, odd q -> W_up,
-        // feature (BN/2) nb + (TN wn + 32 j) / 2 + 8 (q >> 1) + 4 hk + e
-        const int f0 = (BN / 2) * nb + (TN * wn + 32 * j) / 2 + 4 * hk;
-        uint16_t* hrow = g.out0 + grow * 2 * F;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int f = f0 + 8 * p;
-          float hg[4], hu[4], av[4];
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            hg[e2] = acc[i][j][8 * p + e2];
-            hu[e2] = acc[i][j][8 * p + 4 + e2];
-            av[e2] = hg[e2] * sigmoidf_fast(hg[e2]) * hu[e2];
-          }
-          if (TAIL && f >= F) continue;  // features past the edge (4 of them, all or none)
-          if (g.out0 != nullptr) {
-            *(u32x2*)(hrow + f) = u32x2{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3])};
-            *(u32x2*)(hrow + F + f) = u32x2{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3])};
-          }
-          if (g.out1 != nullptr) *(u32x2*)(g.out1 + grow * F + f) = u32x2{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3])};
-        }
-      } else {
-        uint16_t* orow = g.out0 + grow * H;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nb * BN + TN * wn + 32 * j + 8 * q + 4 * hk;
-          if (TAIL && col >= H) continue;  // columns past the edge (4 of them, all or none)
-          *(u32x2*)(orow + col) = u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                        pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-        }
+  // The other products leave through LDS too: the MFMA layout gives a lane 4
+  // consecutive columns of one row per register quad, and storing those 8
+  // bytes straight to memory touches 32 rows per instruction (measured: the
+  // stores took 12-29 % of these kernels' time).  The bf16 results are staged
+  // in the idle stage buffers as [row][columns] with 16-byte chunk c of row r
+  // at chunk c ^ (r & 15) (16 consecutive rows of one chunk land in distinct
+  // bank groups), then leave as whole 16-byte lanes of contiguous row runs.
+  // Gate/up: round 1 stages [hg | hu] of the tile's BN / 2 features (the h
+  // output), round 2 the SwiGLU output a, computed from the fp32 sums.
+  {
+    constexpr int FT = MODE == kGemmGateUp ? BN / 2 : BN;  // columns of one staged matrix
+    constexpr int PITCH = 2 * FT;                          // bytes per staged row
+    constexpr int CH = FT / 8;                             // 16-byte chunks per staged row
+    static_assert(CH >= 16 && (MODE == kGemmGateUp ? 2 : 1) * BM * PITCH <= STAGES * STAGE_BYTES, "staging");
+    auto put = [&](unsigned char* m, int row, int col, u32x2 v) {  // 4 bf16 at columns col .. col + 3
+      *(u32x2*)(m + row * PITCH + 16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7)) = v;
+    };
+    // every staged chunk of every staged matrix goes out: items = BM x CH per matrix
+    auto drain = [&](const unsigned char* m, uint16_t* out, int ld, int col0, int ncols) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+      barrier_no_fence();                   // ... and every wave's
+#pragma unroll 4
+      for (int it = tid; it < BM * CH; it += 64 * NW) {
+        const int row = it / CH, c = it % CH;
+        const int col = col0 + 8 * c;
+        if (row < ts.rows && (!TAIL || col < ncols))  // ncols is a multiple of 8: a chunk is all in or all out
+          *(u32x4*)(out + ((size_t)ts.row_begin + row) * ld + col) =
+              *(const u32x4*)(m + row * PITCH + 16 * (c ^ (row & 15)));
       }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of the staged rows are done
+      barrier_no_fence();                   // ... and every wave's: the buffers can be staged again
+    };
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's last fragment reads are done
+    barrier_no_fence();                   // ... and every wave's: the stage buffers are free
+    if constexpr (MODE == kGemmGateUp) {
+      // register 8 p + e of acc[i][j] -> hg, register 8 p + 4 + e -> hu, of
+      // tile feature (TN wn + 32 j) / 2 + 8 p + 4 hk + e
+      unsigned char* sg = s_dyn;                 // hg, then a
+      unsigned char* su = s_dyn + BM * PITCH;    // hu
+      const int fb = (BN / 2) * nb;              // first feature of the tile
+      if (g.out0 != nullptr) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const int row = TM * wm + 32 * i + l32, fl = (TN * wn + 32 * j) / 2 + 8 * p + 4 * hk;
+              put(sg, row, fl, u32x2{pack_bf2(acc[i][j][8 * p], acc[i][j][8 * p + 1]),
+                                     pack_bf2(acc[i][j][8 * p + 2], acc[i][j][8 * p + 3])});
+              put(su, row, fl, u32x2{pack_bf2(acc[i][j][8 * p + 4], acc[i][j][8 * p + 5]),
+                                     pack_bf2(acc[i][j][8 * p + 6], acc[i][j][8 * p + 7])});
+            }
+        // hg and hu of one row leave together: chunks 0 .. CH-1 of sg, then of su
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        barrier_no_fence();
+#pragma unroll 4
+        for (int it = tid; it < 2 * BM * CH; it += 64 * NW) {
+          const int row = it / (2 * CH), c2 = it % (2 * CH), up = c2 >= CH, c = up ? c2 - CH : c2;
+          const int f = fb + 8 * c;
+          if (row < ts.rows && (!TAIL || f < F))
+            *(u32x4*)(g.out0 + ((size_t)ts.row_begin + row) * 2 * F + (up ? F : 0) + f) =
+                *(const u32x4*)((up ? su : sg) + row * PITCH + 16 * (c ^ (row & 15)));
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        barrier_no_fence();
+      }
+      if (g.out1 != nullptr) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const int row = TM * wm + 32 * i + l32, fl = (TN * wn + 32 * j) / 2 + 8 * p + 4 * hk;
+              float av[4];
+#pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) {
+                const float hgv = acc[i][j][8 * p + e2], huv = acc[i][j][8 * p + 4 + e2];
+                av[e2] = hgv * sigmoidf_fast(hgv) * huv;
+              }
+              put(sg, row, fl, u32x2{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3])});
+            }
+        drain(sg, g.out1, F, fb, F);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            put(s_dyn, TM * wm + 32 * i + l32, TN * wn + 32 * j + 8 * q + 4 * hk,
+                u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                      pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])});
+      drain(s_dyn, g.out0, H, nb * BN, H);
     }
   }
 }
