@@ -220,50 +220,103 @@ __global__ __launch_bounds__(64 * kF8Waves, 1) void big_gemm_fp8_kernel(Fp8GemmA
 
   // ---- epilogue: acc[i][j] register r -> activation row TM wm + 32 i + l32,
   // virtual column TN wn + 32 j + 8 q + 4 hk + (0..3), q = r / 4; scaled by
-  // the row's and the expert's power-of-two scales
+  // the row's and the expert's power-of-two scales.  The bf16 results are
+  // staged in the idle stage buffers as [row][columns] (16-byte chunk c of
+  // row r at chunk c ^ (r & 15)) and leave as 16-byte lanes of contiguous row
+  // runs; storing the MFMA layout's 8-byte pieces straight to memory touches
+  // 32 rows per instruction.  Gate/up: round 1 stages [hg | hu], round 2 the
+  // SwiGLU output a.
   const float sw = g.wscale[e];
+  float sc[kF8MI];  // scale of each of this lane's rows (rows past the tile: any finite value, never stored)
 #pragma unroll
   for (int i = 0; i < kF8MI; ++i) {
-    const int row = kF8TM * wm + 32 * i + l32;
-    if (row >= ts.rows) continue;
-    const int s = ts.row_begin + row;
+    const int s = ts.row_begin + min(kF8TM * wm + 32 * i + l32, ts.rows - 1);
     const int64_t src_row = g.a_map != nullptr ? (int64_t)(g.a_map[s] / g.a_div) : (int64_t)s;
-    const float sc = g.ascale[src_row] * sw;
-    const size_t grow = (size_t)s;
+    sc[i] = g.ascale[src_row] * sw;
+  }
+  constexpr int FT = MODE == kGemmGateUp ? kF8BN / 2 : kF8BN;  // columns of one staged matrix
+  constexpr int PITCH = 2 * FT, CH = FT / 8;
+  static_assert(CH >= 16 && (MODE == kGemmGateUp ? 2 : 1) * kF8BM * PITCH <= kF8Stages * kF8StageBytes, "staging");
+  auto put = [&](unsigned char* m, int row, int col, u32x2 v) {  // 4 bf16 at columns col .. col + 3
+    *(u32x2*)(m + row * PITCH + 16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7)) = v;
+  };
+  auto sync_lds = [] {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS accesses are done
+    barrier_no_fence();                   // ... and every wave's
+  };
+  sync_lds();  // every wave is done reading the stage buffers
+  if (MODE == kGemmGateUp) {
+    unsigned char* sg = s_dyn;                  // hg, then a
+    unsigned char* su = s_dyn + kF8BM * PITCH;  // hu
+    const int fb = (kF8BN / 2) * nb;            // first feature of the tile
+    // a, packed to bf16 up front, so that the accumulators are dead once h is staged
+    u32x2 apk[kF8MI][kF8NJ][2];
 #pragma unroll
-    for (int j = 0; j < kF8NJ; ++j) {
-      if (MODE == kGemmGateUp) {
-        // 8-column chunk (TN wn + 32 j) / 8 + q: even q -> gate, odd q -> up,
-        // feature (BN/2) nb + (TN wn + 32 j) / 2 + 8 (q >> 1) + 4 hk + (0..3)
-        const int f0 = (kF8BN / 2) * nb + (kF8TN * wn + 32 * j) / 2 + 4 * hk;
+    for (int i = 0; i < kF8MI; ++i)
+#pragma unroll
+      for (int j = 0; j < kF8NJ; ++j)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const int f = f0 + 8 * p;
-          if (f >= F) continue;  // features past the edge (4 of them, all or none)
-          float hg[4], hu[4], av[4];
+          float av[4];
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
-            hg[e2] = acc[i][j][8 * p + e2] * sc;
-            hu[e2] = acc[i][j][8 * p + 4 + e2] * sc;
-            av[e2] = hg[e2] * sigmoidf_fast(hg[e2]) * hu[e2];
+            const float hgv = acc[i][j][8 * p + e2] * sc[i], huv = acc[i][j][8 * p + 4 + e2] * sc[i];
+            av[e2] = hgv * sigmoidf_fast(hgv) * huv;
           }
-          if (g.out0 != nullptr) {
-            uint16_t* hrow = g.out0 + grow * 2 * F;
-            *(u32x2*)(hrow + f) = u32x2{pack_bf2(hg[0], hg[1]), pack_bf2(hg[2], hg[3])};
-            *(u32x2*)(hrow + F + f) = u32x2{pack_bf2(hu[0], hu[1]), pack_bf2(hu[2], hu[3])};
-          }
-          *(u32x2*)(g.out1 + grow * F + f) = u32x2{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3])};
+          apk[i][j][p] = u32x2{pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3])};
         }
-      } else {
-        uint16_t* orow = g.out0 + grow * H;
+    if (g.out0 != nullptr) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nb * kF8BN + kF8TN * wn + 32 * j + 8 * q + 4 * hk;
-          if (col >= H) continue;
-          *(u32x2*)(orow + col) = u32x2{pack_bf2(acc[i][j][4 * q] * sc, acc[i][j][4 * q + 1] * sc),
-                                        pack_bf2(acc[i][j][4 * q + 2] * sc, acc[i][j][4 * q + 3] * sc)};
-        }
+      for (int i = 0; i < kF8MI; ++i)
+#pragma unroll
+        for (int j = 0; j < kF8NJ; ++j)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int row = kF8TM * wm + 32 * i + l32, fl = (kF8TN * wn + 32 * j) / 2 + 8 * p + 4 * hk;
+            const f32x16& a = acc[i][j];
+            put(sg, row, fl, u32x2{pack_bf2(a[8 * p] * sc[i], a[8 * p + 1] * sc[i]),
+                                   pack_bf2(a[8 * p + 2] * sc[i], a[8 * p + 3] * sc[i])});
+            put(su, row, fl, u32x2{pack_bf2(a[8 * p + 4] * sc[i], a[8 * p + 5] * sc[i]),
+                                   pack_bf2(a[8 * p + 6] * sc[i], a[8 * p + 7] * sc[i])});
+          }
+      sync_lds();
+      for (int it = tid; it < 2 * kF8BM * CH; it += 64 * kF8Waves) {
+        const int row = it / (2 * CH), c2 = it % (2 * CH), up = c2 >= CH, c = up ? c2 - CH : c2;
+        const int f = fb + 8 * c;
+        if (row < ts.rows && f < F)  // F is a multiple of 8: a chunk is all in or all out
+          *(u32x4*)(g.out0 + ((size_t)ts.row_begin + row) * 2 * F + (up ? F : 0) + f) =
+              *(const u32x4*)((up ? su : sg) + row * PITCH + 16 * (c ^ (row & 15)));
       }
+      sync_lds();
+    }
+#pragma unroll
+    for (int i = 0; i < kF8MI; ++i)
+#pragma unroll
+      for (int j = 0; j < kF8NJ; ++j)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          put(sg, kF8TM * wm + 32 * i + l32, (kF8TN * wn + 32 * j) / 2 + 8 * p + 4 * hk, apk[i][j][p]);
+    sync_lds();
+    for (int it = tid; it < kF8BM * CH; it += 64 * kF8Waves) {
+      const int row = it / CH, c = it % CH, f = fb + 8 * c;
+      if (row < ts.rows && f < F)
+        *(u32x4*)(g.out1 + ((size_t)ts.row_begin + row) * F + f) = *(const u32x4*)(sg + row * PITCH + 16 * (c ^ (row & 15)));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kF8MI; ++i)
+#pragma unroll
+      for (int j = 0; j < kF8NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          put(s_dyn, kF8TM * wm + 32 * i + l32, kF8TN * wn + 32 * j + 8 * q + 4 * hk,
+              u32x2{pack_bf2(acc[i][j][4 * q] * sc[i], acc[i][j][4 * q + 1] * sc[i]),
+                    pack_bf2(acc[i][j][4 * q + 2] * sc[i], acc[i][j][4 * q + 3] * sc[i])});
+    sync_lds();
+    for (int it = tid; it < kF8BM * CH; it += 64 * kF8Waves) {
+      const int row = it / CH, c = it % CH, col = nb * kF8BN + 8 * c;
+      if (row < ts.rows && col < H)  // H is a multiple of 8
+        *(u32x4*)(g.out0 + ((size_t)ts.row_begin + row) * H + col) = *(const u32x4*)(s_dyn + row * PITCH + 16 * (c ^ (row & 15)));
     }
   }
 }
