@@ -7,8 +7,9 @@
 // with the largest score, equal scores to the lower pair id.  That order is a
 // total order on the 64-bit key  (orderable(score) << 32) | ~p , so the kept
 // set is { key >= the q_e-th largest key }.  The threshold key is found by an
-// 8-pass MSB-first radix select (256-bin LDS histograms; the counts do not
-// depend on the order of the LDS atomics).  A block prefix scan over the
+// MSB-first radix select of up to 8 passes (256-bin LDS histograms; the counts
+// do not depend on the order of the LDS atomics), ending early once the q-th
+// key's bin is kept whole.  A block prefix scan over the
 // expert's pairs in sorted order then writes the kept pairs in ascending p.
 // Up to kLdsPairs pairs, the expert's pair ids and score keys are gathered
 // into LDS once (eight independent loads per thread in flight) and every pass
@@ -42,8 +43,12 @@ __device__ __forceinline__ uint64_t lds_key(const uint32_t* s_khi, const int32_t
 
 // The key threshold from a 256-bin histogram pass: thread t looks at bin
 // 255 - t; the keys in higher bins are an exclusive scan.  Updates the prefix
-// class and the rank still to find within it.
-__device__ __forceinline__ void radix_pick(const int* s_hist, int* s_tmp, int* s_pick, int shift, uint64_t& prefix,
+// class and the rank still to find within it.  Returns true (uniformly) when
+// the rank is the last of its bin: every key of the bin is then kept, so the
+// prefix with its lower bits zero is already the threshold and the remaining
+// passes are skipped (with real-valued scores the q-th key is usually alone in
+// its bin after two or three passes).
+__device__ __forceinline__ bool radix_pick(const int* s_hist, int* s_tmp, int* s_pick, int shift, uint64_t& prefix,
                                            uint64_t& mask, int& remaining) {
   const int tid = threadIdx.x;
   const int cnt = s_hist[255 - tid];
@@ -52,12 +57,15 @@ __device__ __forceinline__ void radix_pick(const int* s_hist, int* s_tmp, int* s
   if (above < remaining && remaining <= above + cnt) {
     s_pick[0] = 255 - tid;
     s_pick[1] = remaining - above;
+    s_pick[2] = cnt;
   }
   __syncthreads();
   prefix |= (uint64_t)s_pick[0] << shift;
   mask |= (uint64_t)0xffu << shift;
   remaining = s_pick[1];
+  const bool whole_bin = s_pick[1] == s_pick[2];
   __syncthreads();
+  return whole_bin;
 }
 
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ a, int64_t n, int32_t v) {
@@ -75,7 +83,7 @@ __global__ __launch_bounds__(256) void compact_select_kernel(int E, int cap, con
                                                              int32_t* __restrict__ kept_inv) {
   __shared__ int s_tmp[4];
   __shared__ int s_hist[256];
-  __shared__ int s_pick[2];
+  __shared__ int s_pick[3];
   extern __shared__ __attribute__((aligned(16))) uint32_t s_pairs[];  // [kLdsPairs] keys, then [kLdsPairs] ids
   const int e = blockIdx.x, tid = threadIdx.x;
   // kept base of this expert: exclusive scan of min(n_e', cap)
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(256) void compact_select_kernel(int E, int cap, con
         if ((key & mask) == prefix) atomicAdd(&s_hist[(int)((key >> shift) & 0xffu)], 1);
       }
       __syncthreads();
-      radix_pick(s_hist, s_tmp, s_pick, shift, prefix, mask, remaining);
+      if (radix_pick(s_hist, s_tmp, s_pick, shift, prefix, mask, remaining)) break;
     }
     // kept pairs in ascending order: thread t takes the contiguous chunk
     // [t c, (t + 1) c) and its place follows from a scan of the chunk counts
@@ -184,9 +192,9 @@ __global__ __launch_bounds__(256) void compact_select_kernel(int E, int cap, con
       if ((key & mask) == prefix) atomicAdd(&s_hist[(int)((key >> shift) & 0xffu)], 1);
     }
     __syncthreads();
-    radix_pick(s_hist, s_tmp, s_pick, shift, prefix, mask, remaining);
+    if (radix_pick(s_hist, s_tmp, s_pick, shift, prefix, mask, remaining)) break;
   }
-  const uint64_t thr = prefix;  // the q-th largest key; keep key >= thr
+  const uint64_t thr = prefix;  // keep key >= thr: exactly the q largest keys
   int run = 0;
   for (int i0 = 0; i0 < n; i0 += 256) {
     const int i = i0 + tid;
