@@ -199,17 +199,20 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
     }
   }
 
-  auto issue = [&](int s) {
+  // loads [lo, hi) of stage s in the order A (A_INS), then B (B_INS)
+  auto issue_part = [&](int s, int lo, int hi) {
     unsigned char* st = s_dyn + (s % STAGES) * STAGE_BYTES;
     const int k0 = s * BK;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
+      if (i < lo || i >= hi) continue;
       const uint16_t* src = a_src[i] + k0;
       if (TAIL && k0 + a_k[i] >= K) src = zero_chunk();
       g2lds(src, st + 1024 * (A_INS * w + i));
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
+      if (A_INS + i < lo || A_INS + i >= hi) continue;
       const uint16_t* src;
       if (NN) {
         src = b_src[i] + (size_t)k0 * b_kstride;
@@ -224,6 +227,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
       g2lds(src, st + A_BYTES + 1024 * (B_INS * w + i));
     }
   };
+  auto issue = [&](int s) { issue_part(s, 0, INS); };
 
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -334,14 +338,25 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
     };
     read_frags(s_dyn, 0, f0);
     stage_body(s_dyn);
+    // The next stage's loads go out in two halves, before this stage's first
+    // two MFMA runs.  Issued all at once after the barrier, they made every
+    // wave stall on the full memory-instruction queue with the matrix pipes
+    // idle (measured with cycle counters: 30-40 % of a wave's time spent
+    // issuing them); spreading them over all four runs leaves the last ones
+    // too little time to land.
+    static_assert(SUBS == 4, "four MFMA runs per stage");
     for (int s = 1; s < steps; ++s) {
       const unsigned char* st = s_dyn + (s & 1) * STAGE_BYTES;
       wait_vmcnt<0>();                      // stage s has landed (the only loads in flight)
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s - 1 are done
       barrier_no_fence();                   // ... and every wave's: its buffer can take stage s + 1
-      if (s + 1 < steps) issue(s + 1);
+      const bool more = s + 1 < steps;
+      if (more) issue_part(s + 1, 0, INS / 2);
       mfmas_interleaved(f1, st, 0, f0);     // stage s - 1's last sub-step, stage s's first fragments
-      stage_body(st);
+      if (more) issue_part(s + 1, INS / 2, INS);
+      mfmas_interleaved(f0, st, 1, f1);
+      mfmas_interleaved(f1, st, 2, f0);
+      mfmas_interleaved(f0, st, 3, f1);
     }
     mfmas_interleaved(f1, s_dyn, -1, f0);
   }
