@@ -326,10 +326,12 @@ def cpu_baseline(wl, d, logits, sample_tokens, min_seconds=10.0):
             "phase_s_per_rep": {n: v / reps for n, v in phases.items()}}
 
 
-def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=False):
+def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=False, timers=None):
     """One workload on the GPU: warmup, an untimed pass with every kernel
     bracketed (per-kernel durations, the dominant kernel), then ``steps`` timed
-    steps with only the dominant kernel bracketed.  Returns the record."""
+    steps with only the dominant kernel bracketed.  Returns the record.  With
+    a dict ``timers``, the layer stays resident and timers[wl.name] = f(n)
+    times n more steps (ms per step) for the interleaved rounds."""
     import numpy as np
     import torch
 
@@ -501,9 +503,19 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    del L, t, logits, wq, wt
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    if timers is not None:
+        def timer(n):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                step()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / n
+        timers[wl.name] = timer
+    else:
+        del L, t, logits, wq, wt
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     if cpu_tokens > 0:
         if logits_host is None:  # logits of a router-weight workload: x W_r by the oracle, in fp32
             import oracle
@@ -525,6 +537,25 @@ SUB_CONFIGS = {"tiny_fp32": (64, 3.0), "qwen3_ft_t4096": (64, 5.0), "glm45air_t8
 FP8_CONFIGS = ("glm45air_t8192", "qwen3_compact_t16384")
 
 
+ROUNDS = 2  # interleaved rounds after the first measurement of every workload
+
+
+def round_orders(names, rounds):
+    """Workload order of each round after the first (forward) measurement:
+    reversed, forward, reversed, ..."""
+    return [list(reversed(names)) if r % 2 == 0 else list(names) for r in range(rounds)]
+
+
+def interleaved_rounds(names, timers, steps, rounds):
+    """ms per step of every workload in every round, in round_orders' order."""
+    out = {n: [] for n in names}
+    for order in round_orders(names, rounds):
+        for n in order:
+            print(f"bench: round timing {n}", file=sys.stderr, flush=True)
+            out[n].append(timers[n](steps[n]))
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -538,7 +569,9 @@ def main():
     wl = W.WORKLOADS[args.workload]
     assert wl.dtype == "bf16", "the headline runs a bf16 workload"
     cpu_tokens = 0 if args.no_cpu_baseline else (args.cpu_tokens or min(wl.T, 128))
-    rec = measure(wl, args, args.steps, args.warmup, cpu_tokens, 10.0, dist_and_probes=not args.no_probes)
+    timers = {} if not args.no_configs else None
+    rec = measure(wl, args, args.steps, args.warmup, cpu_tokens, 10.0, dist_and_probes=not args.no_probes,
+                  timers=timers)
     out = {
         "metric": METRIC, "value": rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -564,12 +597,28 @@ def main():
             if name == wl.name:
                 continue
             print(f"bench: measuring {name}", file=sys.stderr, flush=True)
-            out["configs"][name] = measure(W.WORKLOADS[name], base, 10, 3, 0 if args.no_cpu_baseline else toks, secs)
+            out["configs"][name] = measure(W.WORKLOADS[name], base, 10, 3, 0 if args.no_cpu_baseline else toks, secs,
+                                           timers=timers)
         # the forward of the matrix-core-bound layers on the fp8 matrix cores
         fp8 = argparse.Namespace(**{**vars(base), "fp8_mma": True})
         for name in FP8_CONFIGS:
             print(f"bench: measuring {name} forward on fp8", file=sys.stderr, flush=True)
             out["configs"][name + "_fp8_fwd"] = measure(W.WORKLOADS[name], fp8, 10, 3, 0, 0.0)
+        # The bf16 workloads again, interleaved: each round times every one of
+        # them in turn, the order reversed every other round (the first
+        # measurement above is round 0, in forward order), so that a drift of
+        # the box over the run shows up as a spread across rounds instead of
+        # as a difference between workloads.
+        import numpy as np
+        recs = {wl.name: out, **{n: out["configs"][n] for n in timers if n != wl.name}}
+        first = {n: r["ms_per_step"] for n, r in recs.items()}
+        rounds = interleaved_rounds(list(recs), timers, {n: (args.steps if n == wl.name else 10) for n in recs},
+                                    ROUNDS)
+        for n, r in recs.items():
+            seq = [first[n]] + rounds[n]
+            r["rounds_ms_per_step"] = seq
+            r["ms_per_step_median_of_rounds"] = float(np.median(seq))
+        timers.clear()
     print(json.dumps(out), flush=True)
 
 

@@ -82,3 +82,16 @@ def test_fp8_matrix_core_forward_counts_one_byte_per_operand_element():
     # down: fp8 weights, fp8 a rows + their scales, bf16 o out
     assert a[bench.K_DOWN] == (H * F * E + N * F + 4 * N + N * H * 2, 2.0 * H * F * N)
 
+
+
+def test_interleaved_rounds_reverse_the_order_every_other_round():
+    """After the first measurement of every workload (forward order), the
+    rounds alternate reversed / forward, and every workload is timed once per
+    round with its own step count."""
+    names = ["a", "b", "c"]
+    assert bench.round_orders(names, 3) == [["c", "b", "a"], ["a", "b", "c"], ["c", "b", "a"]]
+    calls = []
+    timers = {n: (lambda m: (lambda steps: calls.append((m, steps)) or float(len(calls))))(n) for n in names}
+    out = bench.interleaved_rounds(names, timers, {"a": 20, "b": 10, "c": 10}, 2)
+    assert calls == [("c", 10), ("b", 10), ("a", 20), ("a", 20), ("b", 10), ("c", 10)]
+    assert out == {"a": [3.0, 4.0], "b": [2.0, 5.0], "c": [1.0, 6.0]}
