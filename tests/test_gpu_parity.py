@@ -101,6 +101,10 @@ SMALL_BF16 = [
     # E = 256 with a few experts past 64 and 256 rows among many small ones: both dW kernels and every row regime
     W.custom("bf16_e256_mixed", T=800, H=128, F=128, E=256, k=2, dtype="bf16", skew=True, dw=True),
     W.custom("bf16_e1", T=300, H=128, F=128, E=1, k=1, dtype="bf16", skew=False, dw=True),
+    # E = 256 and k = 16 at once, with 20 experts of 256 rows and more (up to
+    # 1023), 33 of 32-255, 203 below 32 (74 empty): every row regime and both
+    # dW kernels on the largest expert count and top-k the library takes
+    W.custom("bf16_e256_k16_big", T=1024, H=128, F=128, E=256, k=16, dtype="bf16", skew=True, dw=True),
 ]
 
 
