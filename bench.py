@@ -505,6 +505,8 @@ def measure(wl, args, steps, warmup, cpu_tokens, cpu_seconds, dist_and_probes=Fa
         del src, dst
     if timers is not None:
         def timer(n):
+            for _ in range(2):  # untimed, as before the first measurement
+                step()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(n):
