@@ -19,6 +19,8 @@ namespace {
 thread_local int64_t g_launches = 0;  // kernel launches made from this thread
 }  // namespace
 void note_launch() { ++g_launches; }
+thread_local LaunchEvents g_launch_events;
+LaunchEvents& launch_events() { return g_launch_events; }
 }  // namespace moe
 
 namespace {
@@ -36,13 +38,20 @@ thread_local hipEvent_t g_dh_ready = nullptr;
 hipError_t record_if(hipEvent_t ev, hipStream_t s) { return ev == nullptr ? hipSuccess : hipEventRecord(ev, s); }
 
 // Runs one kernel launch `f` (returning hipError_t) between the armed events of `kind`.
+// The phase's launches record the events in their own dispatch (MOE_LAUNCH);
+// a phase that launched nothing records both here, an empty interval.
 template <typename Fn>
 hipError_t timed(int kind, hipStream_t s, Fn&& f) {
   Armed& a = g_armed[kind];
   if (a.start == nullptr) return f();
-  hipError_t err = hipEventRecord(a.start, s);
-  if (err == hipSuccess) err = f();
-  if (err == hipSuccess) err = hipEventRecord(a.stop, s);
+  moe::LaunchEvents& ev = moe::launch_events();
+  ev.start = a.start;
+  ev.stop = a.stop;
+  hipError_t err = f();
+  const bool launched = ev.start == nullptr;
+  ev = moe::LaunchEvents{};
+  if (err == hipSuccess && !launched) err = hipEventRecord(a.start, s);
+  if (err == hipSuccess && !launched) err = hipEventRecord(a.stop, s);
   a = Armed{};
   return err;
 }
