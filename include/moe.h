@@ -121,11 +121,14 @@ typedef enum moe_kernel {
 } moe_kernel;
 
 /* Profiling hook.  Arms a one-shot request on the calling thread: the next
- * launch of `kernel` made from this thread records `start_event` on its stream
- * immediately before the launch and `stop_event` immediately after, so
- * hipEventElapsedTime(start, stop) is that kernel's duration.  Both events are
- * hipEvent_t created by the caller; NULL events disarm.  Several kernels may be
- * armed at once.  Results of the calls are unaffected. */
+ * launch of `kernel` made from this thread (one or more kernel dispatches)
+ * carries the events in its own dispatches -- the first dispatch records
+ * `start_event` as it begins, every dispatch records `stop_event` as it ends --
+ * so hipEventElapsedTime(start, stop) is that kernel's duration and no extra
+ * packet is queued between kernels; a launch that dispatches nothing records
+ * both on its stream.  Both events are hipEvent_t created by the caller, with
+ * timing enabled; NULL events disarm.  Several kernels may be armed at once.
+ * Results of the calls are unaffected. */
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event);
 
 /* Fork point between the input gradient and the weight gradients (issue #14,
