@@ -87,6 +87,10 @@ SMALL = [
     W.custom("fp8_e16_k4", T=96, H=384, F=256, E=16, k=4, dtype="bf16", skew=True, dw=False),
     W.custom("fp8_single_token", T=1, H=128, F=128, E=4, k=4, dtype="bf16", skew=False, dw=False),
     W.custom("fp8_big_expert", T=400, H=256, F=128, E=2, k=1, dtype="bf16", skew=True, dw=False),
+    # widths that are multiples of 8 but not of the kernels' column blocks:
+    # partial column blocks and reduction tails with fp8 weights
+    W.custom("fp8_h200_f136", T=300, H=200, F=136, E=8, k=2, dtype="bf16", skew=True, dw=False),
+    W.custom("fp8_h136_f200", T=160, H=136, F=200, E=16, k=4, dtype="bf16", skew=True, dw=False),
 ]
 
 
