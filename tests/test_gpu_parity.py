@@ -105,6 +105,10 @@ SMALL_BF16 = [
     # 1023), 33 of 32-255, 203 below 32 (74 empty): every row regime and both
     # dW kernels on the largest expert count and top-k the library takes
     W.custom("bf16_e256_k16_big", T=1024, H=128, F=128, E=256, k=16, dtype="bf16", skew=True, dw=True),
+    # extreme aspect ratios: reductions of 8192 with few output columns (gate/up
+    # and dA over H = 8192; dX over 2F = 8192), through every row regime and dW
+    W.custom("bf16_h8192_f64", T=600, H=8192, F=64, E=4, k=2, dtype="bf16", skew=True, dw=True),
+    W.custom("bf16_h64_f4096", T=600, H=64, F=4096, E=4, k=2, dtype="bf16", skew=True, dw=True),
 ]
 
 
