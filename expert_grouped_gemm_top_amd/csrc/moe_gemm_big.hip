@@ -266,50 +266,20 @@ __global__ __launch_bounds__(64 * NW, WPC) void big_gemm_bf16_kernel(RowGemmArgs
       for (int i = 0; i < MI; ++i) acc[i][j] = mfma32(fr.b[j], fr.a[i], acc[i][j]);
   };
   // Sub-steps are software-pipelined: the fragments of sub-step t+1 are read
-  // from LDS while the MFMAs of sub-step t run.
-  // bit 0: raise wave priority over the MFMA runs; bit 1: weave fragment reads between MFMAs
-  constexpr int kSched = 3;
-  // one sub-step's MFMAs with the next sub-step's fragment reads woven in
+  // from LDS while the MFMAs of sub-step t run.  One sub-step's MFMAs, with
+  // the next sub-step's fragment reads woven between them one for one, at
+  // raised wave priority.
   auto mfmas_interleaved = [&](const Frags& cur, const unsigned char* st, int next_sub, Frags& nxt) {
-    if (kSched & 1) __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(1);
     if (next_sub >= 0) read_frags(st, next_sub, nxt);
     mfmas(cur);
-    if (kSched & 2) {
 #pragma unroll
-      for (int q = 0; q < MI * NJ; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      }
+    for (int q = 0; q < MI * NJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-    if (kSched & 1) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
-  };
-  auto compute = [&](int s) {
-    const unsigned char* st = s_dyn + (s % STAGES) * STAGE_BYTES;
-    constexpr int SUBS = BK / 16;
-    Frags f0, f1;
-    read_frags(st, 0, f0);
-    if (kSched != 0) {
-#pragma unroll
-      for (int t = 0; t < SUBS; t += 2) {
-        mfmas_interleaved(f0, st, t + 1 < SUBS ? t + 1 : -1, f1);
-        if (t + 1 < SUBS) mfmas_interleaved(f1, st, t + 2 < SUBS ? t + 2 : -1, f0);
-      }
-      return;
-    }
-#pragma unroll
-    for (int t = 0; t < SUBS; t += 2) {
-      if (t + 1 < SUBS) read_frags(st, t + 1, f1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(f0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < SUBS) {
-        if (t + 2 < SUBS) read_frags(st, t + 2, f0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(f1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
   };
 
   const int steps = (K + BK - 1) / BK;
