@@ -464,9 +464,7 @@ int moe_quantize_rows_fp8(int rows, int cols, const void* x, uint8_t* q, float* 
   REQUIRE((uintptr_t)x % 16 == 0 && (uintptr_t)q % 8 == 0, MOE_ERR_INVALID_ARGUMENT,
           "%s: x must be 16-byte and q 8-byte aligned", fn);
   REQUIRE((int64_t)rows * cols < ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "%s: matrix too large", fn);
-  return hip_status(moe::launch_quantize_fp8(rows, cols, 0, (const uint16_t*)x, nullptr, q, nullptr, scale,
-                                             as_stream(stream)),
-                    fn);
+  return hip_status(moe::launch_quantize_rows_fp8(rows, cols, (const uint16_t*)x, q, scale, as_stream(stream)), fn);
 }
 
 int moe_transpose_fp8(int E, int rows, int cols, const uint8_t* in, uint8_t* out, void* stream) {
@@ -529,7 +527,7 @@ int moe_grouped_swiglu_fwd_fp8(int H, int F, int E, int k, int max_rows, const i
                        fn)))
     return rc;
   // the stored SwiGLU output, one power-of-two scale per row, for the down product
-  if ((rc = hip_status(moe::launch_quantize_fp8(max_rows, F, 0, (const uint16_t*)a_save, nullptr, aq, nullptr, a_scale, s),
+  if ((rc = hip_status(moe::launch_quantize_rows_fp8(max_rows, F, (const uint16_t*)a_save, aq, a_scale, s),
                        fn)))
     return rc;
   g.a = aq;

@@ -1,4 +1,5 @@
-// moe_fp8.hip -- one-time fp8 storage of frozen expert weights.
+// moe_fp8.hip -- one-time fp8 storage of frozen expert weights, and the
+// per-row quantization of activation rows for the fp8 matrix-core forward.
 //
 // In the LoRA step the experts are frozen (npu-train issue #14, section Scope)
 // and their weights stay resident on the device (issue #14, section Proposal),
@@ -107,7 +108,59 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(int64_t n0, int64_t n
   if (a1) chunk_quantize(a1, (u32x2*)(q1 + (size_t)e * n1), n1 / 8, k);
 }
 
+// Activation rows (token rows, SwiGLU outputs): one wave per row, each row
+// its own "expert" of the rule above.  A row is read twice, for its max and
+// then to encode it (the second read hits the cache); no barriers, so rows of
+// a few thousand elements do not leave the CU waiting on workgroup
+// synchronization.
+constexpr int kRowsPerBlock = 4;
+
+__global__ __launch_bounds__(64 * kRowsPerBlock) void quantize_rows_fp8_kernel(int64_t rows, int64_t cols,
+                                                                            const uint16_t* __restrict__ x,
+                                                                            uint8_t* __restrict__ q,
+                                                                            float* __restrict__ scale) {
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= rows) return;  // wave-uniform
+  const int l = threadIdx.x & 63;
+  const int64_t chunks = cols / 8;
+  const u32x4* src = (const u32x4*)(x + r * cols);
+  float m = 0.0f;
+  for (int64_t i = l; i < chunks; i += kWave) {
+    const u32x4 v = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(__builtin_fabsf(bf_to_f(v[j] & 0xffffu)), __builtin_fabsf(bf_to_f(v[j] >> 16))));
+  }
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  const int k = fp8_scale_exp(m);
+  if (l == 0) scale[r] = __builtin_ldexpf(1.0f, k);
+  u32x2* dst = (u32x2*)(q + r * cols);
+  for (int64_t i = l; i < chunks; i += kWave) {
+    const u32x4 v = src[i];
+    u32x2 out;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t h = (b & 1) ? (v[2 * j + (b >> 1)] >> 16) : (v[2 * j + (b >> 1)] & 0xffffu);
+        word |= e4m3_encode(__builtin_ldexpf(bf_to_f(h), -k)) << (8 * b);
+      }
+      out[j] = word;
+    }
+    dst[i] = out;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_rows_fp8(int64_t rows, int64_t cols, const uint16_t* x, uint8_t* q, float* scale,
+                                    hipStream_t stream) {
+  const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks <= 0) return hipSuccess;
+  MOE_LAUNCH(quantize_rows_fp8_kernel, dim3((unsigned)blocks), dim3(64 * kRowsPerBlock), 0, stream, rows, cols, x, q,
+             scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8(int E, int64_t n0, int64_t n1, const uint16_t* w0, const uint16_t* w1, uint8_t* q0,
                                uint8_t* q1, float* scale, hipStream_t stream) {

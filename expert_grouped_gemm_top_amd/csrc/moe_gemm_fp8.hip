@@ -201,22 +201,30 @@ __global__ __launch_bounds__(64 * kF8Waves, 1) void big_gemm_fp8_kernel(Fp8GemmA
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto compute = [&](int s) {
-    const unsigned char* st = s_dyn + (s % kF8Stages) * kF8StageBytes;
-    Frags f0, f1;
-    read_frags(st, 0, f0);
-    mfmas_interleaved(f0, st, 1, f1);
-    mfmas_interleaved(f1, st, -1, f0);
-  };
-
   const int steps = (K + kF8BK - 1) / kF8BK;
+  static_assert(kF8Stages == 2 && kF8BK == 128, "two stage buffers of two sub-steps");
+  // Stage handoff before the last sub-step: stage s is waited for and the
+  // workgroup synchronized while stage s - 1's last fragments are in
+  // registers, so stage s's first fragments are read under stage s - 1's last
+  // MFMAs (no fragment-read bubble at stage starts).  After that barrier every
+  // wave is done reading stage s - 1's buffer, which then takes stage s + 1.
   issue(0);
-  for (int s = 0; s < steps; ++s) {
-    wait_vmcnt<0>();  // stage s has landed (it is the only one in flight)
-    barrier_no_fence();  // ... for every wave, and every wave is done with stage s - 1's buffer
+  wait_vmcnt<0>();
+  barrier_no_fence();
+  if (steps > 1) issue(1);
+  Frags f0, f1;
+  read_frags(s_dyn, 0, f0);
+  mfmas_interleaved(f0, s_dyn, 1, f1);
+  for (int s = 1; s < steps; ++s) {
+    const unsigned char* st = s_dyn + (s & 1) * kF8StageBytes;
+    wait_vmcnt<0>();                      // stage s has landed (the only loads in flight)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s - 1 are done
+    barrier_no_fence();                   // ... and every wave's: its buffer can take stage s + 1
     if (s + 1 < steps) issue(s + 1);
-    compute(s);
+    mfmas_interleaved(f1, st, 0, f0);     // stage s - 1's last sub-step, stage s's first fragments
+    mfmas_interleaved(f0, st, 1, f1);
   }
+  mfmas_interleaved(f1, s_dyn, -1, f0);
 
   // ---- epilogue: acc[i][j] register r -> activation row TM wm + 32 i + l32,
   // virtual column TN wn + 32 j + 8 q + 4 hk + (0..3), q = r / 4; scaled by

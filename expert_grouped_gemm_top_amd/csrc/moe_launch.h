@@ -184,6 +184,10 @@ hipError_t launch_dw_bf16(const DwArgs& g, hipStream_t stream);
 // Row GEMMs with fp8 (E4M3) weights and bf16 activations: every expert, whatever
 // its row count, on the streaming kernel.
 hipError_t launch_row_gemm_fp8w(int mode, const RowGemmArgs& g, int max_rows, hipStream_t stream);
+// E4M3 codes of `rows` rows of `cols` bf16 values, one power-of-two scale per
+// row (moe_fp8.hip).
+hipError_t launch_quantize_rows_fp8(int64_t rows, int64_t cols, const uint16_t* x, uint8_t* q, float* scale,
+                                    hipStream_t stream);
 // Per-expert fp8 storage of w0 [E][n0] and w1 [E][n1] (w1 may be NULL) with one
 // power-of-two scale per expert.
 hipError_t launch_quantize_fp8(int E, int64_t n0, int64_t n1, const uint16_t* w0, const uint16_t* w1, uint8_t* q0,

@@ -356,7 +356,7 @@ int moe_grouped_bwd_dx_fp8w(int T, int H, int F, int E, int k, int max_rows, con
  * aligned; cols a multiple of 8): q [rows, cols] E4M3 codes (device, 8-byte
  * aligned, out) and scale [rows] fp32 (device, out), the smallest power of two
  * s with max_j |x[r,j]| <= 448 s, codes E4M3(x / s) rounded to nearest even,
- * saturating.  One workgroup per row. */
+ * saturating.  One wave per row. */
 int moe_quantize_rows_fp8(int rows, int cols, const void* x, uint8_t* q, float* scale, void* stream);
 
 /* out[e][c][r] = in[e][r][c] for E matrices of rows x cols bytes (device,

@@ -28,13 +28,16 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-2
 
 
-def test_quantize_rows_matches_the_oracle_bitwise():
-    rng = np.random.default_rng(21)
-    rows, cols = 300, 208
+# one wave per row: rows not a multiple of the four per workgroup, rows of
+# fewer than 64 chunks, of several chunks per lane and of a ragged last pass
+@pytest.mark.parametrize("rows,cols", [(300, 208), (7, 4096), (5, 1416), (1, 8), (3, 12296)])
+def test_quantize_rows_matches_the_oracle_bitwise(rows, cols):
+    rng = np.random.default_rng(21 + cols)
     x = (rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-20, 12, size=(rows, 1)))).astype(np.float32)
     x[0] = 0.0
-    x[1, :6] = [448.0, -448.0, 1.0625, 1.1875, -0.0, 2.0 ** -10]
-    x[2] *= 2.0 ** -100
+    if rows > 2:
+        x[1, :6] = [448.0, -448.0, 1.0625, 1.1875, -0.0, 2.0 ** -10]
+        x[2] *= 2.0 ** -100
     x = W.round_bf16(x)
     q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
     s = torch.empty(rows, dtype=torch.float32, device="cuda")
