@@ -54,7 +54,35 @@ __device__ __forceinline__ f32x16 mfma_fp8(const u32x4 (&first)[2], const u32x4 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
 }
 
-template <int MODE>
+// 16 B from sbase + voff straight into LDS at lds_base + 16 * lane: the
+// 64-bit base in scalar registers (wave-uniform), a 32-bit offset per lane,
+// which holds one vector register per load address instead of two.
+__device__ __forceinline__ void g2lds_off(const void* sbase, uint32_t voff, void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+// wave-uniform pointer held in scalar registers
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// OFF32: whole-tile shapes (the reduction a multiple of kF8BK, the output
+// width one of kF8BN: no chunk past an edge) whose operands lie within 4 GiB
+// of their base (activation codes, and one expert's weight matrix): loads
+// address by base + 32-bit offset, and the next stage's loads go out in two
+// halves, A before the stage's first MFMA run and B before its second.
+template <int MODE, bool OFF32>
 __global__ __launch_bounds__(64 * kF8Waves, 1) void big_gemm_fp8_kernel(Fp8GemmArgs g) {
   static_assert(MODE == kGemmGateUp || MODE == kGemmDown, "forward products only");
   __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
@@ -137,20 +165,51 @@ __global__ __launch_bounds__(64 * kF8Waves, 1) void big_gemm_fp8_kernel(Fp8GemmA
     b_k[i] = 16 * c;
     b_src[i] = Wt + (size_t)(b_ok[i] ? n : 0) * K + 16 * c;
   }
-  auto issue = [&](int s) {
+  // OFF32 addressing: bases in scalar registers, offsets per lane
+  // B instructions i and i + 2 read the same chunk position of weight rows
+  // b_step bytes apart (8 features on for gate/up, 16 output columns for down),
+  // so two offsets per lane serve all four.
+  static_assert(kF8BIns == 4, "B offsets: instructions 0, 1 and their successors two on");
+  uint32_t a_off[kF8AIns], b_off[2];
+  const uint32_t b_step = (uint32_t)K * (MODE == kGemmGateUp ? 8u : 16u);
+  const uint8_t* a_base = uniform_ptr(g.a);
+  const uint8_t* b_base0 = uniform_ptr(g.w0 + (size_t)e * F * H);
+  const uint8_t* b_base1 = uniform_ptr((MODE == kGemmGateUp ? g.w1 : g.w0) + (size_t)e * F * H);
+  if constexpr (OFF32) {
+#pragma unroll
+    for (int i = 0; i < kF8AIns; ++i) a_off[i] = (uint32_t)(a_src[i] - g.a);
+    // gate/up: instruction i reads W_up when i is odd (its 8-row chunk index 4 w + i)
+    b_off[0] = (uint32_t)(b_src[0] - b_base0);
+    b_off[1] = (uint32_t)(b_src[1] - (MODE == kGemmGateUp ? b_base1 : b_base0));
+  }
+  auto issue_a = [&](int s) {
     unsigned char* st = s_dyn + (s % kF8Stages) * kF8StageBytes;
     const int k0 = s * kF8BK;
 #pragma unroll
     for (int i = 0; i < kF8AIns; ++i) {
-      const void* src = k0 + a_k[i] < K ? (const void*)(a_src[i] + k0) : (const void*)zero_chunk();
-      g2lds(src, st + 1024 * (kF8AIns * w + i));
-    }
-#pragma unroll
-    for (int i = 0; i < kF8BIns; ++i) {
-      const void* src = (b_ok[i] && k0 + b_k[i] < K) ? (const void*)(b_src[i] + k0) : (const void*)zero_chunk();
-      g2lds(src, st + kF8ABytes + 1024 * (kF8BIns * w + i));
+      if constexpr (OFF32) {
+        g2lds_off(a_base, a_off[i] + (uint32_t)k0, st + 1024 * (kF8AIns * w + i));
+      } else {
+        const void* src = k0 + a_k[i] < K ? (const void*)(a_src[i] + k0) : (const void*)zero_chunk();
+        g2lds(src, st + 1024 * (kF8AIns * w + i));
+      }
     }
   };
+  auto issue_b = [&](int s) {
+    unsigned char* st = s_dyn + (s % kF8Stages) * kF8StageBytes;
+    const int k0 = s * kF8BK;
+#pragma unroll
+    for (int i = 0; i < kF8BIns; ++i) {
+      if constexpr (OFF32) {
+        g2lds_off((MODE == kGemmGateUp && (i & 1)) ? b_base1 : b_base0,
+                  b_off[i & 1] + (i >> 1) * b_step + (uint32_t)k0, st + kF8ABytes + 1024 * (kF8BIns * w + i));
+      } else {
+        const void* src = (b_ok[i] && k0 + b_k[i] < K) ? (const void*)(b_src[i] + k0) : (const void*)zero_chunk();
+        g2lds(src, st + kF8ABytes + 1024 * (kF8BIns * w + i));
+      }
+    }
+  };
+  auto issue = [&](int s) { issue_a(s); issue_b(s); };
 
   f32x16 acc[kF8MI][kF8NJ];
 #pragma unroll
@@ -215,14 +274,37 @@ __global__ __launch_bounds__(64 * kF8Waves, 1) void big_gemm_fp8_kernel(Fp8GemmA
   Frags f0, f1;
   read_frags(s_dyn, 0, f0);
   mfmas_interleaved(f0, s_dyn, 1, f1);
-  for (int s = 1; s < steps; ++s) {
-    const unsigned char* st = s_dyn + (s & 1) * kF8StageBytes;
+  auto stage_sync = [&] {
     wait_vmcnt<0>();                      // stage s has landed (the only loads in flight)
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s - 1 are done
     barrier_no_fence();                   // ... and every wave's: its buffer can take stage s + 1
-    if (s + 1 < steps) issue(s + 1);
-    mfmas_interleaved(f1, st, 0, f0);     // stage s - 1's last sub-step, stage s's first fragments
-    mfmas_interleaved(f0, st, 1, f1);
+  };
+  if constexpr (OFF32) {
+    // stages 1 .. steps - 2 load the next stage in two halves; the last one
+    // loads nothing (peeled, so the loop body has no branch the scheduler
+    // would not move MFMAs across)
+    for (int s = 1; s < steps - 1; ++s) {
+      const unsigned char* st = s_dyn + (s & 1) * kF8StageBytes;
+      stage_sync();
+      issue_a(s + 1);
+      mfmas_interleaved(f1, st, 0, f0);   // stage s - 1's last sub-step, stage s's first fragments
+      issue_b(s + 1);
+      mfmas_interleaved(f0, st, 1, f1);
+    }
+    if (steps > 1) {
+      const unsigned char* st = s_dyn + ((steps - 1) & 1) * kF8StageBytes;
+      stage_sync();
+      mfmas_interleaved(f1, st, 0, f0);
+      mfmas_interleaved(f0, st, 1, f1);
+    }
+  } else {
+    for (int s = 1; s < steps; ++s) {
+      const unsigned char* st = s_dyn + (s & 1) * kF8StageBytes;
+      stage_sync();
+      if (s + 1 < steps) issue(s + 1);
+      mfmas_interleaved(f1, st, 0, f0);   // stage s - 1's last sub-step, stage s's first fragments
+      mfmas_interleaved(f0, st, 1, f1);
+    }
   }
   mfmas_interleaved(f1, s_dyn, -1, f0);
 
@@ -337,9 +419,18 @@ hipError_t launch_fp8_mode(const Fp8GemmArgs& g, int max_rows, hipStream_t strea
   const int64_t wgs = ((tiles * ((ncols + kF8BN - 1) / kF8BN) + 7) / 8) * 8;
   if (wgs <= 0) return hipSuccess;
   const size_t lds = (size_t)kF8Stages * kF8StageBytes;
-  auto kern = big_gemm_fp8_kernel<MODE>;
-  static PerDeviceOnce lds_once;
-  hipError_t err = allow_dynamic_lds(lds_once, (const void*)kern, lds);
+  const int64_t K = MODE == kGemmGateUp ? g.H : g.F;
+  // whole tiles, and every operand byte within 4 GiB of its base: the rows of
+  // a (at most max_rows of them, gathered or not) and one expert's weights
+  // (the down product only: gate/up measured no faster with the split issue)
+  const bool off32 = MODE == kGemmDown && K % kF8BK == 0 && ncols % kF8BN == 0 && N * K < ((int64_t)1 << 32) &&
+                     (int64_t)g.H * g.F < ((int64_t)1 << 32);
+  auto kern = big_gemm_fp8_kernel<MODE, false>;
+  if constexpr (MODE == kGemmDown) {
+    if (off32) kern = big_gemm_fp8_kernel<MODE, true>;
+  }
+  static PerDeviceOnce lds_once[2];
+  hipError_t err = allow_dynamic_lds(lds_once[off32 ? 1 : 0], (const void*)kern, lds);
   if (err != hipSuccess) return err;
   MOE_LAUNCH(kern, dim3((unsigned)wgs), dim3(64 * kF8Waves), lds, stream, g);
   return hipGetLastError();
