@@ -182,22 +182,49 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(int64_t N, int E, co
   }
 }
 
-// One block per token (grid-stride): 16-byte chunks of the row; every chunk of
-// x[t] is read once and written to the k sorted positions of the token's pairs.
+// Row copy x_sorted[inv_perm[t k + j]] = x[t].  Work item = (token, run of
+// 256 16-byte chunks of its row); workgroups take items in a grid-stride loop
+// and load the next item's chunk and destinations before storing the current
+// one, so each lane has a load in flight while it stores (a workgroup per
+// token left every lane waiting one memory latency before its stores).  Every
+// chunk of x[t] is read once and written to the k sorted positions of the
+// token's pairs.
+constexpr int kRowCopyBlocks = 16384;  // workgroups of the row copy at most
+
 __global__ __launch_bounds__(256) void dispatch_rows_kernel(int T, int k, int row_chunks, const u32x4* __restrict__ x,
                                                             const int32_t* __restrict__ inv_perm,
                                                             u32x4* __restrict__ x_sorted) {
-  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+  const int groups = (row_chunks + 255) / 256;
+  const int64_t items = (int64_t)T * groups;
+  int64_t i = blockIdx.x;
+  if (i >= items) return;
+  struct Item {
+    int64_t t;
+    int c;
+    u32x4 v;
     int dst[kMaxTopK];
+  };
+  auto fetch = [&](int64_t it, Item& d) {
+    d.t = it / groups;
+    d.c = (int)(it - d.t * groups) * 256 + (int)threadIdx.x;
+    // x is read once here (the GEMMs read x_sorted): non-temporal
+    if (d.c < row_chunks) d.v = __builtin_nontemporal_load(x + d.t * row_chunks + d.c);
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) dst[j] = (j < k) ? inv_perm[(size_t)t * k + j] : -1;
-    for (int c = threadIdx.x; c < row_chunks; c += 256) {
-      // x is read once here (the GEMMs read x_sorted): non-temporal
-      const u32x4 v = __builtin_nontemporal_load(x + (size_t)t * row_chunks + c);
+    for (int j = 0; j < kMaxTopK; ++j) d.dst[j] = (j < k) ? inv_perm[d.t * k + j] : -1;
+  };
+  Item cur, nxt;
+  fetch(i, cur);
+  for (;;) {
+    const int64_t in = i + gridDim.x;
+    if (in < items) fetch(in, nxt);
+    if (cur.c < row_chunks) {
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j)
-        if (j < k && dst[j] >= 0) x_sorted[(size_t)dst[j] * row_chunks + c] = v;
+        if (j < k && cur.dst[j] >= 0) x_sorted[(size_t)cur.dst[j] * row_chunks + cur.c] = cur.v;
     }
+    if (in >= items) break;
+    i = in;
+    cur = nxt;
   }
 }
 
@@ -261,7 +288,10 @@ hipError_t launch_dispatch_index(int T, int E, int k, const int32_t* idx, int32_
 hipError_t launch_dispatch_rows(int T, int H, int k, int esize, const void* x, const int32_t* inv_perm, void* x_sorted,
                                 hipStream_t stream) {
   const int row_chunks = (int)((int64_t)H * esize / 16);
-  const int grid = T < 16384 ? T : 16384;
+  const int64_t items = (int64_t)T * ((row_chunks + 255) / 256);
+  const int64_t want = (items + 1) / 2;  // two items per workgroup: one load in flight under the other's stores
+  const int grid = (int)(want < kRowCopyBlocks ? want : kRowCopyBlocks);
+  if (grid <= 0) return hipSuccess;
   MOE_LAUNCH(dispatch_rows_kernel, dim3(grid), dim3(256), 0, stream, T, k, row_chunks, (const u32x4*)x,
                      inv_perm, (u32x4*)x_sorted);
   return hipGetLastError();
