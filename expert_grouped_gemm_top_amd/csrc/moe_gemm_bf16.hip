@@ -154,6 +154,15 @@ __host__ __device__ inline int row_gemm_blocks(int H, int F) {
                              : (MODE == kGemmDown ? (H + 127) / 128 : (MODE == kGemmDA ? (F + 63) / 64 : (H + 63) / 64));
 }
 
+// Column blocks of the streaming kernel.  With fp8 weights the gate/up wave
+// covers 128 features of both matrices (its loads then read 128-byte runs of
+// each weight row; 64 features per wave left 64-byte runs, which read
+// memory at 4.5 TB/s where 128-byte runs read 6.2).
+template <int MODE, bool W8>
+__host__ __device__ inline int stream_blocks(int H, int F) {
+  return (W8 && MODE == kGemmGateUp) ? (F + 127) / 128 : row_gemm_blocks<MODE>(H, F);
+}
+
 // Output columns of a row GEMM (gate/up: features, each a gate and an up column).
 template <int MODE>
 __host__ __device__ inline int row_gemm_cols(int H, int F) {
@@ -181,7 +190,10 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   build_tile_starts(g.offsets, g.E, kTileRows, s_start, s_off, s_tmp, 0, W8 ? kNoBigTiles : kBigRows);
 
   const int H = g.H, F = g.F;
-  const int nblk = row_gemm_blocks<MODE>(H, F);
+  // fp8 gate/up: a wave takes 128 features, MFMAs 0..7 on W_gate, 8..15 on W_up
+  constexpr bool WIDE = W8 && MODE == kGemmGateUp;
+  constexpr int NACC = WIDE ? 16 : (NN ? 8 : 4);  // accumulators in use
+  const int nblk = stream_blocks<MODE, W8>(H, F);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
   const int ks = g.stream_ksplit;  // 1, 2 or 4
   const bool split = ks > 1;
@@ -207,12 +219,61 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   // rows past the tile read the tile's last row (always valid) and are zeroed at use
   const uint16_t* a_row = A + a_row_of(g, ts.row_begin + (a_ok ? c : ts.rows - 1)) * K + k_begin;
 
-  f32x4 acc[8];
+  f32x4 acc[WIDE ? 16 : 8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < (WIDE ? 16 : 8); ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  if constexpr (NN) {
+  if constexpr (WIDE) {
+    // lane c reads 8 features f = 128 nb + 8 c of W_gate and of W_up at rows
+    // k0 + 8 gq + (0..7): 16 lanes read 128 contiguous bytes of one weight row
+    // (features past the edge read feature 0: never stored)
+    const int f = nb * 128 + 8 * c;
+    const size_t wofs = (size_t)e * H * F + (f < F ? f : 0) + (size_t)k_begin * F;
+    const WE* g_first = (const WE*)g.w0 + wofs;
+    const WE* u_first = (const WE*)g.w1 + wofs;
+    const uint16_t* a_ptr = a_row + 8 * gq;
+    const int steps = (Kp + 31) / 32, last = steps - 1;
+    auto load = [&](int s, WV* bq, u32x4& aq) {
+      const bool kin = s * 32 + 8 * gq < Kp;
+      const size_t ofs = kin ? (size_t)(s * 32 + 8 * gq) * F : 0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        bq[r] = load_weights<NONTEMP>((const WV*)(g_first + ofs + (size_t)r * F));
+        bq[8 + r] = load_weights<NONTEMP>((const WV*)(u_first + ofs + (size_t)r * F));
+      }
+      aq = *(const u32x4*)(kin ? a_ptr + (size_t)s * 32 : zero_chunk());
+    };
+    auto compute = [&](const WV* bq, const u32x4& aq) {
+      const u32x4 av = a_ok ? aq : zero4;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        u32x4 bw[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) bw[r] = WF::widen(bq[8 * m + r]);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc[8 * m + jj] = mfma_bf16(column_of_8x8(bw, jj), av, acc[8 * m + jj]);
+      }
+    };
+    WV b0[16], b1[16], b2[16];
+    u32x4 a0, a1, a2;
+    load(0, b0, a0);
+    load(min(1, last), b1, a1);
+    for (int s = 0; s < steps; s += 3) {
+      load(min(s + 2, last), b2, a2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(s + 3, last), b0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < steps) compute(b1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(s + 4, last), b1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 2 < steps) compute(b2, a2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if constexpr (NN) {
     // B operand: lane c reads columns [col, col+8) of rows k0 + 8gq + (0..7)
     // (columns past the output edge read column 0: never stored)
     const WE* b_ptr;
@@ -358,9 +419,9 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   if (split) {
     // parts 1.. -> each into its own wave's LDS area (for K-contiguous weights
     // the one only it has used for its stages); part 0 adds them in part order
-    constexpr int NACC = NN ? 8 : 4;
     // a wave's partials go to its own area: 8 KiB (N-contiguous weights use no
-    // other LDS here) or the 16 KiB of its K-contiguous stages
+    // other LDS here; 16 KiB for the fp8 gate/up wave) or the 16 KiB of its
+    // K-contiguous stages
     constexpr int kRedBytes = NN ? NACC * kWave * 16 : 16384;
     if (kpart > 0) {
       f32x4* red = reinterpret_cast<f32x4*>(lds + w * kRedBytes);
@@ -377,7 +438,6 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   }
 
   if constexpr (W8) {  // the weights' scale: a power of two, so the product is exact
-    constexpr int NACC = NN ? 8 : 4;
     const float sc = g.wscale[e];
 #pragma unroll
     for (int j = 0; j < NACC; ++j) acc[j] = acc[j] * sc;
@@ -386,7 +446,31 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   // epilogue straight from registers: lane (c, gq) owns tile row c
   if (!a_ok) return;
   const size_t grow = (size_t)ts.row_begin + c;
-  if (MODE == kGemmGateUp) {
+  if constexpr (WIDE) {
+    // MFMA jj (W_gate) and 8 + jj (W_up), register r: feature
+    // f = 128 nb + 32 gq + 8 r + jj
+    uint16_t* hrow = g.out0 + grow * 2 * F;
+    uint16_t* arow = g.out1 + grow * F;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int f = nb * 128 + 32 * gq + 8 * r;
+      if (f >= F) break;  // features past the edge
+      float G[8], U[8], V[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        G[jj] = acc[jj][r];
+        U[jj] = acc[8 + jj][r];
+        V[jj] = G[jj] * sigmoidf_fast(G[jj]) * U[jj];
+      }
+      if (g.out0 != nullptr) {
+        *(u32x4*)(hrow + f) = u32x4{pack_bf2(G[0], G[1]), pack_bf2(G[2], G[3]), pack_bf2(G[4], G[5]), pack_bf2(G[6], G[7])};
+        *(u32x4*)(hrow + F + f) =
+            u32x4{pack_bf2(U[0], U[1]), pack_bf2(U[2], U[3]), pack_bf2(U[4], U[5]), pack_bf2(U[6], U[7])};
+      }
+      if (g.out1 != nullptr)
+        *(u32x4*)(arow + f) = u32x4{pack_bf2(V[0], V[1]), pack_bf2(V[2], V[3]), pack_bf2(V[4], V[5]), pack_bf2(V[6], V[7])};
+    }
+  } else if (MODE == kGemmGateUp) {
     // MFMA jj, register r: gate (r even) / up (r odd) of feature
     // f = 64 nb + 16 gq + 8 (r >> 1) + jj
     float hg[16], hu[16], av[16];
@@ -757,26 +841,27 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, in
 }
 
 // fp8 weights: every expert on the streaming kernel (one wave per 16-row tile
-// and column block), so weight bytes are read once per 16 rows.  Gate/up and
-// down need only 8 KiB of LDS per wave (split partial sums), which lets more
-// workgroups share a CU (gate/up: four waves per SIMD instead of two).
+// and column block), so weight bytes are read once per 16 rows.  Down needs
+// only 8 KiB of LDS per wave (split partial sums), which lets more workgroups
+// share a CU.
 template <int MODE, bool NONTEMP>
 __global__ __launch_bounds__(256, 2) void row_gemm_fp8w_kernel(RowGemmArgs g) {
   __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
-  // per wave: 8 KiB of split partial sums (N-contiguous) or 16 KiB of stages
-  __shared__ __attribute__((aligned(16))) unsigned char s_lds[RowGemmShape<MODE>::kNN ? 4 * 8192 : 4 * 16384];
+  // per wave: 8 KiB of split partial sums (down), 16 KiB (gate/up: twice the
+  // columns) or 16 KiB of stages (K-contiguous weights)
+  __shared__ __attribute__((aligned(16))) unsigned char s_lds[MODE == kGemmDown ? 4 * 8192 : 4 * 16384];
   stream_gemm<MODE, true, NONTEMP>(g, blockIdx.x, s_start, s_off, s_tmp, s_lds);
 }
 
 // Reduction split of the streaming kernel for this product and row count.
-template <int MODE>
+template <int MODE, bool W8>
 int stream_split(const RowGemmArgs& g, int64_t N) {
   const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? g.H : (MODE == kGemmDown ? g.F : 2 * g.F);
   const int kstep = RowGemmShape<MODE>::kNN ? 32 : 128;  // whole K-steps in each part
   // decode-sized batches (a handful of rows in all) have too few tiles to keep
   // the chip's memory busy: split every product four ways
   int ks = N < kFewRows ? 4 : (kStreamSplitK >> (4 * MODE)) & 0xf;
-  while (ks > 1 && (K % (ks * kstep) != 0 || row_gemm_blocks<MODE>(g.H, g.F) % (4 / ks) != 0)) ks /= 2;
+  while (ks > 1 && (K % (ks * kstep) != 0 || stream_blocks<MODE, W8>(g.H, g.F) % (4 / ks) != 0)) ks /= 2;
   return ks;
 }
 
@@ -788,8 +873,8 @@ hipError_t launch_row_gemm_fp8w_mode(const RowGemmArgs& args, int max_rows, hipS
   g.big_min_rows = kNoBigTiles;
   const int64_t N = max_rows, E = g.E;
   const int64_t tiles = (N + E * (kTileRows - 1)) / kTileRows;
-  g.stream_ksplit = stream_split<MODE>(g, N);
-  const int64_t grid = (tiles * row_gemm_blocks<MODE>(g.H, g.F) * g.stream_ksplit + 3) / 4;
+  g.stream_ksplit = stream_split<MODE, true>(g, N);
+  const int64_t grid = (tiles * stream_blocks<MODE, true>(g.H, g.F) * g.stream_ksplit + 3) / 4;
   if (grid <= 0) return hipSuccess;
   auto kern = N >= kFewRows ? row_gemm_fp8w_kernel<MODE, true> : row_gemm_fp8w_kernel<MODE, false>;
   MOE_LAUNCH(kern, dim3((unsigned)grid), dim3(256), 0, stream, g);
@@ -814,7 +899,7 @@ hipError_t launch_row_gemm_mode(const RowGemmArgs& args, int max_rows, int max_e
   // streaming kernel: experts with n_e < kBigRows, ceil(n_e / 16) tiles each
   const int64_t small_tiles = std::min<int64_t>((N + E * (kTileRows - 1)) / kTileRows,
                                                  E * ((kBigRows - 1 + kTileRows - 1) / kTileRows));
-  g.stream_ksplit = stream_split<MODE>(g, N);
+  g.stream_ksplit = stream_split<MODE, false>(g, N);
   const int64_t n_stream = (small_tiles * row_gemm_blocks<MODE>(g.H, g.F) * g.stream_ksplit + 3) / 4;
   // tiled kernel: experts with kBigRows <= n_e < g.big_min_rows, ceil(n_e / 128) tiles each
   const int64_t big_experts = std::min<int64_t>(E, N / kBigRows);
