@@ -91,6 +91,9 @@ SMALL = [
     # partial column blocks and reduction tails with fp8 weights
     W.custom("fp8_h200_f136", T=300, H=200, F=136, E=8, k=2, dtype="bf16", skew=True, dw=False),
     W.custom("fp8_h136_f200", T=160, H=136, F=200, E=16, k=4, dtype="bf16", skew=True, dw=False),
+    # fewer features than one gate/up column block of 128 (one partial block)
+    W.custom("fp8_h64_f40", T=120, H=64, F=40, E=4, k=2, dtype="bf16", skew=True, dw=False),
+    W.custom("fp8_h104_f72", T=200, H=104, F=72, E=8, k=2, dtype="bf16", skew=True, dw=False),
 ]
 
 
