@@ -169,6 +169,69 @@ __host__ __device__ inline int row_gemm_cols(int H, int F) {
   return (MODE == kGemmGateUp || MODE == kGemmDA) ? F : H;
 }
 
+// Per-wave tile schedule of the streaming kernel: the same tile prefix as
+// build_tile_starts / lookup_tile (experts with min_rows <= n_e < max_rows,
+// ceil(n_e / tile_rows) tiles each, in expert order), derived by every wave
+// on its own from offsets[0..E] with a wave scan and a ballot: no LDS and no
+// workgroup barrier before the first weight loads.  Lane l covers experts
+// 4 l .. 4 l + 3 (E <= 256).
+struct WaveTiles {
+  int off[5];   // offsets[4 l .. 4 l + 4], clamped at E
+  int cnt[4];   // tiles of those experts
+  int excl;     // tiles of the experts before 4 l
+  int total;    // tiles of all experts
+};
+
+__device__ __forceinline__ WaveTiles wave_tile_prefix(const int32_t* __restrict__ offsets, int E, int tile_rows,
+                                                      int min_rows, int max_rows) {
+  WaveTiles t;
+  const int l = __lane_id();
+#pragma unroll
+  for (int i = 0; i < 5; ++i) t.off[i] = offsets[min(4 * l + i, E)];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = t.off[i + 1] - t.off[i];  // 0 past E (both ends clamped)
+    t.cnt[i] = (n >= min_rows && n < max_rows) ? (n + tile_rows - 1) / tile_rows : 0;
+    sum += t.cnt[i];
+  }
+  const int inc = wave_inclusive_scan(sum);
+  t.excl = inc - sum;
+  t.total = __shfl(inc, kWave - 1, kWave);
+  return t;
+}
+
+// The slot of a wave-uniform tile id (expert -1 past the last tile).
+__device__ __forceinline__ TileSlot wave_lookup_tile(const WaveTiles& t, int tile_rows, int tile_id) {
+  TileSlot s;
+  const int l = __lane_id();
+  int start = t.excl, ex = -1, tl = 0, rb = 0, nr = 0, ne = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (tile_id >= start && tile_id < start + t.cnt[i]) {
+      ex = 4 * l + i;
+      tl = tile_id - start;
+      ne = t.off[i + 1] - t.off[i];
+      rb = t.off[i] + tl * tile_rows;
+      nr = min(t.off[i + 1] - rb, tile_rows);
+    }
+    start += t.cnt[i];
+  }
+  const uint64_t hit = __ballot(ex >= 0);
+  if (hit == 0) {
+    s.expert = -1;
+    s.tile = s.row_begin = s.rows = s.expert_rows = 0;
+    return s;
+  }
+  const int src = __ffsll((unsigned long long)hit) - 1;  // the one lane whose range holds tile_id
+  s.expert = __shfl(ex, src, kWave);
+  s.tile = __shfl(tl, src, kWave);
+  s.row_begin = __shfl(rb, src, kWave);
+  s.rows = __shfl(nr, src, kWave);
+  s.expert_rows = __shfl(ne, src, kWave);
+  return s;
+}
+
 //
 // With a reduction split of S = 2 or 4 (g.stream_ksplit), a workgroup takes
 // 4 / S adjacent column blocks of one tile and each block's reduction is cut
@@ -181,13 +244,12 @@ __host__ __device__ inline int row_gemm_cols(int H, int F) {
 // kernel then takes every expert, whatever its row count.
 // NONTEMP: weight loads with the non-temporal hint (load_weights).
 template <int MODE, bool W8, bool NONTEMP>
-__device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s_start, int* s_off, int* s_tmp,
-                                            unsigned char* lds) {
+__device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, unsigned char* lds) {
   constexpr bool NN = RowGemmShape<MODE>::kNN;
   using WF = WeightFmt<W8>;
   using WE = typename WF::Elem;
   using WV = typename WF::Vec;
-  build_tile_starts(g.offsets, g.E, kTileRows, s_start, s_off, s_tmp, 0, W8 ? kNoBigTiles : kBigRows);
+  const WaveTiles wt = wave_tile_prefix(g.offsets, g.E, kTileRows, 0, W8 ? kNoBigTiles : kBigRows);
 
   const int H = g.H, F = g.F;
   // fp8 gate/up: a wave takes 128 features, MFMAs 0..7 on W_gate, 8..15 on W_up
@@ -202,10 +264,10 @@ __device__ __forceinline__ void stream_gemm(const RowGemmArgs& g, int wg, int* s
   // adjacent column blocks of the same tile (when split, nblk is a multiple of
   // cpw, so all blocks of a workgroup fall on one tile).  Workgroups are taken
   // in XCD order, so a tile's activation rows are fetched into one L2.
-  const int real_wgs = (s_start[g.E] * nblk + cpw - 1) / cpw;
+  const int real_wgs = (wt.total * nblk + cpw - 1) / cpw;
   const int item = xcd_item(wg, real_wgs) * cpw + (w % cpw);
   const int kpart = w / cpw;
-  const TileSlot ts = lookup_tile(s_start, s_off, g.E, kTileRows, item / nblk);
+  const TileSlot ts = wave_lookup_tile(wt, kTileRows, item / nblk);
   // uniform across the wave, and across the workgroup when split (before its barrier)
   if (ts.expert < 0) return;
   const int nb = item % nblk;
@@ -835,7 +897,7 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, in
   __shared__ __attribute__((aligned(16))) uint16_t s_ab[2 * kTBM * kTPitch + 2 * kTBN * kTPitch];
   static_assert(sizeof(s_ab) == 4 * 16384, "streaming kernel: 16 KiB of LDS per wave");
   if ((int)blockIdx.x < n_stream)
-    stream_gemm<MODE, false, NONTEMP>(g, blockIdx.x, s_start, s_off, s_tmp, reinterpret_cast<unsigned char*>(s_ab));
+    stream_gemm<MODE, false, NONTEMP>(g, blockIdx.x, reinterpret_cast<unsigned char*>(s_ab));
   else
     tile_gemm<MODE>(g, blockIdx.x - n_stream, s_start, s_off, s_tmp, s_ab, s_ab + 2 * kTBM * kTPitch);
 }
@@ -846,11 +908,10 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, in
 // share a CU.
 template <int MODE, bool NONTEMP>
 __global__ __launch_bounds__(256, 2) void row_gemm_fp8w_kernel(RowGemmArgs g) {
-  __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
   // per wave: 8 KiB of split partial sums (down), 16 KiB (gate/up: twice the
   // columns) or 16 KiB of stages (K-contiguous weights)
   __shared__ __attribute__((aligned(16))) unsigned char s_lds[MODE == kGemmDown ? 4 * 8192 : 4 * 16384];
-  stream_gemm<MODE, true, NONTEMP>(g, blockIdx.x, s_start, s_off, s_tmp, s_lds);
+  stream_gemm<MODE, true, NONTEMP>(g, blockIdx.x, s_lds);
 }
 
 // Reduction split of the streaming kernel for this product and row count.
