@@ -620,30 +620,33 @@ __host__ __device__ inline int tile_gemm_blocks(int H, int F) {
 }
 
 template <int MODE>
-__device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_start, int* s_off, int* s_tmp,
-                                          uint16_t* s_a, uint16_t* s_b) {
+__device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, uint16_t* s_a, uint16_t* s_b) {
   constexpr bool NN = RowGemmShape<MODE>::kNN;
-  build_tile_starts(g.offsets, g.E, kTBM, s_start, s_off, s_tmp, kBigRows, g.big_min_rows);
+  // the schedule, per wave (identical in every wave of the workgroup)
+  const WaveTiles wt = wave_tile_prefix(g.offsets, g.E, kTBM, kBigRows, g.big_min_rows);
   const int H = g.H, F = g.F;
   const int nblk = tile_gemm_blocks<MODE>(H, F);
-  const int item = xcd_item(wg, s_start[g.E] * nblk);
+  const int item = xcd_item(wg, wt.total * nblk);
   // Items of one expert are walked in groups of up to 8 row tiles x all column
   // blocks, column-major inside a group, so the workgroups resident together
   // share both row tiles and weight tiles.
-  if (item >= s_start[g.E] * nblk) return;
-  int lo = 0, hi = g.E;  // expert: s_start[lo] * nblk <= item < s_start[hi] * nblk
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_start[mid] * nblk <= item) lo = mid; else hi = mid;
-  }
-  const int tiles_e = s_start[lo + 1] - s_start[lo];
-  const int li = item - s_start[lo] * nblk;
+  if (item >= wt.total * nblk) return;  // uniform across the workgroup
+  // the expert whose tiles hold tile id item / nblk, its first tile id and tiles
+  const TileSlot first = wave_lookup_tile(wt, kTBM, item / nblk);
+  const int start_e = item / nblk - first.tile;
+  const int tiles_e = (first.expert_rows + kTBM - 1) / kTBM;
+  const int li = item - start_e * nblk;
   const int grp = li / (8 * nblk);
   const int gm = min(8, tiles_e - 8 * grp);
   const int within = li - grp * 8 * nblk;
   const int mt = 8 * grp + within % gm;
   const int nb = within / gm;
-  const TileSlot ts = lookup_tile(s_start, s_off, g.E, kTBM, s_start[lo] + mt);
+  TileSlot ts;
+  ts.expert = first.expert;
+  ts.tile = mt;
+  ts.expert_rows = first.expert_rows;
+  ts.row_begin = first.row_begin + (mt - first.tile) * kTBM;
+  ts.rows = min(first.expert_rows - mt * kTBM, kTBM);
   const int e = ts.expert;
   const int K = (MODE == kGemmGateUp || MODE == kGemmDA) ? H : (MODE == kGemmDown ? F : 2 * F);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lm = l & 15, gq = l >> 4;
@@ -890,7 +893,6 @@ __device__ __forceinline__ void tile_gemm(const RowGemmArgs& g, int wg, int* s_s
 // kernel over the others.  Both schedules are derived on the device.
 template <int MODE, bool NONTEMP>
 __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, int n_stream, int n_tile) {
-  __shared__ int s_start[kMaxExperts + 1], s_off[kMaxExperts + 1], s_tmp[4];
   // 64 KiB: the tiled kernel's double-buffered A and B tiles, or the streaming
   // kernel's four per-wave areas (16 KiB of stages, or 8 KiB of split partial
   // sums for N-contiguous weights)
@@ -899,7 +901,7 @@ __global__ __launch_bounds__(256, 2) void row_gemm_bf16_kernel(RowGemmArgs g, in
   if ((int)blockIdx.x < n_stream)
     stream_gemm<MODE, false, NONTEMP>(g, blockIdx.x, reinterpret_cast<unsigned char*>(s_ab));
   else
-    tile_gemm<MODE>(g, blockIdx.x - n_stream, s_start, s_off, s_tmp, s_ab, s_ab + 2 * kTBM * kTPitch);
+    tile_gemm<MODE>(g, blockIdx.x - n_stream, s_ab, s_ab + 2 * kTBM * kTPitch);
 }
 
 // fp8 weights: every expert on the streaming kernel (one wave per 16-row tile
