@@ -281,8 +281,8 @@ __global__ __launch_bounds__(64 * kF8Waves, 1) void big_gemm_fp8_kernel(Fp8GemmA
   };
   if constexpr (OFF32) {
     // stages 1 .. steps - 2 load the next stage in two halves; the last one
-    // loads nothing (peeled, so the loop body has no branch the scheduler
-    // would not move MFMAs across)
+    // loads nothing and is peeled off: with a branch around each half inside
+    // the loop, the compiler placed both halves ahead of the first MFMA run
     for (int s = 1; s < steps - 1; ++s) {
       const unsigned char* st = s_dyn + (s & 1) * kF8StageBytes;
       stage_sync();
