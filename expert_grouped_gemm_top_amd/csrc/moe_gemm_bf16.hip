@@ -169,7 +169,8 @@ __host__ __device__ inline int row_gemm_cols(int H, int F) {
   return (MODE == kGemmGateUp || MODE == kGemmDA) ? F : H;
 }
 
-// Per-wave tile schedule of the streaming kernel: the same tile prefix as
+// Per-wave tile schedule of the row GEMMs (the streaming kernel and the
+// 128-row tiles): the same tile prefix as
 // build_tile_starts / lookup_tile (experts with min_rows <= n_e < max_rows,
 // ceil(n_e / tile_rows) tiles each, in expert order), derived by every wave
 // on its own from offsets[0..E] with a wave scan and a ballot: no LDS and no
